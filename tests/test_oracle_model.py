@@ -1,0 +1,318 @@
+"""Pins of the oracle's primitives, context injection and draft pass:
+library routines (torch CPU) for the special cases they cover, closed forms,
+invariants and a pure-Python brute force on the tiny shape."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fnn
+
+import oracle
+from oracle.primitives import rms_norm, rope_neox, silu, block_attention
+from workloads import synth
+from workloads.configs import TINY, SMALL_F32_D64
+from tests.helpers import np_weights
+
+
+# ---------------------------------------------------------------- primitives
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 96))
+    g = 1 + 0.1 * rng.standard_normal(96)
+    ref = Fnn.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), eps=1e-6).numpy()
+    assert np.allclose(rms_norm(x, g, 1e-6), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_silu_matches_torch():
+    x = np.linspace(-20, 20, 1001)
+    assert np.allclose(silu(x), Fnn.silu(torch.from_numpy(x)).numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_rope_identity_norm_and_complex_form():
+    rng = np.random.default_rng(1)
+    D = 128
+    x = rng.standard_normal((5, 3, D))
+    assert np.array_equal(rope_neox(x, np.zeros((5, 1)), 1e6), x)
+    p = rng.integers(0, 40000, (5, 1))
+    y = rope_neox(x, p, 1e6)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    # neox layout as a complex rotation: z_i = x_i + i x_{i+D/2}, z_i * exp(i p w_i)
+    w = np.array([1e6 ** (-2 * i / D) for i in range(D // 2)])
+    z = (x[..., :D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * p[..., None] * w)
+    assert np.allclose(y, np.concatenate([z.real, z.imag], axis=-1), rtol=1e-10, atol=1e-10)
+
+
+def test_rope_relative_positions():
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((2, 64))
+    a = rope_neox(q, 1000, 1e4) @ rope_neox(k, 990, 1e4)
+    b = rope_neox(q, 20, 1e4) @ rope_neox(k, 10, 1e4)
+    assert abs(a - b) < 1e-9
+
+
+@pytest.mark.parametrize("window", [0, 7])
+def test_block_attention_matches_torch_sdpa(window):
+    rng = np.random.default_rng(3)
+    S, nq, nkv, D, n = 6, 8, 2, 32, 23
+    q = rng.standard_normal((S, nq, D))
+    kc, vc = rng.standard_normal((2, n, nkv, D))
+    kb, vb = rng.standard_normal((2, S, nkv, D))
+    cpos = np.arange(n) + 4
+    qpos = np.arange(S) + n + 4
+    o = block_attention(q, kc, vc, cpos, kb, vb, qpos, window)
+    keys = torch.from_numpy(np.concatenate([kc, kb])).permute(1, 0, 2)     # [nkv, n+S, D]
+    vals = torch.from_numpy(np.concatenate([vc, vb])).permute(1, 0, 2)
+    keys = keys.repeat_interleave(nq // nkv, 0)
+    vals = vals.repeat_interleave(nq // nkv, 0)
+    mask = torch.ones(S, n + S, dtype=torch.bool)
+    if window:
+        mask[:, :n] = torch.from_numpy((qpos[:, None] - cpos[None, :]) < window)
+    ref = Fnn.scaled_dot_product_attention(torch.from_numpy(q).permute(1, 0, 2), keys, vals,
+                                           attn_mask=mask, is_causal=False)
+    assert np.allclose(o, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_block_attention_bruteforce_loops():
+    """Pure-Python loops over (query, head, key) on the tiny shape."""
+    rng = np.random.default_rng(4)
+    S, nq, nkv, D, n, W = 4, 4, 2, 8, 9, 5
+    q = rng.standard_normal((S, nq, D))
+    kc, vc = rng.standard_normal((2, n, nkv, D))
+    kb, vb = rng.standard_normal((2, S, nkv, D))
+    cpos, qpos = list(range(n)), [n + j for j in range(S)]
+    o = block_attention(q, kc, vc, np.array(cpos), kb, vb, np.array(qpos), W)
+    for j in range(S):
+        for h in range(nq):
+            g = h // (nq // nkv)
+            sc, vs = [], []
+            for i in range(n):
+                if qpos[j] - cpos[i] < W:
+                    sc.append(sum(q[j, h, d] * kc[i, g, d] for d in range(D)) / math.sqrt(D))
+                    vs.append(vc[i, g])
+            for i in range(S):
+                sc.append(sum(q[j, h, d] * kb[i, g, d] for d in range(D)) / math.sqrt(D))
+                vs.append(vb[i, g])
+            m = max(sc)
+            e = [math.exp(s - m) for s in sc]
+            tot = sum(e)
+            ref = sum((ei / tot) * v for ei, v in zip(e, vs))
+            assert np.allclose(o[j, h], ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- fixtures
+def _setup(cfg, seed=0, B=1, L=(40,), extra=32):
+    W = np_weights(synth.weights(cfg, seed))
+    L = np.array(L)
+    pt, npages = synth.page_table(__import__("torch").tensor(L), cfg, seed, extra)
+    return W, pt.numpy(), npages
+
+
+def _inject_prefix(cfg, W, cache, pt, L, seed=5):
+    for r, l in enumerate(L):
+        f = synth.features(l, cfg, seed + r).numpy()
+        pos = np.arange(l)
+        oracle.project_context(cfg, W, cache, f, pos, pt[r, pos // 16] * 16 + pos % 16)
+
+
+# ---------------------------------------------------------------- injection
+def test_injection_matches_torch_composition():
+    cfg = TINY
+    W, pt, npages = _setup(cfg)
+    cache = oracle.OracleCache(cfg, npages * 16)
+    f = synth.features(10, cfg, 9).numpy()
+    pos = np.arange(10) * 3 + 1
+    slots = np.arange(10) + 50
+    oracle.project_context(cfg, W, cache, f, pos, slots)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    c = Fnn.rms_norm(Fnn.linear(t(f), t(W["fc"])), (cfg.hidden,), t(W["hidden_norm"]), eps=cfg.rms_eps)
+    L0 = W["layers"][0]
+    nq, nkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    wk = t(L0["w_qkv"][nq * D:(nq + nkv) * D])
+    wv = t(L0["w_qkv"][(nq + nkv) * D:])
+    k = Fnn.rms_norm(Fnn.linear(c, wk).view(10, nkv, D), (D,), t(L0["k_norm"]), eps=cfg.rms_eps)
+    v = Fnn.linear(c, wv).view(10, nkv, D)
+    # RoPE as a complex rotation (torch.polar), neox halves
+    inv = cfg.rope_theta ** (-torch.arange(D // 2, dtype=torch.float64) * 2 / D)
+    rot = torch.polar(torch.ones(10, D // 2, dtype=torch.float64), t(pos)[:, None] * inv)
+    z = torch.complex(k[..., :D // 2], k[..., D // 2:]) * rot[:, None, :]
+    k = torch.cat([z.real, z.imag], -1)
+    assert np.allclose(cache.k[0][slots], k.float().double().numpy(), rtol=1e-6, atol=1e-6)
+    assert np.allclose(cache.v[0][slots], v.float().double().numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_injection_closed_form_head_norm():
+    """With k_norm gain 1, each stored K head has |k|^2 = D ms / (ms + eps)."""
+    cfg = dataclasses.replace(TINY, kv_dtype="f32")
+    W, pt, npages = _setup(cfg)
+    W["layers"][0]["k_norm"] = np.ones(cfg.head_dim, np.float32)
+    cache = oracle.OracleCache(cfg, npages * 16)
+    f = synth.features(6, cfg, 11).numpy().astype(np.float64)
+    slots = np.arange(6)
+    oracle.project_context(cfg, W, cache, f, np.arange(6) * 1000, slots)
+    c = rms_norm(f @ W["fc"].astype(np.float64).T, W["hidden_norm"], cfg.rms_eps)
+    nq, nkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    kraw = (c @ W["layers"][0]["w_qkv"][nq * D:(nq + nkv) * D].astype(np.float64).T).reshape(6, nkv, D)
+    ms = np.mean(kraw ** 2, -1)
+    got = np.sum(cache.k[0][slots] ** 2, -1)
+    assert np.allclose(got, D * ms / (ms + cfg.rms_eps), rtol=1e-6)
+
+
+def test_injection_scale_invariance_without_eps():
+    cfg = dataclasses.replace(TINY, rms_eps=0.0)
+    W, pt, npages = _setup(cfg)
+    f = synth.features(8, cfg, 12).numpy().astype(np.float64)
+    a = oracle.OracleCache(cfg, 64)
+    b = oracle.OracleCache(cfg, 64)
+    oracle.project_context(cfg, W, a, f, np.arange(8), np.arange(8))
+    oracle.project_context(cfg, W, b, 3.5 * f, np.arange(8), np.arange(8))
+    assert np.allclose(a.k[0][:8], b.k[0][:8], rtol=1e-6) and np.allclose(a.v[0][:8], b.v[0][:8], rtol=1e-6)
+
+
+def test_injection_once_equals_chunked_and_prefix_valid():
+    cfg = TINY
+    W, pt, npages = _setup(cfg)
+    f = synth.features(64, cfg, 13).numpy()
+    pos = np.arange(64)
+    slots = pt[0, pos // 16] * 16 + pos % 16
+    a = oracle.OracleCache(cfg, npages * 16)
+    b = oracle.OracleCache(cfg, npages * 16)
+    oracle.project_context(cfg, W, a, f, pos, slots)
+    for lo, hi in [(0, 5), (5, 33), (33, 64)]:
+        oracle.project_context(cfg, W, b, f[lo:hi], pos[lo:hi], slots[lo:hi])
+    for l in range(cfg.n_layers):
+        assert np.allclose(a.k[l], b.k[l], rtol=1e-12, atol=1e-12, equal_nan=True)
+    # prefix-valid writes over a dense [4, 16] grid: rows j >= valid stay untouched (NaN)
+    c = oracle.OracleCache(cfg, npages * 16)
+    valid = np.array([3, 0, 16, 1])
+    live = oracle.project_context(cfg, W, c, f, pos, slots, valid_rows=valid, rows_per_req=16)
+    assert live.sum() == valid.sum()
+    assert np.isnan(c.k[0][slots[~live]]).all() and not np.isnan(c.k[0][slots[live]]).any()
+    assert np.allclose(c.k[0][slots[live]], a.k[0][slots[live]], rtol=1e-12)
+    # crop then re-append: writing the same rows again leaves the cache bit-identical
+    d = c.copy()
+    oracle.project_context(cfg, W, d, f, pos, slots, valid_rows=valid, rows_per_req=16)
+    for l in range(cfg.n_layers):
+        assert np.array_equal(np.nan_to_num(c.k[l], nan=7.0), np.nan_to_num(d.k[l], nan=7.0))
+
+
+# ---------------------------------------------------------------- draft pass
+def _ctx_cache(cfg, W, pt, npages, L, shift=0, seed=5):
+    cache = oracle.OracleCache(cfg, npages * 16)
+    for r, l in enumerate(L):
+        f = synth.features(l, cfg, seed + r).numpy()
+        pos = np.arange(l)
+        oracle.project_context(cfg, W, cache, f, pos + shift, pt[r, pos // 16] * 16 + pos % 16)
+    return cache
+
+
+def test_draft_zero_residual_branches_closed_form():
+    """With W_o = W_down = 0 the residual stream is the embedding, so every
+    logits row is rms(E[id]; final_norm) W_lm^T."""
+    cfg = TINY
+    W, pt, npages = _setup(cfg)
+    W["layers"][0]["w_o"] = np.zeros_like(W["layers"][0]["w_o"])
+    W["layers"][0]["w_down"] = np.zeros_like(W["layers"][0]["w_down"])
+    cache = _ctx_cache(cfg, W, pt, npages, [40])
+    d = oracle.draft_block(cfg, W, cache, [17], [40], pt)
+    y = rms_norm(W["embed"][cfg.mask_token_id].astype(np.float64), W["final_norm"], cfg.rms_eps)
+    ref = y @ W["lm_head"].astype(np.float64).T
+    for j in range(cfg.block_size - 1):
+        assert np.allclose(d["logits"][0, j], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_draft_mask_rows_equivariant_without_rope():
+    """Without RoPE, non-causal attention treats the MASK rows symmetrically:
+    they share one embedding, so their logits are identical.  With RoPE (and
+    with any causal mask) they differ.  (No sliding window here: the window
+    bound depends on each row's position.)"""
+    cfg = dataclasses.replace(SMALL_F32_D64, sliding_window=())
+    W, pt, npages = _setup(cfg, L=(30, 55))
+    cache = _ctx_cache(cfg, W, pt, npages, [30, 55])
+    d = oracle.draft_block(cfg, W, cache, [3, 9], [30, 55], pt, rope=False)
+    for r in range(2):
+        for j in range(1, cfg.block_size - 1):
+            assert np.allclose(d["logits"][r, j], d["logits"][r, 0], rtol=1e-11, atol=1e-11)
+    d2 = oracle.draft_block(cfg, W, cache, [3, 9], [30, 55], pt)
+    assert not np.allclose(d2["logits"][0, 1], d2["logits"][0, 0], rtol=1e-6)
+    # the anchor is visible to the MASK rows: changing it changes their logits
+    d3 = oracle.draft_block(cfg, W, cache, [4, 9], [30, 55], pt, rope=False)
+    assert not np.allclose(d3["logits"][0, 0], d["logits"][0, 0], rtol=1e-6)
+
+
+def test_draft_translation_invariance():
+    """Shifting every logical position (context and block) by the same amount
+    leaves the logits unchanged: RoPE only sees position differences, and so
+    does the sliding window.  Every layer is a sliding layer here so that the
+    shifted run reads only context it was given."""
+    cfg = dataclasses.replace(SMALL_F32_D64, sliding_window=(20, 17))
+    W, pt, npages = _setup(cfg, L=(45, 61))
+    a = oracle.draft_block(cfg, W, _ctx_cache(cfg, W, pt, npages, [45, 61]), [5, 6], [45, 61], pt)
+    k = 771                                   # shift by whole pages; roll the page table
+    sh = 16 * k
+    cache = _ctx_cache(cfg, W, pt, npages, [45, 61], shift=sh)
+    pt3 = np.zeros((2, pt.shape[1] + k), np.int64)
+    pt3[:, k:] = pt
+    b = oracle.draft_block(cfg, W, cache, [5, 6], [45 + sh, 61 + sh], pt3)
+    # the fp32 cache rounds the rotated keys differently at different positions
+    assert np.allclose(a["logits"], b["logits"], rtol=1e-5, atol=1e-5)
+    assert np.array_equal(a["slots"], b["slots"])
+
+
+def test_draft_planted_argmax():
+    cfg = TINY
+    W, pt, npages = _setup(cfg)
+    cache = _ctx_cache(cfg, W, pt, npages, [40])
+    d = oracle.draft_block(cfg, W, cache, [17], [40], pt)
+    # plant token t's lm_head row as 4x the row of the current argmax (whose
+    # logit is positive): t's logit becomes 4x the maximum, so argmax moves to t.
+    t = 321
+    W2 = dict(W)
+    lm = W["lm_head"].copy()
+    j = 1
+    am = int(d["draft_ids"][0, j])
+    lm[t] = 4.0 * lm[am]
+    W2["lm_head"] = lm
+    d2 = oracle.draft_block(cfg, W2, cache, [17], [40], pt)
+    assert d2["draft_ids"][0, j] == t
+    assert np.allclose(d2["logits"][0, j, t], 4.0 * d["logits"][0, j, am], rtol=1e-12)
+
+
+def test_draft_reads_only_committed_context():
+    """Slots at or beyond the prefix stay NaN in the cache; a finite result
+    shows the pass never reads them (and never reads other requests' pages)."""
+    cfg = SMALL_F32_D64
+    W, pt, npages = _setup(cfg, L=(1, 33))
+    cache = _ctx_cache(cfg, W, pt, npages, [1, 33])
+    d = oracle.draft_block(cfg, W, cache, [0, 1], [1, 33], pt)
+    assert np.isfinite(d["logits"]).all()
+
+
+def test_speculative_decode_equals_greedy_target():
+    """Greedy speculative decoding must emit exactly the target's own greedy
+    continuation, whatever the draft proposes ("Inside SGLang ...", Step 5-7:
+    the target verifies every block and supplies the correction/bonus)."""
+    cfg = TINY
+    W = np_weights(synth.weights(cfg, 0))
+    V = cfg.vocab
+    rng = np.random.default_rng(7)
+    feat_tab = rng.standard_normal((64, cfg.feat_dim)) * 0.02
+
+    def target_next(tok, pos):        # a Markov stand-in for the target model
+        return int((tok * 7 + pos * 3 + 11) % 13)
+
+    def target_feat(tok, pos):
+        return feat_tab[(tok * 5 + pos) % 64]
+
+    prompt = [5, 3, 8, 1, 2, 9, 4]
+    pt = np.arange(8)[None, :]
+    em, commits, L, cache = oracle.speculative_decode(cfg, W, 8 * 16, pt, prompt, 30,
+                                                      target_next, target_feat)
+    ref = [target_next(prompt[-1], len(prompt) - 1)]
+    while len(ref) < len(em):
+        ref.append(target_next(ref[-1], len(prompt) + len(ref) - 1))
+    assert em == ref
+    assert L == len(prompt) + sum(commits)
+    assert len(em) == 1 + sum(commits)
+    assert all(1 <= c <= cfg.block_size for c in commits)
