@@ -1,0 +1,247 @@
+"""Python binding of libdflash.so, the DFlash draft-and-accept path on MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the stream.  The functions carry
+the names of the C entry points (include/dflash.h) and take torch tensors.
+
+Importing fails loudly when the library has not been built
+(``python block_diffusion_drafter_rmsnorm_amd/build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, List, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+MAX_LAYERS = 16
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_DT_CODE = {"f32": F32, "bf16": BF16, "fp8_e4m3": FP8_E4M3}
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
+          -3: "workspace too small", -4: "HIP runtime error"}
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class CConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("feat_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("mask_token_id", ctypes.c_int32),
+                ("page_size", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32 * MAX_LAYERS),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+_LAYER_FIELDS = ["in_norm", "w_qkv", "q_norm", "k_norm", "w_o", "post_norm", "w_gate", "w_up",
+                 "w_down"]
+
+
+class CLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _LAYER_FIELDS]
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("fc", ctypes.c_void_p), ("hidden_norm", ctypes.c_void_p),
+                ("final_norm", ctypes.c_void_p), ("layer", CLayerWeights * MAX_LAYERS)]
+
+
+class CKVCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p * MAX_LAYERS), ("v", ctypes.c_void_p * MAX_LAYERS),
+                ("num_pages", ctypes.c_int64)]
+
+
+EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
+            "dflash_project_context", "dflash_draft_block", "dflash_accept",
+            "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
+            "dflash_status_string", "dflash_last_error"]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python block_diffusion_drafter_rmsnorm_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    missing = [n for n in EXPORTED if not hasattr(lib, n)]
+    if missing:
+        raise ImportError(f"{LIB_PATH} is stale (missing {missing}): rebuild it")
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp, wp, kvp = ctypes.POINTER(CConfig), ctypes.POINTER(CWeights), ctypes.POINTER(CKVCache)
+    lib.dflash_context_workspace_bytes.argtypes = [cfgp, I64]
+    lib.dflash_context_workspace_bytes.restype = SZ
+    lib.dflash_draft_workspace_bytes.argtypes = [cfgp, I32, I32]
+    lib.dflash_draft_workspace_bytes.restype = SZ
+    lib.dflash_project_context.argtypes = [cfgp, wp, kvp, P, I64, P, P, P, I32, I32, P, SZ, P]
+    lib.dflash_project_context.restype = I32
+    lib.dflash_draft_block.argtypes = [cfgp, wp, kvp, P, P, P, I32, I32, I32, P, P, P, P, P, P,
+                                       SZ, P]
+    lib.dflash_draft_block.restype = I32
+    lib.dflash_accept.argtypes = [P, P, P, I32, I32, P, P, P, P, P, P]
+    lib.dflash_accept.restype = I32
+    lib.dflash_lm_head_workspace_bytes.argtypes = [cfgp, I32]
+    lib.dflash_lm_head_workspace_bytes.restype = SZ
+    lib.dflash_lm_head_argmax.argtypes = [cfgp, P, P, I32, P, P, P, SZ, P]
+    lib.dflash_lm_head_argmax.restype = I32
+    lib.dflash_status_string.argtypes = [I32]
+    lib.dflash_status_string.restype = ctypes.c_char_p
+    lib.dflash_last_error.argtypes = []
+    lib.dflash_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise DFlashError(status, _lib.dflash_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        if not torch.cuda.is_available():
+            return None
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_config(cfg) -> CConfig:
+    """C config from a workloads.configs.DFlashConfig-like object."""
+    c = CConfig()
+    c.hidden, c.n_layers, c.n_q_heads = cfg.hidden, cfg.n_layers, cfg.n_q_heads
+    c.n_kv_heads, c.head_dim, c.inter, c.vocab = cfg.n_kv_heads, cfg.head_dim, cfg.inter, cfg.vocab
+    c.feat_dim = cfg.n_target_layers * cfg.target_hidden
+    c.block_size, c.mask_token_id, c.page_size = cfg.block_size, cfg.mask_token_id, cfg.page_size
+    for l in range(MAX_LAYERS):
+        c.sliding_window[l] = int(cfg.sliding_window[l]) if l < len(cfg.sliding_window) else 0
+    c.rms_eps, c.rope_theta = float(cfg.rms_eps), float(cfg.rope_theta)
+    c.act_dtype, c.kv_dtype = _DT_CODE[cfg.act_dtype], _DT_CODE[cfg.kv_dtype]
+    return c
+
+
+def make_weights(W: Dict) -> CWeights:
+    """C weight table from the dict of device tensors (keeps no references:
+    the caller keeps the tensors alive)."""
+    w = CWeights()
+    for n in ("embed", "lm_head", "fc", "hidden_norm", "final_norm"):
+        t = W.get(n)
+        setattr(w, n, None if t is None else t.data_ptr())
+    for l, Lw in enumerate(W["layers"]):
+        if Lw is None:
+            continue
+        for n in _LAYER_FIELDS:
+            t = Lw.get(n)
+            setattr(w.layer[l], n, None if t is None else t.data_ptr())
+    return w
+
+
+@dataclass
+class KVCache:
+    """Paged draft cache: per layer K and V of [num_pages, nkv, page, D]."""
+    k: List[torch.Tensor]
+    v: List[torch.Tensor]
+    num_pages: int
+
+    @staticmethod
+    def allocate(cfg, num_pages: int, device="cuda", fill=None) -> "KVCache":
+        shp = (num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        dt = _TORCH_DT[cfg.kv_dtype]
+        mk = (lambda: torch.empty(shp, dtype=dt, device=device)) if fill is None else \
+            (lambda: torch.full(shp, fill, dtype=dt, device=device))
+        return KVCache([mk() for _ in range(cfg.n_layers)], [mk() for _ in range(cfg.n_layers)],
+                       num_pages)
+
+    def c_struct(self) -> CKVCache:
+        c = CKVCache()
+        for l, (k, v) in enumerate(zip(self.k, self.v)):
+            c.k[l] = k.data_ptr()
+            c.v[l] = v.data_ptr()
+        c.num_pages = self.num_pages
+        return c
+
+
+def context_workspace_bytes(cfg, rows: int) -> int:
+    return int(_lib.dflash_context_workspace_bytes(ctypes.byref(make_config(cfg)), int(rows)))
+
+
+def draft_workspace_bytes(cfg, batch: int, max_prefix_len: int) -> int:
+    return int(_lib.dflash_draft_workspace_bytes(ctypes.byref(make_config(cfg)), int(batch),
+                                                 int(max_prefix_len)))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def dflash_project_context(cfg, weights: CWeights, cache: KVCache, feats: torch.Tensor,
+                           positions: torch.Tensor, slots: torch.Tensor,
+                           valid_rows: Optional[torch.Tensor], n_req: int, rows_per_req: int,
+                           ws: torch.Tensor, stream=None, c_cfg: Optional[CConfig] = None,
+                           c_cache: Optional[CKVCache] = None):
+    c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
+    c_cache = c_cache if c_cache is not None else cache.c_struct()
+    _check(_lib.dflash_project_context(
+        ctypes.byref(c_cfg), ctypes.byref(weights), ctypes.byref(c_cache), _ptr(feats),
+        int(feats.stride(0)), _ptr(positions), _ptr(slots), _ptr(valid_rows), int(n_req),
+        int(rows_per_req), _ptr(ws), int(ws.numel()), _stream(stream)))
+
+
+def dflash_draft_block(cfg, weights: CWeights, cache: KVCache, anchor: torch.Tensor,
+                       prefix_len: torch.Tensor, page_table: torch.Tensor, max_prefix_len: int,
+                       positions: torch.Tensor, slots: torch.Tensor, candidates: torch.Tensor,
+                       ws: torch.Tensor, block_ids: Optional[torch.Tensor] = None,
+                       logits: Optional[torch.Tensor] = None, stream=None,
+                       c_cfg: Optional[CConfig] = None, c_cache: Optional[CKVCache] = None):
+    c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
+    c_cache = c_cache if c_cache is not None else cache.c_struct()
+    _check(_lib.dflash_draft_block(
+        ctypes.byref(c_cfg), ctypes.byref(weights), ctypes.byref(c_cache), _ptr(anchor),
+        _ptr(prefix_len), _ptr(page_table), int(page_table.shape[1]), int(anchor.shape[0]),
+        int(max_prefix_len), _ptr(block_ids), _ptr(positions), _ptr(slots), _ptr(candidates),
+        _ptr(logits), _ptr(ws), int(ws.numel()), _stream(stream)))
+
+
+def dflash_accept(candidates: torch.Tensor, posterior: torch.Tensor, prefix_len: torch.Tensor,
+                  accept_len: torch.Tensor, commit_len: torch.Tensor, out_tokens: torch.Tensor,
+                  next_anchor: torch.Tensor, new_seq_len: torch.Tensor, stream=None):
+    B, S = candidates.shape
+    _check(_lib.dflash_accept(_ptr(candidates), _ptr(posterior), _ptr(prefix_len), int(B), int(S),
+                              _ptr(accept_len), _ptr(commit_len), _ptr(out_tokens),
+                              _ptr(next_anchor), _ptr(new_seq_len), _stream(stream)))
+
+
+def lm_head_workspace_bytes(cfg, rows: int) -> int:
+    return int(_lib.dflash_lm_head_workspace_bytes(ctypes.byref(make_config(cfg)), int(rows)))
+
+
+def dflash_lm_head_argmax(cfg, lm_head: torch.Tensor, hidden: torch.Tensor, ids: torch.Tensor,
+                          ws: torch.Tensor, logits: Optional[torch.Tensor] = None, stream=None,
+                          c_cfg: Optional[CConfig] = None):
+    c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
+    _check(_lib.dflash_lm_head_argmax(ctypes.byref(c_cfg), _ptr(lm_head), _ptr(hidden),
+                                      int(hidden.shape[0]), _ptr(logits), _ptr(ids), _ptr(ws),
+                                      int(ws.numel()), _stream(stream)))
+
+
+def raw_lib():
+    """The ctypes library handle (for ABI tests)."""
+    return _lib

@@ -1,0 +1,437 @@
+// C ABI of the DFlash draft-and-accept path: argument validation, workspace
+// layout and the launch sequence of each entry point.  No allocation, no
+// synchronisation: every launch goes to the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.h"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dflash_status fail(dflash_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dflash_status fail(dflash_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+dflash_status hip_fail(hipError_t e, const char* what) {
+  return fail(DFLASH_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int act_bytes(int dt) { return dt == DFLASH_BF16 ? 2 : 4; }
+
+dflash_status check_config(const dflash_config* c) {
+  if (c == nullptr) return fail(DFLASH_EINVAL, "config is NULL");
+  if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS)
+    return fail(DFLASH_EUNSUPPORTED, "n_layers %d outside 1..%d", c->n_layers, DFLASH_MAX_LAYERS);
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->inter <= 0 ||
+      c->vocab <= 0 || c->feat_dim <= 0 || c->page_size <= 0)
+    return fail(DFLASH_EINVAL, "non-positive model dimension");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(DFLASH_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(DFLASH_EUNSUPPORTED, "n_q_heads %d not a multiple of n_kv_heads %d",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->block_size < 2 || c->block_size > 16)
+    return fail(DFLASH_EUNSUPPORTED, "block_size %d outside 2..16", c->block_size);
+  if ((c->n_q_heads / c->n_kv_heads) * c->block_size > 64)
+    return fail(DFLASH_EUNSUPPORTED, "(n_q_heads / n_kv_heads) * block_size = %d > 64",
+                (c->n_q_heads / c->n_kv_heads) * c->block_size);
+  if (c->hidden % 32 || c->feat_dim % 32 || c->inter % 64)
+    return fail(DFLASH_EUNSUPPORTED, "hidden and feat_dim must be multiples of 32, inter of 64");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
+    return fail(DFLASH_EINVAL, "mask_token_id %d outside the vocabulary", c->mask_token_id);
+  if (c->act_dtype != DFLASH_F32 && c->act_dtype != DFLASH_BF16)
+    return fail(DFLASH_EUNSUPPORTED, "act_dtype %d (supported: F32, BF16)", c->act_dtype);
+  if (c->act_dtype == DFLASH_F32 && c->kv_dtype != DFLASH_F32)
+    return fail(DFLASH_EUNSUPPORTED, "an F32 model needs an F32 cache");
+  if (c->act_dtype == DFLASH_BF16 && c->kv_dtype != DFLASH_BF16 && c->kv_dtype != DFLASH_FP8_E4M3)
+    return fail(DFLASH_EUNSUPPORTED, "a BF16 model needs a BF16 or FP8_E4M3 cache");
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps))
+    return fail(DFLASH_EINVAL, "rms_eps must be finite and >= 0");
+  if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta))
+    return fail(DFLASH_EINVAL, "rope_theta must be finite and > 0");
+  for (int l = 0; l < c->n_layers; ++l)
+    if (c->sliding_window[l] < 0) return fail(DFLASH_EINVAL, "negative sliding_window[%d]", l);
+  return DFLASH_OK;
+}
+
+#define REQUIRE_PTR(p, name)                                                     \
+  do {                                                                           \
+    if ((p) == nullptr) return fail(DFLASH_EINVAL, "%s is NULL", name);          \
+    if (!aligned16(p)) return fail(DFLASH_EINVAL, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+dflash_status check_layer_weights(const dflash_config* c, const dflash_weights* w, bool draft) {
+  if (w == nullptr) return fail(DFLASH_EINVAL, "weights is NULL");
+  char nm[64];
+  for (int l = 0; l < c->n_layers; ++l) {
+    const dflash_layer_weights& L = w->layer[l];
+    snprintf(nm, sizeof nm, "layer[%d].w_qkv", l);
+    REQUIRE_PTR(L.w_qkv, nm);
+    snprintf(nm, sizeof nm, "layer[%d].k_norm", l);
+    REQUIRE_PTR(L.k_norm, nm);
+    if (!draft) continue;
+    const void* ps[] = {L.in_norm, L.q_norm, L.w_o, L.post_norm, L.w_gate, L.w_up, L.w_down};
+    const char* ns[] = {"in_norm", "q_norm", "w_o", "post_norm", "w_gate", "w_up", "w_down"};
+    for (int i = 0; i < 7; ++i) {
+      snprintf(nm, sizeof nm, "layer[%d].%s", l, ns[i]);
+      REQUIRE_PTR(ps[i], nm);
+    }
+  }
+  return DFLASH_OK;
+}
+
+dflash_status check_cache(const dflash_config* c, const dflash_kv_cache* kv) {
+  if (kv == nullptr) return fail(DFLASH_EINVAL, "cache is NULL");
+  if (kv->num_pages <= 0) return fail(DFLASH_EINVAL, "cache.num_pages must be > 0");
+  char nm[64];
+  for (int l = 0; l < c->n_layers; ++l) {
+    snprintf(nm, sizeof nm, "cache.k[%d]", l);
+    REQUIRE_PTR(kv->k[l], nm);
+    snprintf(nm, sizeof nm, "cache.v[%d]", l);
+    REQUIRE_PTR(kv->v[l], nm);
+  }
+  return DFLASH_OK;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned regions).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+constexpr int kInjectChunk = 8192;  // context rows per injection pass
+
+struct ContextWs {
+  float2* cs; float* craw; void* c; GemmScratch gs; size_t bytes;
+};
+
+int64_t inject_chunk_rows(int64_t rows) { return rows < kInjectChunk ? rows : kInjectChunk; }
+
+ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
+  Carver cv(ws);
+  ContextWs L;
+  const int M = (int)chunk;
+  L.cs = (float2*)cv.take(sizeof(float2) * M * (c->head_dim / 2));
+  L.craw = (float*)cv.take(sizeof(float) * (size_t)M * c->hidden);
+  L.c = cv.take((size_t)act_bytes(c->act_dtype) * M * c->hidden);
+  // the last chunk of a call can be any size up to `chunk`: take the worst case
+  size_t pf = 0;
+  int nc = 1;
+  for (int m = 1; m <= M; ++m) {
+    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim),
+                            plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim, c->hidden)};
+    for (const GemmPlan& p : ps) {
+      if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
+      if (p.n_tiles * p.m_tiles > nc) nc = p.n_tiles * p.m_tiles;
+    }
+  }
+  L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
+  L.gs.partial_floats = pf;
+  L.gs.counters = (int*)cv.take(sizeof(int) * nc);
+  L.gs.n_counters = nc;
+  L.bytes = cv.off;
+  return L;
+}
+
+struct DraftWs {
+  float* x; void* h; void* act; void* q; void* kb; void* vb; void* o; float2* cs;
+  float* o_part; float2* ml_part; float2* lm_part; GemmScratch gs; size_t bytes;
+  AttnPlan plans[DFLASH_MAX_LAYERS];
+};
+
+int layer_max_keys(const dflash_config* c, int l, int max_prefix) {
+  const int W = c->sliding_window[l];
+  if (W > 0 && W - 1 < max_prefix) return W - 1;
+  return max_prefix;
+}
+
+DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
+  Carver cv(ws);
+  DraftWs L;
+  const int S = c->block_size, M = B * S, M1 = B * (S - 1), H = c->hidden;
+  const int nq = c->n_q_heads, nkv = c->n_kv_heads, D = c->head_dim, I = c->inter;
+  const size_t ab = act_bytes(c->act_dtype);
+  L.x = (float*)cv.take(sizeof(float) * (size_t)M * H);
+  const int hw = H > nq * D ? H : nq * D;
+  L.h = cv.take(ab * (size_t)M * hw);
+  L.act = cv.take(ab * (size_t)M * I);
+  L.q = cv.take(ab * (size_t)M * nq * D);
+  L.kb = cv.take(ab * (size_t)M * nkv * D);
+  L.vb = cv.take(ab * (size_t)M * nkv * D);
+  L.o = cv.take(ab * (size_t)M * nq * D);
+  L.cs = (float2*)cv.take(sizeof(float2) * (size_t)M * (D / 2));
+  int max_splits = 1;
+  for (int l = 0; l < c->n_layers; ++l) {
+    L.plans[l] = plan_attention(layer_max_keys(c, l, max_prefix), B, nkv);
+    if (L.plans[l].n_splits > max_splits) max_splits = L.plans[l].n_splits;
+  }
+  L.o_part = (float*)cv.take(sizeof(float) * (size_t)B * nkv * max_splits * 64 * D);
+  L.ml_part = (float2*)cv.take(sizeof(float2) * (size_t)B * nkv * max_splits * 64);
+  L.lm_part = (float2*)cv.take(sizeof(float2) * (size_t)M1 * logits_tiles(c->vocab));
+  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H), plan_gemm(M, H, nq * D),
+                         plan_gemm(M, ((I + 63) / 64) * 128, H), plan_gemm(M, H, I),
+                         plan_gemm(M1, c->vocab, H)};
+  size_t pf = 0;
+  int nc = 1;
+  for (const GemmPlan& p : ps) {
+    if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
+    if (p.n_tiles * p.m_tiles > nc) nc = p.n_tiles * p.m_tiles;
+  }
+  L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
+  L.gs.partial_floats = pf;
+  L.gs.counters = (int*)cv.take(sizeof(int) * nc);
+  L.gs.n_counters = nc;
+  L.bytes = cv.off;
+  return L;
+}
+
+struct LmHeadWs {
+  float2* part; GemmScratch gs; size_t bytes;
+};
+
+LmHeadWs layout_lm_head(const dflash_config* c, int rows, void* ws) {
+  Carver cv(ws);
+  LmHeadWs L;
+  L.part = (float2*)cv.take(sizeof(float2) * (size_t)rows * logits_tiles(c->vocab));
+  const GemmPlan p = plan_gemm(rows, c->vocab, c->hidden);
+  const size_t pf = gemm_partial_floats(p);
+  L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
+  L.gs.partial_floats = pf;
+  L.gs.counters = (int*)cv.take(sizeof(int) * p.n_tiles * p.m_tiles);
+  L.gs.n_counters = p.n_tiles * p.m_tiles;
+  L.bytes = cv.off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument";
+    case DFLASH_EUNSUPPORTED: return "unsupported configuration";
+    case DFLASH_EWORKSPACE: return "workspace too small";
+    case DFLASH_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+size_t dflash_context_workspace_bytes(const dflash_config* cfg, int64_t rows) {
+  if (check_config(cfg) != DFLASH_OK || rows < 0) return 0;
+  return layout_context(cfg, inject_chunk_rows(rows > 0 ? rows : 1), nullptr).bytes;
+}
+
+size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch,
+                                    int32_t max_prefix_len) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0 || max_prefix_len < 0) return 0;
+  return layout_draft(cfg, batch, max_prefix_len, nullptr).bytes;
+}
+
+dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weights* w,
+                                     const dflash_kv_cache* cache, const void* feats,
+                                     int64_t feat_row_stride, const int32_t* positions,
+                                     const int32_t* slots, const int32_t* valid_rows,
+                                     int32_t n_req, int32_t rows_per_req, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  dflash_status s = check_config(cfg);
+  if (s != DFLASH_OK) return s;
+  if (n_req < 0 || rows_per_req < 0) return fail(DFLASH_EINVAL, "negative row counts");
+  const int64_t T = (int64_t)n_req * rows_per_req;
+  if (T == 0) return DFLASH_OK;
+  if (T > (int64_t)1 << 30) return fail(DFLASH_EINVAL, "too many rows (%lld)", (long long)T);
+  if ((s = check_layer_weights(cfg, w, false)) != DFLASH_OK) return s;
+  REQUIRE_PTR(w->fc, "weights.fc");
+  REQUIRE_PTR(w->hidden_norm, "weights.hidden_norm");
+  if ((s = check_cache(cfg, cache)) != DFLASH_OK) return s;
+  REQUIRE_PTR(feats, "feats");
+  if (positions == nullptr || slots == nullptr)
+    return fail(DFLASH_EINVAL, "positions and slots must not be NULL");
+  if (feat_row_stride < cfg->feat_dim || feat_row_stride % 8)
+    return fail(DFLASH_EINVAL, "feat_row_stride %lld must be >= feat_dim and a multiple of 8",
+                (long long)feat_row_stride);
+  int64_t chunk = inject_chunk_rows(T);
+  if (valid_rows != nullptr) {
+    if (rows_per_req > kInjectChunk) chunk = rows_per_req;
+    else chunk = (chunk / rows_per_req) * rows_per_req;
+  }
+  const ContextWs L = layout_context(cfg, chunk, workspace);
+  if (workspace == nullptr || workspace_bytes < L.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  KVTargets tg;
+  memset(&tg, 0, sizeof tg);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    tg.w_qkv[l] = w->layer[l].w_qkv;
+    tg.k_norm[l] = w->layer[l].k_norm;
+    tg.kc[l] = cache->k[l];
+    tg.vc[l] = cache->v[l];
+  }
+  const int dt = cfg->act_dtype;
+  hipError_t e = launch_zero_i32(L.gs.counters, L.gs.n_counters, st);
+  if (e != hipSuccess) return hip_fail(e, "zero counters");
+  for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+    const int M = (int)((T - t0) < chunk ? (T - t0) : chunk);
+    const void* f = static_cast<const char*>(feats) + (size_t)t0 * feat_row_stride * act_bytes(dt);
+    if ((e = launch_rope_table(positions + t0, M, cfg->head_dim, cfg->rope_theta, L.cs, st)) != hipSuccess)
+      return hip_fail(e, "rope table");
+    if ((e = gemm_store_f32(dt, f, feat_row_stride, M, cfg->feat_dim, w->fc, cfg->hidden, L.craw,
+                            L.gs, st)) != hipSuccess)
+      return hip_fail(e, "fc gemm");
+    if ((e = launch_rmsnorm(dt, L.craw, M, cfg->hidden, w->hidden_norm, cfg->rms_eps, L.c, 0, st)) != hipSuccess)
+      return hip_fail(e, "hidden_norm");
+    const int32_t* vr = valid_rows ? valid_rows + t0 / rows_per_req : nullptr;
+    if ((e = gemm_kv_inject(dt, cfg->kv_dtype, L.c, M, cfg->hidden, tg, cfg->n_layers,
+                            cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, L.cs,
+                            slots + t0, vr, rows_per_req > 0 ? rows_per_req : 1, cfg->page_size,
+                            cache->num_pages, L.gs, st)) != hipSuccess)
+      return hip_fail(e, "kv inject gemm");
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w,
+                                 const dflash_kv_cache* cache, const int32_t* anchor,
+                                 const int32_t* prefix_len, const int32_t* page_table,
+                                 int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+                                 int32_t* block_ids, int32_t* positions, int32_t* slots,
+                                 int32_t* candidates, void* logits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  dflash_status s = check_config(cfg);
+  if (s != DFLASH_OK) return s;
+  if (batch < 0 || max_pages <= 0 || max_prefix_len < 0)
+    return fail(DFLASH_EINVAL, "batch, max_pages or max_prefix_len out of range");
+  if (batch == 0) return DFLASH_OK;
+  if ((int64_t)batch * cfg->block_size > (1 << 24)) return fail(DFLASH_EINVAL, "batch too large");
+  if ((s = check_layer_weights(cfg, w, true)) != DFLASH_OK) return s;
+  REQUIRE_PTR(w->embed, "weights.embed");
+  REQUIRE_PTR(w->lm_head, "weights.lm_head");
+  REQUIRE_PTR(w->final_norm, "weights.final_norm");
+  if ((s = check_cache(cfg, cache)) != DFLASH_OK) return s;
+  if (!anchor || !prefix_len || !page_table || !positions || !slots || !candidates)
+    return fail(DFLASH_EINVAL, "anchor, prefix_len, page_table, positions, slots and candidates "
+                               "must not be NULL");
+  if (logits != nullptr && !aligned16(logits)) return fail(DFLASH_EINVAL, "logits not aligned");
+  const DraftWs L = layout_draft(cfg, batch, max_prefix_len, workspace);
+  if (workspace == nullptr || workspace_bytes < L.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = cfg->act_dtype, S = cfg->block_size, M = batch * S, M1 = batch * (S - 1);
+  const int H = cfg->hidden, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, D = cfg->head_dim;
+  const int I = cfg->inter;
+  hipError_t e;
+  if ((e = launch_zero_i32(L.gs.counters, L.gs.n_counters, st)) != hipSuccess)
+    return hip_fail(e, "zero counters");
+  if ((e = launch_block_prep(dt, *cfg, w->embed, anchor, prefix_len, page_table, max_pages, batch,
+                             block_ids, positions, slots, candidates, L.x, L.cs, st)) != hipSuccess)
+    return hip_fail(e, "block prep");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dflash_layer_weights& W = w->layer[l];
+    if ((e = launch_rmsnorm(dt, L.x, M, H, W.in_norm, cfg->rms_eps, L.h, 0, st)) != hipSuccess)
+      return hip_fail(e, "input norm");
+    if ((e = gemm_qkv(dt, L.h, M, H, W.w_qkv, W.q_norm, W.k_norm, nq, nkv, D, cfg->rms_eps, L.cs,
+                      L.q, L.kb, L.vb, L.gs, st)) != hipSuccess)
+      return hip_fail(e, "qkv gemm");
+    if ((e = launch_attention(dt, cfg->kv_dtype, D, L.q, L.kb, L.vb, cache->k[l], cache->v[l],
+                              page_table, max_pages, cache->num_pages, prefix_len, max_prefix_len,
+                              batch, S, nq, nkv,
+                              cfg->page_size, cfg->sliding_window[l], L.plans[l], L.o_part,
+                              L.ml_part, L.o, st)) != hipSuccess)
+      return hip_fail(e, "attention");
+    if ((e = gemm_residual(dt, L.o, M, nq * D, W.w_o, H, L.x, L.gs, st)) != hipSuccess)
+      return hip_fail(e, "o-proj gemm");
+    if ((e = launch_rmsnorm(dt, L.x, M, H, W.post_norm, cfg->rms_eps, L.h, 0, st)) != hipSuccess)
+      return hip_fail(e, "post-attention norm");
+    if ((e = gemm_silu_mul(dt, L.h, M, H, W.w_gate, W.w_up, I, L.act, L.gs, st)) != hipSuccess)
+      return hip_fail(e, "gate/up gemm");
+    if ((e = gemm_residual(dt, L.act, M, I, W.w_down, H, L.x, L.gs, st)) != hipSuccess)
+      return hip_fail(e, "down gemm");
+  }
+  if ((e = launch_rmsnorm(dt, L.x, M1, H, w->final_norm, cfg->rms_eps, L.h, S, st)) != hipSuccess)
+    return hip_fail(e, "final norm");
+  if ((e = gemm_logits(dt, L.h, M1, H, w->lm_head, cfg->vocab, logits, L.lm_part, L.gs, st)) !=
+      hipSuccess)
+    return hip_fail(e, "lm_head gemm");
+  if ((e = launch_argmax_reduce(L.lm_part, M1, logits_tiles(cfg->vocab), S, candidates, st)) !=
+      hipSuccess)
+    return hip_fail(e, "argmax");
+  return DFLASH_OK;
+}
+
+size_t dflash_lm_head_workspace_bytes(const dflash_config* cfg, int32_t rows) {
+  if (check_config(cfg) != DFLASH_OK || rows <= 0) return 0;
+  return layout_lm_head(cfg, rows, nullptr).bytes;
+}
+
+dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* lm_head,
+                                    const void* hidden, int32_t rows, void* logits, int32_t* ids,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  dflash_status s = check_config(cfg);
+  if (s != DFLASH_OK) return s;
+  if (rows < 0) return fail(DFLASH_EINVAL, "rows %d < 0", rows);
+  if (rows == 0) return DFLASH_OK;
+  REQUIRE_PTR(lm_head, "lm_head");
+  REQUIRE_PTR(hidden, "hidden");
+  if (ids == nullptr) return fail(DFLASH_EINVAL, "ids is NULL");
+  if (logits != nullptr && !aligned16(logits)) return fail(DFLASH_EINVAL, "logits not aligned");
+  const LmHeadWs L = layout_lm_head(cfg, rows, workspace);
+  if (workspace == nullptr || workspace_bytes < L.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (L.gs.partial_floats && (e = launch_zero_i32(L.gs.counters, L.gs.n_counters, st)) != hipSuccess)
+    return hip_fail(e, "zero counters");
+  if ((e = gemm_logits(cfg->act_dtype, hidden, rows, cfg->hidden, lm_head, cfg->vocab, logits,
+                       L.part, L.gs, st)) != hipSuccess)
+    return hip_fail(e, "lm_head gemm");
+  if ((e = launch_argmax_reduce(L.part, rows, logits_tiles(cfg->vocab), 0, ids, st)) != hipSuccess)
+    return hip_fail(e, "argmax");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
+                            const int32_t* prefix_len, int32_t batch, int32_t block_size,
+                            int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                            int32_t* next_anchor, int32_t* new_seq_len, void* stream) {
+  if (batch < 0) return fail(DFLASH_EINVAL, "batch %d < 0", batch);
+  if (block_size < 1 || block_size > 4096)
+    return fail(DFLASH_EINVAL, "block_size %d outside 1..4096", block_size);
+  if (batch == 0) return DFLASH_OK;
+  if (!candidates || !posterior || !prefix_len || !accept_len || !commit_len || !out_tokens ||
+      !next_anchor || !new_seq_len)
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  hipError_t e = launch_accept(candidates, posterior, prefix_len, batch, block_size, accept_len,
+                               commit_len, out_tokens, next_anchor, new_seq_len,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "accept");
+  return DFLASH_OK;
+}
+
+}  // extern "C"

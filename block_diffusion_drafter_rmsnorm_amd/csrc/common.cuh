@@ -1,0 +1,164 @@
+// Device helpers shared by the gfx950 kernels: number formats, MFMA operand
+// fragments and wave-level reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+
+// bfloat16 held as raw bits; arithmetic always goes through fp32.
+struct bf16_t {
+  uint16_t bits;
+};
+struct fp8_t {
+  uint8_t bits;
+};
+
+// ---------------------------------------------------------------- formats
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bfloat16, round to nearest, ties to even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// OCP E4M3 ("fn"): bias 7, 3 mantissa bits, largest finite 448, no infinity,
+// NaN = S.1111.111.  Encode rounds to nearest even and saturates to +-448.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7fffffffu);
+  if (!(a == a)) return (uint8_t)(sign | 0x7fu);
+  if (a >= 448.0f) return (uint8_t)(sign | 0x7eu);
+  if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (exact scaling, then RNE)
+    const float q = __builtin_rintf(a * 512.0f);
+    return (uint8_t)(sign | (uint32_t)q);  // q == 8 is the smallest normal, code 0x08
+  }
+  const uint32_t ua = __float_as_uint(a);
+  uint32_t e = (ua >> 23) - 127u + 7u;      // 1..15
+  const uint32_t mant = ua & 0x7fffffu;
+  const uint32_t r = mant + 0x7ffffu + ((mant >> 20) & 1u);  // RNE at bit 20
+  uint32_t m3 = r >> 20;                    // 0..8
+  if (m3 == 8u) {
+    m3 = 0u;
+    e += 1u;
+  }
+  uint32_t code = (e << 3) | m3;
+  if (code > 0x7eu) code = 0x7eu;
+  return (uint8_t)(sign | code);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  const uint32_t s = ((uint32_t)c & 0x80u) << 24;
+  const uint32_t e = ((uint32_t)c >> 3) & 15u, m = (uint32_t)c & 7u;
+  float v = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+template <typename T> struct Num;
+template <> struct Num<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+  // value as stored, re-read as fp32 (identity)
+  static __device__ __forceinline__ float round(float x) { return x; }
+};
+template <> struct Num<bf16_t> {
+  static __device__ __forceinline__ float to_f(bf16_t x) { return bf16_to_f32(x.bits); }
+  static __device__ __forceinline__ bf16_t from_f(float x) { return bf16_t{f32_to_bf16(x)}; }
+  static __device__ __forceinline__ float round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+};
+template <> struct Num<fp8_t> {
+  static __device__ __forceinline__ float to_f(fp8_t x) { return e4m3_to_f32(x.bits); }
+  static __device__ __forceinline__ fp8_t from_f(float x) { return fp8_t{f32_to_e4m3(x)}; }
+  static __device__ __forceinline__ float round(float x) { return e4m3_to_f32(f32_to_e4m3(x)); }
+};
+
+// ---------------------------------------------------------------- MFMA fragments
+// A fragment is 8 consecutive K elements held by one lane.  For a 16x16 output
+// tile, lane l supplies row (A) or column (B) l % 16 and the lanes with the same
+// l % 16 (l / 16 = 0..3) supply disjoint K groups, so a 32-wide K step is one
+// bf16 MFMA 16x16x32 or eight fp32 MFMA 16x16x4.  The accumulator holds
+// rows 4 * (l / 16) + i, column l % 16 of the 16x16 tile.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  uint4 v;
+};
+template <> struct Frag<float> {
+  float4 lo, hi;
+};
+
+__device__ __forceinline__ void load_frag(Frag<bf16_t>& f, const bf16_t* p) {
+  f.v = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float>& f, const float* p) {
+  f.lo = *reinterpret_cast<const float4*>(p);
+  f.hi = *reinterpret_cast<const float4*>(p + 4);
+}
+__device__ __forceinline__ void store_frag(bf16_t* p, const Frag<bf16_t>& f) {
+  *reinterpret_cast<uint4*>(p) = f.v;
+}
+__device__ __forceinline__ void store_frag(float* p, const Frag<float>& f) {
+  *reinterpret_cast<float4*>(p) = f.lo;
+  *reinterpret_cast<float4*>(p + 4) = f.hi;
+}
+__device__ __forceinline__ void zero_frag(Frag<bf16_t>& f) { f.v = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void zero_frag(Frag<float>& f) {
+  f.lo = make_float4(0.f, 0.f, 0.f, 0.f);
+  f.hi = f.lo;
+}
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a.v),
+                                                __builtin_bit_cast(bf16x8_v, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+// Build a fragment from 8 fp32 values.
+__device__ __forceinline__ void frag_from_f32(Frag<bf16_t>& f, const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
+  f.lo = make_float4(x[0], x[1], x[2], x[3]);
+  f.hi = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Reduce over the 16 lanes that share l / 16 (one accumulator row group).
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }

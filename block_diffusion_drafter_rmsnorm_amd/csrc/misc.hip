@@ -1,0 +1,197 @@
+// Small kernels of the draft/accept path: block preparation with the embedding
+// gather and the RoPE table, row RMSNorm, the second argmax stage and greedy
+// accept.
+#include "common.cuh"
+#include "internal.h"
+
+namespace dflash {
+
+__global__ void zero_i32_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int* p, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+// (cos, sin) of pos * theta^(-2i/D), angle formed and reduced in fp64.
+__device__ __forceinline__ float2 rope_cs(int pos, int i, int D, double log_theta) {
+  const double inv = exp(-(2.0 * (double)i / (double)D) * log_theta);
+  double s, c;
+  sincos((double)pos * inv, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
+__global__ void rope_table_kernel(const int32_t* __restrict__ pos, int rows, int D,
+                                  double log_theta, float2* __restrict__ cs) {
+  const int half = D / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * half) return;
+  const int row = (int)(idx / half), i = (int)(idx % half);
+  cs[idx] = rope_cs(pos[row], i, D, log_theta);
+}
+
+hipError_t launch_rope_table(const int32_t* positions, int rows, int D, float theta, float2* cs,
+                             hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = (int64_t)rows * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     positions, rows, D, log((double)theta), cs);
+  return hipGetLastError();
+}
+
+// One workgroup per block row (r, j): ids / positions / slots, embedding
+// gather into the fp32 residual stream and the row's RoPE table.
+template <typename T>
+__global__ __launch_bounds__(256) void block_prep_kernel(
+    const T* __restrict__ embed, int V, int H, int S, int mask_id, int P, int D,
+    double log_theta, const int32_t* __restrict__ anchor, const int32_t* __restrict__ prefix_len,
+    const int32_t* __restrict__ pt, int max_pages, int32_t* block_ids, int32_t* positions,
+    int32_t* slots, int32_t* candidates, float* __restrict__ x, float2* __restrict__ cs) {
+  const int row = blockIdx.x, r = row / S, j = row % S, tid = threadIdx.x;
+  int id = (j == 0) ? anchor[r] : mask_id;
+  id = imin(imax(id, 0), V - 1);
+  const int pos = prefix_len[r] + j;
+  const int pidx = imin(imax(pos / P, 0), max_pages - 1);
+  if (tid == 0) {
+    if (block_ids != nullptr) block_ids[row] = (j == 0) ? anchor[r] : mask_id;
+    positions[row] = pos;
+    slots[row] = pt[(int64_t)r * max_pages + pidx] * P + pos % P;
+    if (j == 0) candidates[(int64_t)r * S] = anchor[r];
+  }
+  const T* e = embed + (int64_t)id * H;
+  for (int c = tid; c < H; c += 256) x[(int64_t)row * H + c] = Num<T>::to_f(e[c]);
+  for (int i = tid; i < D / 2; i += 256) cs[(int64_t)row * (D / 2) + i] = rope_cs(pos, i, D, log_theta);
+}
+
+hipError_t launch_block_prep(int dt, const dflash_config& c, const void* embed,
+                             const int32_t* anchor, const int32_t* prefix_len,
+                             const int32_t* page_table, int max_pages, int B, int32_t* block_ids,
+                             int32_t* positions, int32_t* slots, int32_t* candidates, float* x,
+                             float2* cs, hipStream_t st) {
+  const dim3 grid((unsigned)(B * c.block_size));
+  const double lt = log((double)c.rope_theta);
+  if (dt == DFLASH_BF16)
+    hipLaunchKernelGGL(block_prep_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)embed,
+                       c.vocab, c.hidden, c.block_size, c.mask_token_id, c.page_size, c.head_dim,
+                       lt, anchor, prefix_len, page_table, max_pages, block_ids, positions, slots,
+                       candidates, x, cs);
+  else
+    hipLaunchKernelGGL(block_prep_kernel<float>, grid, dim3(256), 0, st, (const float*)embed,
+                       c.vocab, c.hidden, c.block_size, c.mask_token_id, c.page_size, c.head_dim,
+                       lt, anchor, prefix_len, page_table, max_pages, block_ids, positions, slots,
+                       candidates, x, cs);
+  return hipGetLastError();
+}
+
+// Row RMSNorm of an fp32 matrix into the activation dtype.  With S > 0 output
+// row m reads block row (m / (S-1)) * S + m % (S-1) + 1 (rows 1..S-1 of each
+// block: the final norm before lm_head skips the anchor row).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ in, int H,
+                                                      const T* __restrict__ g, float eps,
+                                                      T* __restrict__ out, int S) {
+  __shared__ float red[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int src = (S > 0) ? (m / (S - 1)) * S + m % (S - 1) + 1 : m;
+  const float* xr = in + (int64_t)src * H;
+  float ss = 0.f;
+  for (int c = tid; c < H; c += 256) ss += xr[c] * xr[c];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int c = tid; c < H; c += 256)
+    out[(int64_t)m * H + c] = Num<T>::from_f(xr[c] * inv * Num<T>::to_f(g[c]));
+}
+
+hipError_t launch_rmsnorm(int dt, const float* in, int M, int H, const void* g, float eps,
+                          void* out, int S_skip_anchor, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (dt == DFLASH_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, in, H,
+                       (const bf16_t*)g, eps, (bf16_t*)out, S_skip_anchor);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, in, H, (const float*)g,
+                       eps, (float*)out, S_skip_anchor);
+  return hipGetLastError();
+}
+
+// Second argmax stage: one wave per logits row over the per-tile partials
+// (value, first index); ties go to the lower index.  With S > 0 row m is block
+// row (m / (S-1), 1 + m % (S-1)) of the [B, S] candidates; with S == 0 the id
+// goes to out[m].
+__global__ __launch_bounds__(64) void argmax_reduce_kernel(const float2* __restrict__ part,
+                                                           int n_tiles, int S,
+                                                           int32_t* __restrict__ candidates) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int t = lane; t < n_tiles; t += 64) {
+    const float2 p = part[(int64_t)m * n_tiles + t];
+    const int pi = __float_as_int(p.y);
+    if (p.x > best || (p.x == best && pi < bi)) {
+      best = p.x;
+      bi = pi;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > best || (ov == best && oi < bi)) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    if (S > 0) {
+      const int r = m / (S - 1), j = m % (S - 1);
+      candidates[(int64_t)r * S + 1 + j] = bi;
+    } else {
+      candidates[m] = bi;
+    }
+  }
+}
+
+hipError_t launch_argmax_reduce(const float2* part, int M, int n_tiles, int S, int32_t* candidates,
+                                hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(64), 0, st, part, n_tiles, S, candidates);
+  return hipGetLastError();
+}
+
+// Greedy accept: one thread per request walks the block until the first
+// mismatch between d_{a+1} and the target's choice after position a.
+__global__ void accept_kernel(const int32_t* __restrict__ cand, const int32_t* __restrict__ post,
+                              const int32_t* __restrict__ prefix_len, int B, int S,
+                              int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                              int32_t* next_anchor, int32_t* new_seq_len) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= B) return;
+  const int32_t* c = cand + (int64_t)r * S;
+  const int32_t* p = post + (int64_t)r * S;
+  int a = 0;
+  while (a < S - 1 && c[a + 1] == p[a]) ++a;
+  int32_t* o = out_tokens + (int64_t)r * S;
+  for (int j = 0; j < S; ++j) o[j] = (j < a) ? c[j + 1] : (j == a ? p[a] : 0);
+  accept_len[r] = a;
+  commit_len[r] = a + 1;
+  next_anchor[r] = p[a];
+  new_seq_len[r] = prefix_len[r] + a + 1;
+}
+
+hipError_t launch_accept(const int32_t* cand, const int32_t* post, const int32_t* prefix_len, int B,
+                         int S, int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                         int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(accept_kernel, dim3((B + 63) / 64), dim3(64), 0, st, cand, post, prefix_len,
+                     B, S, accept_len, commit_len, out_tokens, next_anchor, new_seq_len);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

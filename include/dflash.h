@@ -1,0 +1,227 @@
+/*
+ * dflash.h - C ABI of the DFlash draft-and-accept hot path on MI355X (gfx950).
+ *
+ * The library computes the three steps that one speculative-decoding cycle
+ * of a DFlash block-diffusion drafter runs on the GPU:
+ *   dflash_project_context  context injection (target features -> draft K/V cache)
+ *   dflash_draft_block      one non-causal draft pass over [anchor, MASK x (S-1)]
+ *   dflash_accept           greedy verify-accept, commit and logical crop
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory unless its name starts with
+ *     host_.  The caller owns every buffer (weights, cache, page table,
+ *     inputs, outputs, workspace); the library never allocates or frees
+ *     device memory and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  Results are ready when the stream is.
+ *   - Failures come back as a dflash_status; nothing throws across the ABI.
+ *     The library checks what the host can see (null pointers, sizes, dtype
+ *     and shape support, workspace size).  Device-resident values (token ids
+ *     < vocab, slots inside the pool, prefix + block inside the page table)
+ *     are the caller's contract; kernels clamp indices so that a violation
+ *     produces wrong values, never an out-of-bounds access.
+ *     dflash_last_error() returns a message for the last failure on the
+ *     calling thread.
+ *   - Integer tensors are int32.  Matrices are row-major [out, in] (y = x W^T).
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_MAX_LAYERS 16
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_EINVAL = -1,        /* null pointer, negative or inconsistent size        */
+  DFLASH_EUNSUPPORTED = -2,  /* configuration outside what the kernels implement   */
+  DFLASH_EWORKSPACE = -3,    /* workspace smaller than dflash_*_workspace_bytes()  */
+  DFLASH_EHIP = -4           /* a HIP runtime call failed (launch error)           */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_FP8_E4M3 = 2 } dflash_dtype;
+
+/*
+ * Draft model description (the draft checkpoint's config: block size, mask
+ * token id, layer types with their sliding window, head counts and head_dim;
+ * CSDN DFlash article, the Kimi-K2.6-DFlash config sample).
+ * Supported: head_dim 64 or 128; n_q_heads a multiple of n_kv_heads;
+ * (n_q_heads / n_kv_heads) * block_size <= 64; block_size 2..16;
+ * hidden, feat_dim, inter and n_q_heads*head_dim multiples of 32; inter a
+ * multiple of 64; act_dtype F32 or BF16; kv_dtype F32, BF16 or FP8_E4M3
+ * (FP8 and BF16 caches need act_dtype BF16; an F32 cache needs F32).
+ */
+typedef struct {
+  int32_t hidden;          /* H: draft hidden size                                 */
+  int32_t n_layers;        /* draft decoder layers (<= DFLASH_MAX_LAYERS)          */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;        /* D                                                    */
+  int32_t inter;           /* SwiGLU intermediate size                             */
+  int32_t vocab;           /* target vocabulary (shared embedding and lm_head)     */
+  int32_t feat_dim;        /* F: width of the concatenated target-layer features   */
+  int32_t block_size;      /* S: anchor + S-1 MASK positions                       */
+  int32_t mask_token_id;
+  int32_t page_size;       /* tokens per cache page                                */
+  int32_t sliding_window[DFLASH_MAX_LAYERS]; /* per layer; 0 = full attention      */
+  float rms_eps;
+  float rope_theta;        /* neox (rotate-half) RoPE over the whole head_dim      */
+  int32_t act_dtype;       /* dflash_dtype of weights, features and logits         */
+  int32_t kv_dtype;        /* dflash_dtype of the draft K/V cache                  */
+} dflash_config;
+
+/* Weights of one draft decoder layer, all of dtype act_dtype.                    */
+typedef struct {
+  const void* in_norm;     /* [H]                                                  */
+  const void* w_qkv;       /* [(nq + 2 nkv) * D, H]: q rows, then k rows, v rows   */
+  const void* q_norm;      /* [D] per-head RMSNorm gain for q                      */
+  const void* k_norm;      /* [D] per-head RMSNorm gain for k (block and context)  */
+  const void* w_o;         /* [H, nq * D]                                          */
+  const void* post_norm;   /* [H]                                                  */
+  const void* w_gate;      /* [inter, H]                                           */
+  const void* w_up;        /* [inter, H]                                           */
+  const void* w_down;      /* [H, inter]                                           */
+} dflash_layer_weights;
+
+typedef struct {
+  const void* embed;       /* [V, H] the target's token embedding                 */
+  const void* lm_head;     /* [V, H] the target's lm_head                          */
+  const void* fc;          /* [H, F] fuses the concatenated target features        */
+  const void* hidden_norm; /* [H] RMSNorm gain after fc                            */
+  const void* final_norm;  /* [H]                                                  */
+  dflash_layer_weights layer[DFLASH_MAX_LAYERS];
+} dflash_weights;
+
+/*
+ * Paged draft K/V cache.  For layer l, k[l] and v[l] each hold num_pages pages
+ * laid out [num_pages][n_kv_heads][page_size][head_dim] in kv_dtype, so one
+ * (page, kv head) is a contiguous page_size x head_dim block.  Physical slot
+ * s lives at page s / page_size, offset s % page_size.
+ */
+typedef struct {
+  void* k[DFLASH_MAX_LAYERS];
+  void* v[DFLASH_MAX_LAYERS];
+  int64_t num_pages;
+} dflash_kv_cache;
+
+/* Workspace sizes in bytes (host functions; 0 on invalid arguments). */
+size_t dflash_context_workspace_bytes(const dflash_config* cfg, int64_t rows);
+size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch,
+                                    int32_t max_prefix_len);
+
+/*
+ * (1) Context injection ("Inside SGLang: DFlash and DFlash 2 Implementation",
+ * Step 1 and Step 7; CSDN DFlash article, the draft model's target_hidden path
+ * and the fused_kv_materialize section).
+ *
+ * Row t of `feats` holds the concatenated hidden states of the selected target
+ * layers for one token.  The call computes c = RMSNorm(feats_t W_fc^T;
+ * hidden_norm) and, for every draft layer l, K = RoPE(k_norm_l(c W_k,l^T),
+ * positions[t]) and V = c W_v,l^T (W_k,l and W_v,l are the k and v rows of
+ * layer l's w_qkv), rounds both to kv_dtype (round to nearest even; FP8
+ * saturates at +-448) and stores them at cache slot slots[t].
+ *
+ * The rows form a dense grid of n_req requests x rows_per_req rows
+ * (row t = r * rows_per_req + j).  valid_rows (nullable, [n_req]) makes the
+ * write prefix-valid: row j of request r is written only if j < valid_rows[r]
+ * (the committed verify rows; pass the commit_len written by dflash_accept).
+ * NULL writes every row (prefill).
+ *
+ *   feats       [n_req * rows_per_req, F] act_dtype, row stride feat_row_stride
+ *               elements (>= F, a multiple of 8)
+ *   positions   [n_req * rows_per_req] logical token positions (RoPE)
+ *   slots       [n_req * rows_per_req] physical cache slots
+ *   workspace   >= dflash_context_workspace_bytes(cfg, n_req * rows_per_req)
+ * Rows with j >= valid_rows[r] are never read beyond their feature row.
+ */
+dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weights* w,
+                                     const dflash_kv_cache* cache, const void* feats,
+                                     int64_t feat_row_stride, const int32_t* positions,
+                                     const int32_t* slots, const int32_t* valid_rows,
+                                     int32_t n_req, int32_t rows_per_req, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
+ * (2) One draft pass ("Inside SGLang ...", Step 3 and Step 4; CSDN DFlash
+ * article, draft model predict and SGLang flow step 7).
+ *
+ * For request r with committed prefix L_r = prefix_len[r] and anchor token
+ * anchor[r] the block is ids = [anchor, MASK x (S-1)] at logical positions
+ * L_r .. L_r+S-1 and cache slots page_table[r][pos / P] * P + pos % P.
+ * x = embed[ids]; each layer applies q/k/v projection with per-head q/k
+ * RMSNorm and RoPE, attention of the S block queries over the cached context
+ * keys 0..L_r-1 (on a sliding layer with window W only keys i with
+ * pos - i < W) plus all S block keys with no causal mask, o-projection and
+ * residual, then RMSNorm + SwiGLU MLP + residual (pre-norm layers).  The
+ * final RMSNorm of rows 1..S-1 goes through lm_head; the argmax (first index
+ * among equal maxima, taken on the logits as rounded to act_dtype) is the
+ * draft token.  The block's own K/V are not stored.
+ *
+ *   anchor, prefix_len  [batch]
+ *   page_table          [batch, max_pages]; entries up to page (L_r + S - 1) / P
+ *                       must be valid pages of the cache
+ *   max_prefix_len      host upper bound of every prefix_len[r] (sizes the
+ *                       split-KV grid; larger prefixes are truncated to it)
+ *   block_ids           nullable [batch, S] out: [anchor, MASK, ...]
+ *   positions, slots    [batch, S] out: logical positions and cache slots of the
+ *                       block rows (the slots the committed rows are later
+ *                       injected into)
+ *   candidates          [batch, S] out: [anchor, d_1 .. d_{S-1}]
+ *   logits              nullable [batch, S-1, V] act_dtype out
+ *   workspace           >= dflash_draft_workspace_bytes(cfg, batch, max_prefix_len)
+ */
+dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w,
+                                 const dflash_kv_cache* cache, const int32_t* anchor,
+                                 const int32_t* prefix_len, const int32_t* page_table,
+                                 int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+                                 int32_t* block_ids, int32_t* positions, int32_t* slots,
+                                 int32_t* candidates, void* logits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * (3) Greedy verify-accept and commit ("Inside SGLang ...", Step 6 and Step 7;
+ * CSDN DFlash article, the z-lab verify step and SGLang flow steps 7-9).
+ *
+ * candidates[r] = [anchor, d_1 .. d_{S-1}]; posterior[r, j] = the target's
+ * greedy token after reading candidates[r, j].  accept_len = length of the
+ * longest prefix with d_{j+1} == posterior[j]; commit_len = accept_len + 1;
+ * out_tokens[r] = d_1 .. d_a, posterior[a], then zeros; next_anchor =
+ * posterior[a]; new_seq_len = prefix_len + commit_len (the logical crop).
+ *   candidates, posterior, out_tokens  [batch, block_size]
+ *   prefix_len, accept_len, commit_len, next_anchor, new_seq_len  [batch]
+ * Bit-exact integer work; no workspace.
+ */
+dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
+                            const int32_t* prefix_len, int32_t batch, int32_t block_size,
+                            int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                            int32_t* next_anchor, int32_t* new_seq_len, void* stream);
+
+/*
+ * The draft-token selection step alone ("Inside SGLang ...", Step 4: the target
+ * lm_head over the final draft hidden rows, then argmax): logits = hidden
+ * lm_head^T rounded to act_dtype, ids = argmax per row (first index among
+ * equal maxima).  dflash_draft_block runs the same kernels on its rows
+ * 1..S-1; this entry point serves callers that hold the normalised rows.
+ *   hidden     [rows, H] act_dtype (already through the final RMSNorm)
+ *   logits     nullable [rows, V] act_dtype out
+ *   ids        [rows] out
+ *   workspace  >= dflash_lm_head_workspace_bytes(cfg, rows)
+ */
+size_t dflash_lm_head_workspace_bytes(const dflash_config* cfg, int32_t rows);
+dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* lm_head,
+                                    const void* hidden, int32_t rows, void* logits, int32_t* ids,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+const char* dflash_status_string(dflash_status s);
+const char* dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

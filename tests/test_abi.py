@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, the header compiles as plain C, and host-visible argument
+errors come back as status codes before any HIP call."""
+import ctypes
+import dataclasses
+import os
+import re
+import subprocess
+
+import pytest
+
+from workloads.configs import TINY, QWEN3_8B_DRAFT, KIMI_DRAFT
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "dflash.h")
+
+dfl = pytest.importorskip("block_diffusion_drafter_rmsnorm_amd")
+
+
+def declared_functions():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_\w+)\s*\(", txt)))
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HDR],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"dflash_project_context", "dflash_draft_block", "dflash_accept"} <= set(names)
+    lib = dfl.raw_lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", dfl.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (dflash_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header():
+    # 11 int32, 16 windows, 2 floats, 2 int32
+    assert ctypes.sizeof(dfl.CConfig) == 4 * (11 + 16 + 2 + 2)
+    assert ctypes.sizeof(dfl.CWeights) == 8 * (5 + 9 * dfl.MAX_LAYERS)
+    assert ctypes.sizeof(dfl.CKVCache) == 8 * (2 * dfl.MAX_LAYERS + 1)
+
+
+def test_workspace_sizes():
+    assert dfl.context_workspace_bytes(TINY, 64) > 0
+    assert dfl.draft_workspace_bytes(QWEN3_8B_DRAFT, 1, 4096) > 0
+    assert dfl.draft_workspace_bytes(KIMI_DRAFT, 16, 32768) > 0
+    bad = dataclasses.replace(TINY, head_dim=96)
+    assert dfl.context_workspace_bytes(bad, 10) == 0
+    assert dfl.draft_workspace_bytes(TINY, 0, 10) == 0
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_config_errors():
+    lib = dfl.raw_lib()
+    fake = ctypes.c_void_p(0x100000)
+    for field, val, want in [("head_dim", 96, -2), ("block_size", 17, -2), ("n_kv_heads", 3, -2),
+                             ("hidden", 100, -2), ("mask_token_id", 5000, -1), ("n_layers", 0, -2)]:
+        c = dfl.make_config(dataclasses.replace(TINY, **{field: val}))
+        w = dfl.CWeights()
+        kv = dfl.CKVCache()
+        st = lib.dflash_draft_block(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), fake, fake,
+                                    fake, 4, 1, 64, None, fake, fake, fake, None, fake, 1 << 20,
+                                    None)
+        assert st == want, (field, st, lib.dflash_last_error())
+
+
+def test_null_and_workspace_errors():
+    lib = dfl.raw_lib()
+    cfg = dfl.make_config(TINY)
+    fake = 0x100000
+    w = dfl.CWeights()
+    for n in ("embed", "lm_head", "fc", "hidden_norm", "final_norm"):
+        setattr(w, n, fake)
+    for n in dfl._LAYER_FIELDS:
+        setattr(w.layer[0], n, fake)
+    kv = dfl.CKVCache()
+    kv.k[0] = kv.v[0] = fake
+    kv.num_pages = 8
+    F = ctypes.c_void_p(fake)
+    # missing cache page count
+    kv0 = dfl.CKVCache()
+    assert lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv0), F,
+                                      512, F, F, None, 1, 4, F, 1 << 30, None) == -1
+    # misaligned feats
+    assert lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv),
+                                      ctypes.c_void_p(fake + 2), 512, F, F, None, 1, 4, F, 1 << 30,
+                                      None) == -1
+    # stride smaller than feat_dim
+    assert lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F,
+                                      100, F, F, None, 1, 4, F, 1 << 30, None) == -1
+    # workspace too small
+    st = lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, 512,
+                                    F, F, None, 1, 4, F, 16, None)
+    assert st == -3 and b"workspace" in lib.dflash_last_error()
+    st = lib.dflash_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, F, F, 4,
+                                1, 64, None, F, F, F, None, F, 16, None)
+    assert st == -3
+    # zero rows / zero batch: nothing to do, no launch
+    assert lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, 512,
+                                      F, F, None, 0, 4, F, 16, None) == 0
+    assert lib.dflash_accept(F, F, F, 0, 4, F, F, F, F, F, None) == 0
+    assert lib.dflash_accept(F, F, F, -1, 4, F, F, F, F, F, None) == -1
+    assert lib.dflash_accept(None, F, F, 3, 4, F, F, F, F, F, None) == -1
+    assert lib.dflash_status_string(-3) == b"workspace too small"

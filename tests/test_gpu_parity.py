@@ -1,0 +1,243 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+inputs, at sizes the oracle finishes in seconds: several tiles in every
+dimension, ragged vocabularies / prefixes / pages, sliding windows, fp8 and
+fp32 caches.  Integers bit-exact; floating point within the tolerances below.
+
+Tolerances (floating point):
+* bf16 models: logits max|gpu - oracle| / max|oracle| per row <= 2e-2, and the
+  draft id must equal the oracle's argmax wherever the oracle's top-2 margin
+  exceeds 5e-2; injected K/V per (slot, head) max|gpu - oracle| /
+  max|oracle| <= 2e-2.
+* fp32 models: 1e-4 relative, argmax agreement where the margin exceeds 1e-3.
+* fp8 caches: every stored value within one E4M3 step (at that magnitude)
+  plus the bf16-class allowance 2e-2 * max|oracle| of its head, and at least
+  90% of codes identical: the two sides round slightly different values (the
+  GPU's fp32 result of bf16 operands, the oracle's exact fp64 one) to a 3-bit
+  mantissa, so a value near a rounding boundary may land one code away, and
+  near zero, where codes are only 2^-9 apart, a few codes away.
+* a cycle in which each side injects its own fp8 cache: logits 5e-2 (the
+  draft pass then reads caches that differ by those single-code roundings;
+  with identical caches the bf16 bound above holds).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import synth
+from workloads.configs import get_workload
+from tests.gpu_harness import Setup, logits_row_rel_err, top2_margin, e4m3_spacing, dfl
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny_f32", "small_bf16", "small_swa_fp8", "small_f32_d64"]
+
+
+def tol(cfg):
+    return (1e-4, 1e-3) if cfg.act_dtype == "f32" else (2e-2, 5e-2)
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- accept
+@pytest.mark.parametrize("S", [2, 4, 8, 16])
+def test_accept_bitexact(S):
+    m = dfl()
+    B = 2000
+    g = torch.Generator().manual_seed(S)
+    cand = torch.randint(0, 5, (B, S), generator=g, dtype=torch.int32)
+    commit = torch.randint(1, S + 1, (B,), generator=g)
+    post = synth.plant_posterior(cand, commit, 5, seed=S)
+    post[: B // 4] = torch.randint(0, 5, (B // 4, S), generator=g, dtype=torch.int32)
+    L = torch.randint(0, 100000, (B,), generator=g, dtype=torch.int32)
+    outs = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(4)]
+    out_tok = torch.full((B, S), -7, dtype=torch.int32, device="cuda")
+    m.dflash_accept(cand.cuda(), post.cuda(), L.cuda(), outs[0], outs[1], out_tok, outs[2], outs[3])
+    torch.cuda.synchronize()
+    o = oracle.accept(cand.numpy(), post.numpy(), L.numpy())
+    assert np.array_equal(outs[0].cpu().numpy(), o["accept_len"])
+    assert np.array_equal(outs[1].cpu().numpy(), o["commit_len"])
+    assert np.array_equal(out_tok.cpu().numpy(), o["out_tokens"])
+    assert np.array_equal(outs[2].cpu().numpy(), o["next_anchor"])
+    assert np.array_equal(outs[3].cpu().numpy(), o["new_seq_len"])
+    assert np.array_equal(o["commit_len"][B // 4:], commit[B // 4:].numpy())
+
+
+# ---------------------------------------------------------------- draft pass
+@pytest.mark.parametrize("name", SMALL)
+def test_draft_block_parity(name):
+    wl = get_workload(name)
+    cfg = wl.cfg
+    _print(f"[draft parity] {name} B={wl.batch} S={cfg.block_size}")
+    st = Setup(wl)
+    out = st.draft()
+    o = oracle.draft_block(cfg, st.np_W(), st.oracle_cache(), st.anchor.numpy(), st.L.numpy(),
+                           st.pt.numpy())
+    assert np.array_equal(out["positions"].cpu().numpy(), o["positions"])
+    assert np.array_equal(out["slots"].cpu().numpy(), o["slots"])
+    assert np.array_equal(out["block_ids"].cpu().numpy(), o["block_ids"])
+    cand = out["candidates"].cpu().numpy()
+    assert np.array_equal(cand[:, 0], st.anchor.numpy())
+    rel_tol, m_tol = tol(cfg)
+    gl = out["logits"].float().cpu().numpy()
+    rel = logits_row_rel_err(gl, o["logits"])
+    _print(f"  logits max rel err {rel.max():.3e}")
+    assert rel.max() <= rel_tol
+    margin = top2_margin(o["logits"])
+    sure = margin > m_tol
+    assert sure.mean() > 0.3
+    assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
+    # the GPU's ids are the argmax of its own logits (first index on ties)
+    assert np.array_equal(cand[:, 1:], np.argmax(gl, axis=-1))
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "tiny_f32"])
+def test_draft_block_deterministic(name):
+    st = Setup(get_workload(name))
+    a = st.draft()
+    b = st.draft()
+    assert torch.equal(a["logits"], b["logits"])
+    assert torch.equal(a["candidates"], b["candidates"])
+
+
+# ---------------------------------------------------------------- injection
+def _inject_case(st, T, seed, grid=None):
+    cfg = st.cfg
+    feats = synth.features(T, cfg, seed, "inj_feats", "cpu")
+    g = torch.Generator().manual_seed(seed)
+    pos = torch.randint(0, 200000, (T,), generator=g, dtype=torch.int32)
+    slots = torch.randperm(st.num_pages * cfg.page_size, generator=g)[:T].to(torch.int32)
+    valid = None
+    if grid is not None:
+        n_req, rpr = grid
+        valid = torch.randint(0, rpr + 1, (n_req,), generator=g, dtype=torch.int32)
+        valid[0], valid[-1] = 0, rpr
+    return feats, pos, slots, valid
+
+
+def _compare_pools(st, before, o_cache, written):
+    cfg = st.cfg
+    rel_tol, _ = tol(cfg)
+    for l in range(cfg.n_layers):
+        for kind, pool, opool, bpool in (("k", st.cache.k[l], o_cache.k[l], before.k[l]),
+                                         ("v", st.cache.v[l], o_cache.v[l], before.v[l])):
+            got = st._pool_values(pool)
+            untouched = np.ones(got.shape[0], bool)
+            untouched[written] = False
+            assert np.array_equal(np.nan_to_num(got[untouched], nan=1e9),
+                                  np.nan_to_num(bpool[untouched], nan=1e9)), (l, kind)
+            g, o = got[written], opool[written]
+            if cfg.kv_dtype == "fp8_e4m3":
+                d = np.abs(g - o)
+                allow = e4m3_spacing(np.maximum(np.abs(g), np.abs(o))) + \
+                    rel_tol * np.max(np.abs(o), axis=-1, keepdims=True)
+                assert (d <= allow).all(), (l, kind, float((d - allow).max()))
+                frac = (g == o).mean()
+                _print(f"  layer {l} {kind}: fp8 identical codes {frac:.4f}")
+                assert frac >= 0.9
+            else:
+                err = np.max(np.abs(g - o), axis=-1) / np.max(np.abs(o), axis=-1)
+                _print(f"  layer {l} {kind}: max rel err {err.max():.3e}")
+                assert err.max() <= rel_tol, (l, kind)
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("grid", [None, (5, 16)])
+def test_project_context_parity(name, grid):
+    wl = get_workload(name)
+    cfg = wl.cfg
+    _print(f"[inject parity] {name} grid={grid}")
+    st = Setup(wl)
+    T = 77 if grid is None else grid[0] * grid[1]
+    feats, pos, slots, valid = _inject_case(st, T, 100 + wl.seed, grid)
+    before = st.oracle_cache()
+    o_cache = before.copy()
+    n_req, rpr = (1, T) if grid is None else grid
+    st.inject(feats, pos, slots, valid, n_req, rpr)
+    live = oracle.project_context(cfg, st.np_W(), o_cache, feats.float().numpy(), pos.numpy(),
+                                  slots.numpy(), None if valid is None else valid.numpy(), rpr)
+    _compare_pools(st, before, o_cache, slots.numpy()[live])
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_swa_fp8", "tiny_f32"])
+def test_project_context_chunked_equals_once_and_idempotent(name):
+    """Injecting rows in several calls gives the same bits as one call (the
+    K loop of a row does not depend on how many rows share the call), and
+    re-injecting the same rows leaves the cache bit-identical."""
+    wl = get_workload(name)
+    st = Setup(wl)
+    T = 60
+    feats, pos, slots, _ = _inject_case(st, T, 7)
+    st.inject(feats, pos, slots)
+    once = [t.clone() for t in st.cache.k + st.cache.v]
+    st.inject(feats, pos, slots)
+    assert all(torch.equal(a, b) for a, b in zip(once, st.cache.k + st.cache.v))
+    st2 = Setup(wl)
+    for lo, hi in [(0, 9), (9, 40), (40, 60)]:
+        st2.inject(feats[lo:hi], pos[lo:hi], slots[lo:hi])
+    assert all(torch.equal(a, b) for a, b in zip(once, st2.cache.k + st2.cache.v))
+
+
+# ---------------------------------------------------------------- one cycle
+@pytest.mark.parametrize("name", ["small_bf16", "small_swa_fp8", "small_f32_d64"])
+def test_cycle_inject_draft_accept(name):
+    """Prefill injection -> draft -> accept -> injection of the committed
+    verify rows -> second draft, GPU and oracle each on their own state."""
+    wl = get_workload(name)
+    cfg = wl.cfg
+    _print(f"[cycle] {name}")
+    st = Setup(wl, random_cache=False)
+    m = dfl()
+    st.cache = m.KVCache.allocate(cfg, st.num_pages, "cuda", fill=0)
+    o_cache = oracle.OracleCache(cfg, st.num_pages * cfg.page_size)
+    Wn = st.np_W()
+    P = cfg.page_size
+    for r in range(st.B):
+        Lr = int(st.L[r])
+        if Lr == 0:
+            continue
+        f = synth.features(Lr, cfg, 500 + r, "prefill", "cpu")
+        pos = torch.arange(Lr, dtype=torch.int32)
+        sl = (st.pt[r, pos.long() // P] * P + pos % P).to(torch.int32)
+        st.inject(f, pos, sl)
+        oracle.project_context(cfg, Wn, o_cache, f.float().numpy(), pos.numpy(), sl.numpy())
+    rel_tol, m_tol = tol(cfg)
+    if cfg.kv_dtype == "fp8_e4m3":
+        rel_tol = 5e-2
+    out = st.draft()
+    o = oracle.draft_block(cfg, Wn, o_cache, st.anchor.numpy(), st.L.numpy(), st.pt.numpy())
+    rel = logits_row_rel_err(out["logits"].float().cpu().numpy(), o["logits"])
+    _print(f"  cycle-1 logits max rel err {rel.max():.3e}")
+    assert rel.max() <= rel_tol
+    # target posterior planted on the oracle's candidates (commit drawn per request)
+    commit = synth.randint(1, cfg.block_size, (st.B,), wl.seed, "commit")
+    post = synth.plant_posterior(torch.from_numpy(o["candidates"]), commit, cfg.vocab, wl.seed)
+    B, S = st.B, cfg.block_size
+    res = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(4)]
+    out_tok = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    m.dflash_accept(out["candidates"], post.cuda(), st.L.cuda(), res[0], res[1], out_tok, res[2],
+                    res[3])
+    torch.cuda.synchronize()
+    oa = oracle.accept(o["candidates"], post.numpy(), st.L.numpy())
+    same = (out["candidates"].cpu().numpy() == o["candidates"]).all(axis=1)
+    assert same.any()
+    assert np.array_equal(res[1].cpu().numpy()[same], oa["commit_len"][same])
+    assert np.array_equal(out_tok.cpu().numpy()[same], oa["out_tokens"][same])
+    # inject the committed verify rows at the block's slots, then draft again
+    vf = synth.features(B * S, cfg, 900, "verify", "cpu")
+    commit_used = torch.from_numpy(oa["commit_len"]).to(torch.int32)
+    st.inject(vf, out["positions"].reshape(-1).cpu(), out["slots"].reshape(-1).cpu(),
+              commit_used, B, S)
+    oracle.project_context(cfg, Wn, o_cache, vf.float().numpy(), o["positions"].reshape(-1),
+                           o["slots"].reshape(-1), oa["commit_len"], S)
+    st.L = torch.from_numpy(oa["new_seq_len"]).to(torch.int32)
+    st.anchor = torch.from_numpy(oa["next_anchor"]).to(torch.int32)
+    out2 = st.draft()
+    o2 = oracle.draft_block(cfg, Wn, o_cache, st.anchor.numpy(), st.L.numpy(), st.pt.numpy())
+    rel = logits_row_rel_err(out2["logits"].float().cpu().numpy(), o2["logits"])
+    _print(f"  cycle-2 logits max rel err {rel.max():.3e}")
+    assert rel.max() <= rel_tol
+    sure = top2_margin(o2["logits"]) > m_tol
+    assert np.array_equal(out2["candidates"].cpu().numpy()[:, 1:][sure], o2["draft_ids"][sure])
