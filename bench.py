@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft-and-accept hot path on one MI355X.
+
+One step = one cycle of the whole path for every request of the batch:
+dflash_draft_block (block prep, embedding, every draft layer, final norm,
+lm_head, argmax) -> dflash_accept against a planted target posterior ->
+dflash_project_context of the committed verify rows (fc + hidden_norm +
+per-layer K/V with k-norm and RoPE into the paged cache).  The state (prefix
+lengths, anchors, cache) is the same for every step: the crop is logical, so
+re-running a cycle from the same committed prefix is the same work.
+
+Inputs are seeded and synthetic (random-init weights and features
+N(0, 0.02^2), random context K/V, uniform token ids), resident in HBM before
+the timed region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft blocks/s + drafted tokens/s at 1 GPU; % HBM/MFMA roofline (Qwen3-8B, B=16)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def draft_pass_bytes(cfg, L):
+    """Algorithmic HBM bytes of one draft pass: every weight once, the
+    context K/V each layer reads (window-limited on sliding layers), the
+    embedding rows of the block."""
+    H, D, nq, nkv, I, V = cfg.hidden, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.inter, cfg.vocab
+    wb = 2 if cfg.act_dtype == "bf16" else 4
+    kvb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[cfg.kv_dtype]
+    layer_params = (nq + 2 * nkv) * D * H + H * nq * D + 3 * I * H + 2 * H + 2 * D
+    b = cfg.n_layers * layer_params * wb + V * H * wb + H * wb
+    B, S = len(L), cfg.block_size
+    for l in range(cfg.n_layers):
+        W = cfg.window(l)
+        for Lr in L:
+            keys = min(Lr, W - 1) if W else Lr
+            b += keys * nkv * D * 2 * kvb
+    b += B * S * H * wb
+    return b
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_b16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-only", action="store_true", help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path is measured on one MI355X and the "
+              f"batch shards by request with no collectives; --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from workloads import synth
+    from workloads.configs import get_workload
+    import block_diffusion_drafter_rmsnorm_amd as dfl
+
+    wl = get_workload(args.workload)
+    cfg = wl.cfg
+    B, S, P = wl.batch, cfg.block_size, cfg.page_size
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t_setup = time.time()
+    W = synth.weights(cfg, wl.seed, dev)
+    cw = dfl.make_weights(W)
+    L = synth.prefix_lengths(wl, "cpu").to(torch.int32)
+    pt, npages = synth.page_table(L, cfg, wl.seed, 2 * S)
+    K, V = synth.kv_pool_random(cfg, npages, wl.seed, dev)
+    cache = dfl.KVCache(K, V, npages)
+    c_cfg, c_cache = dfl.make_config(cfg), cache.c_struct()
+    anchor = synth.randint(0, cfg.vocab - 1, (B,), wl.seed, "anchor").to(torch.int32).to(dev)
+    Ld, ptd = L.to(dev), pt.to(dev)
+    max_prefix = int(L.max())
+    vfeat = synth.features(B * S, cfg, wl.seed, "verify", dev)
+    positions = torch.empty((B, S), dtype=torch.int32, device=dev)
+    slots = torch.empty_like(positions)
+    cand = torch.empty_like(positions)
+    acc = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
+    out_tok = torch.empty((B, S), dtype=torch.int32, device=dev)
+    dws = dfl.workspace(dfl.draft_workspace_bytes(cfg, B, max_prefix))
+    cws = dfl.workspace(dfl.context_workspace_bytes(cfg, B * S))
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: setup {time.time() - t_setup:.1f}s, pages {npages}, "
+        f"max prefix {max_prefix}")
+
+    def draft():
+        dfl.dflash_draft_block(cfg, cw, cache, anchor, Ld, ptd, max_prefix, positions, slots, cand,
+                               dws, c_cfg=c_cfg, c_cache=c_cache)
+
+    # planted target posterior: commit lengths as the workload states (uniform
+    # in [lo, hi]) or, when it states none, 6: the pages' mean accept length
+    # with a block-16 Qwen3-8B draft is 6.35-6.48.
+    draft()
+    torch.cuda.synchronize()
+    lo, hi = wl.commit
+    if hi == 0:
+        commit = torch.full((B,), 6, dtype=torch.int64)
+    else:
+        commit = synth.randint(lo, hi, (B,), wl.seed, "commit")
+    post = synth.plant_posterior(cand.cpu(), commit, cfg.vocab, wl.seed).to(dev)
+
+    def step():
+        draft()
+        dfl.dflash_accept(cand, post, Ld, acc[0], acc[1], out_tok, acc[2], acc[3])
+        dfl.dflash_project_context(cfg, cw, cache, vfeat, positions.view(-1), slots.view(-1),
+                                   acc[1], B, S, cws, c_cfg=c_cfg, c_cache=c_cache)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    got_commit = acc[1].cpu()
+    assert torch.equal(got_commit, commit.to(torch.int32)), "planted commit lengths not reproduced"
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_step = timed(step, args.steps)
+    ms_draft = timed(draft, args.steps)
+    log(f"[bench] step {ms_step:.3f} ms, draft pass {ms_draft:.3f} ms")
+
+    # dominant kernel: lm_head GEMM + argmax partials over the B*(S-1) rows,
+    # timed alone (per-call events) on the same shapes
+    M1 = B * (S - 1)
+    hid = synth.normal((M1, cfg.hidden), 1.0, wl.seed, "lm_rows", synth._DT[cfg.act_dtype], dev)
+    ids = torch.empty(M1, dtype=torch.int32, device=dev)
+    lws = dfl.workspace(dfl.lm_head_workspace_bytes(cfg, M1))
+    lm_ms = []
+    for i in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dfl.dflash_lm_head_argmax(cfg, W["lm_head"], hid, ids, lws, c_cfg=c_cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            lm_ms.append(e0.elapsed_time(e1))
+    wb = 2 if cfg.act_dtype == "bf16" else 4
+    lm_bytes = cfg.vocab * cfg.hidden * wb + M1 * cfg.hidden * wb + M1 * 4
+    lm_avg_s = float(np.mean(lm_ms)) * 1e-3
+    lm_gbs = lm_bytes / lm_avg_s / 1e9
+
+    # context injection throughput (prefill of one prompt-sized chunk)
+    T = min(int(L.max()), 8192) if wl.inject_rows == 0 else min(wl.inject_rows, 8192)
+    T = max(T, 1)
+    pf = synth.features(T, cfg, wl.seed, "prefill", dev)
+    ppos = torch.arange(T, dtype=torch.int32, device=dev)
+    pslot = torch.arange(T, dtype=torch.int32, device=dev) % (npages * P)
+    pws = dfl.workspace(dfl.context_workspace_bytes(cfg, T))
+
+    def inject_prefill():
+        dfl.dflash_project_context(cfg, cw, cache, pf, ppos, pslot, None, 1, T, pws, c_cfg=c_cfg,
+                                   c_cache=c_cache)
+
+    inject_prefill()
+    ms_inj = timed(inject_prefill, max(3, args.steps // 4))
+    inj_flops = 2.0 * T * (cfg.feat_dim * cfg.hidden + cfg.hidden * cfg.n_layers * 2 *
+                           cfg.n_kv_heads * cfg.head_dim)
+
+    pass_bytes = draft_pass_bytes(cfg, L.tolist())
+    res = {
+        "metric": METRIC,
+        "value": round(B / (ms_step * 1e-3), 3),
+        "unit": "draft blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act_dtype if cfg.kv_dtype != "fp8_e4m3" else "bf16 (fp8 e4m3 KV)",
+        "data": "synthetic (seeded random-init weights, features and context K/V)",
+        "config": {"workload": wl.name, "batch": B, "block_size": S,
+                   "context": list(wl.ctx), "hidden": cfg.hidden, "layers": cfg.n_layers,
+                   "vocab": cfg.vocab, "commit_lens": commit.tolist() if B <= 32 else "seeded",
+                   "step": "draft_block + accept + project_context(committed rows)"},
+        "drafted_tokens_per_s": round(B * (S - 1) / (ms_step * 1e-3), 1),
+        "draft_pass": {"ms": round(ms_draft, 4), "blocks_per_s": round(B / (ms_draft * 1e-3), 2),
+                       "drafted_tokens_per_s": round(B * (S - 1) / (ms_draft * 1e-3), 1),
+                       "algorithmic_bytes": pass_bytes,
+                       "hbm_gbs": round(pass_bytes / (ms_draft * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(pass_bytes / (ms_draft * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "context_injection": {"rows": T, "ms": round(ms_inj, 4),
+                              "context_tokens_per_s": round(T / (ms_inj * 1e-3), 1),
+                              "tflops": round(inj_flops / (ms_inj * 1e-3) / 1e12, 2),
+                              "mfma_frac": round(inj_flops / (ms_inj * 1e-3) / 1e12 /
+                                                 MFMA_BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemm_stream<EpiLogits> lm_head + argmax partials "
+                               "(+ argmax reduce), dflash_lm_head_argmax",
+                     "bytes_per_launch": lm_bytes,
+                     "avg_launch_us": round(lm_avg_s * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, wl, L, W)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, wl, L, W_dev):
+    """The oracle (fp64 numpy, unmodified) on the host cores: one full draft
+    pass for the first request of the workload, plus a 64-row context
+    injection.  It reads the same weights as the GPU run (copied to host) and
+    random context K/V of the same shape."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    t0 = time.time()
+
+    def host(t):
+        return None if t is None else t.detach().to("cpu").float().numpy()
+
+    W = {k: host(v) for k, v in W_dev.items() if k != "layers"}
+    W["layers"] = [{k: host(v) for k, v in Lw.items()} for Lw in W_dev["layers"]]
+    H, D, nkv, F = cfg.hidden, cfg.head_dim, cfg.n_kv_heads, cfg.feat_dim
+    L0 = int(L[0])
+    P = cfg.page_size
+    npg = (L0 + 2 * cfg.block_size + P - 1) // P
+    g = np.random.default_rng(wl.seed)
+    cache = oracle.OracleCache.__new__(oracle.OracleCache)
+    cache.k = [g.standard_normal((npg * P, nkv, D)) for _ in range(cfg.n_layers)]
+    cache.v = [g.standard_normal((npg * P, nkv, D)) for _ in range(cfg.n_layers)]
+    pt = np.arange(npg)[None, :]
+    copy_s = time.time() - t0
+    t1 = time.time()
+    oracle.draft_block(cfg, W, cache, [7], [L0], pt)
+    t_draft = time.time() - t1
+    rows = 64
+    f = (g.standard_normal((rows, F)) * 0.02).astype(np.float32)
+    t2 = time.time()
+    oracle.project_context(cfg, W, cache, f, np.arange(rows), np.arange(rows))
+    t_inj = time.time() - t2
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = blas[0]["num_threads"] if blas else len(os.sched_getaffinity(0))
+    return {"value": round(1.0 / t_draft, 5), "unit": "draft blocks/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"one full draft pass of 1 request ({cfg.n_layers} layers, context {L0}, "
+                      f"block {cfg.block_size}, vocab {cfg.vocab}) in fp64 numpy: {t_draft:.2f} s; "
+                      f"64-row context injection: {t_inj:.2f} s; weights copied from the GPU "
+                      f"run ({copy_s:.1f} s, untimed)",
+            "drafted_tokens_per_s": round((cfg.block_size - 1) / t_draft, 4),
+            "context_tokens_per_s": round(rows / t_inj, 2)}
+
+
+if __name__ == "__main__":
+    main()
