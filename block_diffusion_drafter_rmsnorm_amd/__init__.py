@@ -156,19 +156,24 @@ def make_weights(W: Dict) -> CWeights:
 
 @dataclass
 class KVCache:
-    """Paged draft cache: per layer K and V of [num_pages, nkv, page, D]."""
+    """Paged draft cache: per layer K pages [num_pages, nkv, page, D] and V
+    pages stored transposed, [num_pages, nkv, D, page]."""
     k: List[torch.Tensor]
     v: List[torch.Tensor]
     num_pages: int
 
     @staticmethod
     def allocate(cfg, num_pages: int, device="cuda", fill=None) -> "KVCache":
-        shp = (num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        kshp = (num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        vshp = (num_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size)
         dt = _TORCH_DT[cfg.kv_dtype]
-        mk = (lambda: torch.empty(shp, dtype=dt, device=device)) if fill is None else \
-            (lambda: torch.full(shp, fill, dtype=dt, device=device))
-        return KVCache([mk() for _ in range(cfg.n_layers)], [mk() for _ in range(cfg.n_layers)],
-                       num_pages)
+
+        def mk(shp):
+            if fill is None:
+                return torch.empty(shp, dtype=dt, device=device)
+            return torch.full(shp, fill, dtype=dt, device=device)
+        return KVCache([mk(kshp) for _ in range(cfg.n_layers)],
+                       [mk(vshp) for _ in range(cfg.n_layers)], num_pages)
 
     def c_struct(self) -> CKVCache:
         c = CKVCache()

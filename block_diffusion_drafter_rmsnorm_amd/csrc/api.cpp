@@ -42,6 +42,8 @@ dflash_status check_config(const dflash_config* c) {
   if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->inter <= 0 ||
       c->vocab <= 0 || c->feat_dim <= 0 || c->page_size <= 0)
     return fail(DFLASH_EINVAL, "non-positive model dimension");
+  if (c->page_size % 16)
+    return fail(DFLASH_EUNSUPPORTED, "page_size %d (must be a multiple of 16)", c->page_size);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(DFLASH_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
   if (c->n_q_heads % c->n_kv_heads != 0)
@@ -126,7 +128,7 @@ struct Carver {
 constexpr int kInjectChunk = 8192;  // context rows per injection pass
 
 struct ContextWs {
-  float2* cs; float* craw; void* c; GemmScratch gs; size_t bytes;
+  float2* cs; void* cg; float* ss; GemmScratch gs; size_t bytes;
 };
 
 int64_t inject_chunk_rows(int64_t rows) { return rows < kInjectChunk ? rows : kInjectChunk; }
@@ -136,29 +138,24 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   ContextWs L;
   const int M = (int)chunk;
   L.cs = (float2*)cv.take(sizeof(float2) * M * (c->head_dim / 2));
-  L.craw = (float*)cv.take(sizeof(float) * (size_t)M * c->hidden);
-  L.c = cv.take((size_t)act_bytes(c->act_dtype) * M * c->hidden);
+  L.cg = cv.take((size_t)act_bytes(c->act_dtype) * M * c->hidden);
+  L.ss = (float*)cv.take(sizeof(float) * (size_t)M * ss_tiles(c->hidden));
   // the last chunk of a call can be any size up to `chunk`: take the worst case
   size_t pf = 0;
-  int nc = 1;
   for (int m = 1; m <= M; ++m) {
     const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim),
                             plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim, c->hidden)};
-    for (const GemmPlan& p : ps) {
+    for (const GemmPlan& p : ps)
       if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
-      if (p.n_tiles * p.m_tiles > nc) nc = p.n_tiles * p.m_tiles;
-    }
   }
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
-  L.gs.counters = (int*)cv.take(sizeof(int) * nc);
-  L.gs.n_counters = nc;
   L.bytes = cv.off;
   return L;
 }
 
 struct DraftWs {
-  float* x; void* h; void* act; void* q; void* kb; void* vb; void* o; float2* cs;
+  float* x; float* ss; void* xg; void* act; void* q; void* kb; void* vb; void* o; float2* cs;
   float* o_part; float2* ml_part; float2* lm_part; GemmScratch gs; size_t bytes;
   AttnPlan plans[DFLASH_MAX_LAYERS];
 };
@@ -176,12 +173,12 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   const int nq = c->n_q_heads, nkv = c->n_kv_heads, D = c->head_dim, I = c->inter;
   const size_t ab = act_bytes(c->act_dtype);
   L.x = (float*)cv.take(sizeof(float) * (size_t)M * H);
-  const int hw = H > nq * D ? H : nq * D;
-  L.h = cv.take(ab * (size_t)M * hw);
+  L.ss = (float*)cv.take(sizeof(float) * (size_t)M * ss_tiles(H));
+  L.xg = cv.take(ab * (size_t)M * H);
   L.act = cv.take(ab * (size_t)M * I);
   L.q = cv.take(ab * (size_t)M * nq * D);
-  L.kb = cv.take(ab * (size_t)M * nkv * D);
-  L.vb = cv.take(ab * (size_t)M * nkv * D);
+  L.kb = cv.take(ab * (size_t)B * nkv * 16 * D);
+  L.vb = cv.take(ab * (size_t)B * nkv * 16 * D);
   L.o = cv.take(ab * (size_t)M * nq * D);
   L.cs = (float2*)cv.take(sizeof(float2) * (size_t)M * (D / 2));
   int max_splits = 1;
@@ -196,15 +193,10 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
                          plan_gemm(M, ((I + 63) / 64) * 128, H), plan_gemm(M, H, I),
                          plan_gemm(M1, c->vocab, H)};
   size_t pf = 0;
-  int nc = 1;
-  for (const GemmPlan& p : ps) {
+  for (const GemmPlan& p : ps)
     if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
-    if (p.n_tiles * p.m_tiles > nc) nc = p.n_tiles * p.m_tiles;
-  }
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
-  L.gs.counters = (int*)cv.take(sizeof(int) * nc);
-  L.gs.n_counters = nc;
   L.bytes = cv.off;
   return L;
 }
@@ -221,8 +213,6 @@ LmHeadWs layout_lm_head(const dflash_config* c, int rows, void* ws) {
   const size_t pf = gemm_partial_floats(p);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
-  L.gs.counters = (int*)cv.take(sizeof(int) * p.n_tiles * p.m_tiles);
-  L.gs.n_counters = p.n_tiles * p.m_tiles;
   L.bytes = cv.off;
   return L;
 }
@@ -295,20 +285,22 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
     tg.vc[l] = cache->v[l];
   }
   const int dt = cfg->act_dtype;
-  hipError_t e = launch_zero_i32(L.gs.counters, L.gs.n_counters, st);
-  if (e != hipSuccess) return hip_fail(e, "zero counters");
+  hipError_t e;
   for (int64_t t0 = 0; t0 < T; t0 += chunk) {
     const int M = (int)((T - t0) < chunk ? (T - t0) : chunk);
     const void* f = static_cast<const char*>(feats) + (size_t)t0 * feat_row_stride * act_bytes(dt);
     if ((e = launch_rope_table(positions + t0, M, cfg->head_dim, cfg->rope_theta, L.cs, st)) != hipSuccess)
       return hip_fail(e, "rope table");
-    if ((e = gemm_store_f32(dt, f, feat_row_stride, M, cfg->feat_dim, w->fc, cfg->hidden, L.craw,
-                            L.gs, st)) != hipSuccess)
+    // c = fc(f): the fc epilogue writes c * hidden_norm (act dtype) and the
+    // row sums of squares of c; the K/V GEMM streams the former and scales
+    // its rows by 1/rms(c) (RMSNorm by linearity)
+    if ((e = gemm_store_f32(dt, asrc_plain(f, feat_row_stride), M, cfg->feat_dim, w->fc,
+                            cfg->hidden, nullptr, L.ss, L.cg, w->hidden_norm, L.gs, st)) !=
+        hipSuccess)
       return hip_fail(e, "fc gemm");
-    if ((e = launch_rmsnorm(dt, L.craw, M, cfg->hidden, w->hidden_norm, cfg->rms_eps, L.c, 0, st)) != hipSuccess)
-      return hip_fail(e, "hidden_norm");
     const int32_t* vr = valid_rows ? valid_rows + t0 / rows_per_req : nullptr;
-    if ((e = gemm_kv_inject(dt, cfg->kv_dtype, L.c, M, cfg->hidden, tg, cfg->n_layers,
+    const ASrc cin = asrc_normed(L.cg, cfg->hidden, L.ss, cfg->rms_eps);
+    if ((e = gemm_kv_inject(dt, cfg->kv_dtype, cin, M, cfg->hidden, tg, cfg->n_layers,
                             cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, L.cs,
                             slots + t0, vr, rows_per_req > 0 ? rows_per_req : 1, cfg->page_size,
                             cache->num_pages, L.gs, st)) != hipSuccess)
@@ -347,37 +339,39 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   const int H = cfg->hidden, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, D = cfg->head_dim;
   const int I = cfg->inter;
   hipError_t e;
-  if ((e = launch_zero_i32(L.gs.counters, L.gs.n_counters, st)) != hipSuccess)
-    return hip_fail(e, "zero counters");
+  const int n_ss = ss_tiles(H);
+  const float eps = cfg->rms_eps;
+  // Every RMSNorm is applied by linearity: the producer of the residual x writes
+  // xg = x * g_next (act dtype) and the row sums of squares of x; the consumer
+  // GEMM streams xg and scales its output rows by 1/rms(x).
   if ((e = launch_block_prep(dt, *cfg, w->embed, anchor, prefix_len, page_table, max_pages, batch,
-                             block_ids, positions, slots, candidates, L.x, L.cs, st)) != hipSuccess)
+                             block_ids, positions, slots, candidates, L.x, L.ss, n_ss, L.xg,
+                             w->layer[0].in_norm, L.cs, st)) != hipSuccess)
     return hip_fail(e, "block prep");
+  const ASrc xin = asrc_normed(L.xg, H, L.ss, eps);
   for (int l = 0; l < cfg->n_layers; ++l) {
     const dflash_layer_weights& W = w->layer[l];
-    if ((e = launch_rmsnorm(dt, L.x, M, H, W.in_norm, cfg->rms_eps, L.h, 0, st)) != hipSuccess)
-      return hip_fail(e, "input norm");
-    if ((e = gemm_qkv(dt, L.h, M, H, W.w_qkv, W.q_norm, W.k_norm, nq, nkv, D, cfg->rms_eps, L.cs,
-                      L.q, L.kb, L.vb, L.gs, st)) != hipSuccess)
+    const void* g_after = (l + 1 < cfg->n_layers) ? w->layer[l + 1].in_norm : w->final_norm;
+    if ((e = gemm_qkv(dt, xin, M, H, W.w_qkv, W.q_norm, W.k_norm, nq, nkv, D, eps, L.cs, L.q, L.kb,
+                      L.vb, S, L.gs, st)) != hipSuccess)
       return hip_fail(e, "qkv gemm");
     if ((e = launch_attention(dt, cfg->kv_dtype, D, L.q, L.kb, L.vb, cache->k[l], cache->v[l],
                               page_table, max_pages, cache->num_pages, prefix_len, max_prefix_len,
-                              batch, S, nq, nkv,
-                              cfg->page_size, cfg->sliding_window[l], L.plans[l], L.o_part,
-                              L.ml_part, L.o, st)) != hipSuccess)
+                              batch, S, nq, nkv, cfg->page_size, cfg->sliding_window[l],
+                              L.plans[l], L.o_part, L.ml_part, L.o, st)) != hipSuccess)
       return hip_fail(e, "attention");
-    if ((e = gemm_residual(dt, L.o, M, nq * D, W.w_o, H, L.x, L.gs, st)) != hipSuccess)
+    if ((e = gemm_residual(dt, asrc_plain(L.o, nq * D), M, nq * D, W.w_o, H, L.x, L.ss, L.xg,
+                           W.post_norm, L.gs, st)) != hipSuccess)
       return hip_fail(e, "o-proj gemm");
-    if ((e = launch_rmsnorm(dt, L.x, M, H, W.post_norm, cfg->rms_eps, L.h, 0, st)) != hipSuccess)
-      return hip_fail(e, "post-attention norm");
-    if ((e = gemm_silu_mul(dt, L.h, M, H, W.w_gate, W.w_up, I, L.act, L.gs, st)) != hipSuccess)
+    if ((e = gemm_silu_mul(dt, xin, M, H, W.w_gate, W.w_up, I, L.act, L.gs, st)) != hipSuccess)
       return hip_fail(e, "gate/up gemm");
-    if ((e = gemm_residual(dt, L.act, M, I, W.w_down, H, L.x, L.gs, st)) != hipSuccess)
+    if ((e = gemm_residual(dt, asrc_plain(L.act, I), M, I, W.w_down, H, L.x, L.ss, L.xg, g_after,
+                           L.gs, st)) != hipSuccess)
       return hip_fail(e, "down gemm");
   }
-  if ((e = launch_rmsnorm(dt, L.x, M1, H, w->final_norm, cfg->rms_eps, L.h, S, st)) != hipSuccess)
-    return hip_fail(e, "final norm");
-  if ((e = gemm_logits(dt, L.h, M1, H, w->lm_head, cfg->vocab, logits, L.lm_part, L.gs, st)) !=
-      hipSuccess)
+  // final norm of rows 1..S-1 of every block, applied by the lm_head GEMM
+  if ((e = gemm_logits(dt, asrc_normed(L.xg, H, L.ss, eps, S), M1, H, w->lm_head, cfg->vocab,
+                       logits, L.lm_part, L.gs, st)) != hipSuccess)
     return hip_fail(e, "lm_head gemm");
   if ((e = launch_argmax_reduce(L.lm_part, M1, logits_tiles(cfg->vocab), S, candidates, st)) !=
       hipSuccess)
@@ -406,10 +400,8 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* lm_hea
     return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (L.gs.partial_floats && (e = launch_zero_i32(L.gs.counters, L.gs.n_counters, st)) != hipSuccess)
-    return hip_fail(e, "zero counters");
-  if ((e = gemm_logits(cfg->act_dtype, hidden, rows, cfg->hidden, lm_head, cfg->vocab, logits,
-                       L.part, L.gs, st)) != hipSuccess)
+  if ((e = gemm_logits(cfg->act_dtype, asrc_plain(hidden, cfg->hidden), rows, cfg->hidden, lm_head,
+                       cfg->vocab, logits, L.part, L.gs, st)) != hipSuccess)
     return hip_fail(e, "lm_head gemm");
   if ((e = launch_argmax_reduce(L.part, rows, logits_tiles(cfg->vocab), 0, ids, st)) != hipSuccess)
     return hip_fail(e, "argmax");

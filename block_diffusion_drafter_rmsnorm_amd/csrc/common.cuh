@@ -142,6 +142,116 @@ __device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
   f.hi = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// Eight raw elements of one storage type held in registers (a load issued now,
+// converted to fp32 later so the load overlaps other work).
+template <typename KT> struct Raw8;
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void to_f(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+template <> struct Raw8<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void to_f(float* o) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffffu));
+      o[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  }
+};
+template <> struct Raw8<fp8_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const fp8_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint2(0, 0); }
+  __device__ __forceinline__ void to_f(float* o) const {
+    const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = e4m3_to_f32((uint8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xffu));
+  }
+};
+
+// Four raw elements of one storage type.
+template <typename KT> struct Raw4;
+template <> struct Raw4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void to_f(float* o) const {
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+template <> struct Raw4<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void to_f(float* o) const {
+    o[0] = bf16_to_f32((uint16_t)(v.x & 0xffffu));
+    o[1] = bf16_to_f32((uint16_t)(v.x >> 16));
+    o[2] = bf16_to_f32((uint16_t)(v.y & 0xffffu));
+    o[3] = bf16_to_f32((uint16_t)(v.y >> 16));
+  }
+};
+template <> struct Raw4<fp8_t> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const fp8_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void to_f(float* o) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = e4m3_to_f32((uint8_t)((v >> (8 * i)) & 0xffu));
+  }
+};
+
+// Raw storage -> MFMA operand fragment (bit copy when no conversion is needed).
+template <typename CT, typename KT>
+__device__ __forceinline__ void raw_to_frag(Frag<CT>& f, const Raw8<KT>& r) {
+  float t[8];
+  r.to_f(t);
+  frag_from_f32(f, t);
+}
+template <>
+__device__ __forceinline__ void raw_to_frag<bf16_t, bf16_t>(Frag<bf16_t>& f, const Raw8<bf16_t>& r) {
+  f.v = r.v;
+}
+template <>
+__device__ __forceinline__ void raw_to_frag<float, float>(Frag<float>& f, const Raw8<float>& r) {
+  f.lo = r.a;
+  f.hi = r.b;
+}
+// Two 4-element pieces -> fragment, element e zeroed unless bit e of keep is set.
+template <typename CT, typename KT>
+__device__ __forceinline__ void raw4x2_to_frag(Frag<CT>& f, const Raw4<KT>& a, const Raw4<KT>& b,
+                                               unsigned keep) {
+  float t[8];
+  a.to_f(t);
+  b.to_f(t + 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (!((keep >> e) & 1u)) t[e] = 0.f;
+  frag_from_f32(f, t);
+}
+template <>
+__device__ __forceinline__ void raw4x2_to_frag<bf16_t, bf16_t>(Frag<bf16_t>& f,
+                                                               const Raw4<bf16_t>& a,
+                                                               const Raw4<bf16_t>& b,
+                                                               unsigned keep) {
+  const uint32_t w[4] = {a.v.x, a.v.y, b.v.x, b.v.y};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = (((keep >> (2 * i)) & 1u) ? 0x0000ffffu : 0u) |
+                       (((keep >> (2 * i + 1)) & 1u) ? 0xffff0000u : 0u);
+    o[i] = w[i] & m;
+  }
+  f.v = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

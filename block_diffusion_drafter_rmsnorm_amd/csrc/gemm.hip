@@ -1,4 +1,4 @@
-// Weight-streaming MFMA GEMM for gfx950 with fused epilogues.
+// Weight-streaming MFMA GEMM for gfx950 with fused prologues and epilogues.
 //
 // C[M, Ncols] = A[M, K] * W[Ncols, K]^T, W row-major [out, in] (the layout of
 // every projection of the draft model).  One workgroup (4 waves, 256 threads)
@@ -7,12 +7,19 @@
 // so every weight fragment a lane loads from HBM feeds MB MFMAs straight from
 // registers.  A rows (the small activation matrix) come through L1/L2.
 //
-// After the K loop the fp32 tile is assembled in LDS (summing the split-K
-// partials of the other workgroups in a fixed order when K is split, so the
-// result is deterministic) and handed to an epilogue that sees whole rows of
-// the 128-column tile: a full attention head for the q/k RMSNorm + RoPE of the
-// QKV and K/V-injection epilogues, paired gate/up columns for SwiGLU, a
-// 128-wide vocabulary slice for the argmax partials of lm_head.
+// RMSNorm is applied by linearity: rms(x) * g * W^T = rstd * ((x * g) W^T).  The
+// producer of x (an epilogue) writes x * g_next rounded to T plus the row's
+// sum of squares per 128-column tile; the consumer GEMM streams that as a plain
+// A operand and scales each output row by rstd (sums of squares added in a
+// fixed order) before any other epilogue math.
+//
+// After the K loop the fp32 tile is assembled in LDS (when K is split, a second
+// kernel sums the split partials in a fixed order, so the result is
+// deterministic and needs no cross-workgroup synchronisation) and handed to an
+// epilogue that sees whole rows of the 128-column tile: a full attention head
+// for the q/k RMSNorm + RoPE of the QKV and K/V-injection epilogues, paired
+// gate/up columns for SwiGLU, a 128-wide vocabulary slice for the argmax
+// partials of lm_head, the next RMSNorm's inputs.
 #include "common.cuh"
 #include "internal.h"
 
@@ -52,14 +59,103 @@ size_t gemm_partial_floats(const GemmPlan& p) {
 
 int logits_tiles(int V) { return (V + BN - 1) / BN; }
 
+// ---------------------------------------------------------------- A sources
+// A rows as stored (T).  With S > 0 GEMM row m reads A row
+// (m / (S-1)) * S + m % (S-1) + 1 (rows 1..S-1 of every block: lm_head skips
+// the anchor row).
+__host__ __device__ __forceinline__ int block_row(int m, int S) {
+  return S > 0 ? (m / (S - 1)) * S + m % (S - 1) + 1 : m;
+}
+
+template <typename T> struct ASrcPlain {
+  const T* A;
+  int64_t lda;
+  int S;
+  template <int MB> struct State {
+    const T* p[MB];
+  };
+  template <int MB>
+  __device__ __forceinline__ void setup(State<MB>& s, int m0, int M, int r16) const {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      s.p[mb] = A + (int64_t)block_row(imin(m0 + mb * 16 + r16, M - 1), S) * lda;
+  }
+  template <int MB>
+  __device__ __forceinline__ void load(Frag<T>& f, const State<MB>& s, int mb, int k) const {
+    load_frag(f, s.p[mb] + k);
+  }
+};
+
+// Per-row 1/rms from the sums of squares ss[row * n_ss + t] of a width-H row
+// (ss == null: no scaling).  GEMM row m uses ss row block_row(m, S).
+struct RowScale {
+  const float* ss;
+  int n_ss;
+  int H;
+  float eps;
+  int S;
+  // 1/rms of the tile's rows m0 .. m0+rows-1 into out[] (LDS), one wave per row
+  // (lanes load the row's partial sums in parallel, summed in a fixed tree).
+  // Called by all threads of the workgroup; ends with a barrier.
+  __device__ __forceinline__ void fill(float* out, int rows, int m0, int M, int tid) const {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int r = wave; r < rows; r += 4) {
+      float v = 1.0f;
+      if (ss != nullptr) {
+        const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+        float acc = 0.f;
+        for (int t = lane; t < n_ss; t += 64) acc += p[t];
+        acc = wave_sum(acc);
+        v = 1.0f / sqrtf(acc / (float)H + eps);
+      }
+      if (lane == 0) out[r] = v;
+    }
+    __syncthreads();
+  }
+};
+
+// Inputs of the next RMSNorm written by a producer epilogue: xg = x * g rounded
+// to T (xg == null: nothing written).
+template <typename T> struct NextNorm {
+  T* xg;
+  const T* g;
+};
+
 // ---------------------------------------------------------------- main kernel
-template <typename T, int MB, class Epi>
-__global__ __launch_bounds__(256) void gemm_stream(const T* __restrict__ A, int64_t lda, int M,
-                                                   int K, int KS, int Kc, int m_tiles,
-                                                   float* __restrict__ partial,
-                                                   int* __restrict__ counters, Epi epi) {
+// Fragments of one 64-wide K step: per lane 16 consecutive K elements of its
+// rows (A) and of its two weight rows (B).  The K loop double-buffers them in
+// registers so the next step's weight loads are in flight during the MFMAs.
+template <typename T, int MB, class ASrc> struct Step64 {
+  Frag<T> a0[MB], a1[MB], b0[2], b1[2];
+  __device__ __forceinline__ void load(const ASrc& asrc, const typename ASrc::template State<MB>& as,
+                                       const T* const* bp, int kk) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      load_frag(b0[nb], bp[nb] + kk);
+      load_frag(b1[nb], bp[nb] + kk + 8);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      asrc.template load<MB>(a0[mb], as, mb, kk);
+      asrc.template load<MB>(a1[mb], as, mb, kk + 8);
+    }
+  }
+  __device__ __forceinline__ void mma_into(f32x4 (&acc)[MB][2]) const {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        mma(acc[mb][nb], a0[mb], b0[nb]);
+        mma(acc[mb][nb], a1[mb], b1[nb]);
+      }
+  }
+};
+
+template <typename T, int MB, class ASrc, class Epi>
+__global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int KS, int Kc,
+                                                   int m_tiles, float* __restrict__ partial,
+                                                   Epi epi) {
   __shared__ float tile[16 * MB * LDT];
-  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bid = blockIdx.x;
   const int ks = bid % KS;
@@ -74,9 +170,8 @@ __global__ __launch_bounds__(256) void gemm_stream(const T* __restrict__ A, int6
   const T* bp[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) bp[nb] = epi.brow(nt, wave * 32 + nb * 16 + r16);
-  const T* ap[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) ap[mb] = A + (int64_t)imin(m0 + mb * 16 + r16, M - 1) * lda;
+  typename ASrc::template State<MB> as;
+  asrc.template setup<MB>(as, m0, M, r16);
 
   f32x4 acc[MB][2];
 #pragma unroll
@@ -85,29 +180,7 @@ __global__ __launch_bounds__(256) void gemm_stream(const T* __restrict__ A, int6
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int k = k0;
-  // 64-wide steps: each lane reads 16 consecutive K elements per row (lanes
-  // with the same l % 16 cover one contiguous 64-element span of that row).
-  for (; k + 64 <= k1; k += 64) {
-    const int kk = k + g4 * 16;
-    Frag<T> b0[2], b1[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      load_frag(b0[nb], bp[nb] + kk);
-      load_frag(b1[nb], bp[nb] + kk + 8);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      Frag<T> a0, a1;
-      load_frag(a0, ap[mb] + kk);
-      load_frag(a1, ap[mb] + kk + 8);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        mma(acc[mb][nb], a0, b0[nb]);
-        mma(acc[mb][nb], a1, b1[nb]);
-      }
-    }
-  }
-  if (k < k1) {  // 32-wide tail
+  if ((k1 - k0) & 32) {  // a 32-wide step first when the range is not a multiple of 64
     const int kk = k + g4 * 8;
     Frag<T> b0[2];
 #pragma unroll
@@ -115,10 +188,26 @@ __global__ __launch_bounds__(256) void gemm_stream(const T* __restrict__ A, int6
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       Frag<T> a0;
-      load_frag(a0, ap[mb] + kk);
+      asrc.template load<MB>(a0, as, mb, kk);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) mma(acc[mb][nb], a0, b0[nb]);
     }
+    k += 32;
+  }
+  // 64-wide steps: each lane reads 16 consecutive K elements per row (lanes
+  // with the same l % 16 cover one contiguous 64-element span of that row).
+  const int n64 = (k1 - k) / 64;
+  if (n64 > 0) {
+    Step64<T, MB, ASrc> s0, s1;
+    s0.load(asrc, as, bp, k + g4 * 16);
+    int i = 0;
+    for (; i + 2 <= n64; i += 2) {
+      s1.load(asrc, as, bp, k + (i + 1) * 64 + g4 * 16);
+      s0.mma_into(acc);
+      if (i + 2 < n64) s0.load(asrc, as, bp, k + (i + 2) * 64 + g4 * 16);
+      s1.mma_into(acc);
+    }
+    if (i < n64) s0.mma_into(acc);
   }
 
   if (KS == 1) {
@@ -133,11 +222,10 @@ __global__ __launch_bounds__(256) void gemm_stream(const T* __restrict__ A, int6
     epi.apply(tile, 16 * MB, m0, M, nt, tid);
     return;
   }
-
+  // Split K: store this split's partial tile; gemm_splitk_reduce sums the
+  // splits in a fixed order in the next kernel and runs the epilogue.
   const int tile_elems = 16 * MB * BN;
-  const int tix = nt * m_tiles + mt;
-  float* base = partial + (int64_t)tix * KS * tile_elems;
-  float* mine = base + (int64_t)ks * tile_elems;
+  float* mine = partial + ((int64_t)(nt * m_tiles + mt) * KS + ks) * tile_elems;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -145,61 +233,123 @@ __global__ __launch_bounds__(256) void gemm_stream(const T* __restrict__ A, int6
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         mine[(mb * 16 + g4 * 4 + i) * BN + wave * 32 + nb * 16 + r16] = acc[mb][nb][i];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counters[tix], 1) == KS - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int idx = tid; idx < tile_elems; idx += 256) {
-    float s = 0.f;
-    for (int q = 0; q < KS; ++q) s += __builtin_nontemporal_load(base + (int64_t)q * tile_elems + idx);
-    tile[(idx / BN) * LDT + idx % BN] = s;
+}
+
+// Split-K reduction: one workgroup per 4 rows of a tile.  Thread t sums the
+// splits q = t/128, t/128 + 2, ... of one float4 column (all loads issued before
+// the adds); the two halves are then added in a fixed order, so the result
+// does not depend on timing.
+constexpr int RROWS = 4;
+template <int MB, class Epi>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, int M,
+                                                          const float* __restrict__ partial,
+                                                          Epi epi) {
+  __shared__ float tile[RROWS * LDT];
+  __shared__ float4 half1[RROWS * BN / 4];
+  const int tid = threadIdx.x;
+  constexpr int RB = 16 * MB / RROWS;  // row blocks per tile
+  const int tix = blockIdx.x / RB, rb = blockIdx.x % RB;
+  const int mt = tix % m_tiles, nt = tix / m_tiles;
+  const int tile_elems = 16 * MB * BN;
+  const int i4 = tid & 127, h = tid >> 7;
+  const int row = i4 / (BN / 4), c = (i4 % (BN / 4)) * 4;
+  const float* p = partial + (int64_t)tix * KS * tile_elems + (int64_t)(rb * RROWS + row) * BN + c;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int q = h; q < KS; q += 2) {
+    const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)q * tile_elems);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
   }
-  if (tid == 0) counters[tix] = 0;
+  if (h == 1) half1[i4] = s;
   __syncthreads();
-  epi.apply(tile, 16 * MB, m0, M, nt, tid);
+  if (h == 0) {
+    const float4 o = half1[i4];
+    float* t = tile + row * LDT + c;
+    t[0] = s.x + o.x;
+    t[1] = s.y + o.y;
+    t[2] = s.z + o.z;
+    t[3] = s.w + o.w;
+  }
+  __syncthreads();
+  epi.apply(tile, RROWS, mt * 16 * MB + rb * RROWS, M, nt, tid);
 }
 
 // ---------------------------------------------------------------- epilogues
+// Row-wise pass over a [rows, 128] fp32 tile (one wave per row, two columns per
+// lane); f returns the value stored for (row, col), whose squares are summed
+// into the row's partial sum of squares over the tile when ss != null.
+template <typename T, typename F>
+__device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N, int tid,
+                                         float* ss, int n_ss, const NextNorm<T>& nn, F&& f) {
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int r = wave; r < rows; r += 4) {
+    const int m = m0 + r;
+    if (m >= M) continue;
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + 64 * h, n = nt * BN + c;
+      if (n < N) {
+        const float v = f(r, c, m, n);
+        acc += v * v;
+        if (nn.xg != nullptr)
+          nn.xg[(int64_t)m * N + n] = Num<T>::from_f(v * Num<T>::to_f(nn.g[n]));
+      }
+    }
+    if (ss != nullptr) {
+      acc = wave_sum(acc);
+      if (lane == 0) ss[(int64_t)m * n_ss + nt] = acc;
+    }
+  }
+}
+
 template <typename T> struct EpiStoreF32 {
-  const T* W; int N; int K; float* out; int ldo;
+  const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn;
   __device__ const T* brow(int nt, int c) const {
     return W + (int64_t)imin(nt * BN + c, N - 1) * K;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    for (int idx = tid; idx < rows * BN; idx += 256) {
-      const int r = idx / BN, c = idx % BN, m = m0 + r, n = nt * BN + c;
-      if (m < M && n < N) out[(int64_t)m * ldo + n] = t[r * LDT + c];
-    }
+    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int r, int c, int m, int n) {
+      const float v = t[r * LDT + c];
+      if (out != nullptr) out[(int64_t)m * ldo + n] = v;
+      return v;
+    });
   }
 };
 
 template <typename T> struct EpiResidual {
-  const T* W; int N; int K; float* x;
+  const T* W; int N; int K; float* x; float* ss; NextNorm<T> nn;
   __device__ const T* brow(int nt, int c) const {
     return W + (int64_t)imin(nt * BN + c, N - 1) * K;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    for (int idx = tid; idx < rows * BN; idx += 256) {
-      const int r = idx / BN, c = idx % BN, m = m0 + r, n = nt * BN + c;
-      if (m < M && n < N) x[(int64_t)m * N + n] += t[r * LDT + c];
-    }
+    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int r, int c, int m, int n) {
+      float* p = x + (int64_t)m * N + n;
+      const float v = *p + t[r * LDT + c];
+      *p = v;
+      return v;
+    });
   }
 };
 
 // Tile columns 0..63 are gate rows nt*64.., columns 64..127 the matching up rows.
 template <typename T> struct EpiSiluMul {
-  const T* Wg; const T* Wu; int I; int K; T* act;
+  const T* Wg; const T* Wu; int I; int K; T* act; RowScale rs;
   __device__ const T* brow(int nt, int c) const {
     const int n = imin(nt * 64 + (c & 63), I - 1);
     return (c < 64 ? Wg : Wu) + (int64_t)n * K;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
+    __shared__ float srs[64];
+    rs.fill(srs, rows, m0, M, tid);
     for (int idx = tid; idx < rows * 64; idx += 256) {
       const int r = idx / 64, c = idx % 64, m = m0 + r, n = nt * 64 + c;
       if (m < M && n < I) {
-        const float g = t[r * LDT + c], u = t[r * LDT + 64 + c];
+        const float sc = srs[r];
+        const float g = t[r * LDT + c] * sc, u = t[r * LDT + 64 + c] * sc;
         act[(int64_t)m * I + n] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
       }
     }
@@ -222,35 +372,49 @@ __device__ __forceinline__ void norm_rope_pair(float x0, float x1, int i, int D,
   o1 = y1 * c.x + y0 * c.y;
 }
 
+// q -> [M, nq, D]; the block's k and v -> one 16-key "page" per (request, kv
+// head) in the attention kernel's cache layout: kblk [B][nkv][16][D] and
+// vblk [B][nkv][D][16] (V transposed), block row j = m % S of request m / S.
 template <typename T> struct EpiQKV {
   const T* W; int H; int nq, nkv, D; const T* qn; const T* kn; float eps;
-  const float2* cs; T* q; T* k; T* v;
+  const float2* cs; T* q; T* k; T* v; RowScale rs; int S;
   __device__ const T* brow(int nt, int c) const {
     return W + (int64_t)imin(nt * BN + c, (nq + 2 * nkv) * D - 1) * H;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
+    __shared__ float srs[64];
+    rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
     for (int item = wave; item < rows * HP; item += 4) {
       const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
       if (m >= M || gh >= nq + 2 * nkv) continue;
       const bool act = lane < half;
-      const float x0 = act ? t[r * LDT + hh * D + lane] : 0.f;
-      const float x1 = act ? t[r * LDT + hh * D + lane + half] : 0.f;
+      const float sc = srs[r];
+      const float x0 = act ? t[r * LDT + hh * D + lane] * sc : 0.f;
+      const float x1 = act ? t[r * LDT + hh * D + lane + half] * sc : 0.f;
       float o0 = x0, o1 = x1;
-      T* dst;
+      const int rq = m / S, j = m % S;
       if (gh < nq) {
         norm_rope_pair<T>(x0, x1, lane, D, act, qn, eps, cs + (int64_t)m * half, o0, o1);
-        dst = q + ((int64_t)m * nq + gh) * D;
+        T* dst = q + ((int64_t)m * nq + gh) * D;
+        if (act) {
+          dst[lane] = Num<T>::from_f(o0);
+          dst[lane + half] = Num<T>::from_f(o1);
+        }
       } else if (gh < nq + nkv) {
         norm_rope_pair<T>(x0, x1, lane, D, act, kn, eps, cs + (int64_t)m * half, o0, o1);
-        dst = k + ((int64_t)m * nkv + (gh - nq)) * D;
+        T* dst = k + (((int64_t)rq * nkv + (gh - nq)) * 16 + j) * D;
+        if (act) {
+          dst[lane] = Num<T>::from_f(o0);
+          dst[lane + half] = Num<T>::from_f(o1);
+        }
       } else {
-        dst = v + ((int64_t)m * nkv + (gh - nq - nkv)) * D;
-      }
-      if (act) {
-        dst[lane] = Num<T>::from_f(o0);
-        dst[lane + half] = Num<T>::from_f(o1);
+        T* dst = v + ((int64_t)rq * nkv + (gh - nq - nkv)) * D * 16 + j;
+        if (act) {
+          dst[(int64_t)lane * 16] = Num<T>::from_f(o0);
+          dst[(int64_t)(lane + half) * 16] = Num<T>::from_f(o1);
+        }
       }
     }
   }
@@ -260,7 +424,7 @@ template <typename T> struct EpiQKV {
 // k rows and v rows of that layer's w_qkv (which start after the nq*D q rows).
 template <typename T, typename KT> struct EpiKVInject {
   KVTargets tg; int H; int n_layers, nq, nkv, D; float eps; const float2* cs;
-  const int32_t* slots; const int32_t* valid; int rpr; int P; int64_t num_slots;
+  const int32_t* slots; const int32_t* valid; int rpr; int P; int64_t num_slots; RowScale rs;
   __device__ const T* brow(int nt, int c) const {
     const int per = 2 * nkv * D;
     const int n = imin(nt * BN + c, n_layers * per - 1);
@@ -268,27 +432,35 @@ template <typename T, typename KT> struct EpiKVInject {
     return static_cast<const T*>(tg.w_qkv[l]) + (int64_t)(nq * D + w) * H;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
+    __shared__ float srs[64];
+    rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
     for (int item = wave; item < rows * HP; item += 4) {
       const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
       if (m >= M || gh >= n_layers * 2 * nkv) continue;
       if (valid != nullptr && (m % rpr) >= valid[m / rpr]) continue;
+      const int64_t slot = slots[m];
+      if (slot < 0 || slot >= num_slots) continue;  // outside the pool: never written
       const int l = gh / (2 * nkv), rem = gh % (2 * nkv);
       const bool is_v = rem >= nkv;
       const int head = rem % nkv;
       const bool act = lane < half;
-      const float x0 = act ? t[r * LDT + hh * D + lane] : 0.f;
-      const float x1 = act ? t[r * LDT + hh * D + lane + half] : 0.f;
+      const float sc = srs[r];
+      const float x0 = act ? t[r * LDT + hh * D + lane] * sc : 0.f;
+      const float x1 = act ? t[r * LDT + hh * D + lane + half] * sc : 0.f;
       float o0 = x0, o1 = x1;
       if (!is_v)
         norm_rope_pair<T>(x0, x1, lane, D, act, static_cast<const T*>(tg.k_norm[l]), eps,
                           cs + (int64_t)m * half, o0, o1);
-      const int64_t slot = slots[m];
-      if (slot < 0 || slot >= num_slots) continue;  // outside the pool: never written
       const int64_t page = slot / P, off = slot % P;
-      KT* dst = static_cast<KT*>(is_v ? tg.vc[l] : tg.kc[l]) + ((page * nkv + head) * P + off) * D;
-      if (act) {
+      if (!act) continue;
+      if (is_v) {  // V pages are stored transposed: [page][head][D][P]
+        KT* dst = static_cast<KT*>(tg.vc[l]) + ((page * nkv + head) * D) * P + off;
+        dst[(int64_t)lane * P] = Num<KT>::from_f(o0);
+        dst[(int64_t)(lane + half) * P] = Num<KT>::from_f(o1);
+      } else {     // K pages: [page][head][P][D]
+        KT* dst = static_cast<KT*>(tg.kc[l]) + ((page * nkv + head) * P + off) * D;
         dst[lane] = Num<KT>::from_f(o0);
         dst[lane + half] = Num<KT>::from_f(o1);
       }
@@ -299,22 +471,25 @@ template <typename T, typename KT> struct EpiKVInject {
 // Logits of a 128-wide vocabulary slice: rounded to T (and stored when asked),
 // then the (max, first index) of every row over the slice.
 template <typename T> struct EpiLogits {
-  const T* W; int V; int H; T* logits; float2* part; int n_tiles;
+  const T* W; int V; int H; T* logits; float2* part; int n_tiles; RowScale rs;
   __device__ const T* brow(int nt, int c) const {
     return W + (int64_t)imin(nt * BN + c, V - 1) * H;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
+    __shared__ float srs[64];
+    rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     for (int r = wave; r < rows; r += 4) {
       const int m = m0 + r;
       if (m >= M) continue;
       float best = -INFINITY;
       int bi = 0x7fffffff;
+      const float sc = srs[r];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = lane + 64 * h, n = nt * BN + c;
         if (n < V) {
-          const T tv = Num<T>::from_f(t[r * LDT + c]);
+          const T tv = Num<T>::from_f(t[r * LDT + c] * sc);
           if (logits != nullptr) logits[(int64_t)m * V + n] = tv;
           float v = Num<T>::to_f(tv);
           if (!(v == v)) v = -INFINITY;
@@ -339,78 +514,95 @@ template <typename T> struct EpiLogits {
 };
 
 // ---------------------------------------------------------------- launchers
-template <typename T, class Epi>
-static hipError_t run_gemm(const T* A, int64_t lda, int M, int K, int Ncols, const Epi& epi,
+template <typename T, int MB, class AS, class Epi>
+static void launch_mb(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
+                      float* partial, hipStream_t st) {
+  const dim3 grid((unsigned)(p.n_tiles * p.m_tiles * p.KS));
+  hipLaunchKernelGGL((gemm_stream<T, MB, AS, Epi>), grid, dim3(256), 0, st, asrc, M, K, p.KS,
+                     p.Kc, p.m_tiles, partial, epi);
+  if (p.KS > 1)
+    hipLaunchKernelGGL((gemm_splitk_reduce<MB, Epi>),
+                       dim3((unsigned)(p.n_tiles * p.m_tiles * (16 * MB / RROWS))), dim3(256), 0,
+                       st, p.KS, p.m_tiles, M, (const float*)partial, epi);
+}
+
+template <typename T, class AS, class Epi>
+static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& epi,
                            const GemmScratch& ws, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const GemmPlan p = plan_gemm(M, Ncols, K);
-  if (p.KS > 1 && (gemm_partial_floats(p) > ws.partial_floats ||
-                   p.n_tiles * p.m_tiles > ws.n_counters))
-    return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(p.n_tiles * p.m_tiles * p.KS));
+  if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
   switch (p.MB) {
-    case 1:
-      hipLaunchKernelGGL((gemm_stream<T, 1, Epi>), grid, dim3(256), 0, st, A, lda, M, K, p.KS,
-                         p.Kc, p.m_tiles, ws.partial, ws.counters, epi);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm_stream<T, 2, Epi>), grid, dim3(256), 0, st, A, lda, M, K, p.KS,
-                         p.Kc, p.m_tiles, ws.partial, ws.counters, epi);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_stream<T, 4, Epi>), grid, dim3(256), 0, st, A, lda, M, K, p.KS,
-                         p.Kc, p.m_tiles, ws.partial, ws.counters, epi);
-      break;
+    case 1: launch_mb<T, 1>(asrc, M, K, p, epi, ws.partial, st); break;
+    case 2: launch_mb<T, 2>(asrc, M, K, p, epi, ws.partial, st); break;
+    default: launch_mb<T, 4>(asrc, M, K, p, epi, ws.partial, st); break;
   }
   return hipGetLastError();
 }
 
-hipError_t gemm_store_f32(int dt, const void* A, int64_t lda, int M, int K, const void* W, int N,
-                          float* out, const GemmScratch& ws, hipStream_t st) {
-  if (dt == DFLASH_BF16) {
-    EpiStoreF32<bf16_t> e{(const bf16_t*)W, N, K, out, N};
-    return run_gemm((const bf16_t*)A, lda, M, K, N, e, ws, st);
-  }
-  EpiStoreF32<float> e{(const float*)W, N, K, out, N};
-  return run_gemm((const float*)A, lda, M, K, N, e, ws, st);
+template <typename T, class Epi>
+static hipError_t run_any(const ASrc& a, int M, int K, int Ncols, const Epi& epi,
+                          const GemmScratch& ws, hipStream_t st) {
+  const ASrcPlain<T> s{static_cast<const T*>(a.a), a.lda, a.S_skip};
+  return run_gemm<T>(s, M, K, Ncols, epi, ws, st);
 }
 
-hipError_t gemm_residual(int dt, const void* A, int M, int K, const void* W, int N, float* x,
-                         const GemmScratch& ws, hipStream_t st) {
-  if (dt == DFLASH_BF16) {
-    EpiResidual<bf16_t> e{(const bf16_t*)W, N, K, x};
-    return run_gemm((const bf16_t*)A, K, M, K, N, e, ws, st);
-  }
-  EpiResidual<float> e{(const float*)W, N, K, x};
-  return run_gemm((const float*)A, K, M, K, N, e, ws, st);
+static RowScale row_scale(const ASrc& a) {
+  return RowScale{a.ss, a.n_ss, a.H, a.eps, a.S_skip};
 }
 
-hipError_t gemm_silu_mul(int dt, const void* A, int M, int K, const void* Wg, const void* Wu,
+hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, int N, float* out,
+                          float* ss, void* xg, const void* g_next, const GemmScratch& ws,
+                          hipStream_t st) {
+  if (dt == DFLASH_BF16) {
+    EpiStoreF32<bf16_t> e{(const bf16_t*)W, N, K, out, N, ss,
+                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next}};
+    return run_any<bf16_t>(a, M, K, N, e, ws, st);
+  }
+  EpiStoreF32<float> e{(const float*)W, N, K, out, N, ss,
+                       NextNorm<float>{(float*)xg, (const float*)g_next}};
+  return run_any<float>(a, M, K, N, e, ws, st);
+}
+
+hipError_t gemm_residual(int dt, const ASrc& a, int M, int K, const void* W, int N, float* x,
+                         float* ss, void* xg, const void* g_next, const GemmScratch& ws,
+                         hipStream_t st) {
+  if (dt == DFLASH_BF16) {
+    EpiResidual<bf16_t> e{(const bf16_t*)W, N, K, x, ss,
+                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next}};
+    return run_any<bf16_t>(a, M, K, N, e, ws, st);
+  }
+  EpiResidual<float> e{(const float*)W, N, K, x, ss,
+                       NextNorm<float>{(float*)xg, (const float*)g_next}};
+  return run_any<float>(a, M, K, N, e, ws, st);
+}
+
+hipError_t gemm_silu_mul(int dt, const ASrc& a, int M, int K, const void* Wg, const void* Wu,
                          int I, void* act, const GemmScratch& ws, hipStream_t st) {
   const int ncols = ((I + 63) / 64) * BN;
   if (dt == DFLASH_BF16) {
-    EpiSiluMul<bf16_t> e{(const bf16_t*)Wg, (const bf16_t*)Wu, I, K, (bf16_t*)act};
-    return run_gemm((const bf16_t*)A, K, M, K, ncols, e, ws, st);
+    EpiSiluMul<bf16_t> e{(const bf16_t*)Wg, (const bf16_t*)Wu, I, K, (bf16_t*)act, row_scale(a)};
+    return run_any<bf16_t>(a, M, K, ncols, e, ws, st);
   }
-  EpiSiluMul<float> e{(const float*)Wg, (const float*)Wu, I, K, (float*)act};
-  return run_gemm((const float*)A, K, M, K, ncols, e, ws, st);
+  EpiSiluMul<float> e{(const float*)Wg, (const float*)Wu, I, K, (float*)act, row_scale(a)};
+  return run_any<float>(a, M, K, ncols, e, ws, st);
 }
 
-hipError_t gemm_qkv(int dt, const void* A, int M, int H, const void* Wqkv, const void* qn,
+hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const void* qn,
                     const void* kn, int nq, int nkv, int D, float eps, const float2* cs, void* q,
-                    void* k, void* v, const GemmScratch& ws, hipStream_t st) {
+                    void* k, void* v, int S, const GemmScratch& ws, hipStream_t st) {
   const int ncols = (nq + 2 * nkv) * D;
   if (dt == DFLASH_BF16) {
     EpiQKV<bf16_t> e{(const bf16_t*)Wqkv, H, nq, nkv, D, (const bf16_t*)qn, (const bf16_t*)kn,
-                     eps, cs, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v};
-    return run_gemm((const bf16_t*)A, H, M, H, ncols, e, ws, st);
+                     eps, cs, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, row_scale(a), S};
+    return run_any<bf16_t>(a, M, H, ncols, e, ws, st);
   }
   EpiQKV<float> e{(const float*)Wqkv, H, nq, nkv, D, (const float*)qn, (const float*)kn, eps, cs,
-                  (float*)q, (float*)k, (float*)v};
-  return run_gemm((const float*)A, H, M, H, ncols, e, ws, st);
+                  (float*)q, (float*)k, (float*)v, row_scale(a), S};
+  return run_any<float>(a, M, H, ncols, e, ws, st);
 }
 
-hipError_t gemm_kv_inject(int dt, int kv_dt, const void* A, int M, int H, const KVTargets& t,
+hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
                           const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
                           int page_size, int64_t num_pages, const GemmScratch& ws,
@@ -418,30 +610,29 @@ hipError_t gemm_kv_inject(int dt, int kv_dt, const void* A, int M, int H, const 
   const int64_t ns = num_pages * page_size;
   const int ncols = n_layers * 2 * nkv * D;
   if (dt == DFLASH_BF16) {
-    const bf16_t* a = (const bf16_t*)A;
     if (kv_dt == DFLASH_FP8_E4M3) {
       EpiKVInject<bf16_t, fp8_t> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,
-                                   rows_per_req, page_size, ns};
-      return run_gemm(a, H, M, H, ncols, e, ws, st);
+                                   rows_per_req, page_size, ns, row_scale(a)};
+      return run_any<bf16_t>(a, M, H, ncols, e, ws, st);
     }
     EpiKVInject<bf16_t, bf16_t> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,
-                                  rows_per_req, page_size, ns};
-    return run_gemm(a, H, M, H, ncols, e, ws, st);
+                                  rows_per_req, page_size, ns, row_scale(a)};
+    return run_any<bf16_t>(a, M, H, ncols, e, ws, st);
   }
   EpiKVInject<float, float> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,
-                              rows_per_req, page_size, ns};
-  return run_gemm((const float*)A, H, M, H, ncols, e, ws, st);
+                              rows_per_req, page_size, ns, row_scale(a)};
+  return run_any<float>(a, M, H, ncols, e, ws, st);
 }
 
-hipError_t gemm_logits(int dt, const void* A, int M, int H, const void* Wlm, int V, void* logits,
+hipError_t gemm_logits(int dt, const ASrc& a, int M, int H, const void* Wlm, int V, void* logits,
                        float2* part, const GemmScratch& ws, hipStream_t st) {
   const int nt = logits_tiles(V);
   if (dt == DFLASH_BF16) {
-    EpiLogits<bf16_t> e{(const bf16_t*)Wlm, V, H, (bf16_t*)logits, part, nt};
-    return run_gemm((const bf16_t*)A, H, M, H, V, e, ws, st);
+    EpiLogits<bf16_t> e{(const bf16_t*)Wlm, V, H, (bf16_t*)logits, part, nt, row_scale(a)};
+    return run_any<bf16_t>(a, M, H, V, e, ws, st);
   }
-  EpiLogits<float> e{(const float*)Wlm, V, H, (float*)logits, part, nt};
-  return run_gemm((const float*)A, H, M, H, V, e, ws, st);
+  EpiLogits<float> e{(const float*)Wlm, V, H, (float*)logits, part, nt, row_scale(a)};
+  return run_any<float>(a, M, H, V, e, ws, st);
 }
 
 }  // namespace dflash

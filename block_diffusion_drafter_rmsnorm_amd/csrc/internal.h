@@ -8,14 +8,11 @@
 
 namespace dflash {
 
-// Split-K scratch of the weight-streaming GEMM: fp32 partial tiles plus one
-// arrival counter per output tile (counters are zero between launches: the
-// last arriving workgroup of a tile resets its counter).
+// Split-K scratch of the weight-streaming GEMM: fp32 partial tiles, summed in
+// a fixed order by a second kernel that runs the epilogue.
 struct GemmScratch {
   float* partial;
   size_t partial_floats;
-  int* counters;
-  int n_counters;
 };
 
 // Launch geometry of the weight-streaming GEMM C[M, Ncols] = A[M, K] W^T.
@@ -36,43 +33,68 @@ struct KVTargets {
   void* vc[DFLASH_MAX_LAYERS];
 };
 
-// fc: out[M, N] (fp32) = A[M, K] W[N, K]^T
-hipError_t gemm_store_f32(int dt, const void* A, int64_t lda, int M, int K, const void* W, int N,
-                          float* out, const GemmScratch& ws, hipStream_t st);
-// x[M, N] += A[M, K] W[N, K]^T   (x fp32, ld N)
-hipError_t gemm_residual(int dt, const void* A, int M, int K, const void* W, int N, float* x,
-                         const GemmScratch& ws, hipStream_t st);
+// A operand of a GEMM: rows of T with row stride lda.  S_skip > 0 maps GEMM row
+// m to A row (m / (S-1)) * S + m % (S-1) + 1.  When ss != null the A rows are
+// x * g of an RMSNorm and each output row is scaled by 1/rms(x), from the sums
+// of squares ss[row * n_ss + t] of columns [128 t, 128 t + 128) of x (width H).
+struct ASrc {
+  const void* a;
+  int64_t lda;
+  const float* ss;
+  int n_ss;
+  int H;
+  float eps;
+  int S_skip;
+};
+inline ASrc asrc_plain(const void* a, int64_t lda, int S_skip = 0) {
+  return ASrc{a, lda, nullptr, 0, 0, 0.f, S_skip};
+}
+inline ASrc asrc_normed(const void* xg, int H, const float* ss, float eps, int S_skip = 0) {
+  return ASrc{xg, H, ss, (H + 127) / 128, H, eps, S_skip};
+}
+// 128-column tiles of a row (the granularity of the row sums of squares)
+__host__ __device__ inline int ss_tiles(int H) { return (H + 127) / 128; }
+
+// y = A W^T: out[M, N] fp32 (nullable), per-128-column row sums of squares of y
+// into ss (nullable) and xg = y * g_next rounded to the act dtype (nullable)
+hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, int N, float* out,
+                          float* ss, void* xg, const void* g_next, const GemmScratch& ws,
+                          hipStream_t st);
+// x[M, N] += A W^T (x fp32, ld N), then ss / xg of the new x as above
+hipError_t gemm_residual(int dt, const ASrc& a, int M, int K, const void* W, int N, float* x,
+                         float* ss, void* xg, const void* g_next, const GemmScratch& ws,
+                         hipStream_t st);
 // act[M, I] = silu(A Wg^T) * (A Wu^T)
-hipError_t gemm_silu_mul(int dt, const void* A, int M, int K, const void* Wg, const void* Wu,
+hipError_t gemm_silu_mul(int dt, const ASrc& a, int M, int K, const void* Wg, const void* Wu,
                          int I, void* act, const GemmScratch& ws, hipStream_t st);
-// q/k/v of the block rows with per-head RMSNorm + RoPE on q and k
-hipError_t gemm_qkv(int dt, const void* A, int M, int H, const void* Wqkv, const void* qn,
-                    const void* kn, int nq, int nkv, int D, float eps, const float2* cs,
-                    void* q, void* k, void* v, const GemmScratch& ws, hipStream_t st);
+// q/k/v of the block rows with per-head RMSNorm + RoPE on q and k; q -> [M, nq, D],
+// k -> kblk [B][nkv][16][D], v -> vblk [B][nkv][D][16] (block row j = m % S)
+hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const void* qn,
+                    const void* kn, int nq, int nkv, int D, float eps, const float2* cs, void* q,
+                    void* kblk, void* vblk, int S, const GemmScratch& ws, hipStream_t st);
 // stacked K/V of all layers for context rows -> paged cache
-hipError_t gemm_kv_inject(int dt, int kv_dt, const void* A, int M, int H, const KVTargets& t,
+hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
                           const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
                           int page_size, int64_t num_pages, const GemmScratch& ws,
                           hipStream_t st);
 // logits[M, V] (nullable) and per-tile argmax partials (value, index) [M, n_tiles]
-hipError_t gemm_logits(int dt, const void* A, int M, int H, const void* Wlm, int V, void* logits,
+hipError_t gemm_logits(int dt, const ASrc& a, int M, int H, const void* Wlm, int V, void* logits,
                        float2* part, const GemmScratch& ws, hipStream_t st);
 int logits_tiles(int V);
 
 // ---- elementwise / small kernels
-hipError_t launch_zero_i32(int* p, int n, hipStream_t st);
+// block ids / positions / slots, the embedding rows into x (fp32) with their
+// sums of squares (ss[row * n_ss] = total, the other n_ss - 1 entries zero),
+// xg = x * g_first rounded to the act dtype, and the RoPE table of the block rows
 hipError_t launch_block_prep(int dt, const dflash_config& c, const void* embed,
                              const int32_t* anchor, const int32_t* prefix_len,
                              const int32_t* page_table, int max_pages, int B, int32_t* block_ids,
                              int32_t* positions, int32_t* slots, int32_t* candidates, float* x,
-                             float2* cs, hipStream_t st);
+                             float* ss, int n_ss, void* xg, const void* g_first, float2* cs,
+                             hipStream_t st);
 hipError_t launch_rope_table(const int32_t* positions, int rows, int D, float theta, float2* cs,
                              hipStream_t st);
-// out[m] = rms(in[src(m)]) * g; src(m) = m when S == 0, else the block row
-// m / (S-1) * S + m % (S-1) + 1 (rows 1..S-1 of every block).
-hipError_t launch_rmsnorm(int dt, const float* in, int M, int H, const void* g, float eps,
-                          void* out, int S_skip_anchor, hipStream_t st);
 hipError_t launch_argmax_reduce(const float2* part, int M, int n_tiles, int S, int32_t* candidates,
                                 hipStream_t st);
 hipError_t launch_accept(const int32_t* cand, const int32_t* post, const int32_t* prefix_len, int B,
@@ -85,7 +107,8 @@ struct AttnPlan {
   int n_splits;   // grid splits per (request, kv head)
 };
 AttnPlan plan_attention(int max_keys, int B, int nkv);
-hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void* kb, const void* vb,
+hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void* kblk,
+                            const void* vblk,
                             const void* kc, const void* vc, const int32_t* page_table,
                             int max_pages, int64_t num_pages, const int32_t* prefix_len,
                             int max_prefix, int B,

@@ -6,17 +6,6 @@
 
 namespace dflash {
 
-__global__ void zero_i32_kernel(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
-
-hipError_t launch_zero_i32(int* p, int n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
-  return hipGetLastError();
-}
-
 // (cos, sin) of pos * theta^(-2i/D), angle formed and reduced in fp64.
 __device__ __forceinline__ float2 rope_cs(int pos, int i, int D, double log_theta) {
   const double inv = exp(-(2.0 * (double)i / (double)D) * log_theta);
@@ -44,13 +33,16 @@ hipError_t launch_rope_table(const int32_t* positions, int rows, int D, float th
 }
 
 // One workgroup per block row (r, j): ids / positions / slots, embedding
-// gather into the fp32 residual stream and the row's RoPE table.
+// gather into the fp32 residual stream with the row's sum of squares (for the
+// first layer's input RMSNorm) and the row's RoPE table.
 template <typename T>
 __global__ __launch_bounds__(256) void block_prep_kernel(
     const T* __restrict__ embed, int V, int H, int S, int mask_id, int P, int D,
     double log_theta, const int32_t* __restrict__ anchor, const int32_t* __restrict__ prefix_len,
     const int32_t* __restrict__ pt, int max_pages, int32_t* block_ids, int32_t* positions,
-    int32_t* slots, int32_t* candidates, float* __restrict__ x, float2* __restrict__ cs) {
+    int32_t* slots, int32_t* candidates, float* __restrict__ x, float* __restrict__ ss, int n_ss,
+    T* __restrict__ xg, const T* __restrict__ g_first, float2* __restrict__ cs) {
+  __shared__ float red[4];
   const int row = blockIdx.x, r = row / S, j = row % S, tid = threadIdx.x;
   int id = (j == 0) ? anchor[r] : mask_id;
   id = imin(imax(id, 0), V - 1);
@@ -63,61 +55,39 @@ __global__ __launch_bounds__(256) void block_prep_kernel(
     if (j == 0) candidates[(int64_t)r * S] = anchor[r];
   }
   const T* e = embed + (int64_t)id * H;
-  for (int c = tid; c < H; c += 256) x[(int64_t)row * H + c] = Num<T>::to_f(e[c]);
+  float acc = 0.f;
+  for (int c = tid; c < H; c += 256) {
+    const float v = Num<T>::to_f(e[c]);
+    x[(int64_t)row * H + c] = v;
+    xg[(int64_t)row * H + c] = Num<T>::from_f(v * Num<T>::to_f(g_first[c]));
+    acc += v * v;
+  }
   for (int i = tid; i < D / 2; i += 256) cs[(int64_t)row * (D / 2) + i] = rope_cs(pos, i, D, log_theta);
+  acc = wave_sum(acc);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  for (int t = tid; t < n_ss; t += 256)
+    ss[(int64_t)row * n_ss + t] = (t == 0) ? (red[0] + red[1]) + (red[2] + red[3]) : 0.f;
 }
 
 hipError_t launch_block_prep(int dt, const dflash_config& c, const void* embed,
                              const int32_t* anchor, const int32_t* prefix_len,
                              const int32_t* page_table, int max_pages, int B, int32_t* block_ids,
                              int32_t* positions, int32_t* slots, int32_t* candidates, float* x,
-                             float2* cs, hipStream_t st) {
+                             float* ss, int n_ss, void* xg, const void* g_first, float2* cs,
+                             hipStream_t st) {
   const dim3 grid((unsigned)(B * c.block_size));
   const double lt = log((double)c.rope_theta);
   if (dt == DFLASH_BF16)
     hipLaunchKernelGGL(block_prep_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)embed,
                        c.vocab, c.hidden, c.block_size, c.mask_token_id, c.page_size, c.head_dim,
                        lt, anchor, prefix_len, page_table, max_pages, block_ids, positions, slots,
-                       candidates, x, cs);
+                       candidates, x, ss, n_ss, (bf16_t*)xg, (const bf16_t*)g_first, cs);
   else
     hipLaunchKernelGGL(block_prep_kernel<float>, grid, dim3(256), 0, st, (const float*)embed,
                        c.vocab, c.hidden, c.block_size, c.mask_token_id, c.page_size, c.head_dim,
                        lt, anchor, prefix_len, page_table, max_pages, block_ids, positions, slots,
-                       candidates, x, cs);
-  return hipGetLastError();
-}
-
-// Row RMSNorm of an fp32 matrix into the activation dtype.  With S > 0 output
-// row m reads block row (m / (S-1)) * S + m % (S-1) + 1 (rows 1..S-1 of each
-// block: the final norm before lm_head skips the anchor row).
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ in, int H,
-                                                      const T* __restrict__ g, float eps,
-                                                      T* __restrict__ out, int S) {
-  __shared__ float red[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const int src = (S > 0) ? (m / (S - 1)) * S + m % (S - 1) + 1 : m;
-  const float* xr = in + (int64_t)src * H;
-  float ss = 0.f;
-  for (int c = tid; c < H; c += 256) ss += xr[c] * xr[c];
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int c = tid; c < H; c += 256)
-    out[(int64_t)m * H + c] = Num<T>::from_f(xr[c] * inv * Num<T>::to_f(g[c]));
-}
-
-hipError_t launch_rmsnorm(int dt, const float* in, int M, int H, const void* g, float eps,
-                          void* out, int S_skip_anchor, hipStream_t st) {
-  if (M <= 0) return hipSuccess;
-  if (dt == DFLASH_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, in, H,
-                       (const bf16_t*)g, eps, (bf16_t*)out, S_skip_anchor);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, in, H, (const float*)g,
-                       eps, (float*)out, S_skip_anchor);
+                       candidates, x, ss, n_ss, (float*)xg, (const float*)g_first, cs);
   return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_FP8_E4M3 = 2 } dflash_dty
  * Draft model description (the draft checkpoint's config: block size, mask
  * token id, layer types with their sliding window, head counts and head_dim;
  * CSDN DFlash article, the Kimi-K2.6-DFlash config sample).
- * Supported: head_dim 64 or 128; n_q_heads a multiple of n_kv_heads;
+ * Supported: head_dim 64 or 128; n_q_heads a multiple of n_kv_heads; page_size a
+ * multiple of 16;
  * (n_q_heads / n_kv_heads) * block_size <= 64; block_size 2..16;
  * hidden, feat_dim, inter and n_q_heads*head_dim multiples of 32; inter a
  * multiple of 64; act_dtype F32 or BF16; kv_dtype F32, BF16 or FP8_E4M3
@@ -100,9 +101,10 @@ typedef struct {
 
 /*
  * Paged draft K/V cache.  For layer l, k[l] and v[l] each hold num_pages pages
- * laid out [num_pages][n_kv_heads][page_size][head_dim] in kv_dtype, so one
- * (page, kv head) is a contiguous page_size x head_dim block.  Physical slot
- * s lives at page s / page_size, offset s % page_size.
+ * in kv_dtype.  K pages are [num_pages][n_kv_heads][page_size][head_dim]; V
+ * pages are stored transposed, [num_pages][n_kv_heads][head_dim][page_size],
+ * so that attention reads both as matrix-core operands straight from memory.
+ * Physical slot s lives at page s / page_size, offset s % page_size.
  */
 typedef struct {
   void* k[DFLASH_MAX_LAYERS];

@@ -57,15 +57,15 @@ class Setup:
         c.k, c.v = [], []
         for k, v in zip(self.cache.k, self.cache.v):
             c.k.append(self._pool_values(k))
-            c.v.append(self._pool_values(v))
+            c.v.append(self._pool_values(v, transposed=True))
         return c
 
-    def _pool_values(self, pool):
+    def _pool_values(self, pool, transposed=False):
         if self.cfg.kv_dtype == "fp8_e4m3":
             a = e4m3_decode(pool.cpu().numpy())
         else:
             a = pool.detach().to("cpu", torch.float64).numpy()
-        return paged_to_slots(a, self.P)
+        return paged_to_slots(a, self.P, transposed)
 
     # ------------------------------------------------------------ GPU calls
     def draft(self, max_prefix=None, logits=True, ws=None):

@@ -19,9 +19,12 @@ def np_weights(W):
     return out
 
 
-def paged_to_slots(pool, page_size):
-    """[pages, nkv, P, D] -> [pages * P, nkv, D] (slot = page * P + offset)."""
+def paged_to_slots(pool, page_size, transposed=False):
+    """K pool [pages, nkv, P, D] (or a V pool [pages, nkv, D, P] when
+    transposed) -> [pages * P, nkv, D] (slot = page * P + offset)."""
     a = pool if isinstance(pool, np.ndarray) else to_np(pool)
+    if transposed:
+        a = a.transpose(0, 1, 3, 2)
     pages, nkv, P, D = a.shape
     assert P == page_size
     return a.transpose(0, 2, 1, 3).reshape(pages * P, nkv, D)

@@ -123,7 +123,7 @@ def _compare_pools(st, before, o_cache, written):
     for l in range(cfg.n_layers):
         for kind, pool, opool, bpool in (("k", st.cache.k[l], o_cache.k[l], before.k[l]),
                                          ("v", st.cache.v[l], o_cache.v[l], before.v[l])):
-            got = st._pool_values(pool)
+            got = st._pool_values(pool, transposed=(kind == "v"))
             untouched = np.ones(got.shape[0], bool)
             untouched[written] = False
             assert np.array_equal(np.nan_to_num(got[untouched], nan=1e9),

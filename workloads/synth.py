@@ -133,18 +133,20 @@ def features(rows: int, cfg: DFlashConfig, seed: int, name: str = "feats", devic
 
 
 def kv_pool_random(cfg: DFlashConfig, num_pages: int, seed: int, device="cpu"):
-    """Random cache contents in the cache layout [pages, nkv, page, D].
+    """Random cache contents in the cache layout: K pages [pages, nkv, page, D],
+    V pages transposed [pages, nkv, D, page].
 
     f32/bf16 pools hold N(0, 1) values rounded to the pool dtype.  fp8 pools
     hold raw e4m3 byte codes drawn field by field: a random sign, an exponent
     field uniform in 3..8 and a random 3-bit mantissa, i.e. magnitudes
     between 1/16 and 3.75 (no zero, subnormal or NaN codes)."""
-    shp = (num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+    kshp = (num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+    vshp = (num_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size)
     K, Vv = [], []
     for l in range(cfg.n_layers):
         if cfg.kv_dtype == "fp8_e4m3":
             pools = []
-            for kv in ("k", "v"):
+            for kv, shp in (("k", kshp), ("v", vshp)):
                 sign = randint(0, 1, shp, seed, f"kv.{kv}{l}.sign", device)
                 expo = randint(3, 8, shp, seed, f"kv.{kv}{l}.exp", device)
                 mant = randint(0, 7, shp, seed, f"kv.{kv}{l}.mant", device)
@@ -153,8 +155,8 @@ def kv_pool_random(cfg: DFlashConfig, num_pages: int, seed: int, device="cpu"):
             Vv.append(pools[1])
         else:
             dt = _DT[cfg.kv_dtype]
-            K.append(normal(shp, 1.0, seed, f"kv.k{l}", dt, device))
-            Vv.append(normal(shp, 1.0, seed, f"kv.v{l}", dt, device))
+            K.append(normal(kshp, 1.0, seed, f"kv.k{l}", dt, device))
+            Vv.append(normal(vshp, 1.0, seed, f"kv.v{l}", dt, device))
     return K, Vv
 
 
