@@ -316,3 +316,81 @@ def test_speculative_decode_equals_greedy_target():
     assert L == len(prompt) + sum(commits)
     assert len(em) == 1 + sum(commits)
     assert all(1 <= c <= cfg.block_size for c in commits)
+
+
+# ---------------------------------------------------------------- library cross-check
+@pytest.mark.parametrize("windowed", [False, True])
+def test_draft_pass_matches_transformers_qwen3_layers(windowed):
+    """The draft backbone is a stack of Qwen3 decoder layers whose attention
+    reads the injected context K/V as a pre-filled cache, with no causal mask
+    inside the block.  transformers' own Qwen3DecoderLayer (an independent
+    implementation of the pre-norm layer, per-head q/k RMSNorm, neox RoPE, GQA
+    and SwiGLU) must give the oracle's logits."""
+    from transformers import Qwen3Config
+    from transformers.cache_utils import DynamicCache
+    from transformers.models.qwen3 import modeling_qwen3 as q3
+
+    cfg = SMALL_F32_D64 if windowed else dataclasses.replace(SMALL_F32_D64, sliding_window=())
+    W, pt, npages = _setup(cfg, L=(45, 61))
+    L = [45, 61]
+    cache = _ctx_cache(cfg, W, pt, npages, L)
+    anchors = [5, 6]
+    o = oracle.draft_block(cfg, W, cache, anchors, L, pt)
+
+    hc = Qwen3Config(hidden_size=cfg.hidden, intermediate_size=cfg.inter,
+                     num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_q_heads,
+                     num_key_value_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
+                     rms_norm_eps=cfg.rms_eps, vocab_size=cfg.vocab, attention_bias=False,
+                     rope_theta=cfg.rope_theta, max_position_embeddings=1 << 20)
+    hc._attn_implementation = "eager"
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    nq, nkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    layers = []
+    for l in range(cfg.n_layers):
+        lay = q3.Qwen3DecoderLayer(hc, l).double()
+        Lw = W["layers"][l]
+        wqkv = t(Lw["w_qkv"])
+        with torch.no_grad():
+            lay.self_attn.q_proj.weight.copy_(wqkv[:nq * D])
+            lay.self_attn.k_proj.weight.copy_(wqkv[nq * D:(nq + nkv) * D])
+            lay.self_attn.v_proj.weight.copy_(wqkv[(nq + nkv) * D:])
+            lay.self_attn.o_proj.weight.copy_(t(Lw["w_o"]))
+            lay.self_attn.q_norm.weight.copy_(t(Lw["q_norm"]))
+            lay.self_attn.k_norm.weight.copy_(t(Lw["k_norm"]))
+            lay.input_layernorm.weight.copy_(t(Lw["in_norm"]))
+            lay.post_attention_layernorm.weight.copy_(t(Lw["post_norm"]))
+            lay.mlp.gate_proj.weight.copy_(t(Lw["w_gate"]))
+            lay.mlp.up_proj.weight.copy_(t(Lw["w_up"]))
+            lay.mlp.down_proj.weight.copy_(t(Lw["w_down"]))
+        layers.append(lay)
+    rope = q3.Qwen3RotaryEmbedding(hc).double()
+    final = q3.Qwen3RMSNorm(cfg.hidden, eps=cfg.rms_eps).double()
+    with torch.no_grad():
+        final.weight.copy_(t(W["final_norm"]))
+    S, P = cfg.block_size, cfg.page_size
+    for r in range(2):
+        ids = [anchors[r]] + [cfg.mask_token_id] * (S - 1)
+        x = t(W["embed"][ids])[None]                                 # [1, S, H]
+        pos = torch.arange(L[r], L[r] + S)[None]
+        pe = rope(x, pos)
+        kv = DynamicCache()
+        cpos = np.arange(L[r])
+        cslot = pt[r, cpos // P] * P + cpos % P
+        for l in range(cfg.n_layers):
+            kv.update(t(cache.k[l][cslot]).permute(1, 0, 2)[None],
+                      t(cache.v[l][cslot]).permute(1, 0, 2)[None], l)
+        with torch.no_grad():
+            for l, lay in enumerate(layers):
+                mask = torch.zeros(1, 1, S, L[r] + S, dtype=torch.float64)
+                Wl = cfg.window(l)
+                if Wl:
+                    qp = torch.arange(L[r], L[r] + S)[:, None]
+                    vis = (qp - torch.arange(L[r])[None, :]) < Wl
+                    mask[0, 0, :, :L[r]] = torch.where(vis, 0.0, float("-inf"))
+                out = lay(x, attention_mask=mask, position_ids=pos, past_key_values=kv,
+                          use_cache=True, position_embeddings=pe)
+                x = out[0] if isinstance(out, tuple) else out
+            logits = final(x[:, 1:]) @ t(W["lm_head"]).T
+        # transformers builds its RoPE frequency table in fp32 (relative error
+        # ~1e-7); any structural difference would show at the 1e-1 scale
+        assert np.allclose(logits[0].numpy(), o["logits"][r], rtol=1e-5, atol=1e-5)
