@@ -143,8 +143,9 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   // the last chunk of a call can be any size up to `chunk`: take the worst case
   size_t pf = 0;
   for (int m = 1; m <= M; ++m) {
-    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim),
-                            plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim, c->hidden)};
+    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim, c->act_dtype == DFLASH_BF16),
+                            plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim, c->hidden,
+                                      c->act_dtype == DFLASH_BF16)};
     for (const GemmPlan& p : ps)
       if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
   }
@@ -189,9 +190,10 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   L.o_part = (float*)cv.take(sizeof(float) * (size_t)B * nkv * max_splits * 64 * D);
   L.ml_part = (float2*)cv.take(sizeof(float2) * (size_t)B * nkv * max_splits * 64);
   L.lm_part = (float2*)cv.take(sizeof(float2) * (size_t)M1 * logits_tiles(c->vocab));
-  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H), plan_gemm(M, H, nq * D),
-                         plan_gemm(M, ((I + 63) / 64) * 128, H), plan_gemm(M, H, I),
-                         plan_gemm(M1, c->vocab, H)};
+  const bool bf = c->act_dtype == DFLASH_BF16;
+  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H, bf), plan_gemm(M, H, nq * D, bf),
+                         plan_gemm(M, ((I + 63) / 64) * 128, H, bf), plan_gemm(M, H, I, bf),
+                         plan_gemm(M1, c->vocab, H, bf)};
   size_t pf = 0;
   for (const GemmPlan& p : ps)
     if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
@@ -209,7 +211,7 @@ LmHeadWs layout_lm_head(const dflash_config* c, int rows, void* ws) {
   Carver cv(ws);
   LmHeadWs L;
   L.part = (float2*)cv.take(sizeof(float2) * (size_t)rows * logits_tiles(c->vocab));
-  const GemmPlan p = plan_gemm(rows, c->vocab, c->hidden);
+  const GemmPlan p = plan_gemm(rows, c->vocab, c->hidden, c->act_dtype == DFLASH_BF16);
   const size_t pf = gemm_partial_floats(p);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;

@@ -28,9 +28,28 @@ namespace dflash {
 constexpr int BN = 128;      // output columns per workgroup tile
 constexpr int LDT = BN + 4;  // LDS tile row stride in floats (bank-conflict padding)
 
-GemmPlan plan_gemm(int M, int Ncols, int K) {
+GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
   GemmPlan p;
+  p.fat = bf16 && M > 64;
+  if (p.fat) {
+    // LDS-tiled MFMA GEMM: 256 x 128 (or 128 x 128) tiles, K split until the
+    // grid covers the 256 CUs
+    p.BM = M > 128 ? 256 : 128;
+    p.MB = 0;
+    p.m_tiles = (M + p.BM - 1) / p.BM;
+    p.n_tiles = (Ncols + BN - 1) / BN;
+    const int base = p.m_tiles * p.n_tiles;
+    int ks = base >= 256 ? 1 : (256 + base - 1) / base;
+    ks = ks < K / 1024 ? ks : K / 1024;
+    if (ks < 1) ks = 1;
+    int kc = (K + ks - 1) / ks;
+    kc = (kc + 63) / 64 * 64;
+    p.Kc = kc;
+    p.KS = (K + kc - 1) / kc;
+    return p;
+  }
   p.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.BM = 16 * p.MB;
   p.m_tiles = (M + 16 * p.MB - 1) / (16 * p.MB);
   p.n_tiles = (Ncols + BN - 1) / BN;
   int ks = 1;
@@ -54,7 +73,7 @@ GemmPlan plan_gemm(int M, int Ncols, int K) {
 
 size_t gemm_partial_floats(const GemmPlan& p) {
   if (p.KS <= 1) return 0;
-  return (size_t)p.KS * p.m_tiles * p.n_tiles * 16 * p.MB * BN;
+  return (size_t)p.KS * p.m_tiles * p.n_tiles * p.BM * BN;
 }
 
 int logits_tiles(int V) { return (V + BN - 1) / BN; }
@@ -235,22 +254,180 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
         mine[(mb * 16 + g4 * 4 + i) * BN + wave * 32 + nb * 16 + r16] = acc[mb][nb][i];
 }
 
+// ---------------------------------------------------------------- tiled kernel
+// LDS-tiled MFMA GEMM for M > 64 (bf16): a BM x 128 tile per workgroup, 4 waves
+// in a 2 x 2 grid (each BM/2 x 64), K in 64-wide stages double-buffered in LDS
+// (rows padded to 144 bytes so the 16-row fragment reads are conflict-free),
+// the next stage's global loads in flight during the current stage's MFMAs.
+// The grid keeps the M tiles of one column tile on one XCD (workgroup i runs on
+// XCD i % 8), so the weight tile one of them fetched is still in that XCD's L2
+// when the others read it.  Epilogue in 128-row halves through the staging LDS.
+constexpr int FBK = 64;          // K per stage
+constexpr int FLD = FBK + 8;     // LDS row stride (elements)
+constexpr int FGM = 4;           // row tiles per group of the tile order
+
+// Workgroups of a tiled launch: the tile count rounded up to a multiple of 8.
+__host__ __forceinline__ int fat_grid(const GemmPlan& p) {
+  return (p.KS * p.m_tiles * p.n_tiles + 7) / 8 * 8;
+}
+
+template <int BMt, class Epi>
+__global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, int K, int KS,
+                                                int Kc, int m_tiles, int n_tiles,
+                                                float* __restrict__ partial, Epi epi) {
+  constexpr int TM = BMt / 32;                         // 16-row blocks per wave
+  constexpr int STAGE = (BMt + BN) * FLD;              // bf16 elements per stage
+  constexpr int LDS_BYTES = 2 * STAGE * 2;
+  constexpr int EPI_BYTES = 128 * LDT * 4;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES > EPI_BYTES ? LDS_BYTES : EPI_BYTES];
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, g4 = lane >> 4;
+
+  // Workgroup i is dispatched to XCD i % 8: give every XCD a contiguous range
+  // of tiles, ordered (ks slowest) in groups of FGM row tiles, so the ~32
+  // workgroups an XCD runs at once cover FGM row tiles x 32/FGM column tiles
+  // and share both operands' stages in that XCD's L2.
+  const int n_all = KS * m_tiles * n_tiles;
+  const int per = (n_all + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= n_all) return;  // padding of the last XCD's range
+  const int MN = m_tiles * n_tiles;
+  const int ks = t / MN, r = t % MN;
+  const int first = (r / (FGM * n_tiles)) * FGM;
+  const int gsz = imin(m_tiles - first, FGM);
+  const int within = r % (FGM * n_tiles);
+  const int mt = first + within % gsz, nt = within / gsz;
+  const int m0 = mt * BMt;
+  const int k0 = ks * Kc, k1 = imin(K, k0 + Kc);
+
+  // global -> register chunks: A BMt x 64 (BMt*8 chunks of 16 B), B 128 x 64 (1024 chunks)
+  constexpr int ACH = BMt * 8 / 256, BCH = 1024 / 256;
+  const bf16_t* ap[ACH];
+  const bf16_t* bp[BCH];
+  int acol[ACH], bcol[BCH];
+#pragma unroll
+  for (int u = 0; u < ACH; ++u) {
+    const int c = tid + 256 * u, row = c / 8;
+    acol[u] = (c % 8) * 8;
+    ap[u] = asrc.A + (int64_t)block_row(imin(m0 + row, M - 1), asrc.S) * asrc.lda;
+  }
+#pragma unroll
+  for (int u = 0; u < BCH; ++u) {
+    const int c = tid + 256 * u, row = c / 8;
+    bcol[u] = (c % 8) * 8;
+    bp[u] = epi.brow(nt, row);
+  }
+  uint4 ra[ACH], rb[BCH];
+  auto gload = [&](int k) {
+#pragma unroll
+    for (int u = 0; u < ACH; ++u)
+      ra[u] = (k + acol[u] < k1) ? *reinterpret_cast<const uint4*>(ap[u] + k + acol[u])
+                                 : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < BCH; ++u)
+      rb[u] = (k + bcol[u] < k1) ? *reinterpret_cast<const uint4*>(bp[u] + k + bcol[u])
+                                 : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&](int buf) {
+    bf16_t* As = lds + buf * STAGE;
+    bf16_t* Bs = As + BMt * FLD;
+#pragma unroll
+    for (int u = 0; u < ACH; ++u) {
+      const int c = tid + 256 * u;
+      *reinterpret_cast<uint4*>(As + (c / 8) * FLD + acol[u]) = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < BCH; ++u) {
+      const int c = tid + 256 * u;
+      *reinterpret_cast<uint4*>(Bs + (c / 8) * FLD + bcol[u]) = rb[u];
+    }
+  };
+
+  f32x4 acc[TM][4];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_it = (k1 - k0 + FBK - 1) / FBK;
+  if (n_it > 0) {
+    gload(k0);
+    sstore(0);
+    __syncthreads();
+    for (int it = 0; it < n_it; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < n_it) gload(k0 + (it + 1) * FBK);
+      const bf16_t* As = lds + buf * STAGE;
+      const bf16_t* Bs = As + BMt * FLD;
+#pragma unroll
+      for (int kk = 0; kk < FBK / 32; ++kk) {
+        Frag<bf16_t> bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          load_frag(bf[j], Bs + (wn * 64 + j * 16 + r16) * FLD + kk * 32 + g4 * 8);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          Frag<bf16_t> af;
+          load_frag(af, As + (wm * (BMt / 2) + i * 16 + r16) * FLD + kk * 32 + g4 * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mma(acc[i][j], af, bf[j]);
+        }
+      }
+      if (it + 1 < n_it) sstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (KS > 1) {
+    // split partial tile [BMt][128] of this K range
+    float* mine = partial + ((int64_t)(nt * m_tiles + mt) * KS + ks) * (BMt * BN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mine[(wm * (BMt / 2) + i * 16 + g4 * 4 + e) * BN + wn * 64 + j * 16 + r16] = acc[i][j][e];
+    return;
+  }
+  float* tile = reinterpret_cast<float*>(smem);
+  constexpr int HALVES = BMt / 128;
+#pragma unroll
+  for (int h = 0; h < HALVES; ++h) {
+    // rows [128 h, 128 h + 128) of the tile: written by the waves that own them
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * (BMt / 2) + i * 16;   // tile row of this block
+      if (row / 128 != h) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          tile[(row % 128 + g4 * 4 + e) * LDT + wn * 64 + j * 16 + r16] = acc[i][j][e];
+    }
+    __syncthreads();
+    epi.apply(tile, 128, m0 + 128 * h, M, nt, tid);
+    __syncthreads();
+  }
+}
+
 // Split-K reduction: one workgroup per 4 rows of a tile.  Thread t sums the
 // splits q = t/128, t/128 + 2, ... of one float4 column (all loads issued before
 // the adds); the two halves are then added in a fixed order, so the result
 // does not depend on timing.
 constexpr int RROWS = 4;
-template <int MB, class Epi>
+template <int TROWS, class Epi>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, int M,
                                                           const float* __restrict__ partial,
                                                           Epi epi) {
   __shared__ float tile[RROWS * LDT];
   __shared__ float4 half1[RROWS * BN / 4];
   const int tid = threadIdx.x;
-  constexpr int RB = 16 * MB / RROWS;  // row blocks per tile
+  constexpr int RB = TROWS / RROWS;  // row blocks per tile
   const int tix = blockIdx.x / RB, rb = blockIdx.x % RB;
   const int mt = tix % m_tiles, nt = tix / m_tiles;
-  const int tile_elems = 16 * MB * BN;
+  const int tile_elems = TROWS * BN;
   const int i4 = tid & 127, h = tid >> 7;
   const int row = i4 / (BN / 4), c = (i4 % (BN / 4)) * 4;
   const float* p = partial + (int64_t)tix * KS * tile_elems + (int64_t)(rb * RROWS + row) * BN + c;
@@ -274,7 +451,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
     t[3] = s.w + o.w;
   }
   __syncthreads();
-  epi.apply(tile, RROWS, mt * 16 * MB + rb * RROWS, M, nt, tid);
+  epi.apply(tile, RROWS, mt * TROWS + rb * RROWS, M, nt, tid);
 }
 
 // ---------------------------------------------------------------- epilogues
@@ -343,7 +520,7 @@ template <typename T> struct EpiSiluMul {
     return (c < 64 ? Wg : Wu) + (int64_t)n * K;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[64];
+    __shared__ float srs[128];
     rs.fill(srs, rows, m0, M, tid);
     for (int idx = tid; idx < rows * 64; idx += 256) {
       const int r = idx / 64, c = idx % 64, m = m0 + r, n = nt * 64 + c;
@@ -382,7 +559,7 @@ template <typename T> struct EpiQKV {
     return W + (int64_t)imin(nt * BN + c, (nq + 2 * nkv) * D - 1) * H;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[64];
+    __shared__ float srs[128];
     rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
@@ -432,7 +609,7 @@ template <typename T, typename KT> struct EpiKVInject {
     return static_cast<const T*>(tg.w_qkv[l]) + (int64_t)(nq * D + w) * H;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[64];
+    __shared__ float srs[128];
     rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
@@ -476,7 +653,7 @@ template <typename T> struct EpiLogits {
     return W + (int64_t)imin(nt * BN + c, V - 1) * H;
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[64];
+    __shared__ float srs[128];
     rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     for (int r = wave; r < rows; r += 4) {
@@ -521,17 +698,36 @@ static void launch_mb(const AS& asrc, int M, int K, const GemmPlan& p, const Epi
   hipLaunchKernelGGL((gemm_stream<T, MB, AS, Epi>), grid, dim3(256), 0, st, asrc, M, K, p.KS,
                      p.Kc, p.m_tiles, partial, epi);
   if (p.KS > 1)
-    hipLaunchKernelGGL((gemm_splitk_reduce<MB, Epi>),
+    hipLaunchKernelGGL((gemm_splitk_reduce<16 * MB, Epi>),
                        dim3((unsigned)(p.n_tiles * p.m_tiles * (16 * MB / RROWS))), dim3(256), 0,
                        st, p.KS, p.m_tiles, M, (const float*)partial, epi);
+}
+
+template <int BMt, class Epi>
+static void launch_fat(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPlan& p,
+                       const Epi& epi, float* partial, hipStream_t st) {
+  const dim3 grid((unsigned)fat_grid(p));
+  hipLaunchKernelGGL((gemm_fat<BMt, Epi>), grid, dim3(256), 0, st, asrc, M, K, p.KS, p.Kc,
+                     p.m_tiles, p.n_tiles, partial, epi);
+  if (p.KS > 1)
+    hipLaunchKernelGGL((gemm_splitk_reduce<BMt, Epi>),
+                       dim3((unsigned)(p.n_tiles * p.m_tiles * (BMt / RROWS))), dim3(256), 0, st,
+                       p.KS, p.m_tiles, M, (const float*)partial, epi);
 }
 
 template <typename T, class AS, class Epi>
 static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& epi,
                            const GemmScratch& ws, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  const GemmPlan p = plan_gemm(M, Ncols, K);
+  const GemmPlan p = plan_gemm(M, Ncols, K, sizeof(T) == 2);
   if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    if (p.fat) {
+      if (p.BM == 256) launch_fat<256>(asrc, M, K, p, epi, ws.partial, st);
+      else launch_fat<128>(asrc, M, K, p, epi, ws.partial, st);
+      return hipGetLastError();
+    }
+  }
   switch (p.MB) {
     case 1: launch_mb<T, 1>(asrc, M, K, p, epi, ws.partial, st); break;
     case 2: launch_mb<T, 2>(asrc, M, K, p, epi, ws.partial, st); break;

@@ -15,15 +15,18 @@ struct GemmScratch {
   size_t partial_floats;
 };
 
-// Launch geometry of the weight-streaming GEMM C[M, Ncols] = A[M, K] W^T.
+// Launch geometry of a GEMM C[M, Ncols] = A[M, K] W^T: the weight-streaming
+// kernel (M <= 64, or fp32) or the LDS-tiled kernel (bf16, M > 64).
 struct GemmPlan {
-  int MB;        // 16-row blocks per workgroup tile (1, 2, 4 or 8)
-  int m_tiles;   // ceil(M / (16 MB))
+  bool fat;      // LDS-tiled kernel
+  int BM;        // rows per tile (16 MB for the streaming kernel; 128 or 256)
+  int MB;        // 16-row blocks per workgroup tile of the streaming kernel (1, 2, 4)
+  int m_tiles;   // ceil(M / BM)
   int n_tiles;   // ceil(Ncols / 128)
   int KS;        // split-K factor
-  int Kc;        // K elements per split (multiple of 32)
+  int Kc;        // K elements per split
 };
-GemmPlan plan_gemm(int M, int Ncols, int K);
+GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16);
 size_t gemm_partial_floats(const GemmPlan& p);
 
 struct KVTargets {

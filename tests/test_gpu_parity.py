@@ -30,7 +30,7 @@ from tests.gpu_harness import Setup, logits_row_rel_err, top2_margin, e4m3_spaci
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny_f32", "small_bf16", "small_swa_fp8", "small_f32_d64"]
+SMALL = ["tiny_f32", "small_bf16", "small_swa_fp8", "small_f32_d64", "small_bf16_wide"]
 
 
 def tol(cfg):
@@ -144,13 +144,18 @@ def _compare_pools(st, before, o_cache, written):
 
 
 @pytest.mark.parametrize("name", SMALL)
-@pytest.mark.parametrize("grid", [None, (5, 16)])
+@pytest.mark.parametrize("grid", [None, (5, 16), (19, 16), 300])
 def test_project_context_parity(name, grid):
+    """Rows 77 and 5 x 16 (one 128-row tile), 19 x 16 and 300 (256-row tiles,
+    ragged last tile), with and without a prefix-valid request grid."""
     wl = get_workload(name)
     cfg = wl.cfg
     _print(f"[inject parity] {name} grid={grid}")
-    st = Setup(wl)
-    T = 77 if grid is None else grid[0] * grid[1]
+    if isinstance(grid, int):
+        T, grid = grid, None
+    else:
+        T = 77 if grid is None else grid[0] * grid[1]
+    st = Setup(wl, extra_tokens=max(2 * cfg.block_size, T))  # a pool of >= T slots
     feats, pos, slots, valid = _inject_case(st, T, 100 + wl.seed, grid)
     before = st.oracle_cache()
     o_cache = before.copy()
@@ -163,9 +168,10 @@ def test_project_context_parity(name, grid):
 
 @pytest.mark.parametrize("name", ["small_bf16", "small_swa_fp8", "tiny_f32"])
 def test_project_context_chunked_equals_once_and_idempotent(name):
-    """Injecting rows in several calls gives the same bits as one call (the
-    K loop of a row does not depend on how many rows share the call), and
-    re-injecting the same rows leaves the cache bit-identical."""
+    """Injecting rows in several calls of at most 64 rows gives the same bits
+    as one such call (in the weight-streaming GEMM the K split of a row does
+    not depend on how many rows share the call), and re-injecting the same
+    rows leaves the cache bit-identical."""
     wl = get_workload(name)
     st = Setup(wl)
     T = 60

@@ -97,6 +97,13 @@ SMALL_F32_D64 = DFlashConfig(hidden=192, n_layers=2, n_q_heads=6, n_kv_heads=3, 
                              inter=320, vocab=777, n_target_layers=3, target_hidden=96,
                              block_size=5, mask_token_id=775, sliding_window=(0, 33),
                              act_dtype="f32", kv_dtype="f32")
+# Wide enough (hidden 2048) and batched enough (24 x 16 rows) that every GEMM
+# of the draft pass and of a >128-row injection takes the LDS-tiled path with
+# a split K and a ragged last row tile.
+SMALL_BF16_WIDE = DFlashConfig(hidden=2048, n_layers=1, n_q_heads=16, n_kv_heads=4,
+                               head_dim=128, inter=2560, vocab=4099, n_target_layers=2,
+                               target_hidden=1088, block_size=16, mask_token_id=4097,
+                               sliding_window=(96,))
 
 WORKLOADS = {
     "tiny_f32": Workload("tiny_f32", TINY, batch=1, ctx=(64, 64), inject_rows=64,
@@ -120,6 +127,8 @@ WORKLOADS = {
                               commit=(1, 8), seed=2),
     "small_f32_d64": Workload("small_f32_d64", SMALL_F32_D64, batch=2, ctx=(1, 70),
                               commit=(1, 5), seed=3),
+    "small_bf16_wide": Workload("small_bf16_wide", SMALL_BF16_WIDE, batch=24, ctx=(20, 200),
+                                commit=(1, 16), seed=4),
 }
 
 
