@@ -178,7 +178,7 @@ def main():
     for i in range(args.warmup + args.steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        dfl.dflash_lm_head_argmax(cfg, W["lm_head"], hid, ids, lws, c_cfg=c_cfg)
+        dfl.dflash_lm_head_argmax(cfg, cw.packed["lm_head"], hid, ids, lws, c_cfg=c_cfg)
         e1.record()
         torch.cuda.synchronize()
         if i >= args.warmup:

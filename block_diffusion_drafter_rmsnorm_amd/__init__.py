@@ -67,6 +67,7 @@ class CKVCache(ctypes.Structure):
 EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
+            "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_status_string", "dflash_last_error"]
 
 
@@ -95,6 +96,10 @@ def _load():
     lib.dflash_lm_head_workspace_bytes.restype = SZ
     lib.dflash_lm_head_argmax.argtypes = [cfgp, P, P, I32, P, P, P, SZ, P]
     lib.dflash_lm_head_argmax.restype = I32
+    lib.dflash_packed_matrix_bytes.argtypes = [I32, I32, I32]
+    lib.dflash_packed_matrix_bytes.restype = SZ
+    lib.dflash_pack_matrix.argtypes = [P, P, I32, I32, I32, P]
+    lib.dflash_pack_matrix.restype = I32
     lib.dflash_status_string.argtypes = [I32]
     lib.dflash_status_string.restype = ctypes.c_char_p
     lib.dflash_last_error.argtypes = []
@@ -138,19 +143,52 @@ def make_config(cfg) -> CConfig:
     return c
 
 
+PACKED_FIELDS = ("lm_head", "fc")
+PACKED_LAYER_FIELDS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down")
+_MAT_DT = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def packed_matrix_bytes(rows: int, cols: int, dtype: torch.dtype) -> int:
+    return int(_lib.dflash_packed_matrix_bytes(int(rows), int(cols), _MAT_DT[dtype]))
+
+
+def dflash_pack_matrix(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Fragment-packed copy (a new 1-D tensor) of a row-major [rows, cols] matrix."""
+    rows, cols = w.shape
+    n = packed_matrix_bytes(rows, cols, w.dtype)
+    if n == 0:
+        raise DFlashError(-2, f"cannot pack a {tuple(w.shape)} {w.dtype} matrix")
+    src = w.contiguous()
+    out = torch.empty(n // w.element_size(), dtype=w.dtype, device=w.device)
+    _check(_lib.dflash_pack_matrix(_ptr(src), _ptr(out), rows, cols, _MAT_DT[w.dtype],
+                                   _stream(stream)))
+    return out
+
+
 def make_weights(W: Dict) -> CWeights:
-    """C weight table from the dict of device tensors (keeps no references:
-    the caller keeps the tensors alive)."""
+    """C weight table from the dict of device tensors (row-major matrices).
+
+    The projection matrices are packed into new tensors, which the returned
+    table keeps alive in its ``packed`` attribute ({name: tensor} and, per
+    layer, ``packed["layers"][l]``); the other tensors (embedding, gains) are
+    referenced in place and the caller keeps them alive."""
     w = CWeights()
+    packed = {"layers": []}
     for n in ("embed", "lm_head", "fc", "hidden_norm", "final_norm"):
         t = W.get(n)
+        if t is not None and n in PACKED_FIELDS:
+            t = packed[n] = dflash_pack_matrix(t)
         setattr(w, n, None if t is None else t.data_ptr())
     for l, Lw in enumerate(W["layers"]):
+        packed["layers"].append({})
         if Lw is None:
             continue
         for n in _LAYER_FIELDS:
             t = Lw.get(n)
+            if t is not None and n in PACKED_LAYER_FIELDS:
+                t = packed["layers"][l][n] = dflash_pack_matrix(t)
             setattr(w.layer[l], n, None if t is None else t.data_ptr())
+    w.packed = packed
     return w
 
 
@@ -241,6 +279,7 @@ def lm_head_workspace_bytes(cfg, rows: int) -> int:
 def dflash_lm_head_argmax(cfg, lm_head: torch.Tensor, hidden: torch.Tensor, ids: torch.Tensor,
                           ws: torch.Tensor, logits: Optional[torch.Tensor] = None, stream=None,
                           c_cfg: Optional[CConfig] = None):
+    """lm_head: the packed matrix (dflash_pack_matrix or make_weights(W).packed)."""
     c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
     _check(_lib.dflash_lm_head_argmax(ctypes.byref(c_cfg), _ptr(lm_head), _ptr(hidden),
                                       int(hidden.shape[0]), _ptr(logits), _ptr(ids), _ptr(ws),

@@ -236,6 +236,27 @@ const char* dflash_status_string(dflash_status s) {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
+size_t dflash_packed_matrix_bytes(int32_t rows, int32_t cols, int32_t dtype) {
+  if (rows <= 0 || cols <= 0 || cols % 32 || (dtype != DFLASH_F32 && dtype != DFLASH_BF16))
+    return 0;
+  return packed_matrix_elems(rows, cols) * act_bytes(dtype);
+}
+
+dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32_t cols,
+                                 int32_t dtype, void* stream) {
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16)
+    return fail(DFLASH_EUNSUPPORTED, "dtype %d (supported: F32, BF16)", dtype);
+  if (rows <= 0 || cols <= 0) return fail(DFLASH_EINVAL, "non-positive matrix size");
+  if (cols % 32) return fail(DFLASH_EUNSUPPORTED, "cols %d not a multiple of 32", cols);
+  REQUIRE_PTR(src, "src");
+  REQUIRE_PTR(dst, "dst");
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (size_t)rows * cols * act_bytes(dtype);
+  const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + dflash_packed_matrix_bytes(rows, cols, dtype);
+  if (s0 < d1 && d0 < s1) return fail(DFLASH_EINVAL, "src and dst overlap");
+  const hipError_t e = pack_matrix(dtype, src, dst, rows, cols, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DFLASH_OK : hip_fail(e, "pack");
+}
+
 size_t dflash_context_workspace_bytes(const dflash_config* cfg, int64_t rows) {
   if (check_config(cfg) != DFLASH_OK || rows < 0) return 0;
   return layout_context(cfg, inject_chunk_rows(rows > 0 ? rows : 1), nullptr).bytes;

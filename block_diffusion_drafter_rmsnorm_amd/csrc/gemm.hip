@@ -1,11 +1,14 @@
 // Weight-streaming MFMA GEMM for gfx950 with fused prologues and epilogues.
 //
-// C[M, Ncols] = A[M, K] * W[Ncols, K]^T, W row-major [out, in] (the layout of
-// every projection of the draft model).  One workgroup (4 waves, 256 threads)
-// owns a 16*MB x 128 output tile and one K range of a split-K decomposition;
-// each wave owns 32 columns (two 16-column MFMA blocks) for all 16*MB rows,
-// so every weight fragment a lane loads from HBM feeds MB MFMAs straight from
-// registers.  A rows (the small activation matrix) come through L1/L2.
+// C[M, Ncols] = A[M, K] * W[Ncols, K]^T with W[out, in] stored fragment-packed
+// (pack_matrix): 16-row slabs, each a run of 32-column chunks, each chunk the
+// 64 lane records of one MFMA B operand, so a wave's weight load is one
+// contiguous 1 KB (bf16) and a wave streams its slab front to back.
+// One workgroup (4 waves, 256 threads) owns a 16*MB x 128 output tile and one
+// K range of a split-K decomposition; each wave owns two slabs (32 columns) for
+// all 16*MB rows, so every weight fragment a lane loads from HBM feeds MB
+// MFMAs straight from registers.  A rows (the small activation matrix) come
+// through L1/L2 with the same K order as the packed records.
 //
 // RMSNorm is applied by linearity: rms(x) * g * W^T = rstd * ((x * g) W^T).  The
 // producer of x (an epilogue) writes x * g_next rounded to T plus the row's
@@ -27,6 +30,12 @@ namespace dflash {
 
 constexpr int BN = 128;      // output columns per workgroup tile
 constexpr int LDT = BN + 4;  // LDS tile row stride in floats (bank-conflict padding)
+constexpr int kChunkElems = 64 * 8;  // elements of one packed chunk (64 lane records of 8)
+
+// Elements of one packed 16-row slab of a matrix with K columns.
+__host__ __device__ __forceinline__ int64_t slab_elems(int K) {
+  return (int64_t)(K / 32) * kChunkElems;
+}
 
 GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
   GemmPlan p;
@@ -141,22 +150,23 @@ template <typename T> struct NextNorm {
 };
 
 // ---------------------------------------------------------------- main kernel
-// Fragments of one 64-wide K step: per lane 16 consecutive K elements of its
-// rows (A) and of its two weight rows (B).  The K loop double-buffers them in
+// Fragments of one 64-wide K step (two 32-column chunks c, c+1): the lane's
+// record of each chunk of its two slabs (B) and the matching 8 K elements
+// 32 c + 8 (l / 16) .. of its A rows.  The K loop double-buffers steps in
 // registers so the next step's weight loads are in flight during the MFMAs.
 template <typename T, int MB, class ASrc> struct Step64 {
   Frag<T> a0[MB], a1[MB], b0[2], b1[2];
   __device__ __forceinline__ void load(const ASrc& asrc, const typename ASrc::template State<MB>& as,
-                                       const T* const* bp, int kk) {
+                                       const T* const* bp, int c, int g4) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      load_frag(b0[nb], bp[nb] + kk);
-      load_frag(b1[nb], bp[nb] + kk + 8);
+      load_frag(b0[nb], bp[nb] + (int64_t)c * kChunkElems);
+      load_frag(b1[nb], bp[nb] + (int64_t)(c + 1) * kChunkElems);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      asrc.template load<MB>(a0[mb], as, mb, kk);
-      asrc.template load<MB>(a1[mb], as, mb, kk + 8);
+      asrc.template load<MB>(a0[mb], as, mb, c * 32 + g4 * 8);
+      asrc.template load<MB>(a1[mb], as, mb, c * 32 + 32 + g4 * 8);
     }
   }
   __device__ __forceinline__ void mma_into(f32x4 (&acc)[MB][2]) const {
@@ -186,9 +196,9 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
   const int k1 = imin(K, k0 + Kc);
   const int r16 = lane & 15, g4 = lane >> 4;
 
-  const T* bp[2];
+  const T* bp[2];  // this lane's record in chunk 0 of the wave's two slabs
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) bp[nb] = epi.brow(nt, wave * 32 + nb * 16 + r16);
+  for (int nb = 0; nb < 2; ++nb) bp[nb] = epi.bslab(nt, wave * 2 + nb) + lane * 8;
   typename ASrc::template State<MB> as;
   asrc.template setup<MB>(as, m0, M, r16);
 
@@ -198,32 +208,29 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int k = k0;
-  if ((k1 - k0) & 32) {  // a 32-wide step first when the range is not a multiple of 64
-    const int kk = k + g4 * 8;
+  int c = k0 / 32;  // chunk index (k0, k1 are multiples of 32)
+  if ((k1 - k0) & 32) {  // a single chunk first when the range is not a multiple of 64
     Frag<T> b0[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) load_frag(b0[nb], bp[nb] + kk);
+    for (int nb = 0; nb < 2; ++nb) load_frag(b0[nb], bp[nb] + (int64_t)c * kChunkElems);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       Frag<T> a0;
-      asrc.template load<MB>(a0, as, mb, kk);
+      asrc.template load<MB>(a0, as, mb, c * 32 + g4 * 8);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) mma(acc[mb][nb], a0, b0[nb]);
     }
-    k += 32;
+    ++c;
   }
-  // 64-wide steps: each lane reads 16 consecutive K elements per row (lanes
-  // with the same l % 16 cover one contiguous 64-element span of that row).
-  const int n64 = (k1 - k) / 64;
+  const int n64 = (k1 / 32 - c) / 2;
   if (n64 > 0) {
     Step64<T, MB, ASrc> s0, s1;
-    s0.load(asrc, as, bp, k + g4 * 16);
+    s0.load(asrc, as, bp, c, g4);
     int i = 0;
     for (; i + 2 <= n64; i += 2) {
-      s1.load(asrc, as, bp, k + (i + 1) * 64 + g4 * 16);
+      s1.load(asrc, as, bp, c + 2 * (i + 1), g4);
       s0.mma_into(acc);
-      if (i + 2 < n64) s0.load(asrc, as, bp, k + (i + 2) * 64 + g4 * 16);
+      if (i + 2 < n64) s0.load(asrc, as, bp, c + 2 * (i + 2), g4);
       s1.mma_into(acc);
     }
     if (i < n64) s0.mma_into(acc);
@@ -257,7 +264,8 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
 // ---------------------------------------------------------------- tiled kernel
 // LDS-tiled MFMA GEMM for M > 64 (bf16): a BM x 128 tile per workgroup, 4 waves
 // in a 2 x 2 grid (each BM/2 x 64), K in 64-wide stages double-buffered in LDS
-// (rows padded to 144 bytes so the 16-row fragment reads are conflict-free),
+// (A rows padded to 144 bytes so the 16-row fragment reads are conflict-free;
+// the B stage is the packed records as they lie in memory, read 1 KB per wave),
 // the next stage's global loads in flight during the current stage's MFMAs.
 // The grid keeps the M tiles of one column tile on one XCD (workgroup i runs on
 // XCD i % 8), so the weight tile one of them fetched is still in that XCD's L2
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
                                                 int Kc, int m_tiles, int n_tiles,
                                                 float* __restrict__ partial, Epi epi) {
   constexpr int TM = BMt / 32;                         // 16-row blocks per wave
-  constexpr int STAGE = (BMt + BN) * FLD;              // bf16 elements per stage
+  constexpr int STAGE = BMt * FLD + BN * FBK;          // bf16 elements per stage
   constexpr int LDS_BYTES = 2 * STAGE * 2;
   constexpr int EPI_BYTES = 128 * LDT * 4;
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES > EPI_BYTES ? LDS_BYTES : EPI_BYTES];
@@ -301,11 +309,12 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
   const int m0 = mt * BMt;
   const int k0 = ks * Kc, k1 = imin(K, k0 + Kc);
 
-  // global -> register chunks: A BMt x 64 (BMt*8 chunks of 16 B), B 128 x 64 (1024 chunks)
+  // global -> register pieces of 16 B: A BMt x 64 (BMt*8 pieces); B the two
+  // packed chunks of the stage for each of the tile's 8 slabs (1024 records)
   constexpr int ACH = BMt * 8 / 256, BCH = 1024 / 256;
   const bf16_t* ap[ACH];
   const bf16_t* bp[BCH];
-  int acol[ACH], bcol[BCH];
+  int acol[ACH];
 #pragma unroll
   for (int u = 0; u < ACH; ++u) {
     const int c = tid + 256 * u, row = c / 8;
@@ -314,9 +323,8 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
   }
 #pragma unroll
   for (int u = 0; u < BCH; ++u) {
-    const int c = tid + 256 * u, row = c / 8;
-    bcol[u] = (c % 8) * 8;
-    bp[u] = epi.brow(nt, row);
+    const int rec = tid + 256 * u;  // slab rec / 128, chunk (rec / 64) % 2, lane rec % 64
+    bp[u] = epi.bslab(nt, rec / 128) + ((rec / 64) % 2) * kChunkElems + (rec % 64) * 8;
   }
   uint4 ra[ACH], rb[BCH];
   auto gload = [&](int k) {
@@ -326,8 +334,9 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
                                  : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < BCH; ++u)
-      rb[u] = (k + bcol[u] < k1) ? *reinterpret_cast<const uint4*>(bp[u] + k + bcol[u])
-                                 : make_uint4(0, 0, 0, 0);
+      rb[u] = (k + ((tid + 256 * u) / 64) % 2 * 32 < k1)
+                  ? *reinterpret_cast<const uint4*>(bp[u] + (int64_t)(k / 32) * kChunkElems)
+                  : make_uint4(0, 0, 0, 0);
   };
   auto sstore = [&](int buf) {
     bf16_t* As = lds + buf * STAGE;
@@ -338,10 +347,8 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
       *reinterpret_cast<uint4*>(As + (c / 8) * FLD + acol[u]) = ra[u];
     }
 #pragma unroll
-    for (int u = 0; u < BCH; ++u) {
-      const int c = tid + 256 * u;
-      *reinterpret_cast<uint4*>(Bs + (c / 8) * FLD + bcol[u]) = rb[u];
-    }
+    for (int u = 0; u < BCH; ++u)
+      *reinterpret_cast<uint4*>(Bs + (tid + 256 * u) * 8) = rb[u];
   };
 
   f32x4 acc[TM][4];
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
         Frag<bf16_t> bf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          load_frag(bf[j], Bs + (wn * 64 + j * 16 + r16) * FLD + kk * 32 + g4 * 8);
+          load_frag(bf[j], Bs + ((wn * 4 + j) * 2 + kk) * kChunkElems + lane * 8);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           Frag<bf16_t> af;
@@ -485,8 +492,8 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
 
 template <typename T> struct EpiStoreF32 {
   const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn;
-  __device__ const T* brow(int nt, int c) const {
-    return W + (int64_t)imin(nt * BN + c, N - 1) * K;
+  __device__ const T* bslab(int nt, int s) const {
+    return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int r, int c, int m, int n) {
@@ -499,8 +506,8 @@ template <typename T> struct EpiStoreF32 {
 
 template <typename T> struct EpiResidual {
   const T* W; int N; int K; float* x; float* ss; NextNorm<T> nn;
-  __device__ const T* brow(int nt, int c) const {
-    return W + (int64_t)imin(nt * BN + c, N - 1) * K;
+  __device__ const T* bslab(int nt, int s) const {
+    return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int r, int c, int m, int n) {
@@ -515,9 +522,9 @@ template <typename T> struct EpiResidual {
 // Tile columns 0..63 are gate rows nt*64.., columns 64..127 the matching up rows.
 template <typename T> struct EpiSiluMul {
   const T* Wg; const T* Wu; int I; int K; T* act; RowScale rs;
-  __device__ const T* brow(int nt, int c) const {
-    const int n = imin(nt * 64 + (c & 63), I - 1);
-    return (c < 64 ? Wg : Wu) + (int64_t)n * K;
+  __device__ const T* bslab(int nt, int s) const {
+    const int n = imin(nt * 64 + (16 * s & 63), I - 1);
+    return (s < 4 ? Wg : Wu) + (int64_t)(n / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     __shared__ float srs[128];
@@ -555,8 +562,8 @@ __device__ __forceinline__ void norm_rope_pair(float x0, float x1, int i, int D,
 template <typename T> struct EpiQKV {
   const T* W; int H; int nq, nkv, D; const T* qn; const T* kn; float eps;
   const float2* cs; T* q; T* k; T* v; RowScale rs; int S;
-  __device__ const T* brow(int nt, int c) const {
-    return W + (int64_t)imin(nt * BN + c, (nq + 2 * nkv) * D - 1) * H;
+  __device__ const T* bslab(int nt, int s) const {
+    return W + (int64_t)(imin(nt * BN + 16 * s, (nq + 2 * nkv) * D - 1) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     __shared__ float srs[128];
@@ -602,11 +609,11 @@ template <typename T> struct EpiQKV {
 template <typename T, typename KT> struct EpiKVInject {
   KVTargets tg; int H; int n_layers, nq, nkv, D; float eps; const float2* cs;
   const int32_t* slots; const int32_t* valid; int rpr; int P; int64_t num_slots; RowScale rs;
-  __device__ const T* brow(int nt, int c) const {
+  __device__ const T* bslab(int nt, int s) const {
     const int per = 2 * nkv * D;
-    const int n = imin(nt * BN + c, n_layers * per - 1);
+    const int n = imin(nt * BN + 16 * s, n_layers * per - 1);
     const int l = n / per, w = n % per;
-    return static_cast<const T*>(tg.w_qkv[l]) + (int64_t)(nq * D + w) * H;
+    return static_cast<const T*>(tg.w_qkv[l]) + (int64_t)((nq * D + w) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     __shared__ float srs[128];
@@ -649,8 +656,8 @@ template <typename T, typename KT> struct EpiKVInject {
 // then the (max, first index) of every row over the slice.
 template <typename T> struct EpiLogits {
   const T* W; int V; int H; T* logits; float2* part; int n_tiles; RowScale rs;
-  __device__ const T* brow(int nt, int c) const {
-    return W + (int64_t)imin(nt * BN + c, V - 1) * H;
+  __device__ const T* bslab(int nt, int s) const {
+    return W + (int64_t)(imin(nt * BN + 16 * s, V - 1) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     __shared__ float srs[128];
@@ -689,6 +696,47 @@ template <typename T> struct EpiLogits {
     }
   }
 };
+
+// ---------------------------------------------------------------- packing
+// Fragment-packed copy of a row-major [rows, cols] matrix: record i (8
+// elements) of slab i / (64 cols/32), chunk (i / 64) % (cols/32), lane i % 64
+// holds W[16 slab + lane % 16][32 chunk + 8 (lane / 16) + e], zero past the
+// last row.  One thread per record; the writes are contiguous.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_matrix_kernel(const T* __restrict__ src,
+                                                          T* __restrict__ dst, int rows,
+                                                          int cols, int64_t n_rec) {
+  const int per_slab = (cols / 32) * 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_rec;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t slab = i / per_slab;
+    const int rem = (int)(i % per_slab);
+    const int l = rem % 64;
+    const int64_t row = slab * 16 + (l & 15);
+    const int col = (rem / 64) * 32 + (l >> 4) * 8;
+    Frag<T> f;
+    if (row < rows) load_frag(f, src + row * cols + col);
+    else zero_frag(f);
+    store_frag(dst + i * 8, f);
+  }
+}
+
+size_t packed_matrix_elems(int rows, int cols) { return (size_t)((rows + 15) / 16) * 16 * cols; }
+
+hipError_t pack_matrix(int dt, const void* src, void* dst, int rows, int cols, hipStream_t st) {
+  const int64_t n_rec = (int64_t)packed_matrix_elems(rows, cols) / 8;
+  const int64_t want = (n_rec + 255) / 256;
+  const dim3 grid((unsigned)(want < 8192 ? want : 8192));
+  if (dt == DFLASH_BF16)
+    hipLaunchKernelGGL(pack_matrix_kernel<bf16_t>, grid, dim3(256), 0, st,
+                       static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst), rows, cols,
+                       n_rec);
+  else
+    hipLaunchKernelGGL(pack_matrix_kernel<float>, grid, dim3(256), 0, st,
+                       static_cast<const float*>(src), static_cast<float*>(dst), rows, cols,
+                       n_rec);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- launchers
 template <typename T, int MB, class AS, class Epi>

@@ -60,6 +60,10 @@ __host__ __device__ inline int ss_tiles(int H) { return (H + 127) / 128; }
 
 // y = A W^T: out[M, N] fp32 (nullable), per-128-column row sums of squares of y
 // into ss (nullable) and xg = y * g_next rounded to the act dtype (nullable)
+// Fragment-packed weight layout read by every GEMM (see gemm.hip).
+size_t packed_matrix_elems(int rows, int cols);
+hipError_t pack_matrix(int dt, const void* src, void* dst, int rows, int cols, hipStream_t st);
+
 hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, int N, float* out,
                           float* ss, void* xg, const void* g_next, const GemmScratch& ws,
                           hipStream_t st);

@@ -22,7 +22,10 @@
  *     produces wrong values, never an out-of-bounds access.
  *     dflash_last_error() returns a message for the last failure on the
  *     calling thread.
- *   - Integer tensors are int32.  Matrices are row-major [out, in] (y = x W^T).
+ *   - Integer tensors are int32.  Token embeddings are row-major [V, H].  The
+ *     projection matrices (fc, w_qkv, w_o, w_gate, w_up, w_down, lm_head) are
+ *     passed fragment-packed: dflash_pack_matrix turns a row-major [out, in]
+ *     matrix (y = x W^T) into that layout once, when the weights are loaded.
  *   - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef DFLASH_H
@@ -77,7 +80,8 @@ typedef struct {
   int32_t kv_dtype;        /* dflash_dtype of the draft K/V cache                  */
 } dflash_config;
 
-/* Weights of one draft decoder layer, all of dtype act_dtype.                    */
+/* Weights of one draft decoder layer, all of dtype act_dtype; the matrices
+ * fragment-packed (dflash_pack_matrix), shapes given as the row-major [out, in]. */
 typedef struct {
   const void* in_norm;     /* [H]                                                  */
   const void* w_qkv;       /* [(nq + 2 nkv) * D, H]: q rows, then k rows, v rows   */
@@ -92,8 +96,8 @@ typedef struct {
 
 typedef struct {
   const void* embed;       /* [V, H] the target's token embedding                 */
-  const void* lm_head;     /* [V, H] the target's lm_head                          */
-  const void* fc;          /* [H, F] fuses the concatenated target features        */
+  const void* lm_head;     /* [V, H] the target's lm_head (packed)                 */
+  const void* fc;          /* [H, F] fuses the concatenated target features (packed) */
   const void* hidden_norm; /* [H] RMSNorm gain after fc                            */
   const void* final_norm;  /* [H]                                                  */
   dflash_layer_weights layer[DFLASH_MAX_LAYERS];
@@ -111,6 +115,29 @@ typedef struct {
   void* v[DFLASH_MAX_LAYERS];
   int64_t num_pages;
 } dflash_kv_cache;
+
+/*
+ * Fragment-packed weight layout.  The draft model's projections and the
+ * target's lm_head ("Inside SGLang: DFlash and DFlash 2 Implementation", the
+ * draft model structure; CSDN DFlash article, the fc / hidden_norm and decoder
+ * layer description) are the operands the GEMMs stream from HBM once per
+ * pass.  For a row-major [rows, cols] matrix W (cols a multiple of 32) the
+ * packed matrix holds ceil(rows / 16) slabs of 16 rows; slab s holds cols / 32
+ * chunks; chunk c holds 64 records; record l holds the 8 elements
+ *   W[16 s + l % 16][32 c + 8 (l / 16) + e],  e = 0..7
+ * (zero for rows >= rows).  A record is the part of one matrix-core operand
+ * that one lane supplies, so a wavefront reads a chunk as one contiguous
+ * 1 KB (bf16) and streams a slab front to back.
+ *   dflash_packed_matrix_bytes  bytes of the packed copy (0 on invalid
+ *                               arguments): ceil(rows / 16) * 16 * cols * elem
+ *   dflash_pack_matrix          writes the packed copy of src [rows, cols]
+ *                               (dtype F32 or BF16) to dst; src and dst must not
+ *                               overlap, both 16-byte aligned; asynchronous on
+ *                               `stream`.
+ */
+size_t dflash_packed_matrix_bytes(int32_t rows, int32_t cols, int32_t dtype);
+dflash_status dflash_pack_matrix(const void* src, void* dst, int32_t rows, int32_t cols,
+                                 int32_t dtype, void* stream);
 
 /* Workspace sizes in bytes (host functions; 0 on invalid arguments). */
 size_t dflash_context_workspace_bytes(const dflash_config* cfg, int64_t rows);
@@ -210,6 +237,7 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
  * lm_head^T rounded to act_dtype, ids = argmax per row (first index among
  * equal maxima).  dflash_draft_block runs the same kernels on its rows
  * 1..S-1; this entry point serves callers that hold the normalised rows.
+ *   lm_head    [V, H] fragment-packed (dflash_pack_matrix)
  *   hidden     [rows, H] act_dtype (already through the final RMSNorm)
  *   logits     nullable [rows, V] act_dtype out
  *   ids        [rows] out

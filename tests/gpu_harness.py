@@ -45,6 +45,13 @@ class Setup:
             self.cache = m.KVCache([k.to(device) for k in K], [v.to(device) for v in V],
                                    self.num_pages)
         self._npW = None
+        self._cw = None
+
+    def c_weights(self):
+        """The C weight table (projection matrices packed once, on first use)."""
+        if self._cw is None:
+            self._cw = dfl().make_weights(self.W)
+        return self._cw
 
     # ------------------------------------------------------------ oracle views
     def np_W(self):
@@ -82,7 +89,7 @@ class Setup:
             block_ids=torch.empty((B, S), dtype=torch.int32, device=dev),
             logits=torch.empty((B, S - 1, cfg.vocab), dtype=synth._DT[cfg.act_dtype],
                                device=dev) if logits else None)
-        cw = m.make_weights(self.W)
+        cw = self.c_weights()
         m.dflash_draft_block(cfg, cw, self.cache, self.anchor.to(dev), self.L.to(dev),
                              self.pt.to(dev), mp, out["positions"], out["slots"],
                              out["candidates"], ws, block_ids=out["block_ids"],
@@ -98,7 +105,7 @@ class Setup:
             n_req, rows_per_req = 1, T
         if ws is None:
             ws = m.workspace(m.context_workspace_bytes(self.cfg, T), dev)
-        cw = m.make_weights(self.W)
+        cw = self.c_weights()
         m.dflash_project_context(self.cfg, cw, self.cache, feats.to(dev), positions.to(dev),
                                  slots.to(dev), None if valid is None else valid.to(dev), n_req,
                                  rows_per_req, ws)

@@ -113,3 +113,23 @@ def test_null_and_workspace_errors():
     assert lib.dflash_accept(F, F, F, -1, 4, F, F, F, F, F, None) == -1
     assert lib.dflash_accept(None, F, F, 3, 4, F, F, F, F, F, None) == -1
     assert lib.dflash_status_string(-3) == b"workspace too small"
+
+
+def test_packed_matrix_sizes_and_errors():
+    """Packed size = ceil(rows / 16) * 16 * cols * element size; invalid shapes
+    and dtypes, NULL, misaligned or overlapping buffers fail before any launch."""
+    lib = dfl.raw_lib()
+    assert lib.dflash_packed_matrix_bytes(15, 64, dfl.BF16) == 16 * 64 * 2
+    assert lib.dflash_packed_matrix_bytes(16, 64, dfl.F32) == 16 * 64 * 4
+    assert lib.dflash_packed_matrix_bytes(151936, 4096, dfl.BF16) == 151936 * 4096 * 2
+    assert lib.dflash_packed_matrix_bytes(5003, 512, dfl.BF16) == 5008 * 512 * 2
+    assert lib.dflash_packed_matrix_bytes(16, 40, dfl.BF16) == 0
+    assert lib.dflash_packed_matrix_bytes(16, 64, dfl.FP8_E4M3) == 0
+    assert lib.dflash_packed_matrix_bytes(0, 64, dfl.BF16) == 0
+    a, b = 0x100000, 0x900000
+    assert lib.dflash_pack_matrix(a, b, 16, 40, dfl.BF16, None) == -2
+    assert lib.dflash_pack_matrix(a, b, 16, 64, dfl.FP8_E4M3, None) == -2
+    assert lib.dflash_pack_matrix(None, b, 16, 64, dfl.BF16, None) == -1
+    assert lib.dflash_pack_matrix(a, a + 8, 16, 64, dfl.BF16, None) == -1
+    assert lib.dflash_pack_matrix(a, a + 1024, 16, 64, dfl.BF16, None) == -1  # overlap
+    assert lib.dflash_pack_matrix(a, b, -1, 64, dfl.BF16, None) == -1

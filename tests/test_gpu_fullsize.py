@@ -123,7 +123,7 @@ class Setup:
         return out
 
     def free(self):
-        del self.W, self.cache
+        del self.W, self.cw, self.cache
         gc.collect()
         torch.cuda.empty_cache()
 

@@ -65,6 +65,35 @@ def test_accept_bitexact(S):
     assert np.array_equal(o["commit_len"][B // 4:], commit[B // 4:].numpy())
 
 
+# ---------------------------------------------------------------- weight packing
+def _packed_reference(w):
+    """The packed layout written out from its definition: record l of chunk c
+    of slab s holds w[16 s + l % 16, 32 c + 8 (l // 16) + e], e = 0..7, zero
+    past the last row."""
+    rows, cols = w.shape
+    n_slab = (rows + 15) // 16
+    wp = np.zeros((n_slab * 16, cols), w.dtype)
+    wp[:rows] = w
+    out = np.zeros((n_slab, cols // 32, 64, 8), w.dtype)
+    for lane in range(64):
+        for e in range(8):
+            out[:, :, lane, e] = wp[lane % 16::16][:, 8 * (lane // 16) + e::32]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(37, 96), (16, 32), (160, 512)])
+def test_pack_matrix_layout(dtype, shape):
+    m = dfl()
+    g = torch.Generator().manual_seed(shape[0] * 1000 + shape[1])
+    w = torch.randn(shape, generator=g).to(dtype)
+    got = m.dflash_pack_matrix(w.cuda())
+    torch.cuda.synchronize()
+    want = _packed_reference(w.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy())
+    gi = got.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy()
+    assert np.array_equal(gi, want)
+
+
 # ---------------------------------------------------------------- draft pass
 @pytest.mark.parametrize("name", SMALL)
 def test_draft_block_parity(name):
