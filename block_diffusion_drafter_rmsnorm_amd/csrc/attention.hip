@@ -27,15 +27,28 @@
 namespace dflash {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int kMaxChunk = 4096;                   // context keys per workgroup
+constexpr int kMaxChunkPages = kMaxChunk / 16 + 8;  // page-table entries it can touch
 
 AttnPlan plan_attention(int max_keys, int B, int nkv) {
   AttnPlan p;
-  // about 1024 waves over the largest context, at least 4 steps (128 keys) each
-  const int64_t work = (int64_t)(max_keys + 32) * B * nkv;
-  int chunk = (int)((work / 1024 + 31) / 32 * 32);
+  const int64_t base = (int64_t)B * nkv;
+  const int64_t keys = (int64_t)max_keys + 32;
+  const int64_t steps = (keys + 31) / 32 * base;  // 32-key steps over all (request, kv head)
+  int64_t chunk;
+  if (steps <= 2048) {
+    // latency-bound (a short context or a small batch): one round of at most
+    // 256 workgroups, one per CU, so that none waits for a second round
+    const int64_t splits = base >= 256 ? 1 : 256 / base;
+    chunk = ((keys + splits - 1) / splits + 31) / 32 * 32;
+  } else {
+    // about 1024 workgroups over the largest context: rounds balance ragged work
+    chunk = (keys * base / 1024 + 31) / 32 * 32;
+  }
   if (chunk < 128) chunk = 128;
-  p.chunk = chunk;
-  p.n_splits = max_keys <= 0 ? 1 : (max_keys + 31 + chunk - 1) / chunk;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  p.chunk = (int)chunk;
+  p.n_splits = max_keys <= 0 ? 1 : (int)((max_keys + 31 + chunk - 1) / chunk);
   return p;
 }
 
@@ -83,15 +96,35 @@ template <typename KT, int D> struct KVStep {
 
 template <typename CT, typename KT, int D>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
+  // physical pages of this workgroup's key range, read from the page table
+  // once: the K/V loads of a step then depend on LDS only, so the next step's
+  // loads go out while the current step computes
+  __shared__ int pages[kMaxChunkPages];
   const int split = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int lane = threadIdx.x & 63, qb = threadIdx.x >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
-  if (qb * 16 >= R) return;  // no barriers below: idle waves leave
   int L, lo, a0, nvalid;
   key_range(a, r, L, lo, a0, nvalid);
-  if (split >= nvalid) return;
+  if (split >= nvalid) {
+    // no keys here: an empty partial, which the combine weighs zero
+    const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits + split) * 64;
+    if (threadIdx.x < R) a.ml_part[base + threadIdx.x] = make_float2(-INFINITY, 0.f);
+    return;
+  }
   const int kbeg = a0 + split * a.chunk;
   const int kend = imin(L, kbeg + a.chunk);
+  const int n_ctx = (kend > kbeg) ? (kend - kbeg + 31) / 32 : 0;
+  const int pfirst = kbeg / a.P;
+  if (n_ctx > 0) {
+    const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
+    for (int i = threadIdx.x; i < npages; i += 256) {
+      const int pi = imin(pfirst + i, a.max_pages - 1);
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + pi];
+      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
+    }
+  }
+  __syncthreads();
+  if (qb * 16 >= R) return;  // no barriers below: idle waves leave
 
   // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
   Frag<CT> qf[D / 32];
@@ -111,11 +144,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 
   const KT* kc = static_cast<const KT*>(a.kc);
   const KT* vc = static_cast<const KT*>(a.vc);
-  auto page_of = [&](int key) -> int64_t {
-    const int pi = imin(key / a.P, a.max_pages - 1);
-    const int64_t page = a.pt[(int64_t)r * a.max_pages + pi];
-    return page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-  };
+  auto page_of = [&](int key) -> int64_t { return pages[key / a.P - pfirst]; };
   auto load_ctx = [&](KVStep<KT, D>& st, int t0) {
     const KT *kb[2], *vb[2];
 #pragma unroll
@@ -187,7 +216,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     }
   };
 
-  const int n_ctx = (kend > kbeg) ? (kend - kbeg + 31) / 32 : 0;
   if (n_ctx > 0) {
     KVStep<KT, D> s0, s1;
     load_ctx(s0, kbeg);
@@ -222,7 +250,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// Combine the splits of one query row: one wave per row.
+// Combine the splits of one query row: one wave per row.  Empty splits carry
+// m = -inf and weigh zero (their O is never read).  Lane s holds split s's
+// (m, l); the O loads of 16 splits go out together.
 template <typename CT, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __restrict__ out,
                                                            int B) {
@@ -230,23 +260,48 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __res
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= B * a.nkv * R) return;
   const int rho = row % R, g = (row / R) % a.nkv, r = row / (R * a.nkv);
-  int L, lo, a0, nvalid;
-  key_range(a, r, L, lo, a0, nvalid);
   const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits) * 64 + rho;
   float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, a.ml_part[base + (int64_t)s * 64].x);
+  for (int s = lane; s < a.n_splits; s += 64) M = fmaxf(M, a.ml_part[base + (int64_t)s * 64].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   float den = 0.f, acc[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < nvalid; ++s) {
-    const float2 ml = a.ml_part[base + (int64_t)s * 64];
-    const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
-    den += wgt * ml.y;
+  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
+    // this lane's split s0 + lane: its weight and weighted l
+    float wl = 0.f, wm = 0.f;
+    if (s0 + lane < a.n_splits) {
+      const float2 ml = a.ml_part[base + (int64_t)(s0 + lane) * 64];
+      wm = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      wl = wm * ml.y;
+    }
+    const int ns = imin(64, a.n_splits - s0);
+    for (int s1 = 0; s1 < ns; s1 += 16) {
+      float v[16][D / 64];
+      float w[16], l[16];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e)
-      acc[e] += wgt * a.o_part[(base + (int64_t)s * 64) * D + lane + 64 * e];
+      for (int u = 0; u < 16; ++u) {
+        const int src = (s1 + u) & 63;  // uniform across the wave
+        w[u] = __shfl(wm, src, 64);
+        l[u] = __shfl(wl, src, 64);
+        if (s1 + u >= ns) w[u] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e)
+          v[u][e] = w[u] != 0.f
+                        ? a.o_part[(base + (int64_t)(s0 + s1 + u) * 64) * D + lane + 64 * e]
+                        : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (w[u] != 0.f) {
+          den += l[u];
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) acc[e] += w[u] * v[u][e];
+        }
+    }
   }
   const int hl = rho / a.S, j = rho % a.S;
   CT* dst = out + ((int64_t)(r * a.S + j) * a.nq + g * a.G + hl) * D;

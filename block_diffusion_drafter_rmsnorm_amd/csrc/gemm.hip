@@ -127,7 +127,7 @@ struct RowScale {
   // Called by all threads of the workgroup; ends with a barrier.
   __device__ __forceinline__ void fill(float* out, int rows, int m0, int M, int tid) const {
     const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < rows; r += 4) {
+    for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
       float v = 1.0f;
       if (ss != nullptr) {
         const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
@@ -222,18 +222,24 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
     }
     ++c;
   }
+  // 64-wide steps through a ring of NB register buffers: NB - 1 steps of
+  // weight loads stay in flight while a step's MFMAs run (buffer indices are
+  // compile-time constants: step s lives in buf[s % NB])
+  constexpr int NB = MB == 4 ? 3 : 4;
   const int n64 = (k1 / 32 - c) / 2;
-  if (n64 > 0) {
-    Step64<T, MB, ASrc> s0, s1;
-    s0.load(asrc, as, bp, c, g4);
-    int i = 0;
-    for (; i + 2 <= n64; i += 2) {
-      s1.load(asrc, as, bp, c + 2 * (i + 1), g4);
-      s0.mma_into(acc);
-      if (i + 2 < n64) s0.load(asrc, as, bp, c + 2 * (i + 2), g4);
-      s1.mma_into(acc);
+  Step64<T, MB, ASrc> buf[NB];
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b)
+    if (b < n64) buf[b].load(asrc, as, bp, c + 2 * b, g4);
+  for (int i = 0; i < n64; i += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int st = i + b, nxt = st + NB - 1;
+      if (st < n64) {
+        if (nxt < n64) buf[(b + NB - 1) % NB].load(asrc, as, bp, c + 2 * nxt, g4);
+        buf[b].mma_into(acc);
+      }
     }
-    if (i < n64) s0.mma_into(acc);
   }
 
   if (KS == 1) {
@@ -462,6 +468,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
 }
 
 // ---------------------------------------------------------------- epilogues
+// Epilogues run on every thread of the workgroup (any multiple of 64 threads).
 // Row-wise pass over a [rows, 128] fp32 tile (one wave per row, two columns per
 // lane); f returns the value stored for (row, col), whose squares are summed
 // into the row's partial sum of squares over the tile when ss != null.
@@ -469,7 +476,7 @@ template <typename T, typename F>
 __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N, int tid,
                                          float* ss, int n_ss, const NextNorm<T>& nn, F&& f) {
   const int lane = tid & 63, wave = tid >> 6;
-  for (int r = wave; r < rows; r += 4) {
+  for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
     const int m = m0 + r;
     if (m >= M) continue;
     float acc = 0.f;
@@ -529,7 +536,7 @@ template <typename T> struct EpiSiluMul {
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     __shared__ float srs[128];
     rs.fill(srs, rows, m0, M, tid);
-    for (int idx = tid; idx < rows * 64; idx += 256) {
+    for (int idx = tid; idx < rows * 64; idx += (int)blockDim.x) {
       const int r = idx / 64, c = idx % 64, m = m0 + r, n = nt * 64 + c;
       if (m < M && n < I) {
         const float sc = srs[r];
@@ -570,7 +577,7 @@ template <typename T> struct EpiQKV {
     rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
-    for (int item = wave; item < rows * HP; item += 4) {
+    for (int item = wave; item < rows * HP; item += (int)(blockDim.x >> 6)) {
       const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
       if (m >= M || gh >= nq + 2 * nkv) continue;
       const bool act = lane < half;
@@ -620,7 +627,7 @@ template <typename T, typename KT> struct EpiKVInject {
     rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
-    for (int item = wave; item < rows * HP; item += 4) {
+    for (int item = wave; item < rows * HP; item += (int)(blockDim.x >> 6)) {
       const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
       if (m >= M || gh >= n_layers * 2 * nkv) continue;
       if (valid != nullptr && (m % rpr) >= valid[m / rpr]) continue;
@@ -663,7 +670,7 @@ template <typename T> struct EpiLogits {
     __shared__ float srs[128];
     rs.fill(srs, rows, m0, M, tid);
     const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < rows; r += 4) {
+    for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
       const int m = m0 + r;
       if (m >= M) continue;
       float best = -INFINITY;

@@ -54,13 +54,26 @@ __global__ __launch_bounds__(256) void block_prep_kernel(
     slots[row] = pt[(int64_t)r * max_pages + pidx] * P + pos % P;
     if (j == 0) candidates[(int64_t)r * S] = anchor[r];
   }
+  // 8 consecutive columns per thread and pass: all loads of a pass issued
+  // before any of its stores (H is a multiple of 32)
   const T* e = embed + (int64_t)id * H;
   float acc = 0.f;
-  for (int c = tid; c < H; c += 256) {
-    const float v = Num<T>::to_f(e[c]);
-    x[(int64_t)row * H + c] = v;
-    xg[(int64_t)row * H + c] = Num<T>::from_f(v * Num<T>::to_f(g_first[c]));
-    acc += v * v;
+  for (int c0 = tid * 8; c0 < H; c0 += 256 * 8) {
+    Raw8<T> re, rg;
+    re.load(e + c0);
+    rg.load(g_first + c0);
+    float v[8], g[8];
+    re.to_f(v);
+    rg.to_f(g);
+    float* xo = x + (int64_t)row * H + c0;
+    *reinterpret_cast<float4*>(xo) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(xo + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    T* go = xg + (int64_t)row * H + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      go[i] = Num<T>::from_f(v[i] * g[i]);
+      acc += v[i] * v[i];
+    }
   }
   for (int i = tid; i < D / 2; i += 256) cs[(int64_t)row * (D / 2) + i] = rope_cs(pos, i, D, log_theta);
   acc = wave_sum(acc);
@@ -91,24 +104,37 @@ hipError_t launch_block_prep(int dt, const dflash_config& c, const void* embed,
   return hipGetLastError();
 }
 
-// Second argmax stage: one wave per logits row over the per-tile partials
+// Second argmax stage: one workgroup per logits row over the per-tile partials
 // (value, first index); ties go to the lower index.  With S > 0 row m is block
 // row (m / (S-1), 1 + m % (S-1)) of the [B, S] candidates; with S == 0 the id
 // goes to out[m].
-__global__ __launch_bounds__(64) void argmax_reduce_kernel(const float2* __restrict__ part,
-                                                           int n_tiles, int S,
-                                                           int32_t* __restrict__ candidates) {
-  const int m = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __restrict__ part,
+                                                            int n_tiles, int S,
+                                                            int32_t* __restrict__ candidates) {
+  __shared__ float wv[4];
+  __shared__ int wi[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float2* p = part + (int64_t)m * n_tiles;
+  constexpr int U = 8;  // partials per thread and pass, all loaded before the compares
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int t = lane; t < n_tiles; t += 64) {
-    const float2 p = part[(int64_t)m * n_tiles + t];
-    const int pi = __float_as_int(p.y);
-    if (p.x > best || (p.x == best && pi < bi)) {
-      best = p.x;
-      bi = pi;
+  for (int t0 = 0; t0 < n_tiles; t0 += 256 * U) {
+    float2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * 256 + tid;
+      v[u] = t < n_tiles ? p[t] : make_float2(-INFINITY, __int_as_float(0x7fffffff));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pi = __float_as_int(v[u].y);
+      if (v[u].x > best || (v[u].x == best && pi < bi)) {
+        best = v[u].x;
+        bi = pi;
+      }
     }
   }
+  // (value, lower index) is a total order: the reduction order does not matter
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(best, o, 64);
@@ -118,7 +144,17 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float2* __restr
       bi = oi;
     }
   }
-  if (lane == 0) {
+  if ((tid & 63) == 0) {
+    wv[tid >> 6] = best;
+    wi[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (wv[w] > best || (wv[w] == best && wi[w] < bi)) {
+        best = wv[w];
+        bi = wi[w];
+      }
     if (S > 0) {
       const int r = m / (S - 1), j = m % (S - 1);
       candidates[(int64_t)r * S + 1 + j] = bi;
@@ -131,7 +167,8 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float2* __restr
 hipError_t launch_argmax_reduce(const float2* part, int M, int n_tiles, int S, int32_t* candidates,
                                 hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(64), 0, st, part, n_tiles, S, candidates);
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, st, part, n_tiles, S,
+                     candidates);
   return hipGetLastError();
 }
 
