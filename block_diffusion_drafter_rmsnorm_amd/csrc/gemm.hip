@@ -40,6 +40,19 @@ __host__ __device__ __forceinline__ int64_t slab_elems(int K) {
 GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
   GemmPlan p;
   p.fat = bf16 && M > 64;
+  p.big = false;
+  if (p.fat && M > 192 && ((M + 255) / 256) * ((Ncols + 255) / 256) >= 256) {
+    // enough 256 x 256 tiles to fill the chip without splitting K (with 128
+    // rows or fewer the 128-row tiles of gemm_fat waste less)
+    p.big = true;
+    p.BM = 256;
+    p.MB = 0;
+    p.m_tiles = (M + 255) / 256;
+    p.n_tiles = (Ncols + 255) / 256;
+    p.KS = 1;
+    p.Kc = K;
+    return p;
+  }
   if (p.fat) {
     // LDS-tiled MFMA GEMM: 256 x 128 (or 128 x 128) tiles, K split until the
     // grid covers the 256 CUs
@@ -425,6 +438,137 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
   }
 }
 
+// ---------------------------------------------------------------- large tiles
+// LDS-tiled MFMA GEMM for many rows (bf16, no split K): a 256 x 256 tile per
+// workgroup of 8 waves (2 x 4, each 128 x 64), K in 32-wide stages that go
+// from global memory straight into LDS (global_load_lds, 16 bytes per lane, so
+// one wave instruction fills 1 KB: 16 A rows of 64 bytes, or one packed B
+// chunk), a ring of 4 stages with 3 in flight and one barrier per stage.  The
+// A rows of a stage are unpadded; a fragment read covers 1 KB contiguously.
+// Same XCD-grouped tile order as gemm_fat; epilogue in 128 x 128 quarters.
+constexpr int GB_STAGE = 256 * 32 + 256 * 32;  // bf16 elements: A [256][32], B [16 slabs][64][8]
+constexpr int GB_NS = 4;
+
+// 16 bytes per lane from global memory into LDS at (wave-uniform base) + 16 *
+// lane.  Inline assembly, so the compiler's wait insertion does not treat the
+// load as a pending LDS write before every LDS read (it would wait for all
+// stages in flight); the kernel waits for its stages itself, before the
+// barrier that precedes the reads.
+__device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
+               : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <class Epi>
+__global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, int K, int m_tiles,
+                                                int n_tiles, int n_tiles128, Epi epi) {
+  constexpr int SMEM = 2 * 128 * LDT * 4 > GB_NS * GB_STAGE * 2 ? 2 * 128 * LDT * 4
+                                                                 : GB_NS * GB_STAGE * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  bf16_t* const st0 = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, r16 = lane & 15, g4 = lane >> 4;
+  const int n_all = m_tiles * n_tiles;
+  const int per = (n_all + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= n_all) return;  // padding of the last XCD's range
+  const int first = (t / (FGM * n_tiles)) * FGM;
+  const int gsz = imin(m_tiles - first, FGM);
+  const int within = t % (FGM * n_tiles);
+  const int mt = first + within % gsz, nt = within / gsz;
+  const int m0 = mt * 256;
+  // this wave's two A pieces (16 rows x 32 K; lane: row l / 4, 8 columns at
+  // 8 (l % 4)) and two B slabs (slab s of the 256 columns: 128-column tile
+  // 2 nt + s / 8, slab s % 8 of it)
+  const bf16_t* ag[2];
+  const bf16_t* bg[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int row = (wave * 2 + v) * 16 + lane / 4;
+    ag[v] = asrc.A + (int64_t)block_row(imin(m0 + row, M - 1), asrc.S) * asrc.lda + (lane % 4) * 8;
+    const int s = wave * 2 + v;
+    bg[v] = epi.bslab(imin(2 * nt + s / 8, n_tiles128 - 1), s % 8) + lane * 8;
+  }
+  auto issue = [&](bf16_t* stg, int c) {  // stage of K columns [32 c, 32 c + 32)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) dma16(ag[v] + c * 32, stg + (wave * 2 + v) * 512);
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      dma16(bg[v] + (int64_t)c * kChunkElems, stg + 256 * 32 + (wave * 2 + v) * 512);
+  };
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const bf16_t* stg) {
+    Frag<bf16_t> bf[4], af[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_frag(bf[j], stg + 256 * 32 + (wn * 4 + j) * 512 + lane * 8);
+    load_frag(af[0], stg + (wm * 128 + r16) * 32 + g4 * 8);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 1 < 8) load_frag(af[(i + 1) & 1], stg + (wm * 128 + (i + 1) * 16 + r16) * 32 + g4 * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i & 1], bf[j]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read,
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then four MFMAs
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  const int n_it = K / 32;
+  bf16_t* const st1 = st0 + GB_STAGE;
+  bf16_t* const st2 = st1 + GB_STAGE;
+  bf16_t* const st3 = st2 + GB_STAGE;
+  if (0 < n_it) issue(st0, 0);
+  if (1 < n_it) issue(st1, 1);
+  if (2 < n_it) issue(st2, 2);
+  auto step = [&](int it, bf16_t* cur, bf16_t* nxt) {
+    if (it >= n_it) return;
+    // this lane's loads of stage it are done once at most those of the later
+    // stages (4 per stage) are outstanding; the barrier then covers all lanes,
+    // and also guarantees that every wave has finished reading stage it - 1,
+    // whose buffer the next issue overwrites
+    if (it + 2 < n_it) wait_vmcnt<8>();
+    else if (it + 1 < n_it) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (it + 3 < n_it) issue(nxt, it + 3);
+    compute(cur);
+  };
+  for (int it0 = 0; it0 < n_it; it0 += 4) {
+    step(it0, st0, st3);
+    step(it0 + 1, st1, st0);
+    step(it0 + 2, st2, st1);
+    step(it0 + 3, st3, st2);
+  }
+  __syncthreads();
+  float* tile0 = reinterpret_cast<float*>(smem);
+  float* tile1 = tile0 + 128 * LDT;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // rows [128 h, 128 h + 128): waves (h, 0..1) hold columns 0..127, (h, 2..3) 128..255
+    if (wm == h) {
+      float* tl = (wn < 2 ? tile0 : tile1) + (wn & 1) * 64;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tl[(i * 16 + g4 * 4 + e) * LDT + j * 16 + r16] = acc[i][j][e];
+    }
+    __syncthreads();
+    epi.apply(tile0, 128, m0 + 128 * h, M, 2 * nt, tid);
+    epi.apply(tile1, 2 * nt + 1 < n_tiles128 ? 128 : 0, m0 + 128 * h, M, 2 * nt + 1, tid);
+    __syncthreads();
+  }
+}
+
 // Split-K reduction: one workgroup per 4 rows of a tile.  Thread t sums the
 // splits q = t/128, t/128 + 2, ... of one float4 column (all loads issued before
 // the adds); the two halves are then added in a fixed order, so the result
@@ -770,6 +914,14 @@ static void launch_fat(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPl
                        p.KS, p.m_tiles, M, (const float*)partial, epi);
 }
 
+template <class Epi>
+static void launch_big(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPlan& p,
+                       int n_tiles128, const Epi& epi, hipStream_t st) {
+  const int grid = (p.m_tiles * p.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_big<Epi>), dim3(grid), dim3(512), 0, st, asrc, M, K, p.m_tiles,
+                     p.n_tiles, n_tiles128, epi);
+}
+
 template <typename T, class AS, class Epi>
 static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& epi,
                            const GemmScratch& ws, hipStream_t st) {
@@ -777,6 +929,10 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
   const GemmPlan p = plan_gemm(M, Ncols, K, sizeof(T) == 2);
   if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
+    if (p.big) {
+      launch_big(asrc, M, K, p, (Ncols + BN - 1) / BN, epi, st);
+      return hipGetLastError();
+    }
     if (p.fat) {
       if (p.BM == 256) launch_fat<256>(asrc, M, K, p, epi, ws.partial, st);
       else launch_fat<128>(asrc, M, K, p, epi, ws.partial, st);

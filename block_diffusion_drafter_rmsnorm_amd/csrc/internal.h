@@ -19,6 +19,7 @@ struct GemmScratch {
 // kernel (M <= 64, or fp32) or the LDS-tiled kernel (bf16, M > 64).
 struct GemmPlan {
   bool fat;      // LDS-tiled kernel
+  bool big;      // 256 x 256 tiles, no split K (n_tiles counts 256 columns)
   int BM;        // rows per tile (16 MB for the streaming kernel; 128 or 256)
   int MB;        // 16-row blocks per workgroup tile of the streaming kernel (1, 2, 4)
   int m_tiles;   // ceil(M / BM)

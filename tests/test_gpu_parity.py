@@ -30,7 +30,8 @@ from tests.gpu_harness import Setup, logits_row_rel_err, top2_margin, e4m3_spaci
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny_f32", "small_bf16", "small_swa_fp8", "small_f32_d64", "small_bf16_wide"]
+SMALL = ["tiny_f32", "small_bf16", "small_swa_fp8", "small_f32_d64", "small_bf16_wide",
+         "small_bf16_vocab"]
 
 
 def tol(cfg):
@@ -193,6 +194,30 @@ def test_project_context_parity(name, grid):
     live = oracle.project_context(cfg, st.np_W(), o_cache, feats.float().numpy(), pos.numpy(),
                                   slots.numpy(), None if valid is None else valid.numpy(), rpr)
     _compare_pools(st, before, o_cache, slots.numpy()[live])
+
+
+def test_project_context_large_tiles():
+    """8192 rows of the hidden-2048 model: the fc GEMM takes the 256 x 256-tile
+    path.  The oracle recomputes a sample of rows (injection is row-local)."""
+    wl = get_workload("small_bf16_wide")
+    cfg = wl.cfg
+    T = 8192
+    st = Setup(wl, extra_tokens=T)
+    feats, pos, slots, _ = _inject_case(st, T, 321)
+    st.inject(feats, pos, slots)
+    rows = np.arange(0, T, 37)
+    o_cache = oracle.OracleCache(cfg, st.num_pages * cfg.page_size)
+    oracle.project_context(cfg, st.np_W(), o_cache, feats[rows].float().numpy(),
+                           pos.numpy()[rows], slots.numpy()[rows])
+    sl = slots.numpy()[rows]
+    for l in range(cfg.n_layers):
+        for kind, pool, opool in (("k", st.cache.k[l], o_cache.k[l]),
+                                  ("v", st.cache.v[l], o_cache.v[l])):
+            g = st._pool_values(pool, transposed=(kind == "v"))[sl]
+            o = opool[sl]
+            err = np.max(np.abs(g - o), axis=-1) / np.max(np.abs(o), axis=-1)
+            _print(f"  layer {l} {kind}: {len(rows)} sampled rows, max rel err {err.max():.3e}")
+            assert err.max() <= 2e-2
 
 
 @pytest.mark.parametrize("name", ["small_bf16", "small_swa_fp8", "tiny_f32"])

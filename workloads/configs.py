@@ -104,6 +104,12 @@ SMALL_BF16_WIDE = DFlashConfig(hidden=2048, n_layers=1, n_q_heads=16, n_kv_heads
                                head_dim=128, inter=2560, vocab=4099, n_target_layers=2,
                                target_hidden=1088, block_size=16, mask_token_id=4097,
                                sliding_window=(96,))
+# A vocabulary wide enough (32777, an odd number of 128-column tiles) that the
+# lm_head of 24 x 15 rows takes the 256 x 256-tile path with a ragged last
+# row tile and a half-empty last column tile.
+SMALL_BF16_VOCAB = DFlashConfig(hidden=512, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                inter=1024, vocab=32777, n_target_layers=2, target_hidden=256,
+                                block_size=16, mask_token_id=32770)
 
 WORKLOADS = {
     "tiny_f32": Workload("tiny_f32", TINY, batch=1, ctx=(64, 64), inject_rows=64,
@@ -129,6 +135,8 @@ WORKLOADS = {
                               commit=(1, 5), seed=3),
     "small_bf16_wide": Workload("small_bf16_wide", SMALL_BF16_WIDE, batch=24, ctx=(20, 200),
                                 commit=(1, 16), seed=4),
+    "small_bf16_vocab": Workload("small_bf16_vocab", SMALL_BF16_VOCAB, batch=24, ctx=(3, 90),
+                                 commit=(1, 16), seed=5),
 }
 
 
