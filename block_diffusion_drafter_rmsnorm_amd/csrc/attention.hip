@@ -21,6 +21,8 @@
 // visible to the row at logical position p iff p - i < W; the range starts at
 // L - W + 1 (rounded down to 32 keys, the extra keys masked).  fp8 caches are
 // decoded to bf16 in registers.
+#include <type_traits>
+
 #include "common.cuh"
 #include "internal.h"
 
@@ -94,21 +96,154 @@ template <typename KT, int D> struct KVStep {
   }
 };
 
+// K/V of one 32-key step staged in LDS for the four waves, in fragment order
+// (so every fragment read is one contiguous 512 B / 1 KB wave access):
+//   K: [h][ks][lane][8]   record = K[key 16 h + l % 16][32 ks + 8 (l / 16) .. +8]
+//   V: [db][h][lane][4]   record = V^T[dim 16 db + l % 16][keys 16 h + 4 (l / 16) .. +4]
+// in the compute type CT (an fp8 cache is decoded once here, not per wave).
+// A step is moved as 16-byte pieces of the cache: K pieces first (key fastest,
+// so that a wave's LDS writes are conflict-free), then V (dim-major).
+template <typename ST, int D> struct StepPieces {
+  static constexpr int EPP = 16 / (int)sizeof(ST);          // elements per piece
+  static constexpr int NK = 2 * 16 * D / EPP;               // K pieces (both halves)
+  static constexpr int N = 2 * NK;                          // K and V pieces
+  static constexpr int PPT = N / 256;                       // pieces per thread
+};
+
+// Store the EPP values of one piece (16 raw bytes of ST) at their fragment
+// records, as 32-bit words (bf16 pairs or fp32).  K piece: key, first column
+// col0; V^T piece: dim, first key key0; both within half h.
+template <typename CT, typename ST, int D>
+__device__ __forceinline__ void stage_piece(CT* stg, const uint4& raw, int q) {
+  using SP = StepPieces<ST, D>;
+  constexpr int EPP = SP::EPP;
+  constexpr int NW = EPP * (int)sizeof(CT) / 4;  // words of the piece in CT
+  uint32_t w[NW];
+  if constexpr (std::is_same<ST, fp8_t>::value) {  // E4M3 -> bf16, exact
+    const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e4m3x4_to_bf16x4(r4[i], w[2 * i], w[2 * i + 1]);
+  } else {  // same type: the bits as they are
+    w[0] = raw.x; w[1] = raw.y; w[2] = raw.z; w[3] = raw.w;
+  }
+  uint32_t* Ks = reinterpret_cast<uint32_t*>(stg);
+  uint32_t* Vs = reinterpret_cast<uint32_t*>(stg + 32 * D);
+  constexpr int RW8 = 8 * (int)sizeof(CT) / 4;  // words of a K record (8 elements)
+  constexpr int RW4 = 4 * (int)sizeof(CT) / 4;  // words of a V record (4 elements)
+  if (q < SP::NK) {
+    // key fastest: the 16 lanes of a piece column write 16 consecutive records
+    const int h = q / (16 * (D / EPP)), rem = q % (16 * (D / EPP));
+    const int key = rem % 16, col0 = (rem / 16) * EPP;
+#pragma unroll
+    for (int i = 0; i < EPP; i += (EPP < 8 ? EPP : 8)) {
+      const int col = col0 + i;
+      const int ks = col / 32, g = (col % 32) / 8, within = col % 8;
+      uint32_t* rec = Ks + ((h * (D / 32) + ks) * 64 + key + 16 * g) * RW8 +
+                      within * (int)sizeof(CT) / 4;
+      constexpr int n = (EPP < 8 ? EPP : 8) * (int)sizeof(CT) / 4;  // words written
+      const int w0 = i * (int)sizeof(CT) / 4;
+      if constexpr (n == 4) {
+        *reinterpret_cast<uint4*>(rec) = make_uint4(w[w0], w[w0 + 1], w[w0 + 2], w[w0 + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < n; e += 4)
+          *reinterpret_cast<uint4*>(rec + e) = make_uint4(w[w0 + e], w[w0 + e + 1], w[w0 + e + 2], w[w0 + e + 3]);
+      }
+    }
+  } else {
+    const int qv = q - SP::NK;
+    const int h = qv / (D * (16 / EPP)), rem = qv % (D * (16 / EPP));
+    const int dim = rem / (16 / EPP), key0 = (rem % (16 / EPP)) * EPP;
+#pragma unroll
+    for (int i = 0; i < EPP; i += 4) {
+      const int key = key0 + i;
+      uint32_t* rec = Vs + (((dim / 16) * 2 + h) * 64 + dim % 16 + 16 * (key / 4)) * RW4;
+      const int w0 = i * (int)sizeof(CT) / 4;
+      if constexpr (RW4 == 2) *reinterpret_cast<uint2*>(rec) = make_uint2(w[w0], w[w0 + 1]);
+      else *reinterpret_cast<uint4*>(rec) = make_uint4(w[w0], w[w0 + 1], w[w0 + 2], w[w0 + 3]);
+    }
+  }
+}
+
+// 16 bytes from global memory (a global, not a flat, load: flat loads count
+// against the LDS wait counter, so the LDS barriers would wait for them)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t*>(
+      reinterpret_cast<uintptr_t>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Global address of piece q of a step whose K halves start at kp[h] (16 keys
+// x D, row stride D) and V^T halves at vp[h] (D rows x 16 keys, row stride P).
+template <typename ST, int D>
+__device__ __forceinline__ const ST* piece_src(const ST* const* kp, const ST* const* vp, int P,
+                                               int q) {
+  using SP = StepPieces<ST, D>;
+  constexpr int EPP = SP::EPP;
+  if (q < SP::NK) {
+    const int h = q / (16 * (D / EPP)), rem = q % (16 * (D / EPP));
+    return kp[h] + (rem % 16) * D + (rem / 16) * EPP;
+  }
+  const int qv = q - SP::NK;
+  const int h = qv / (D * (16 / EPP)), rem = qv % (D * (16 / EPP));
+  return vp[h] + (int64_t)(rem / (16 / EPP)) * P + (rem % (16 / EPP)) * EPP;
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its global loads in flight (a plain __syncthreads() waits for those
+// too, which would drain the prefetch pipeline at every step).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename CT, typename KT, int D>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
-  // physical pages of this workgroup's key range, read from the page table
-  // once: the K/V loads of a step then depend on LDS only, so the next step's
-  // loads go out while the current step computes
+  using SPK = StepPieces<KT, D>;
+  using SPB = StepPieces<CT, D>;
+  constexpr int STAGE = 64 * D;  // CT elements of one staged step
   __shared__ int pages[kMaxChunkPages];
+  __shared__ __attribute__((aligned(16))) CT stg_s[2][STAGE];
   const int split = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x & 63, qb = threadIdx.x >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, qb = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
+  const bool qlive = qb * 16 < R;
+  const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits + split) * 64;
+
+  // Work that does not depend on the prefix length goes first, so the memory
+  // round trips overlap: the query loads, the block's own keys (split 0), the
+  // prefix length, and on a full-attention layer (whose range starts at key
+  // split * chunk) the page-table entries of the range.
+  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
+  const int rho = imin(qb * 16 + r16, R - 1);
+  const int jrow = rho % S;
+  Frag<CT> qf[D / 32];
+  {
+    const int hl = rho / S;
+    const CT* qp = static_cast<const CT*>(a.q) + ((int64_t)(r * S + jrow) * a.nq + g * a.G + hl) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
+  }
+  uint4 rb[SPB::PPT];  // the block's own keys: one 16-key page (both halves point at it)
+  if (split == 0) {
+    const CT* kb = static_cast<const CT*>(a.kblk) + (int64_t)(r * a.nkv + g) * 16 * D;
+    const CT* vb = static_cast<const CT*>(a.vblk) + (int64_t)(r * a.nkv + g) * D * 16;
+    const CT* kp[2] = {kb, kb};
+    const CT* vp[2] = {vb, vb};
+#pragma unroll
+    for (int u = 0; u < SPB::PPT; ++u)
+      rb[u] = gload16(piece_src<CT, D>(kp, vp, 16, tid + 256 * u));
+  }
+  int pre = 0;
+  if (a.window == 0 && tid < kMaxChunkPages)
+    pre = a.pt[(int64_t)r * a.max_pages + imin((split * a.chunk) / a.P + tid, a.max_pages - 1)];
   int L, lo, a0, nvalid;
   key_range(a, r, L, lo, a0, nvalid);
   if (split >= nvalid) {
     // no keys here: an empty partial, which the combine weighs zero
-    const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits + split) * 64;
-    if (threadIdx.x < R) a.ml_part[base + threadIdx.x] = make_float2(-INFINITY, 0.f);
+    if (tid < R) a.ml_part[base + tid] = make_float2(-INFINITY, 0.f);
     return;
   }
   const int kbeg = a0 + split * a.chunk;
@@ -117,62 +252,80 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   const int pfirst = kbeg / a.P;
   if (n_ctx > 0) {
     const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
-    for (int i = threadIdx.x; i < npages; i += 256) {
-      const int pi = imin(pfirst + i, a.max_pages - 1);
-      const int64_t page = a.pt[(int64_t)r * a.max_pages + pi];
-      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
+    if (a.window == 0) {  // kbeg == split * chunk: the entries loaded above
+      if (tid < npages)
+        pages[tid] = pre < 0 ? 0 : (pre >= a.num_pages ? (int)(a.num_pages - 1) : pre);
+      for (int i = tid + 256; i < npages; i += 256) {
+        const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
+        pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
+      }
+    } else {
+      for (int i = tid; i < npages; i += 256) {
+        const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
+        pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
+      }
     }
   }
-  __syncthreads();
-  if (qb * 16 >= R) return;  // no barriers below: idle waves leave
+  lds_barrier();
 
-  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
-  Frag<CT> qf[D / 32];
-  int qpos;
-  {
-    const int rho = imin(qb * 16 + r16, R - 1);
-    const int hl = rho / S, j = rho % S;
-    const CT* qp = static_cast<const CT*>(a.q) + ((int64_t)(r * S + j) * a.nq + g * a.G + hl) * D;
+  const KT* kc = static_cast<const KT*>(a.kc);
+  const KT* vc = static_cast<const KT*>(a.vc);
+  // global loads of context step t (keys kbeg + 32 t ..) into a register set
+  auto issue = [&](uint4 (&rr)[SPK::PPT], int t) {
+    const KT *kp[2], *vp[2];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
-    qpos = L + j;
-  }
+    for (int h = 0; h < 2; ++h) {
+      const int key0 = kbeg + 32 * t + 16 * h;
+      const int64_t page = pages[key0 / a.P - pfirst];
+      const int off = key0 % a.P;
+      kp[h] = kc + ((page * a.nkv + g) * a.P + off) * D;
+      vp[h] = vc + (page * a.nkv + g) * (int64_t)D * a.P + off;
+    }
+#pragma unroll
+    for (int u = 0; u < SPK::PPT; ++u)
+      rr[u] = gload16(piece_src<KT, D>(kp, vp, a.P, tid + 256 * u));
+  };
+  auto stage_ctx = [&](CT* stg, const uint4 (&rr)[SPK::PPT]) {
+#pragma unroll
+    for (int u = 0; u < SPK::PPT; ++u) stage_piece<CT, KT, D>(stg, rr[u], tid + 256 * u);
+  };
+
+  const int qpos = L + jrow;
   float mq = -INFINITY, lq = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const KT* kc = static_cast<const KT*>(a.kc);
-  const KT* vc = static_cast<const KT*>(a.vc);
-  auto page_of = [&](int key) -> int64_t { return pages[key / a.P - pfirst]; };
-  auto load_ctx = [&](KVStep<KT, D>& st, int t0) {
-    const KT *kb[2], *vb[2];
+  // One staged 32-key step; key (16 h + 4 g4 + i) of the step is this lane's
+  // element h * 4 + i of the S^T accumulators and of the V^T / P^T fragments.
+  auto compute = [&](const CT* stg, int t0, bool is_blk) {
+    if (!qlive) return;
+    const CT* Ks = stg;
+    const CT* Vs = stg + 32 * D;
+    // keys of the step inside [lo, kend) (the block: its first S keys); an
+    // interior step has all 32 (the test is uniform across the wave)
+    const bool full = is_blk ? false : (t0 >= lo && t0 + 32 <= kend);
+    unsigned keep = 0xffu;
+    if (!full) {
+      keep = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key0 = t0 + 16 * h;
-      const int64_t page = page_of(key0);
-      const int off = key0 % a.P;
-      kb[h] = kc + ((page * a.nkv + g) * a.P + off) * D;
-      vb[h] = vc + (page * a.nkv + g) * (int64_t)D * a.P + off;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = 16 * h + 4 * g4 + i;
+          const bool ok = is_blk ? (h == 0 && kk < S) : (t0 + kk >= lo && t0 + kk < kend);
+          keep |= (ok ? 1u : 0u) << (h * 4 + i);
+        }
     }
-    st.load(kb[0], kb[1], vb[0], vb[1], a.P, r16, g4);
-  };
-
-  // One 32-key step; key (16 h + 4 g4 + i) of the step is this lane's element
-  // h * 4 + i of the S^T accumulators and of the V^T / P^T fragments.
-  auto compute = [&](const auto& st, int t0, bool is_blk, int nk) {
-    unsigned keep = 0, vis = 0;
+    unsigned vis = keep;
+    if (!is_blk && a.window > 0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * h + 4 * g4 + i;
-        const bool ok = is_blk ? (h == 0 && kk < nk) : (t0 + kk >= lo && t0 + kk < kend);
-        bool v = ok;
-        if (v && !is_blk && a.window > 0) v = (qpos - (t0 + kk)) < a.window;
-        keep |= (ok ? 1u : 0u) << (h * 4 + i);
-        vis |= (v ? 1u : 0u) << (h * 4 + i);
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 16 * (e >> 2) + 4 * g4 + (e & 3);
+        if ((qpos - (t0 + kk)) >= a.window) vis &= ~(1u << e);
       }
+    }
+    const bool masked = !full || (!is_blk && a.window > 0);
     f32x4 sacc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -180,73 +333,104 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         Frag<CT> kf;
-        raw_to_frag(kf, st.k[h][ks]);
+        load_frag(kf, Ks + ((h * (D / 32) + ks) * 64 + lane) * 8);
         mma(sacc[h], kf, qf[ks]);
       }
     }
-    float s[8];
+    Frag<CT> vf[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      load_frag_halves(vf[db], Vs + ((db * 2 + 0) * 64 + lane) * 4, Vs + ((db * 2 + 1) * 64 + lane) * 4);
+    if (!full) {
+      // keys outside the range (first and last steps only) are zeroed: their
+      // memory may hold anything
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) frag_keep(vf[db], keep);
+    }
+    float sv[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      s[e] = ((vis >> e) & 1u) ? sacc[e >> 2][e & 3] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[e]);
+      sv[e] = sacc[e >> 2][e & 3] * a.scale_log2;
+      if (masked && !((vis >> e) & 1u)) sv[e] = -INFINITY;
+      mx = fmaxf(mx, sv[e]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(mq, mx);
-    const float alpha = (mq == -INFINITY) ? 0.f : exp2f(mq - mn);
+    // The reference maximum moves only when the step's maximum exceeds it by
+    // more than 8 (log2 units): probabilities relative to it stay below 2^8,
+    // and O and l are rescaled rarely.  The final O / l does not depend on the
+    // reference (the combine and the split-level normalisation use m, l as a
+    // pair).
+    const float mold = mq;
+    const bool move = __any(mx > mold + 8.f);
+    const float mn = move ? fmaxf(mold, mx) : mold;
+    // exp2 by the hardware instruction: exp2(-inf) = 0; the subtrahend is kept
+    // finite so that a column with no visible key yet stays all zero
+    const float msub = (mn == -INFINITY) ? 0.f : mn;
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      s[e] = (s[e] == -INFINITY) ? 0.f : exp2f(s[e] - mn);
-      sum += s[e];
+      sv[e] = __builtin_amdgcn_exp2f(sv[e] - msub);
+      sum += sv[e];
     }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
-    lq = lq * alpha + sum;
+    if (move) {
+      const float alpha = __builtin_amdgcn_exp2f(mold - msub);
+      lq *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
+    }
+    lq += sum;
     mq = mn;
     Frag<CT> pf;
-    frag_from_f32(pf, s);
+    frag_from_f32(pf, sv);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      Frag<CT> vf;
-      raw4x2_to_frag(vf, st.v[db][0], st.v[db][1], keep);  // keys past the range may hold garbage
-      o[db] *= alpha;
-      mma(o[db], vf, pf);
-    }
+    for (int db = 0; db < D / 16; ++db) mma(o[db], vf[db], pf);
   };
 
-  if (n_ctx > 0) {
-    KVStep<KT, D> s0, s1;
-    load_ctx(s0, kbeg);
-    int t = 0;
-    for (; t + 2 <= n_ctx; t += 2) {
-      load_ctx(s1, kbeg + (t + 1) * 32);
-      compute(s0, kbeg + t * 32, false, 0);
-      if (t + 2 < n_ctx) load_ctx(s0, kbeg + (t + 2) * 32);
-      compute(s1, kbeg + (t + 1) * 32, false, 0);
-    }
-    if (t < n_ctx) compute(s0, kbeg + t * 32, false, 0);
-  }
+  // context steps: loads four steps ahead in registers, LDS double buffer
+  uint4 rr0[SPK::PPT], rr1[SPK::PPT], rr2[SPK::PPT], rr3[SPK::PPT], rr4[SPK::PPT];
+  if (0 < n_ctx) issue(rr0, 0);
+  if (1 < n_ctx) issue(rr1, 1);
+  if (2 < n_ctx) issue(rr2, 2);
+  if (3 < n_ctx) issue(rr3, 3);
   if (split == 0) {
-    // the block's own keys: one 16-key page of K and V^T in the block buffers
-    KVStep<CT, D> sb;
-    const CT* kb = static_cast<const CT*>(a.kblk) + (int64_t)(r * a.nkv + g) * 16 * D;
-    const CT* vb = static_cast<const CT*>(a.vblk) + (int64_t)(r * a.nkv + g) * D * 16;
-    sb.load(kb, kb, vb, vb, 16, r16, g4);
-    compute(sb, 0, true, S);
+#pragma unroll
+    for (int u = 0; u < SPB::PPT; ++u) stage_piece<CT, CT, D>(stg_s[1], rb[u], tid + 256 * u);
+    lds_barrier();
+    compute(stg_s[1], 0, true);
+  }
+  if (n_ctx > 0) {
+    stage_ctx(stg_s[0], rr0);
+    lds_barrier();
+    auto step = [&](int t, uint4 (&cur_next)[SPK::PPT], uint4 (&nxt)[SPK::PPT]) {
+      // cur_next: the set that held step t - 1 (free now) -> step t + 4;
+      // nxt: the set holding step t + 1
+      if (t >= n_ctx) return;
+      if (t + 4 < n_ctx) issue(cur_next, t + 4);
+      compute(stg_s[t & 1], kbeg + 32 * t, false);
+      if (t + 1 < n_ctx) stage_ctx(stg_s[(t + 1) & 1], nxt);
+      lds_barrier();
+    };
+    for (int t0 = 0; t0 < n_ctx; t0 += 5) {
+      step(t0, rr4, rr1);
+      step(t0 + 1, rr0, rr2);
+      step(t0 + 2, rr1, rr3);
+      step(t0 + 3, rr2, rr4);
+      step(t0 + 4, rr3, rr0);
+    }
   }
 
   // unnormalised O^T, and (m, l) per query row
-  const int rho = qb * 16 + r16;
-  if (rho < R) {
-    const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits + split) * 64;
-    float* dst = a.o_part + (base + rho) * D;
+  if (qlive && qb * 16 + r16 < R) {
+    float* dst = a.o_part + (base + qb * 16 + r16) * D;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       *reinterpret_cast<float4*>(dst + db * 16 + g4 * 4) =
           make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-    if (g4 == 0) a.ml_part[base + rho] = make_float2(mq, lq);
+    if (g4 == 0) a.ml_part[base + qb * 16 + r16] = make_float2(mq, lq);
   }
 }
 
@@ -287,11 +471,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __res
         l[u] = __shfl(wl, src, 64);
         if (s1 + u >= ns) w[u] = 0.f;
       }
+      // the O loads do not wait for the weights: an empty split's O (never
+      // written, any bits) is dropped by the select below, not multiplied
 #pragma unroll
       for (int u = 0; u < 16; ++u)
 #pragma unroll
         for (int e = 0; e < D / 64; ++e)
-          v[u][e] = w[u] != 0.f
+          v[u][e] = s1 + u < ns
                         ? a.o_part[(base + (int64_t)(s0 + s1 + u) * 64) * D + lane + 64 * e]
                         : 0.f;
 #pragma unroll

@@ -6,6 +6,7 @@
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_hw;
 
 // bfloat16 held as raw bits; arithmetic always goes through fp32.
 struct bf16_t {
@@ -130,12 +131,15 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag
 }
 
 // Build a fragment from 8 fp32 values.
+// Two fp32 -> two bf16 (round to nearest even) in one instruction on gfx950;
+// equal to f32_to_bf16 on every non-NaN input.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_hw v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 __device__ __forceinline__ void frag_from_f32(Frag<bf16_t>& f, const float* x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
-  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+  f.v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7]));
 }
 __device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
   f.lo = make_float4(x[0], x[1], x[2], x[3]);
@@ -250,6 +254,78 @@ __device__ __forceinline__ void raw4x2_to_frag<bf16_t, bf16_t>(Frag<bf16_t>& f,
     o[i] = w[i] & m;
   }
   f.v = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Four E4M3 bytes -> two words of two bf16 each, by the gfx950 conversion
+// instruction (exact: every E4M3 value is a bf16 value; equal to
+// f32_to_bf16(e4m3_to_f32(.)) on every code but the NaN payload).
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ __forceinline__ void raw_to_frag<bf16_t, fp8_t>(Frag<bf16_t>& f, const Raw8<fp8_t>& r) {
+  uint32_t w[4];
+  e4m3x4_to_bf16x4(r.v.x, w[0], w[1]);
+  e4m3x4_to_bf16x4(r.v.y, w[2], w[3]);
+  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+// Two 4-element pieces -> fragment, without masking.
+template <typename CT, typename KT>
+__device__ __forceinline__ void raw4x2_to_frag_all(Frag<CT>& f, const Raw4<KT>& a,
+                                                   const Raw4<KT>& b) {
+  float t[8];
+  a.to_f(t);
+  b.to_f(t + 4);
+  frag_from_f32(f, t);
+}
+template <>
+__device__ __forceinline__ void raw4x2_to_frag_all<bf16_t, bf16_t>(Frag<bf16_t>& f,
+                                                                   const Raw4<bf16_t>& a,
+                                                                   const Raw4<bf16_t>& b) {
+  f.v = make_uint4(a.v.x, a.v.y, b.v.x, b.v.y);
+}
+template <>
+__device__ __forceinline__ void raw4x2_to_frag_all<bf16_t, fp8_t>(Frag<bf16_t>& f,
+                                                                  const Raw4<fp8_t>& a,
+                                                                  const Raw4<fp8_t>& b) {
+  uint32_t w[4];
+  e4m3x4_to_bf16x4(a.v, w[0], w[1]);
+  e4m3x4_to_bf16x4(b.v, w[2], w[3]);
+  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ void raw4x2_to_frag_all<float, float>(Frag<float>& f,
+                                                                 const Raw4<float>& a,
+                                                                 const Raw4<float>& b) {
+  f.lo = a.v;
+  f.hi = b.v;
+}
+// Fragment from two 4-element halves (elements 0..3 at p0, 4..7 at p1).
+__device__ __forceinline__ void load_frag_halves(Frag<bf16_t>& f, const bf16_t* p0, const bf16_t* p1) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
+  f.v = make_uint4(a.x, a.y, b.x, b.y);
+}
+__device__ __forceinline__ void load_frag_halves(Frag<float>& f, const float* p0, const float* p1) {
+  f.lo = *reinterpret_cast<const float4*>(p0);
+  f.hi = *reinterpret_cast<const float4*>(p1);
+}
+// Element e of a fragment zeroed unless bit e of keep is set.
+__device__ __forceinline__ void frag_keep(Frag<bf16_t>& f, unsigned keep) {
+  uint32_t w[4] = {f.v.x, f.v.y, f.v.z, f.v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] &= (((keep >> (2 * i)) & 1u) ? 0x0000ffffu : 0u) |
+            (((keep >> (2 * i + 1)) & 1u) ? 0xffff0000u : 0u);
+  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void frag_keep(Frag<float>& f, unsigned keep) {
+  float t[8] = {f.lo.x, f.lo.y, f.lo.z, f.lo.w, f.hi.x, f.hi.y, f.hi.z, f.hi.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (!((keep >> e) & 1u)) t[e] = 0.f;
+  f.lo = make_float4(t[0], t[1], t[2], t[3]);
+  f.hi = make_float4(t[4], t[5], t[6], t[7]);
 }
 
 // ---------------------------------------------------------------- reductions
