@@ -76,9 +76,10 @@ GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
   p.n_tiles = (Ncols + BN - 1) / BN;
   int ks = 1;
   if (M <= 64) {
-    // Split K so that the grid reaches ~512 workgroups.  The split depends on
+    // Split K so that the grid reaches ~1024 workgroups (4 per CU: enough
+    // weight loads in flight for the HBM rate).  The split depends on
     // (Ncols, K) only, so the same rows give the same bits at any M <= 64.
-    ks = (512 + p.n_tiles - 1) / p.n_tiles;
+    ks = (1024 + p.n_tiles - 1) / p.n_tiles;
     ks = ks < K / 256 ? ks : K / 256;
   } else {
     const int base = p.n_tiles * p.m_tiles;
@@ -154,6 +155,14 @@ struct RowScale {
     __syncthreads();
   }
 };
+
+// 1/rms of the rows of the tile an epilogue works on: filled by the
+// epilogue's prepare() (before the tile is complete where possible), read by
+// its apply().
+__device__ __forceinline__ float* row_scale_lds() {
+  __shared__ float srs[128];
+  return srs;
+}
 
 // Inputs of the next RMSNorm written by a producer epilogue: xg = x * g rounded
 // to T (xg == null: nothing written).
@@ -264,6 +273,7 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
         for (int i = 0; i < 4; ++i)
           tile[(mb * 16 + g4 * 4 + i) * LDT + wave * 32 + nb * 16 + r16] = acc[mb][nb][i];
     __syncthreads();
+    epi.prepare(16 * MB, m0, M, tid);
     epi.apply(tile, 16 * MB, m0, M, nt, tid);
     return;
   }
@@ -433,6 +443,7 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
           tile[(row % 128 + g4 * 4 + e) * LDT + wn * 64 + j * 16 + r16] = acc[i][j][e];
     }
     __syncthreads();
+    epi.prepare(128, m0 + 128 * h, M, tid);
     epi.apply(tile, 128, m0 + 128 * h, M, nt, tid);
     __syncthreads();
   }
@@ -563,6 +574,7 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
           for (int e = 0; e < 4; ++e) tl[(i * 16 + g4 * 4 + e) * LDT + j * 16 + r16] = acc[i][j][e];
     }
     __syncthreads();
+    epi.prepare(128, m0 + 128 * h, M, tid);
     epi.apply(tile0, 128, m0 + 128 * h, M, 2 * nt, tid);
     epi.apply(tile1, 2 * nt + 1 < n_tiles128 ? 128 : 0, m0 + 128 * h, M, 2 * nt + 1, tid);
     __syncthreads();
@@ -570,9 +582,9 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
 }
 
 // Split-K reduction: one workgroup per 4 rows of a tile.  Thread t sums the
-// splits q = t/128, t/128 + 2, ... of one float4 column (all loads issued before
-// the adds); the two halves are then added in a fixed order, so the result
-// does not depend on timing.
+// splits q = t/128, t/128 + 2, ... of one float4 column (in split order, all
+// loads issued before the adds); the two halves are then added in a fixed
+// order, so the result does not depend on timing.
 constexpr int RROWS = 4;
 template <int TROWS, class Epi>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, int M,
@@ -588,14 +600,29 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
   const int i4 = tid & 127, h = tid >> 7;
   const int row = i4 / (BN / 4), c = (i4 % (BN / 4)) * 4;
   const float* p = partial + (int64_t)tix * KS * tile_elems + (int64_t)(rb * RROWS + row) * BN + c;
+  // the loads of (up to) the first 32 splits go out first; the epilogue's
+  // own inputs (row scales) are fetched while they are in flight
+  constexpr int QB = 16;
+  float4 v[QB];
+#pragma unroll
+  for (int u = 0; u < QB; ++u)
+    v[u] = (h + 2 * u < KS) ? *reinterpret_cast<const float4*>(p + (int64_t)(h + 2 * u) * tile_elems)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  epi.prepare(RROWS, mt * TROWS + rb * RROWS, M, tid);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int q = h; q < KS; q += 2) {
-    const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)q * tile_elems);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+#pragma unroll
+  for (int u = 0; u < QB; ++u) {
+    s.x += v[u].x;
+    s.y += v[u].y;
+    s.z += v[u].z;
+    s.w += v[u].w;
+  }
+  for (int q = h + 2 * QB; q < KS; q += 2) {
+    const float4 w = *reinterpret_cast<const float4*>(p + (int64_t)q * tile_elems);
+    s.x += w.x;
+    s.y += w.y;
+    s.z += w.z;
+    s.w += w.w;
   }
   if (h == 1) half1[i4] = s;
   __syncthreads();
@@ -643,6 +670,7 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
 
 template <typename T> struct EpiStoreF32 {
   const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn;
+  __device__ void prepare(int, int, int, int) const {}
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
@@ -657,6 +685,7 @@ template <typename T> struct EpiStoreF32 {
 
 template <typename T> struct EpiResidual {
   const T* W; int N; int K; float* x; float* ss; NextNorm<T> nn;
+  __device__ void prepare(int, int, int, int) const {}
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
@@ -673,13 +702,15 @@ template <typename T> struct EpiResidual {
 // Tile columns 0..63 are gate rows nt*64.., columns 64..127 the matching up rows.
 template <typename T> struct EpiSiluMul {
   const T* Wg; const T* Wu; int I; int K; T* act; RowScale rs;
+  __device__ void prepare(int rows, int m0, int M, int tid) const {
+    rs.fill(row_scale_lds(), rows, m0, M, tid);
+  }
   __device__ const T* bslab(int nt, int s) const {
     const int n = imin(nt * 64 + (16 * s & 63), I - 1);
     return (s < 4 ? Wg : Wu) + (int64_t)(n / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[128];
-    rs.fill(srs, rows, m0, M, tid);
+    const float* srs = row_scale_lds();
     for (int idx = tid; idx < rows * 64; idx += (int)blockDim.x) {
       const int r = idx / 64, c = idx % 64, m = m0 + r, n = nt * 64 + c;
       if (m < M && n < I) {
@@ -713,12 +744,14 @@ __device__ __forceinline__ void norm_rope_pair(float x0, float x1, int i, int D,
 template <typename T> struct EpiQKV {
   const T* W; int H; int nq, nkv, D; const T* qn; const T* kn; float eps;
   const float2* cs; T* q; T* k; T* v; RowScale rs; int S;
+  __device__ void prepare(int rows, int m0, int M, int tid) const {
+    rs.fill(row_scale_lds(), rows, m0, M, tid);
+  }
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, (nq + 2 * nkv) * D - 1) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[128];
-    rs.fill(srs, rows, m0, M, tid);
+    const float* srs = row_scale_lds();
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
     for (int item = wave; item < rows * HP; item += (int)(blockDim.x >> 6)) {
@@ -760,6 +793,9 @@ template <typename T> struct EpiQKV {
 template <typename T, typename KT> struct EpiKVInject {
   KVTargets tg; int H; int n_layers, nq, nkv, D; float eps; const float2* cs;
   const int32_t* slots; const int32_t* valid; int rpr; int P; int64_t num_slots; RowScale rs;
+  __device__ void prepare(int rows, int m0, int M, int tid) const {
+    rs.fill(row_scale_lds(), rows, m0, M, tid);
+  }
   __device__ const T* bslab(int nt, int s) const {
     const int per = 2 * nkv * D;
     const int n = imin(nt * BN + 16 * s, n_layers * per - 1);
@@ -767,8 +803,7 @@ template <typename T, typename KT> struct EpiKVInject {
     return static_cast<const T*>(tg.w_qkv[l]) + (int64_t)((nq * D + w) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[128];
-    rs.fill(srs, rows, m0, M, tid);
+    const float* srs = row_scale_lds();
     const int lane = tid & 63, wave = tid >> 6;
     const int HP = BN / D, half = D / 2;
     for (int item = wave; item < rows * HP; item += (int)(blockDim.x >> 6)) {
@@ -807,12 +842,14 @@ template <typename T, typename KT> struct EpiKVInject {
 // then the (max, first index) of every row over the slice.
 template <typename T> struct EpiLogits {
   const T* W; int V; int H; T* logits; float2* part; int n_tiles; RowScale rs;
+  __device__ void prepare(int rows, int m0, int M, int tid) const {
+    rs.fill(row_scale_lds(), rows, m0, M, tid);
+  }
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, V - 1) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    __shared__ float srs[128];
-    rs.fill(srs, rows, m0, M, tid);
+    const float* srs = row_scale_lds();
     const int lane = tid & 63, wave = tid >> 6;
     for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
       const int m = m0 + r;
