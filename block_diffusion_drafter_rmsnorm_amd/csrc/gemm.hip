@@ -137,20 +137,32 @@ struct RowScale {
   float eps;
   int S;
   // 1/rms of the tile's rows m0 .. m0+rows-1 into out[] (LDS), one wave per row
-  // (lanes load the row's partial sums in parallel, summed in a fixed tree).
+  // (lanes load the row's partial sums in parallel, summed in a fixed tree;
+  // a wave issues the loads of 8 rows before it sums any).
   // Called by all threads of the workgroup; ends with a barrier.
   __device__ __forceinline__ void fill(float* out, int rows, int m0, int M, int tid) const {
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
-      float v = 1.0f;
-      if (ss != nullptr) {
+    const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
+    constexpr int G = 8;
+    for (int r0 = wave; r0 < rows; r0 += nw * G) {
+      float acc[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int r = r0 + nw * u;
         const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
-        float acc = 0.f;
-        for (int t = lane; t < n_ss; t += 64) acc += p[t];
-        acc = wave_sum(acc);
-        v = 1.0f / sqrtf(acc / (float)H + eps);
+        acc[u] = (ss != nullptr && r < rows && lane < n_ss) ? p[lane] : 0.f;
       }
-      if (lane == 0) out[r] = v;
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int r = r0 + nw * u;
+        if (r >= rows) break;
+        float v = 1.0f;
+        if (ss != nullptr) {
+          const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+          for (int t = lane + 64; t < n_ss; t += 64) acc[u] += p[t];
+          v = 1.0f / sqrtf(wave_sum(acc[u]) / (float)H + eps);
+        }
+        if (lane == 0) out[r] = v;
+      }
     }
     __syncthreads();
   }
@@ -643,27 +655,50 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
 // Row-wise pass over a [rows, 128] fp32 tile (one wave per row, two columns per
 // lane); f returns the value stored for (row, col), whose squares are summed
 // into the row's partial sum of squares over the tile when ss != null.
-template <typename T, typename F>
+template <typename T, typename FL, typename F>
 __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N, int tid,
-                                         float* ss, int n_ss, const NextNorm<T>& nn, F&& f) {
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
-    const int m = m0 + r;
-    if (m >= M) continue;
-    float acc = 0.f;
+                                         float* ss, int n_ss, const NextNorm<T>& nn, FL&& in,
+                                         F&& f) {
+  const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
+  float gn[2] = {0.f, 0.f};  // the next norm's gain at this lane's two columns
+  if (nn.xg != nullptr) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int c = lane + 64 * h, n = nt * BN + c;
-      if (n < N) {
-        const float v = f(r, c, m, n);
-        acc += v * v;
-        if (nn.xg != nullptr)
-          nn.xg[(int64_t)m * N + n] = Num<T>::from_f(v * Num<T>::to_f(nn.g[n]));
-      }
+      const int n = nt * BN + lane + 64 * h;
+      gn[h] = n < N ? Num<T>::to_f(nn.g[n]) : 0.f;
     }
-    if (ss != nullptr) {
-      acc = wave_sum(acc);
-      if (lane == 0) ss[(int64_t)m * n_ss + nt] = acc;
+  }
+  // rows in groups of 4 per wave: the group's input loads go out before any
+  // of its rows is finished
+  constexpr int G = 4;
+  for (int r0 = wave; r0 < rows; r0 += nw * G) {
+    float iv[G][2];
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = r0 + nw * u, m = m0 + r, n = nt * BN + lane + 64 * h;
+        iv[u][h] = (r < rows && m < M && n < N) ? in(m, n) : 0.f;
+      }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int r = r0 + nw * u, m = m0 + r;
+      if (r >= rows) break;
+      if (m >= M) continue;
+      float acc = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = lane + 64 * h, n = nt * BN + c;
+        if (n < N) {
+          const float v = f(r, c, m, n, iv[u][h]);
+          acc += v * v;
+          if (nn.xg != nullptr) nn.xg[(int64_t)m * N + n] = Num<T>::from_f(v * gn[h]);
+        }
+      }
+      if (ss != nullptr) {
+        acc = wave_sum(acc);
+        if (lane == 0) ss[(int64_t)m * n_ss + nt] = acc;
+      }
     }
   }
 }
@@ -675,11 +710,12 @@ template <typename T> struct EpiStoreF32 {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int r, int c, int m, int n) {
-      const float v = t[r * LDT + c];
-      if (out != nullptr) out[(int64_t)m * ldo + n] = v;
-      return v;
-    });
+    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int, int) { return 0.f; },
+             [&](int r, int c, int m, int n, float) {
+               const float v = t[r * LDT + c];
+               if (out != nullptr) out[(int64_t)m * ldo + n] = v;
+               return v;
+             });
   }
 };
 
@@ -690,12 +726,13 @@ template <typename T> struct EpiResidual {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
-    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int r, int c, int m, int n) {
-      float* p = x + (int64_t)m * N + n;
-      const float v = *p + t[r * LDT + c];
-      *p = v;
-      return v;
-    });
+    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn,
+             [&](int m, int n) { return x[(int64_t)m * N + n]; },
+             [&](int r, int c, int m, int n, float res) {
+               const float v = res + t[r * LDT + c];
+               x[(int64_t)m * N + n] = v;
+               return v;
+             });
   }
 };
 
@@ -790,11 +827,58 @@ template <typename T> struct EpiQKV {
 
 // Stacked K/V rows of every layer: column n -> layer n / (2 nkv D), then the
 // k rows and v rows of that layer's w_qkv (which start after the nq*D q rows).
+// Sixteen consecutive values of one Vᵀ cache row (16 keys of one dim) stored
+// as one contiguous run.
+__device__ __forceinline__ void store_run16(bf16_t* dst, const float* v) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+  reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+__device__ __forceinline__ void store_run16(fp8_t* dst, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_e4m3(v[4 * i]) | ((uint32_t)f32_to_e4m3(v[4 * i + 1]) << 8) |
+           ((uint32_t)f32_to_e4m3(v[4 * i + 2]) << 16) | ((uint32_t)f32_to_e4m3(v[4 * i + 3]) << 24);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void store_run16(float* dst, const float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    reinterpret_cast<float4*>(dst)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+// Per 16-row block of an epilogue tile: 1 when all 16 rows are written to 16
+// consecutive slots starting at a multiple of 16 (so within one page, whose
+// size is a multiple of 16): their Vᵀ values then go out as contiguous runs.
+__device__ __forceinline__ int* kv_block_flags() {
+  __shared__ int f[8];
+  return f;
+}
+
 template <typename T, typename KT> struct EpiKVInject {
   KVTargets tg; int H; int n_layers, nq, nkv, D; float eps; const float2* cs;
   const int32_t* slots; const int32_t* valid; int rpr; int P; int64_t num_slots; RowScale rs;
+  __device__ bool row_written(int m, int M) const {
+    if (m >= M) return false;
+    if (valid != nullptr && (m % rpr) >= valid[m / rpr]) return false;
+    const int64_t slot = slots[m];
+    return slot >= 0 && slot < num_slots;  // outside the pool: never written
+  }
   __device__ void prepare(int rows, int m0, int M, int tid) const {
-    rs.fill(row_scale_lds(), rows, m0, M, tid);
+    // thread r checks row r against the first row of its 16-row block; a
+    // block qualifies when all 16 lanes of its group agree (one ballot)
+    if (rows >= 16 && tid < (rows & ~15)) {
+      const int r = tid, m = m0 + r, mb = m0 + (r & ~15);
+      const int32_t s0 = slots[imin(mb, M - 1)];
+      const bool ok = row_written(m, M) && slots[m] == s0 + (r & 15) && (s0 % 16) == 0;
+      const uint64_t b = __ballot(ok);
+      if ((r & 15) == 0) kv_block_flags()[r / 16] = ((b >> (tid & 63 & ~15)) & 0xffffull) == 0xffffull;
+    }
+    rs.fill(row_scale_lds(), rows, m0, M, tid);  // ends with a barrier
   }
   __device__ const T* bslab(int nt, int s) const {
     const int per = 2 * nkv * D;
@@ -804,35 +888,92 @@ template <typename T, typename KT> struct EpiKVInject {
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
     const float* srs = row_scale_lds();
-    const int lane = tid & 63, wave = tid >> 6;
-    const int HP = BN / D, half = D / 2;
-    for (int item = wave; item < rows * HP; item += (int)(blockDim.x >> 6)) {
-      const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
-      if (m >= M || gh >= n_layers * 2 * nkv) continue;
-      if (valid != nullptr && (m % rpr) >= valid[m / rpr]) continue;
-      const int64_t slot = slots[m];
-      if (slot < 0 || slot >= num_slots) continue;  // outside the pool: never written
-      const int l = gh / (2 * nkv), rem = gh % (2 * nkv);
-      const bool is_v = rem >= nkv;
-      const int head = rem % nkv;
-      const bool act = lane < half;
-      const float sc = srs[r];
-      const float x0 = act ? t[r * LDT + hh * D + lane] * sc : 0.f;
-      const float x1 = act ? t[r * LDT + hh * D + lane + half] * sc : 0.f;
-      float o0 = x0, o1 = x1;
-      if (!is_v)
-        norm_rope_pair<T>(x0, x1, lane, D, act, static_cast<const T*>(tg.k_norm[l]), eps,
-                          cs + (int64_t)m * half, o0, o1);
-      const int64_t page = slot / P, off = slot % P;
-      if (!act) continue;
-      if (is_v) {  // V pages are stored transposed: [page][head][D][P]
-        KT* dst = static_cast<KT*>(tg.vc[l]) + ((page * nkv + head) * D) * P + off;
-        dst[(int64_t)lane * P] = Num<KT>::from_f(o0);
-        dst[(int64_t)(lane + half) * P] = Num<KT>::from_f(o1);
-      } else {     // K pages: [page][head][P][D]
-        KT* dst = static_cast<KT*>(tg.kc[l]) + ((page * nkv + head) * P + off) * D;
-        dst[lane] = Num<KT>::from_f(o0);
-        dst[lane + half] = Num<KT>::from_f(o1);
+    const int* bok = kv_block_flags();
+    const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
+    const int HP = BN / D, half = D / 2, n_items = rows * HP;
+    // k_norm gains of the tile's K heads (a tile holds HP <= 2 heads), loaded once
+    float gk[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    for (int hh = 0; hh < HP; ++hh) {
+      const int gh = nt * HP + hh;
+      if (gh < n_layers * 2 * nkv && (gh % (2 * nkv)) < nkv && lane < half) {
+        const T* g = static_cast<const T*>(tg.k_norm[gh / (2 * nkv)]);
+        gk[hh][0] = Num<T>::to_f(g[lane]);
+        gk[hh][1] = Num<T>::to_f(g[lane + half]);
+      }
+    }
+    constexpr int G = 4;  // items per wave whose loads go out together
+    for (int ib = wave; ib < n_items; ib += nw * G) {
+      int32_t sl[G], vr[G];
+      float2 c[G];
+      int kind[G];  // 0 skip, 1 K row, 2 V row, 3 V block of 16 rows
+      // loads first, unconditionally (clamped rows), so that none waits for
+      // another's result; the decisions follow
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int item = ib + nw * u;
+        const int m = imin(m0 + imin(item, n_items - 1) / HP, M - 1);
+        sl[u] = slots[m];
+        vr[u] = valid != nullptr ? valid[m / rpr] : rpr;
+        c[u] = lane < half ? cs[(int64_t)m * half + lane] : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int item = ib + nw * u;
+        const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
+        kind[u] = 0;
+        if (item >= n_items || m >= M || gh >= n_layers * 2 * nkv) continue;
+        const bool is_v = (gh % (2 * nkv)) >= nkv;
+        if (is_v && rows >= 16 && bok[r / 16]) {
+          kind[u] = (r % 16 == 0) ? 3 : 0;
+          continue;
+        }
+        const bool written = (m % rpr) < vr[u] && sl[u] >= 0 && sl[u] < num_slots;
+        if (written) kind[u] = is_v ? 2 : 1;
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (kind[u] == 0) continue;
+        const int item = ib + nw * u;
+        const int r = item / HP, hh = item % HP, gh = nt * HP + hh;
+        const int l = gh / (2 * nkv), head = gh % nkv;
+        const int64_t page = sl[u] / P, off = sl[u] % P;
+        if (kind[u] == 3) {
+          // the block's first row: this wave writes all 16 rows, lane = dim
+          KT* base = static_cast<KT*>(tg.vc[l]) + ((page * nkv + head) * D) * P + off;
+          for (int d = lane; d < D; d += 64) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = t[(r + i) * LDT + hh * D + d] * srs[r + i];
+            store_run16(base + (int64_t)d * P, v);
+          }
+          continue;
+        }
+        const bool act = lane < half;
+        const float sc = srs[r];
+        const float x0 = act ? t[r * LDT + hh * D + lane] * sc : 0.f;
+        const float x1 = act ? t[r * LDT + hh * D + lane + half] * sc : 0.f;
+        float o0 = x0, o1 = x1;
+        if (kind[u] == 1) {
+          // per-head RMSNorm (gain k_norm) and neox RoPE with the row's (cos, sin)
+          const float ss = wave_sum(act ? x0 * x0 + x1 * x1 : 0.f);
+          const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+          if (act) {
+            const float y0 = x0 * inv * (hh ? gk[1][0] : gk[0][0]);
+            const float y1 = x1 * inv * (hh ? gk[1][1] : gk[0][1]);
+            o0 = y0 * c[u].x - y1 * c[u].y;
+            o1 = y1 * c[u].x + y0 * c[u].y;
+          }
+        }
+        if (!act) continue;
+        if (kind[u] == 2) {  // V pages are stored transposed: [page][head][D][P]
+          KT* dst = static_cast<KT*>(tg.vc[l]) + ((page * nkv + head) * D) * P + off;
+          dst[(int64_t)lane * P] = Num<KT>::from_f(o0);
+          dst[(int64_t)(lane + half) * P] = Num<KT>::from_f(o1);
+        } else {             // K pages: [page][head][P][D]
+          KT* dst = static_cast<KT*>(tg.kc[l]) + ((page * nkv + head) * P + off) * D;
+          dst[lane] = Num<KT>::from_f(o0);
+          dst[lane + half] = Num<KT>::from_f(o1);
+        }
       }
     }
   }
