@@ -157,7 +157,7 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
 
 struct DraftWs {
   float* x; float* ss; void* xg; void* act; void* q; void* kb; void* vb; void* o; float2* cs;
-  float* o_part; float2* ml_part; float2* lm_part; GemmScratch gs; size_t bytes;
+  float* o_part; float2* ml_part; int4* seg; float2* lm_part; GemmScratch gs; size_t bytes;
   AttnPlan plans[DFLASH_MAX_LAYERS];
 };
 
@@ -182,13 +182,16 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   L.vb = cv.take(ab * (size_t)B * nkv * 16 * D);
   L.o = cv.take(ab * (size_t)M * nq * D);
   L.cs = (float2*)cv.take(sizeof(float2) * (size_t)M * (D / 2));
-  int max_splits = 1;
+  // one (O, m, l) partial of 64 query rows per attention workgroup
+  const bool dma = c->act_dtype == DFLASH_BF16 && c->kv_dtype == DFLASH_BF16;
+  size_t max_launch = 1;
   for (int l = 0; l < c->n_layers; ++l) {
-    L.plans[l] = plan_attention(layer_max_keys(c, l, max_prefix), B, nkv);
-    if (L.plans[l].n_splits > max_splits) max_splits = L.plans[l].n_splits;
+    L.plans[l] = plan_attention(layer_max_keys(c, l, max_prefix), B, nkv, dma);
+    if ((size_t)L.plans[l].n_partials > max_launch) max_launch = (size_t)L.plans[l].n_partials;
   }
-  L.o_part = (float*)cv.take(sizeof(float) * (size_t)B * nkv * max_splits * 64 * D);
-  L.ml_part = (float2*)cv.take(sizeof(float2) * (size_t)B * nkv * max_splits * 64);
+  L.o_part = (float*)cv.take(sizeof(float) * max_launch * 64 * D);
+  L.ml_part = (float2*)cv.take(sizeof(float2) * max_launch * 64);
+  L.seg = (int4*)cv.take(sizeof(int4) * (size_t)B);
   L.lm_part = (float2*)cv.take(sizeof(float2) * (size_t)M1 * logits_tiles(c->vocab));
   const bool bf = c->act_dtype == DFLASH_BF16;
   const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H, bf), plan_gemm(M, H, nq * D, bf),
@@ -381,7 +384,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     if ((e = launch_attention(dt, cfg->kv_dtype, D, L.q, L.kb, L.vb, cache->k[l], cache->v[l],
                               page_table, max_pages, cache->num_pages, prefix_len, max_prefix_len,
                               batch, S, nq, nkv, cfg->page_size, cfg->sliding_window[l],
-                              L.plans[l], L.o_part, L.ml_part, L.o, st)) != hipSuccess)
+                              L.plans[l], L.o_part, L.ml_part, L.seg, L.o, st)) != hipSuccess)
       return hip_fail(e, "attention");
     if ((e = gemm_residual(dt, asrc_plain(L.o, nq * D), M, nq * D, W.w_o, H, L.x, L.ss, L.xg,
                            W.post_norm, L.gs, st)) != hipSuccess)

@@ -29,28 +29,48 @@
 namespace dflash {
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int kMaxChunk = 4096;                   // context keys per workgroup
-constexpr int kMaxChunkPages = kMaxChunk / 16 + 8;  // page-table entries it can touch
+constexpr int kMaxSteps = 128;                      // 32-key steps per workgroup (at most)
+constexpr int kMaxChunkPages = kMaxSteps * 32 / 16 + 8;  // page-table entries it can touch
+constexpr int kCUs = 256;                           // compute units the plan fills
+constexpr int kDeepSteps = 8;                       // workgroup size of the deep pipeline
 
-AttnPlan plan_attention(int max_keys, int B, int nkv) {
+// Work partition (the split of flash decoding, cut by bytes).  A (request r,
+// kv head g) pair -- a segment -- needs units_r = 1 + the number of 32-key
+// context steps of r (unit 0 is the block's own keys).  Segments are laid
+// end to end, request-major, into one sequence of U = nkv * sum_r units_r
+// units, and workgroup w of the W in the grid takes the units
+// [floor(w U / W), floor((w + 1) U / W)): every workgroup streams the same
+// number of bytes whatever the mix of context lengths.  A workgroup whose
+// range crosses segment boundaries takes its parts one after the other and
+// writes one (O, m, l) partial per part, at slot w + s for segment s (the
+// (w, s) pairs that meet form a staircase, so w + s is unique).  The range
+// is cut on the device from the context lengths; the host knows only their
+// maximum.  The dispatcher deals workgroup w to CU slot w mod 256, so W a
+// multiple of 256 gives every CU the same load.
+//   bf16 cache: when the job is small enough, at most one workgroup per CU
+//   with all of its steps in flight at once (kDeepSteps LDS stages);
+//   otherwise W = 768 (three per CU, 3 stages).  Other caches: 512.  W
+//   grows (in multiples of 256) so that no range exceeds kMaxSteps units.
+AttnPlan plan_attention(int max_keys, int B, int nkv, bool dma) {
   AttnPlan p;
-  const int64_t base = (int64_t)B * nkv;
-  const int64_t keys = (int64_t)max_keys + 32;
-  const int64_t steps = (keys + 31) / 32 * base;  // 32-key steps over all (request, kv head)
-  int64_t chunk;
-  if (steps <= 2048) {
-    // latency-bound (a short context or a small batch): one round of at most
-    // 256 workgroups, one per CU, so that none waits for a second round
-    const int64_t splits = base >= 256 ? 1 : 256 / base;
-    chunk = ((keys + splits - 1) / splits + 31) / 32 * 32;
+  const int64_t units_max = 1 + ((int64_t)(max_keys > 0 ? max_keys : 0) + 31 + 31) / 32;
+  const int64_t u_max = units_max * B * nkv;
+  int64_t W;
+  if (dma && u_max <= (int64_t)kDeepSteps * kCUs) {
+    // at most one workgroup per CU, with at least ~5 steps each: fewer
+    // would add (O, m, l) partials faster than they split the streaming
+    p.stages = kDeepSteps;
+    W = (u_max + 4) / 5;
+    W = W < kCUs ? (W > 0 ? W : 1) : kCUs;
   } else {
-    // about 1024 workgroups over the largest context: rounds balance ragged work
-    chunk = (keys * base / 1024 + 31) / 32 * 32;
+    p.stages = dma ? 3 : 0;
+    W = (int64_t)(dma ? 3 : 2) * kCUs;
   }
-  if (chunk < 128) chunk = 128;
-  if (chunk > kMaxChunk) chunk = kMaxChunk;
-  p.chunk = (int)chunk;
-  p.n_splits = max_keys <= 0 ? 1 : (int)((max_keys + 31 + chunk - 1) / chunk);
+  const int64_t by_cap = (u_max + kMaxSteps - 1) / kMaxSteps;
+  if (by_cap > W) W = (by_cap + kCUs - 1) / kCUs * kCUs;
+  p.n_launch = (int)W;
+  p.n_partials = (int)(W + (int64_t)B * nkv);
+  p.fits = u_max < (1ll << 31) / 2;  // unit positions (and (x + 1) W) stay exact
   return p;
 }
 
@@ -61,40 +81,149 @@ struct AttnArgs {
                                        // V [pages][nkv][D][P]
   const int32_t* pt; int max_pages; int64_t num_pages;
   const int32_t* prefix_len; int max_prefix;
-  int S, G, nq, nkv, P, window, chunk, n_splits;
+  int B, S, G, nq, nkv, P, window, W;
   float scale_log2;
-  float* o_part; float2* ml_part;
+  float* o_part; float2* ml_part;  // per partial slot: [64 rows][D], [64 rows]
+  int4* seg;                       // per request: (units before it per head, units, U, -)
 };
 
-// Context-key range of request r on this layer: keys [lo, L), walked from the
-// 32-aligned a0 <= lo, and the number of splits it uses.
-__device__ __forceinline__ void key_range(const AttnArgs& a, int r, int& L, int& lo, int& a0,
-                                          int& nvalid) {
-  L = imin(imax(a.prefix_len[r], 0), imin(a.max_prefix, a.max_pages * a.P));
-  lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
-  a0 = lo & ~31;
-  nvalid = imax(1, (L - a0 + a.chunk - 1) / a.chunk);
+// Inclusive prefix sum over a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
-// Fragments of one 32-key step: K rows for two 16-key halves x D/32 dim groups,
-// V^T rows for D/16 dim blocks x two halves (4 keys each).
-template <typename KT, int D> struct KVStep {
-  Raw8<KT> k[2][D / 32];
-  Raw4<KT> v[D / 16][2];
-  __device__ __forceinline__ void load(const KT* kbase0, const KT* kbase1, const KT* vbase0,
-                                       const KT* vbase1, int P, int r16, int g4) {
-    const KT* kb[2] = {kbase0, kbase1};
-    const KT* vb[2] = {vbase0, vbase1};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) k[h][ks].load(kb[h] + r16 * D + ks * 32 + g4 * 8);
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        v[db][h].load(vb[h] + (int64_t)(db * 16 + r16) * P + g4 * 4);
-    }
-  }
+// Context length clamped as the kernels use it, and the units of a request
+// of that length.
+__device__ __forceinline__ int clamped_len(const AttnArgs& a, int r) {
+  return imin(imax(a.prefix_len[r], 0), imin(a.max_prefix, a.max_pages * a.P));
+}
+__device__ __forceinline__ int units_of_len(const AttnArgs& a, int L) {
+  const int lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
+  const int a0 = lo & ~31;
+  return 1 + (L > a0 ? (L - a0 + 31) / 32 : 0);
+}
+
+// The units of every request and the units before it.  With B <= 64 every
+// wave holds them in registers, request i in lane i.  Otherwise thread tid
+// owns requests tid * c .. tid * c + c - 1 and keeps only the units before
+// its first one; find_segment reloads the lengths.  find_segment(x) returns
+// the segment holding unit x of the sequence; all threads call it together
+// (the large form uses LDS and barriers).
+struct UnitTable {
+  bool small;
+  int c;
+  int u, pre, L;  // small: this lane's request; large: pre = units before the thread's first
+  int64_t U;      // units of the whole sequence
 };
+struct SegPos {
+  int r, g, L;
+  int units;       // units of the segment
+  int64_t start;   // its first unit in the sequence
+};
+__device__ UnitTable unit_table(const AttnArgs& a, int* red) {
+  UnitTable t;
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+  t.small = a.B <= 64;
+  if (t.small) {
+    t.c = 1;
+    t.L = lane < a.B ? clamped_len(a, lane) : 0;
+    t.u = lane < a.B ? units_of_len(a, t.L) : 0;
+    const int inc = wave_incl_scan(t.u, lane);
+    t.pre = inc - t.u;
+    t.U = (int64_t)__shfl(inc, 63, 64) * a.nkv;
+    return t;
+  }
+  t.c = (a.B + 255) / 256;
+  t.u = t.L = 0;
+  int sum = 0;
+  for (int i = 0; i < t.c; ++i)
+    if (tid * t.c + i < a.B) sum += units_of_len(a, clamped_len(a, tid * t.c + i));
+  const int inc = wave_incl_scan(sum, lane);
+  if (lane == 63) red[wave] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? red[w] : 0;
+    tot += red[w];
+  }
+  __syncthreads();
+  t.pre = off + inc - sum;
+  t.U = (int64_t)tot * a.nkv;
+  return t;
+}
+__device__ SegPos find_segment(const AttnArgs& a, const UnitTable& t, int64_t x, int* red) {
+  SegPos sp;
+  const int tid = threadIdx.x & 255, lane = tid & 63;
+  int64_t base;
+  if (t.small) {
+    const bool hit = lane < a.B && x >= (int64_t)t.pre * a.nkv &&
+                     x < (int64_t)(t.pre + t.u) * a.nkv;
+    const unsigned long long m = __ballot(hit);
+    const int src = m ? __ffsll((long long)m) - 1 : 0;
+    sp.r = src;
+    sp.units = __shfl(t.u, src, 64);
+    sp.L = __shfl(t.L, src, 64);
+    base = (int64_t)__shfl(t.pre, src, 64) * a.nkv;
+  } else {
+    int pre = t.pre;
+    for (int i = 0; i < t.c; ++i) {
+      const int r = tid * t.c + i;
+      if (r >= a.B) break;
+      const int L = clamped_len(a, r), u = units_of_len(a, L);
+      if (x >= (int64_t)pre * a.nkv && x < (int64_t)(pre + u) * a.nkv) {
+        red[8] = r;
+        red[9] = u;
+        red[10] = pre;
+        red[11] = L;
+      }
+      pre += u;
+    }
+    __syncthreads();
+    sp.r = red[8];
+    sp.units = red[9];
+    sp.L = red[11];
+    base = (int64_t)red[10] * a.nkv;
+    __syncthreads();
+  }
+  sp.g = (int)((x - base) / imax(sp.units, 1));
+  sp.start = base + (int64_t)sp.g * sp.units;
+  return sp;
+}
+// The range of workgroup w: units [first, end) of the sequence.
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t U, int W) { return w * U / W; }
+// Workgroup whose range holds unit x.
+__device__ __forceinline__ int range_owner(int64_t x, int64_t U, int W) {
+  return (int)(((x + 1) * W - 1) / U);
+}
+// Workgroup 0 writes the table the combine reads: per request the units
+// before it, its units, and U.
+__device__ __forceinline__ void write_seg_table(const AttnArgs& a, const UnitTable& t) {
+  if (blockIdx.x != 0) return;
+  const int tid = threadIdx.x & 255;
+  if (t.small) {
+    if (tid < a.B) a.seg[tid] = make_int4(t.pre, t.u, (int)t.U, 0);
+    return;
+  }
+  int pre = t.pre;
+  for (int i = 0; i < t.c; ++i) {
+    const int r = tid * t.c + i;
+    if (r >= a.B) break;
+    const int u = units_of_len(a, clamped_len(a, r));
+    a.seg[r] = make_int4(pre, u, (int)t.U, 0);
+    pre += u;
+  }
+}
 
 // K/V of one 32-key step staged in LDS for the four waves, in fragment order
 // (so every fragment read is one contiguous 512 B / 1 KB wave access):
@@ -206,19 +335,23 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   constexpr int STAGE = 64 * D;  // CT elements of one staged step
   __shared__ int pages[kMaxChunkPages];
   __shared__ __attribute__((aligned(16))) CT stg_s[2][STAGE];
-  const int split = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, qb = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  __shared__ int red[12];
+  const int tid = threadIdx.x & 255, lane = tid & 63, qb = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
   const bool qlive = qb * 16 < R;
-  const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits + split) * 64;
-
-  // Work that does not depend on the prefix length goes first, so the memory
-  // round trips overlap: the query loads, the block's own keys (split 0), the
-  // prefix length, and on a full-attention layer (whose range starts at key
-  // split * chunk) the page-table entries of the range.
-  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
   const int rho = imin(qb * 16 + r16, R - 1);
   const int jrow = rho % S;
+  const UnitTable tab = unit_table(a, red);
+  write_seg_table(a, tab);
+  const int64_t x_end = range_start((int64_t)blockIdx.x + 1, tab.U, a.W);
+  for (int64_t x = range_start(blockIdx.x, tab.U, a.W); x < x_end;) {
+  const SegPos sp = find_segment(a, tab, x, red);
+  const int g = sp.g, r = sp.r, L = sp.L;
+  const int u0 = (int)(x - sp.start);
+  const int u1 = (int)((x_end < sp.start + sp.units ? x_end : sp.start + sp.units) - sp.start);
+  const int64_t base = ((int64_t)blockIdx.x + r * a.nkv + g) * 64;  // partial slot w + s
+  x = sp.start + u1;
+  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
   Frag<CT> qf[D / 32];
   {
     const int hl = rho / S;
@@ -226,8 +359,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
   }
-  uint4 rb[SPB::PPT];  // the block's own keys: one 16-key page (both halves point at it)
-  if (split == 0) {
+  // the block's own keys: one 16-key page (both halves point at it).  Every
+  // part loads and stages it, only a segment's first uses it: a load whose
+  // wait is conditional makes the compiler wait for all loads in flight later.
+  uint4 rb[SPB::PPT];
+  {
     const CT* kb = static_cast<const CT*>(a.kblk) + (int64_t)(r * a.nkv + g) * 16 * D;
     const CT* vb = static_cast<const CT*>(a.vblk) + (int64_t)(r * a.nkv + g) * D * 16;
     const CT* kp[2] = {kb, kb};
@@ -236,34 +372,21 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     for (int u = 0; u < SPB::PPT; ++u)
       rb[u] = gload16(piece_src<CT, D>(kp, vp, 16, tid + 256 * u));
   }
-  int pre = 0;
-  if (a.window == 0 && tid < kMaxChunkPages)
-    pre = a.pt[(int64_t)r * a.max_pages + imin((split * a.chunk) / a.P + tid, a.max_pages - 1)];
-  int L, lo, a0, nvalid;
-  key_range(a, r, L, lo, a0, nvalid);
-  if (split >= nvalid) {
-    // no keys here: an empty partial, which the combine weighs zero
-    if (tid < R) a.ml_part[base + tid] = make_float2(-INFINITY, 0.f);
-    return;
-  }
-  const int kbeg = a0 + split * a.chunk;
-  const int kend = imin(L, kbeg + a.chunk);
-  const int n_ctx = (kend > kbeg) ? (kend - kbeg + 31) / 32 : 0;
+  const int lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
+  const int a0 = lo & ~31;
+  const bool has_blk = u0 == 0;
+  const int t_first = imax(u0 - 1, 0);             // first context step
+  const int n_ctx = u1 - 1 - t_first;              // context steps of the part
+  const int kbeg = a0 + 32 * t_first;
+  const int kend = imin(L, kbeg + 32 * n_ctx);
   const int pfirst = kbeg / a.P;
-  if (n_ctx > 0) {
-    const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
-    if (a.window == 0) {  // kbeg == split * chunk: the entries loaded above
-      if (tid < npages)
-        pages[tid] = pre < 0 ? 0 : (pre >= a.num_pages ? (int)(a.num_pages - 1) : pre);
-      for (int i = tid + 256; i < npages; i += 256) {
-        const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
-        pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
-      }
-    } else {
-      for (int i = tid; i < npages; i += 256) {
-        const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
-        pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
-      }
+  {
+    // with no context keys (n_ctx == 0) the entries of step 0 are still
+    // filled: the loads issued below read step 0 unconditionally
+    const int npages = (kbeg + 32 * imax(n_ctx, 1) - 1) / a.P - pfirst + 1;
+    for (int i = tid; i < npages; i += 256) {
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
+      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
     }
   }
   lds_barrier();
@@ -390,36 +513,44 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     for (int db = 0; db < D / 16; ++db) mma(o[db], vf[db], pf);
   };
 
-  // context steps: loads four steps ahead in registers, LDS double buffer
+  // context steps: loads four steps ahead in registers, LDS double buffer.
+  // Every step issues one step's loads and stages one set without a branch
+  // (past the last step the loads repeat the last step's addresses and the
+  // staged copy is never read): with conditional loads the compiler's wait
+  // counting merges the paths and waits for every load in flight, which
+  // drains the prefetch at each step.  Loop exits are the only branches.
   uint4 rr0[SPK::PPT], rr1[SPK::PPT], rr2[SPK::PPT], rr3[SPK::PPT], rr4[SPK::PPT];
-  if (0 < n_ctx) issue(rr0, 0);
-  if (1 < n_ctx) issue(rr1, 1);
-  if (2 < n_ctx) issue(rr2, 2);
-  if (3 < n_ctx) issue(rr3, 3);
-  if (split == 0) {
+  const int t_last = imax(n_ctx - 1, 0);
+  issue(rr0, 0);
+  issue(rr1, imin(1, t_last));
+  issue(rr2, imin(2, t_last));
+  issue(rr3, imin(3, t_last));
 #pragma unroll
-    for (int u = 0; u < SPB::PPT; ++u) stage_piece<CT, CT, D>(stg_s[1], rb[u], tid + 256 * u);
-    lds_barrier();
-    compute(stg_s[1], 0, true);
-  }
+  for (int u = 0; u < SPB::PPT; ++u) stage_piece<CT, CT, D>(stg_s[1], rb[u], tid + 256 * u);
+  lds_barrier();
+  if (has_blk) compute(stg_s[1], 0, true);
   if (n_ctx > 0) {
     stage_ctx(stg_s[0], rr0);
     lds_barrier();
+    // cur_next: the set that held step t - 1 (free now) -> step t + 4;
+    // nxt: the set holding step t + 1
     auto step = [&](int t, uint4 (&cur_next)[SPK::PPT], uint4 (&nxt)[SPK::PPT]) {
-      // cur_next: the set that held step t - 1 (free now) -> step t + 4;
-      // nxt: the set holding step t + 1
-      if (t >= n_ctx) return;
-      if (t + 4 < n_ctx) issue(cur_next, t + 4);
+      issue(cur_next, imin(t + 4, t_last));
       compute(stg_s[t & 1], kbeg + 32 * t, false);
-      if (t + 1 < n_ctx) stage_ctx(stg_s[(t + 1) & 1], nxt);
+      stage_ctx(stg_s[(t + 1) & 1], nxt);
       lds_barrier();
     };
-    for (int t0 = 0; t0 < n_ctx; t0 += 5) {
+    for (int t0 = 0;; t0 += 5) {
       step(t0, rr4, rr1);
+      if (t0 + 1 > t_last) break;
       step(t0 + 1, rr0, rr2);
+      if (t0 + 2 > t_last) break;
       step(t0 + 2, rr1, rr3);
+      if (t0 + 3 > t_last) break;
       step(t0 + 3, rr2, rr4);
+      if (t0 + 4 > t_last) break;
       step(t0 + 4, rr3, rr0);
+      if (t0 + 5 > t_last) break;
     }
   }
 
@@ -432,78 +563,374 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
           make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
     if (g4 == 0) a.ml_part[base + qb * 16 + r16] = make_float2(mq, lq);
   }
+  // the next part reuses the staging buffers and the page list
+  __syncthreads();
+  }
 }
 
-// Combine the splits of one query row: one wave per row.  Empty splits carry
-// m = -inf and weigh zero (their O is never read).  Lane s holds split s's
-// (m, l); the O loads of 16 splits go out together.
-template <typename CT, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __restrict__ out,
-                                                           int B) {
-  const int R = a.G * a.S;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= B * a.nkv * R) return;
-  const int rho = row % R, g = (row / R) % a.nkv, r = row / (R * a.nkv);
-  const int64_t base = ((int64_t)(r * a.nkv + g) * a.n_splits) * 64 + rho;
-  float M = -INFINITY;
-  for (int s = lane; s < a.n_splits; s += 64) M = fmaxf(M, a.ml_part[base + (int64_t)s * 64].x);
+// ---------------------------------------------------------------------------
+// bf16 cache: the K/V of a step go straight from global memory into LDS
+// (global_load_lds_dwordx4, 64 lanes x 16 bytes per instruction), into NS
+// stage buffers, NS - 1 steps ahead of the step being computed.  No register
+// staging, so no register sets to rotate and no compiler-counted loads in the
+// loop: the kernel waits for its own loads with explicit counts.
+//
+// Key order inside a 32-key step: for the K fragments of half h, row rho of
+// the 16 x 32 A operand holds key 8 (rho / 4) + 4 h + rho % 4.  The S^T
+// accumulator element i of half h in lane group g4 is then key 8 g4 + 4 h + i,
+// so a lane's 8 scores are the 8 consecutive keys 8 g4 .. 8 g4 + 7, and its
+// V^T fragment (A operand of O^T += V^T P^T, keys 8 g4 .. + 8 of one dim) is
+// one 16-byte run of a V^T row: every fragment, K or V, is one 16-byte record
+// per lane and one 1 KB DMA per wave.
+//   LDS stage: K [kop = h * D/32 + ks][lane][8]   kop < D/16
+//              V [db][lane][8]                     db  < D/16
+
+// 16 bytes per lane from global memory into LDS at lds_wave_base + 16 lane.
+// Inline asm: the compiler does not count these loads (it would otherwise wait
+// for every one in flight before each LDS read); the kernel waits for them.
+__device__ __forceinline__ void attn_dma16(const void* g, const void* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
+               : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void attn_wait_vmcnt() {
+  static_assert(N <= 63, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most `later` steps of DPW loads each are still in flight
+// (later <= K).
+template <int DPW, int K> __device__ __forceinline__ void attn_wait_steps(int later) {
+  if constexpr (K <= 0) {
+    attn_wait_vmcnt<0>();
+  } else {
+    if (later >= K) attn_wait_vmcnt<K * DPW>();
+    else attn_wait_steps<DPW, K - 1>(later);
+  }
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs a) {
+  using CT = bf16_t;
+  constexpr int STAGE = 64 * D;       // elements of one staged step
+  constexpr int OPW = D / 64;         // K (and V) DMAs per wave per step
+  constexpr int DPW = 2 * OPW;        // DMAs per wave per step
+  __shared__ int pages[kMaxChunkPages];
+  __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
+  __shared__ int red[12];
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, r16 = lane & 15,
+            g4 = lane >> 4;
+  const int S = a.S, R = a.G * S;
+  const bool qlive = wave * 16 < R;
+  const int rho = imin(wave * 16 + r16, R - 1);
+  const int jrow = rho % S;
+  const UnitTable tab = unit_table(a, red);
+  write_seg_table(a, tab);
+  const int64_t x_end = range_start((int64_t)blockIdx.x + 1, tab.U, a.W);
+  for (int64_t x = range_start(blockIdx.x, tab.U, a.W); x < x_end;) {
+  const SegPos sp = find_segment(a, tab, x, red);
+  const int g = sp.g, r = sp.r, L = sp.L;
+  const int u0 = (int)(x - sp.start);
+  const int u1 = (int)((x_end < sp.start + sp.units ? x_end : sp.start + sp.units) - sp.start);
+  const int64_t base = ((int64_t)blockIdx.x + r * a.nkv + g) * 64;  // partial slot w + s
+  x = sp.start + u1;
+  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
+  Frag<CT> qf[D / 32];
+  {
+    const int hl = rho / S;
+    const CT* qp = static_cast<const CT*>(a.q) + ((int64_t)(r * S + jrow) * a.nq + g * a.G + hl) * D;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  float den = 0.f, acc[D / 64];
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
-    // this lane's split s0 + lane: its weight and weighted l
-    float wl = 0.f, wm = 0.f;
-    if (s0 + lane < a.n_splits) {
-      const float2 ml = a.ml_part[base + (int64_t)(s0 + lane) * 64];
-      wm = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
-      wl = wm * ml.y;
-    }
-    const int ns = imin(64, a.n_splits - s0);
-    for (int s1 = 0; s1 < ns; s1 += 16) {
-      float v[16][D / 64];
-      float w[16], l[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int src = (s1 + u) & 63;  // uniform across the wave
-        w[u] = __shfl(wm, src, 64);
-        l[u] = __shfl(wl, src, 64);
-        if (s1 + u >= ns) w[u] = 0.f;
-      }
-      // the O loads do not wait for the weights: an empty split's O (never
-      // written, any bits) is dropped by the select below, not multiplied
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e)
-          v[u][e] = s1 + u < ns
-                        ? a.o_part[(base + (int64_t)(s0 + s1 + u) * 64) * D + lane + 64 * e]
-                        : 0.f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (w[u] != 0.f) {
-          den += l[u];
-#pragma unroll
-          for (int e = 0; e < D / 64; ++e) acc[e] += w[u] * v[u][e];
-        }
+    for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
+  }
+  const int lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
+  const int a0 = lo & ~31;
+  const int blk = u0 == 0 ? 1 : 0;                 // the part starts with the block's keys
+  const int t_first = imax(u0 - 1, 0);             // first context step
+  const int n_ctx = u1 - 1 - t_first;              // context steps of the part
+  const int kbeg = a0 + 32 * t_first;
+  const int kend = imin(L, kbeg + 32 * n_ctx);
+  const int pfirst = kbeg / a.P;
+  if (n_ctx > 0) {
+    const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
+    for (int i = tid; i < npages; i += 256) {
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
+      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
     }
   }
-  const int hl = rho / a.S, j = rho % a.S;
-  CT* dst = out + ((int64_t)(r * a.S + j) * a.nq + g * a.G + hl) * D;
+  // every load the compiler issued (Q, page table) is complete from here on,
+  // and it knows so: it does not wait again, behind the DMAs, before the
+  // first use of Q
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  lds_barrier();
+
+  // Steps: the first part of a segment starts with the block's own keys
+  // (one 16-key page, both halves pointing at it), then the context steps.
+  const int n_seq = n_ctx + blk;
+  const CT* kc = static_cast<const CT*>(a.kc);
+  const CT* vc = static_cast<const CT*>(a.vc);
+  const CT* kblk = static_cast<const CT*>(a.kblk) + (int64_t)(r * a.nkv + g) * 16 * D;
+  const CT* vblk = static_cast<const CT*>(a.vblk) + (int64_t)(r * a.nkv + g) * D * 16;
+  // this lane's K row inside a half (key 8 (r16/4) + 4h + r16%4 of the step:
+  // page half r16 / 8, row within it) and V^T key offset (page half g4 / 2)
+  const int krow0 = (8 * (r16 >> 2) + (r16 & 3)) & 15;  // + 4 h
+  const int khalf = r16 >> 3, vhalf = g4 >> 1, voff = 8 * (g4 & 1);
+  auto issue = [&](int s) {
+    CT* stg = stg_s[s % NS];
+    const CT* kp[2];
+    const CT* vp[2];
+    int vstride;
+    if (s < blk) {
+      kp[0] = kp[1] = kblk;
+      vp[0] = vp[1] = vblk;
+      vstride = 16;
+    } else {
+      const int key0 = kbeg + 32 * (s - blk);
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) dst[lane + 64 * e] = Num<CT>::from_f(acc[e] / den);
+      for (int j = 0; j < 2; ++j) {
+        const int kj = key0 + 16 * j;
+        const int64_t page = pages[kj / a.P - pfirst];
+        const int off = kj % a.P;
+        kp[j] = kc + ((page * a.nkv + g) * a.P + off) * D;
+        vp[j] = vc + (page * a.nkv + g) * (int64_t)D * a.P + off;
+      }
+      vstride = a.P;
+    }
+    const CT* kl = khalf ? kp[1] : kp[0];
+    const CT* vl = vhalf ? vp[1] : vp[0];
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+      const int kop = wave * OPW + i, h = kop / (D / 32), ks = kop % (D / 32);
+      attn_dma16(kl + (krow0 + 4 * h) * D + 32 * ks + 8 * g4, stg + kop * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < OPW; ++i) {
+      const int db = wave * OPW + i;
+      attn_dma16(vl + (int64_t)(16 * db + r16) * vstride + voff, stg + 32 * D + db * 512);
+    }
+  };
+
+  const int qpos = L + jrow;
+  float mq = -INFINITY, lq = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one staged step: keys t0 + 8 g4 + e are this lane's elements e = 0..7
+  auto compute = [&](const CT* stg, int t0, bool is_blk) {
+    const CT* Ks = stg;
+    const CT* Vs = stg + 32 * D;
+    const bool full = is_blk ? false : (t0 >= lo && t0 + 32 <= kend);
+    unsigned keep = 0xffu;
+    if (!full) {
+      keep = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 8 * g4 + e;
+        const bool ok = is_blk ? (kk < S) : (t0 + kk >= lo && t0 + kk < kend);
+        keep |= (ok ? 1u : 0u) << e;
+      }
+    }
+    unsigned vis = keep;
+    if (!is_blk && a.window > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((qpos - (t0 + 8 * g4 + e)) >= a.window) vis &= ~(1u << e);
+    }
+    const bool masked = !full || (!is_blk && a.window > 0);
+    f32x4 sacc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sacc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        Frag<CT> kf;
+        load_frag(kf, Ks + ((h * (D / 32) + ks) * 64 + lane) * 8);
+        mma(sacc[h], kf, qf[ks]);
+      }
+    }
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = sacc[e >> 2][e & 3] * a.scale_log2;
+      if (masked && !((vis >> e) & 1u)) sv[e] = -INFINITY;
+      mx = fmaxf(mx, sv[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // lazy reference maximum: it moves only when a step's maximum exceeds it
+    // by more than 8 (log2 units), so probabilities stay below 2^8 and O, l
+    // are rescaled rarely; O / l does not depend on the reference
+    const float mold = mq;
+    const bool move = __any(mx > mold + 8.f);
+    const float mn = move ? fmaxf(mold, mx) : mold;
+    const float msub = (mn == -INFINITY) ? 0.f : mn;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = __builtin_amdgcn_exp2f(sv[e] - msub);
+      sum += sv[e];
+    }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    if (move) {
+      const float alpha = __builtin_amdgcn_exp2f(mold - msub);
+      lq *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
+    }
+    lq += sum;
+    mq = mn;
+    Frag<CT> pf;
+    frag_from_f32(pf, sv);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      Frag<CT> vf;
+      load_frag(vf, Vs + (db * 64 + lane) * 8);
+      // keys outside the range (first and last steps only) are zeroed: their
+      // memory may hold anything
+      if (!full) frag_keep(vf, keep);
+      mma(o[db], vf, pf);
+    }
+  };
+
+  // pipeline: steps s + 1 .. s + NS - 1 in flight while step s computes
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < n_seq) issue(s);
+  for (int s = 0; s < n_seq; ++s) {
+    // wait for this wave's DMAs of step s (those of later steps may stay in
+    // flight), then for every wave's
+    attn_wait_steps<DPW, NS - 2>(imin(NS - 2, n_seq - 1 - s));
+    lds_barrier();
+    // the buffer of step s - 1: every wave has finished with it
+    if (s + NS - 1 < n_seq) issue(s + NS - 1);
+    if (qlive) {
+      const bool is_blk = s < blk;
+      compute(stg_s[s % NS], is_blk ? 0 : kbeg + 32 * (s - blk), is_blk);
+    }
+  }
+
+  // unnormalised O^T, and (m, l) per query row
+  if (qlive && wave * 16 + r16 < R) {
+    float* dst = a.o_part + (base + wave * 16 + r16) * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<float4*>(dst + db * 16 + g4 * 4) =
+          make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+    if (g4 == 0) a.ml_part[base + wave * 16 + r16] = make_float2(mq, lq);
+  }
+  // the next part reuses the stage buffers and the page list
+  __syncthreads();
+  }
+}
+
+// Combine the partials of one query row: one wave per row.  A partial in
+// which the row saw no key carries m = -inf and weighs zero (its O is never
+// used).  Up to 32 partials at a time: lane s holds partial s's (m, l), and
+// the O rows go out in one batch of float4 loads (D/4 lanes per partial, so a
+// wave instruction covers 256 / D partials) at the same time as the (m, l)
+// loads; the weights are applied once both are in.
+template <typename CT, int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __restrict__ out) {
+  constexpr int LPP = D / 4;           // lanes per partial row
+  constexpr int PPI = 64 / LPP;        // partials per load instruction
+  constexpr int CH = 32;               // partials per chunk
+  constexpr int NI = CH / PPI;         // load instructions for a chunk
+  const int R = a.G * a.S;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= a.B * a.nkv * R) return;
+  const int rho = row % R, g = (row / R) % a.nkv, r = row / (R * a.nkv);
+  // the workgroups whose ranges meet segment s = (r, g); that of workgroup
+  // w is written at partial slot w + s
+  const int4 sg = a.seg[r];
+  const int64_t U = sg.z, s0 = ((int64_t)sg.x * a.nkv + (int64_t)g * sg.y);
+  const int w_lo = range_owner(s0, U, a.W), w_hi = range_owner(s0 + sg.y - 1, U, a.W);
+  const int n = w_hi - w_lo + 1;
+  auto prow = [&](int s) { return ((int64_t)w_lo + s + r * a.nkv + g) * 64 + rho; };
+  // with U < W some ranges are empty: those workgroups wrote nothing
+  auto has_range = [&](int s) {
+    const int64_t w = (int64_t)w_lo + s;
+    return range_start(w + 1, U, a.W) > range_start(w, U, a.W);
+  };
+  const int sub = lane / LPP, d0 = (lane % LPP) * 4;
+  float den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float mref = -INFINITY;  // reference of acc and den so far
+  // one chunk of up to CH partials; NIC load instructions cover its O rows
+  auto chunk = [&](auto nic_tag, int c0, int nc) {
+    constexpr int NIC = decltype(nic_tag)::value;
+    const bool mine = lane < nc && has_range(c0 + lane);
+    float2 ml = make_float2(-INFINITY, 0.f);
+    if (mine) ml = a.ml_part[prow(c0 + lane)];
+    float4 v[NIC];
+#pragma unroll
+    for (int i = 0; i < NIC; ++i) {
+      const int s = i * PPI + sub;
+      v[i] = s < nc ? *reinterpret_cast<const float4*>(a.o_part + prow(c0 + s) * D + d0)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mc = ml.x;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+    const float mn = fmaxf(mref, mc);
+    if (mn == -INFINITY) return;  // nothing seen yet
+    const float alpha = mref == -INFINITY ? 0.f : exp2f(mref - mn);
+    acc.x *= alpha; acc.y *= alpha; acc.z *= alpha; acc.w *= alpha;
+    den *= alpha;
+    const float wm = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mn);
+    den += wave_sum(wm * ml.y);
+#pragma unroll
+    for (int i = 0; i < NIC; ++i) {
+      const int s = i * PPI + sub;
+      const float w = __shfl(wm, s & 63, 64);
+      // an O with no key (any bits) is dropped, not multiplied
+      if (s < nc && w != 0.f) {
+        acc.x += w * v[i].x; acc.y += w * v[i].y; acc.z += w * v[i].z; acc.w += w * v[i].w;
+      }
+    }
+    mref = mn;
+  };
+  for (int c0 = 0; c0 < n; c0 += CH) {
+    const int nc = imin(CH, n - c0);
+    if (nc <= 2 * PPI) chunk(std::integral_constant<int, 2>(), c0, nc);
+    else if (nc <= 8 * PPI && 8 < NI) chunk(std::integral_constant<int, (8 < NI ? 8 : NI)>(), c0, nc);
+    else chunk(std::integral_constant<int, NI>(), c0, nc);
+  }
+  // the PPI lane groups hold disjoint partials of the same dims
+#pragma unroll
+  for (int o = LPP; o < 64; o <<= 1) {
+    acc.x += __shfl_xor(acc.x, o, 64);
+    acc.y += __shfl_xor(acc.y, o, 64);
+    acc.z += __shfl_xor(acc.z, o, 64);
+    acc.w += __shfl_xor(acc.w, o, 64);
+  }
+  if (lane < LPP) {
+    const int hl = rho / a.S, j = rho % a.S;
+    CT* dst = out + ((int64_t)(r * a.S + j) * a.nq + g * a.G + hl) * D + d0;
+    const float inv = 1.0f / den;
+    dst[0] = Num<CT>::from_f(acc.x * inv);
+    dst[1] = Num<CT>::from_f(acc.y * inv);
+    dst[2] = Num<CT>::from_f(acc.z * inv);
+    dst[3] = Num<CT>::from_f(acc.w * inv);
+  }
 }
 
 template <typename CT, typename KT, int D>
-static hipError_t run_attn(const AttnArgs& a, int B, void* out, hipStream_t st) {
-  hipLaunchKernelGGL((attn_split_kernel<CT, KT, D>), dim3(a.n_splits, a.nkv, B), dim3(256), 0, st,
-                     a);
+static hipError_t run_attn(const AttnArgs& a, const AttnPlan& plan, void* out, hipStream_t st) {
+  const dim3 grid((unsigned)plan.n_launch);
+  if constexpr (std::is_same<CT, bf16_t>::value && std::is_same<KT, bf16_t>::value) {
+    if (plan.stages == kDeepSteps)
+      hipLaunchKernelGGL((attn_dma_kernel<D, kDeepSteps>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_dma_kernel<D, 3>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_split_kernel<CT, KT, D>), grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = B * a.nkv * a.G * a.S;
+  const int rows = a.B * a.nkv * a.G * a.S;
   hipLaunchKernelGGL((attn_combine_kernel<CT, D>), dim3((rows + 3) / 4), dim3(256), 0, st, a,
-                     (CT*)out, B);
+                     (CT*)out);
   return hipGetLastError();
 }
 
@@ -512,25 +939,28 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             const int32_t* page_table, int max_pages, int64_t num_pages,
                             const int32_t* prefix_len, int max_prefix, int B, int S, int nq,
                             int nkv, int page_size, int window, const AttnPlan& plan,
-                            float* o_part, float2* ml_part, void* out, hipStream_t st) {
+                            float* o_part, float2* ml_part, int4* seg, void* out,
+                            hipStream_t st) {
+  const bool dma = dt != DFLASH_F32 && kv_dt != DFLASH_FP8_E4M3;
+  if ((plan.stages != 0) != dma || !plan.fits) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q; a.kblk = kblk; a.vblk = vblk; a.kc = kc; a.vc = vc;
   a.pt = page_table; a.max_pages = max_pages; a.num_pages = num_pages;
   a.prefix_len = prefix_len; a.max_prefix = max_prefix;
-  a.S = S; a.G = nq / nkv; a.nq = nq; a.nkv = nkv; a.P = page_size; a.window = window;
-  a.chunk = plan.chunk; a.n_splits = plan.n_splits;
+  a.B = B; a.S = S; a.G = nq / nkv; a.nq = nq; a.nkv = nkv; a.P = page_size; a.window = window;
+  a.W = plan.n_launch;
   a.scale_log2 = LOG2E / sqrtf((float)D);
-  a.o_part = o_part; a.ml_part = ml_part;
+  a.o_part = o_part; a.ml_part = ml_part; a.seg = seg;
   if (dt == DFLASH_F32) {
-    if (D == 64) return run_attn<float, float, 64>(a, B, out, st);
-    return run_attn<float, float, 128>(a, B, out, st);
+    if (D == 64) return run_attn<float, float, 64>(a, plan, out, st);
+    return run_attn<float, float, 128>(a, plan, out, st);
   }
   if (kv_dt == DFLASH_FP8_E4M3) {
-    if (D == 64) return run_attn<bf16_t, fp8_t, 64>(a, B, out, st);
-    return run_attn<bf16_t, fp8_t, 128>(a, B, out, st);
+    if (D == 64) return run_attn<bf16_t, fp8_t, 64>(a, plan, out, st);
+    return run_attn<bf16_t, fp8_t, 128>(a, plan, out, st);
   }
-  if (D == 64) return run_attn<bf16_t, bf16_t, 64>(a, B, out, st);
-  return run_attn<bf16_t, bf16_t, 128>(a, B, out, st);
+  if (D == 64) return run_attn<bf16_t, bf16_t, 64>(a, plan, out, st);
+  return run_attn<bf16_t, bf16_t, 128>(a, plan, out, st);
 }
 
 }  // namespace dflash

@@ -111,16 +111,20 @@ hipError_t launch_accept(const int32_t* cand, const int32_t* post, const int32_t
 
 // ---- attention
 struct AttnPlan {
-  int chunk;      // context keys per split
-  int n_splits;   // grid splits per (request, kv head)
+  int stages;      // LDS stages of the bf16-cache kernel (0: the register-staged kernel)
+  int n_launch;    // workgroups W (a multiple of 256)
+  int n_partials;  // (O, m, l) partial slots: W + B * nkv
+  bool fits;       // the unit count fits the kernels' 32-bit bookkeeping
 };
-AttnPlan plan_attention(int max_keys, int B, int nkv);
+// max_keys: the most context keys a request sees on the layer; dma: the cache
+// and compute types are bf16 (the direct-to-LDS kernel runs).
+AttnPlan plan_attention(int max_keys, int B, int nkv, bool dma);
 hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void* kblk,
                             const void* vblk,
                             const void* kc, const void* vc, const int32_t* page_table,
                             int max_pages, int64_t num_pages, const int32_t* prefix_len,
                             int max_prefix, int B,
                             int S, int nq, int nkv, int page_size, int window, const AttnPlan& plan,
-                            float* o_part, float2* ml_part, void* out, hipStream_t st);
+                            float* o_part, float2* ml_part, int4* seg, void* out, hipStream_t st);
 
 }  // namespace dflash
