@@ -2,25 +2,24 @@
 // context keys (flash-decoding style) with a log-sum-exp combine.
 //
 // For one request r and kv head g the G = nq / nkv query heads of the S block
-// rows form R = G * S <= 64 query rows (row rho = h_local * S + j).  One
-// workgroup owns all of them for one range of context keys (wave w takes query
-// rows 16w .. 16w+15; the four waves read the same K/V, so HBM sees each byte
-// once per (request, kv head) and the repeats hit L1/L2).  Each wave walks the
-// range in 32-key steps (two 16-key halves, each inside one cache page) and
-// works in transposed form, which needs no LDS at all:
-//   S^T = K Q^T      A operand = K rows straight from the page ([P][D] per
+// rows form R = G * S <= 64 query rows (row rho = h_local * S + j).  A
+// workgroup owns all of them for a range of 32-key steps (wave w takes query
+// rows 16w .. 16w+15); the four waves share each step's K/V through LDS, so
+// HBM sees each byte once.  The products run in transposed form:
+//   S^T = K Q^T      A operand = K rows of the step (K pages are [P][D] per
 //                    page and head), B operand = Q^T held in registers;
-//   O^T += V^T P^T   A operand = V^T rows straight from the page (V is stored
-//                    [D][P] per page and head), B operand = P^T, which is
-//                    exactly the S^T accumulator layout (the two operands only
-//                    have to agree on the order of the 8 keys a lane holds).
-// The online softmax runs per query column in the exp2 domain; the next step's
-// K/V fragments are loaded while the current step computes.  Split 0 also
-// takes the S block keys (every block row sees them: no causal mask), laid out
-// by the QKV epilogue as one extra page.  On a sliding layer context key i is
-// visible to the row at logical position p iff p - i < W; the range starts at
-// L - W + 1 (rounded down to 32 keys, the extra keys masked).  fp8 caches are
-// decoded to bf16 in registers.
+//   O^T += V^T P^T   A operand = V^T rows (V pages are stored [D][P] per page
+//                    and head), B operand = P^T, which is exactly the S^T
+//                    accumulator layout (the two operands only have to agree
+//                    on the order of the 8 keys a lane holds).
+// The online softmax runs per query column in the exp2 domain.  The first
+// unit of every (request, kv head) is the block's own S keys (every block row
+// sees them: no causal mask), laid out by the QKV epilogue as one extra page.
+// On a sliding layer context key i is visible to the row at logical position
+// p iff p - i < W; the range starts at L - W + 1 (rounded down to 32 keys,
+// the extra keys masked).  Two staging kernels: a bf16 cache is copied
+// straight from global memory into LDS; fp8 (decoded once, exactly, to bf16)
+// and fp32 caches go through registers.
 #include <type_traits>
 
 #include "common.cuh"
