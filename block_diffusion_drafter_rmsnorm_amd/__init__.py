@@ -66,6 +66,7 @@ class CKVCache(ctypes.Structure):
 
 EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
+            "dflash_accept_sampling_workspace_bytes", "dflash_accept_sampling",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_status_string", "dflash_last_error"]
@@ -92,6 +93,12 @@ def _load():
     lib.dflash_draft_block.restype = I32
     lib.dflash_accept.argtypes = [P, P, P, I32, I32, P, P, P, P, P, P]
     lib.dflash_accept.restype = I32
+    lib.dflash_accept_sampling_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.dflash_accept_sampling_workspace_bytes.restype = SZ
+    F = ctypes.c_float
+    lib.dflash_accept_sampling.argtypes = [P, P, P, I32, I32, F, F, P, P, I32, I32, P, P, P, P, P,
+                                           P, SZ, P]
+    lib.dflash_accept_sampling.restype = I32
     lib.dflash_lm_head_workspace_bytes.argtypes = [cfgp, I32]
     lib.dflash_lm_head_workspace_bytes.restype = SZ
     lib.dflash_lm_head_argmax.argtypes = [cfgp, P, P, I32, P, P, P, SZ, P]
@@ -270,6 +277,39 @@ def dflash_accept(candidates: torch.Tensor, posterior: torch.Tensor, prefix_len:
     _check(_lib.dflash_accept(_ptr(candidates), _ptr(posterior), _ptr(prefix_len), int(B), int(S),
                               _ptr(accept_len), _ptr(commit_len), _ptr(out_tokens),
                               _ptr(next_anchor), _ptr(new_seq_len), _stream(stream)))
+
+
+def accept_sampling_workspace_bytes(batch: int, block_size: int, vocab: int,
+                                    has_draft_logits: bool) -> int:
+    return int(_lib.dflash_accept_sampling_workspace_bytes(int(batch), int(block_size),
+                                                           int(vocab), int(bool(has_draft_logits))))
+
+
+_LOGITS_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def dflash_accept_sampling(candidates: torch.Tensor, target_logits: torch.Tensor,
+                           uniforms: torch.Tensor, prefix_len: torch.Tensor,
+                           accept_len: torch.Tensor, commit_len: torch.Tensor,
+                           out_tokens: torch.Tensor, next_anchor: torch.Tensor,
+                           new_seq_len: torch.Tensor, ws: torch.Tensor,
+                           target_temperature: float = 1.0,
+                           draft_logits: Optional[torch.Tensor] = None,
+                           draft_temperature: float = 1.0, stream=None):
+    """target_logits [B, S, V]; draft_logits None (argmax drafts) or [B, S-1, V] of the
+    same dtype; uniforms [B, S] f32; ws from workspace(accept_sampling_workspace_bytes())."""
+    B, S = candidates.shape
+    V = int(target_logits.shape[-1])
+    if draft_logits is not None and draft_logits.dtype != target_logits.dtype:
+        raise DFlashError(-1, "draft_logits and target_logits must share a dtype")
+    dt = _LOGITS_DT.get(target_logits.dtype)
+    if dt is None:
+        raise DFlashError(-2, f"logits dtype {target_logits.dtype} (supported: f32, bf16)")
+    _check(_lib.dflash_accept_sampling(
+        _ptr(candidates), _ptr(target_logits), _ptr(draft_logits), dt, V,
+        float(target_temperature), float(draft_temperature), _ptr(uniforms), _ptr(prefix_len),
+        int(B), int(S), _ptr(accept_len), _ptr(commit_len), _ptr(out_tokens), _ptr(next_anchor),
+        _ptr(new_seq_len), _ptr(ws), int(ws.numel()), _stream(stream)))
 
 
 def lm_head_workspace_bytes(cfg, rows: int) -> int:

@@ -452,4 +452,56 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
   return DFLASH_OK;
 }
 
+size_t dflash_accept_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab,
+                                              int32_t has_draft_logits) {
+  if (batch <= 0 || block_size < 2 || block_size > 64 || vocab <= 0) return 0;
+  return plan_spec(batch, block_size, vocab, has_draft_logits != 0).bytes;
+}
+
+dflash_status dflash_accept_sampling(const int32_t* candidates, const void* target_logits,
+                                     const void* draft_logits, int32_t logits_dtype,
+                                     int32_t vocab, float target_temperature,
+                                     float draft_temperature, const float* uniforms,
+                                     const int32_t* prefix_len, int32_t batch,
+                                     int32_t block_size, int32_t* accept_len,
+                                     int32_t* commit_len, int32_t* out_tokens,
+                                     int32_t* next_anchor, int32_t* new_seq_len, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(DFLASH_EINVAL, "batch %d < 0", batch);
+  if (block_size < 2 || block_size > 64)
+    return fail(DFLASH_EUNSUPPORTED, "block_size %d outside 2..64", block_size);
+  if (vocab <= 0) return fail(DFLASH_EINVAL, "vocab %d <= 0", vocab);
+  if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16)
+    return fail(DFLASH_EUNSUPPORTED, "logits_dtype %d (supported: F32, BF16)", logits_dtype);
+  if (!(target_temperature > 0.f) || !isfinite(target_temperature))
+    return fail(DFLASH_EINVAL, "target_temperature must be finite and > 0");
+  if (draft_logits && (!(draft_temperature > 0.f) || !isfinite(draft_temperature)))
+    return fail(DFLASH_EINVAL, "draft_temperature must be finite and > 0");
+  if ((int64_t)batch * (2 * block_size - 1) > (int64_t)1 << 30)
+    return fail(DFLASH_EUNSUPPORTED, "batch %d too large", batch);
+  if (batch == 0) return DFLASH_OK;
+  if (!candidates || !target_logits || !uniforms || !prefix_len || !accept_len || !commit_len ||
+      !out_tokens || !next_anchor || !new_seq_len)
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  const SpecPlan pl = plan_spec(batch, block_size, vocab, draft_logits != nullptr);
+  if (workspace == nullptr || workspace_bytes < pl.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.bytes);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
+  // 16-byte loads when every row starts on a 16-byte boundary
+  const int esz = logits_dtype == DFLASH_BF16 ? 2 : 4;
+  int vec = 16 / esz;
+  if (vocab % vec || !aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)))
+    vec = 1;
+  const double log2e = 1.4426950408889634;
+  const float ct = (float)(log2e / (double)target_temperature);
+  const float cd = draft_logits ? (float)(log2e / (double)draft_temperature) : 0.f;
+  hipError_t e = launch_accept_sampling(logits_dtype, vec, candidates, target_logits, draft_logits,
+                                        uniforms, prefix_len, batch, block_size, vocab, ct, cd, pl,
+                                        workspace, accept_len, commit_len, out_tokens,
+                                        next_anchor, new_seq_len,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "accept_sampling");
+  return DFLASH_OK;
+}
+
 }  // extern "C"

@@ -109,6 +109,24 @@ hipError_t launch_accept(const int32_t* cand, const int32_t* post, const int32_t
                          int S, int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
                          int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st);
 
+// ---- rejection-sampling verify (sampling.hip)
+// Vocabulary chunking and workspace layout: stats partials (max, sum) per
+// row and chunk, weight sums (residual, p) per request and chunk, walk records.
+struct SpecPlan {
+  int rows;                  // B*S target rows (+ B*(S-1) draft rows)
+  int chunk1, n_chunks1;     // chunking of the statistics pass
+  int chunk2, n_chunks2;     // chunking of the weight sums and the pick (<= 64)
+  size_t off_stats, off_csum, off_walk, bytes;
+};
+SpecPlan plan_spec(int B, int S, int V, bool has_draft);
+// vec: 8 (bf16) / 4 (f32) for 16-byte loads, else 1; ct, cd = log2(e) / temperature
+hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const void* tl,
+                                  const void* dl, const float* uni, const int32_t* prefix_len,
+                                  int B, int S, int V, float ct, float cd, const SpecPlan& pl,
+                                  void* ws, int32_t* accept_len, int32_t* commit_len,
+                                  int32_t* out_tokens, int32_t* next_anchor,
+                                  int32_t* new_seq_len, hipStream_t st);
+
 // ---- attention
 struct AttnPlan {
   int stages;      // LDS stages of the bf16-cache kernel (0: the register-staged kernel)

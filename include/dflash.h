@@ -6,6 +6,7 @@
  *   dflash_project_context  context injection (target features -> draft K/V cache)
  *   dflash_draft_block      one non-causal draft pass over [anchor, MASK x (S-1)]
  *   dflash_accept           greedy verify-accept, commit and logical crop
+ *   dflash_accept_sampling  rejection-sampling verify-accept and commit
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory unless its name starts with
@@ -230,6 +231,49 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
                             const int32_t* prefix_len, int32_t batch, int32_t block_size,
                             int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
                             int32_t* next_anchor, int32_t* new_seq_len, void* stream);
+
+/*
+ * (3') Rejection-sampling verify-accept and commit ("Inside SGLang ...", the
+ * section on sampling with the proposal distribution the drafter used, and
+ * Step 6 for the outputs; CSDN DFlash article, SGLang flow step 7: non-greedy
+ * requests take a speculative-sampling verify).
+ *
+ * p_j = softmax(target_logits[r, j] / target_temperature) is the target's
+ * distribution after reading candidates[r, j]; q_j = softmax(draft_logits[r, j]
+ * / draft_temperature), or, when draft_logits is NULL (argmax drafts), the
+ * point mass on d_{j+1}.  Walking j = 0 .. S-2, d_{j+1} survives when
+ * uniforms[r, j] * q_j(d_{j+1}) < p_j(d_{j+1}); at the first rejection (a = j)
+ * the token is drawn from [p_j - q_j]_+, after full acceptance (a = S-1) from
+ * p_{S-1}.  The draw is an inverse CDF: the smallest token t whose running sum
+ * of weights exceeds uniforms[r, S-1] * (sum of the weights); a residual with
+ * no mass falls back to p_j; a draw past the last running sum takes the last
+ * token with weight.  Outputs as dflash_accept: accept_len = a, commit_len =
+ * a + 1, out_tokens = d_1 .. d_a, the drawn token, then zeros; next_anchor =
+ * the drawn token; new_seq_len = prefix_len + commit_len.
+ *
+ *   candidates     [batch, block_size]      [anchor, d_1 .. d_{S-1}], ids < vocab
+ *   target_logits  [batch, block_size, vocab] logits_dtype
+ *   draft_logits   nullable [batch, block_size - 1, vocab] logits_dtype (the
+ *                  layout dflash_draft_block writes)
+ *   uniforms       [batch, block_size] f32 draws in [0, 1), supplied by the caller
+ *   prefix_len     [batch]
+ *   workspace      >= dflash_accept_sampling_workspace_bytes(batch, block_size,
+ *                  vocab, draft_logits != NULL), 16-byte aligned
+ * Arithmetic is fp32 with fixed-order sums (deterministic).  block_size 2..64;
+ * logits_dtype F32 or BF16; temperatures finite and > 0 (draft_temperature is
+ * read only with draft_logits).  NaN or +inf logits give unspecified tokens.
+ */
+size_t dflash_accept_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab,
+                                              int32_t has_draft_logits);
+dflash_status dflash_accept_sampling(const int32_t* candidates, const void* target_logits,
+                                     const void* draft_logits, int32_t logits_dtype,
+                                     int32_t vocab, float target_temperature,
+                                     float draft_temperature, const float* uniforms,
+                                     const int32_t* prefix_len, int32_t batch,
+                                     int32_t block_size, int32_t* accept_len,
+                                     int32_t* commit_len, int32_t* out_tokens,
+                                     int32_t* next_anchor, int32_t* new_seq_len, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /*
  * The draft-token selection step alone ("Inside SGLang ...", Step 4: the target

@@ -66,8 +66,9 @@ def accept_sampling(candidates, target_logits, prefix_len, uniforms, target_temp
     uniforms      [B, S]     draws in [0, 1): acceptance draws, then the token draw
     Returns the greedy accept's outputs (accept_len, commit_len, out_tokens,
     next_anchor, new_seq_len) plus, per request, what a checker needs to judge
-    a computation done in another precision: `margin` (the smallest
-    |u q(y) - p(y)| over the decisions taken), `weights` (the unnormalised
+    a computation done in another precision: `margin` (the smallest relative
+    gap |u q(y) - p(y)| / max(u q(y), p(y)) over the decisions taken; inf when
+    both sides are exactly 0), `weights` (the unnormalised
     weights the final token was drawn from) and `draw` (u * their sum).
     """
     cand = np.asarray(candidates, np.int64)
@@ -96,7 +97,8 @@ def accept_sampling(candidates, target_logits, prefix_len, uniforms, target_temp
             else:
                 q = _softmax(dl[r, a] / Td)
             lhs, rhs = u[r, a] * q[y], p[y]
-            margin[r] = min(margin[r], abs(lhs - rhs))
+            if max(lhs, rhs) > 0:
+                margin[r] = min(margin[r], abs(lhs - rhs) / max(lhs, rhs))
             if lhs < rhs:
                 a += 1
                 continue

@@ -133,3 +133,30 @@ def test_packed_matrix_sizes_and_errors():
     assert lib.dflash_pack_matrix(a, a + 8, 16, 64, dfl.BF16, None) == -1
     assert lib.dflash_pack_matrix(a, a + 1024, 16, 64, dfl.BF16, None) == -1  # overlap
     assert lib.dflash_pack_matrix(a, b, -1, 64, dfl.BF16, None) == -1
+
+
+def test_accept_sampling_argument_errors():
+    """Host-visible errors of dflash_accept_sampling come back before any launch."""
+    lib = dfl.raw_lib()
+    F = ctypes.c_void_p(0x100000)
+    big = 1 << 30
+
+    def call(B=2, S=4, V=1000, dt=dfl.BF16, Tt=1.0, Td=1.0, draft=F, cand=F, ws=F, wsb=big):
+        return lib.dflash_accept_sampling(cand, F, draft, dt, V, Tt, Td, F, F, B, S, F, F, F, F, F,
+                                          ws, wsb, None)
+
+    assert call(B=0) == 0                       # nothing to do, no launch
+    assert call(B=-1) == -1
+    assert call(S=1) == -2 and call(S=65) == -2
+    assert call(V=0) == -1
+    assert call(dt=dfl.FP8_E4M3) == -2
+    assert call(Tt=0.0) == -1 and call(Tt=float("nan")) == -1
+    assert call(Td=-1.0) == -1
+    assert call(cand=None) == -1
+    assert call(wsb=16) == -3 and b"workspace" in lib.dflash_last_error()
+    assert call(ws=ctypes.c_void_p(0x100004)) == -1
+    assert dfl.accept_sampling_workspace_bytes(32, 16, 151936, True) > 0
+    assert dfl.accept_sampling_workspace_bytes(32, 16, 151936, False) < \
+        dfl.accept_sampling_workspace_bytes(32, 16, 151936, True)
+    assert dfl.accept_sampling_workspace_bytes(0, 16, 151936, True) == 0
+    assert dfl.accept_sampling_workspace_bytes(4, 1, 100, True) == 0

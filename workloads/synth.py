@@ -174,3 +174,28 @@ def plant_posterior(cand: torch.Tensor, commit: torch.Tensor, vocab: int, seed: 
         if c < S and post[r, c - 1] == cand[r, c]:
             post[r, c - 1] = (cand[r, c] + 1) % vocab
     return post.to(torch.int32)
+
+
+def verify_inputs(B: int, S: int, V: int, seed: int, dtype=torch.bfloat16, device="cpu",
+                  spread: float = 2.0, bump: float = 12.0, draft_noise: float = 0.5,
+                  bump_lo: float = 0.0):
+    """Synthetic inputs of a sampled verify step.
+
+    candidates [B, S]: anchor and drafts uniform in [0, V); target logits
+    [B, S, V]: N(0, spread^2), with the logit of the draft each row verifies
+    (row j, token candidates[j + 1]) raised by U(bump_lo, bump) so that acceptance
+    probabilities spread over (0, 1); draft logits [B, S-1, V]: the target's
+    rows 0..S-2 plus N(0, draft_noise^2) (a drafter close to the target);
+    uniforms [B, S] in [0, 1).  Logits are rounded once to `dtype`.
+    """
+    cand = randint(0, V - 1, (B, S), seed, "verify_cand", device).to(torch.int32)
+    tl = normal((B, S, V), spread, seed, "verify_target", torch.float32, device)
+    up = torch.rand(B, S - 1, generator=_gen(seed, "verify_bump", device), device=device)
+    up = bump_lo + up * (bump - bump_lo)
+    rows = torch.arange(S - 1, device=device)
+    for r in range(B):
+        tl[r, rows, cand[r, 1:].long()] += up[r]
+    dl = tl[:, :S - 1] + normal((B, S - 1, V), draft_noise, seed, "verify_draft",
+                                torch.float32, device)
+    u = torch.rand(B, S, generator=_gen(seed, "verify_uniform", device), device=device)
+    return cand, tl.to(dtype), dl.to(dtype), u
