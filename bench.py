@@ -204,6 +204,11 @@ def main():
     inj_flops = 2.0 * T * (cfg.feat_dim * cfg.hidden + cfg.hidden * cfg.n_layers * 2 *
                            cfg.n_kv_heads * cfg.head_dim)
 
+    # rejection-sampling verify at the same batch: synthetic target logits
+    # [B, S, V], the draft pass's own logits [B, S-1, V] as the proposal q
+    sv = sampling_verify(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, c_cfg,
+                         c_cache, timed, max(args.steps, 10), dev)
+
     if args.copy_probe:
         # a plain copy of known size: under a counter-collection run its
         # FETCH_SIZE / WRITE_SIZE give the scale of those counters
@@ -250,11 +255,50 @@ def main():
                                "(+ argmax reduce), dflash_lm_head_argmax",
                      "bytes_per_launch": lm_bytes,
                      "avg_launch_us": round(lm_avg_s * 1e6, 2)},
+        "sampling_verify": sv,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, wl, L, W)
     print(json.dumps(res), flush=True)
+
+
+def sampling_verify(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, c_cfg, c_cache,
+                    timed, n, dev):
+    """Time dflash_accept_sampling on the workload's batch: argmax drafts (q a
+    point mass) and drafts with q = softmax(draft logits).  Algorithmic bytes:
+    every target (and draft) logit read once, plus ids, draws and outputs."""
+    import torch
+    B, S, V = wl.batch, cfg.block_size, cfg.vocab
+    dt = synth._DT[cfg.act_dtype]
+    positions = torch.empty((B, S), dtype=torch.int32, device=dev)
+    slots, cand = torch.empty_like(positions), torch.empty_like(positions)
+    dlog = torch.empty((B, S - 1, V), dtype=dt, device=dev)
+    dws = dfl.workspace(dfl.draft_workspace_bytes(cfg, B, max_prefix))
+    dfl.dflash_draft_block(cfg, cw, cache, anchor, Ld, ptd, max_prefix, positions, slots, cand, dws,
+                           logits=dlog, c_cfg=c_cfg, c_cache=c_cache)
+    # candidates and target rows from the verify generator (the target favours
+    # the drafts, so accept lengths spread over the block)
+    vc, tl, _, u = synth.verify_inputs(B, S, V, wl.seed, dtype=dt, device=dev, bump=22.0,
+                                       bump_lo=13.0)
+    outs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
+    ot = torch.empty((B, S), dtype=torch.int32, device=dev)
+    esz = 2 if cfg.act_dtype == "bf16" else 4
+    res = {}
+    for mode, dl in (("argmax_drafts", None), ("draft_logits", dlog)):
+        ws = dfl.workspace(dfl.accept_sampling_workspace_bytes(B, S, V, dl is not None))
+
+        def call():
+            dfl.dflash_accept_sampling(vc, tl, u, Ld, outs[0], outs[1], ot, outs[2], outs[3], ws,
+                                       1.0, dl, 1.0)
+        call()
+        ms = timed(call, n)
+        nbytes = (B * S * V + (B * (S - 1) * V if dl is not None else 0)) * esz + B * S * 12
+        res[mode] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+                     "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "mean_commit": round(float(outs[1].float().mean()), 3)}
+    return res
 
 
 def cpu_baseline(cfg, wl, L, W_dev):

@@ -454,7 +454,7 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
 
 size_t dflash_accept_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab,
                                               int32_t has_draft_logits) {
-  if (batch <= 0 || block_size < 2 || block_size > 64 || vocab <= 0) return 0;
+  if (batch <= 0 || block_size < 2 || block_size > 64 || vocab <= 0 || vocab > 524288) return 0;
   return plan_spec(batch, block_size, vocab, has_draft_logits != 0).bytes;
 }
 
@@ -471,6 +471,7 @@ dflash_status dflash_accept_sampling(const int32_t* candidates, const void* targ
   if (block_size < 2 || block_size > 64)
     return fail(DFLASH_EUNSUPPORTED, "block_size %d outside 2..64", block_size);
   if (vocab <= 0) return fail(DFLASH_EINVAL, "vocab %d <= 0", vocab);
+  if (vocab > 524288) return fail(DFLASH_EUNSUPPORTED, "vocab %d > 524288", vocab);
   if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16)
     return fail(DFLASH_EUNSUPPORTED, "logits_dtype %d (supported: F32, BF16)", logits_dtype);
   if (!(target_temperature > 0.f) || !isfinite(target_temperature))

@@ -16,8 +16,9 @@
 //      lanes take the S-1 decisions at once and a ballot finds the first
 //      rejection; then every workgroup sums the weights of its chunk of the
 //      row the token is drawn from.
-//   3. spec_pick_kernel: per request, the chunk holding the draw, then the
-//      token inside it by a block-wide scan of per-thread runs.
+//   3. spec_pick_kernel: per request, the chunk holding the draw; its weights
+//      are staged in LDS with 16-byte loads, then a block-wide scan of
+//      per-thread runs over LDS finds the token.
 #include <math.h>
 
 #include "common.cuh"
@@ -27,6 +28,8 @@ namespace dflash {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxChunk2 = 8192;  // logits per pick chunk (weights staged in 32 KB of LDS)
+constexpr int kMaxStatsPartials = 4096;  // (2S - 1) * n_chunks1 per request, staged in LDS
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Walk result of one request, written by chunk 0 of the walk kernel.
@@ -176,25 +179,43 @@ __global__ __launch_bounds__(kThreads) void spec_walk_kernel(
     const float2* __restrict__ stats, int n_chunks1, float ct, float cd, int chunk2,
     int n_chunks2, float2* __restrict__ csum, SpecWalk* __restrict__ walk, int32_t* accept_len,
     int32_t* commit_len, int32_t* out_tokens, int32_t* new_seq_len) {
-  const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int B = gridDim.x;
   const bool has_draft = dl != nullptr;
   __shared__ float2 st_t[64], st_d[64];  // (max, 1 / sum) per row of this request
   __shared__ SpecWalk sw;
   __shared__ float red[kThreads / 64];
+  __shared__ float2 part[kMaxStatsPartials];
 
-  // merge the stats partials of each row (one thread per row, fixed order)
-  if (tid < S) {
-    const float2* p = stats + ((int64_t)r * S + tid) * n_chunks1;
-    float m = p[0].x, s = p[0].y;
-    for (int k = 1; k < n_chunks1; ++k) lse_merge(m, s, p[k].x, p[k].y, ct);
-    st_t[tid] = make_float2(m, 1.f / s);
-  } else if (has_draft && tid >= 64 && tid - 64 < S - 1) {
-    const int j = tid - 64;
-    const float2* p = stats + ((int64_t)B * S + (int64_t)r * (S - 1) + j) * n_chunks1;
-    float m = p[0].x, s = p[0].y;
-    for (int k = 1; k < n_chunks1; ++k) lse_merge(m, s, p[k].x, p[k].y, cd);
-    st_d[j] = make_float2(m, 1.f / s);
+  // this request's stats partials into LDS in one coalesced pass (target rows
+  // then draft rows, n_chunks1 per row), then one wave merges each row with a
+  // fixed butterfly
+  const int n_rows = has_draft ? 2 * S - 1 : S;
+  {
+    const float2* pt_ = stats + (int64_t)r * S * n_chunks1;
+    const float2* pd_ = stats + ((int64_t)B * S + (int64_t)r * (S - 1)) * n_chunks1;
+    const int nt = S * n_chunks1, nall = n_rows * n_chunks1;
+    for (int k = tid; k < nall; k += kThreads) part[k] = (k < nt) ? pt_[k] : pd_[k - nt];
+  }
+  __syncthreads();
+  for (int row = tid >> 6; row < n_rows; row += kThreads / 64) {
+    const float sc = (row < S) ? ct : cd;
+    float m = kNegInf, s = 0.f;
+    if (lane < n_chunks1) {
+      m = part[row * n_chunks1 + lane].x;
+      s = part[row * n_chunks1 + lane].y;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+      lse_merge(m, s, m2, s2, sc);
+    }
+    if (lane == 0) {
+      if (row < S)
+        st_t[row] = make_float2(m, 1.f / s);
+      else
+        st_d[row - S] = make_float2(m, 1.f / s);
+    }
   }
   __syncthreads();
 
@@ -293,13 +314,14 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
 }
 
 // grid (B); 256 threads.
-template <typename T>
+template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
     const T* __restrict__ tl, const T* __restrict__ dl, const float* __restrict__ uni, int S,
     int V, float ct, float cd, int chunk2, int n_chunks2, const float2* __restrict__ csum,
     const SpecWalk* __restrict__ walk, int32_t* out_tokens, int32_t* next_anchor) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const SpecWalk w = walk[r];
+  __shared__ float wl[kMaxChunk2];
   __shared__ int s_chunk, s_use_p;
   __shared__ float s_rem;
   __shared__ float wsum[kThreads / 64];
@@ -340,21 +362,32 @@ __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
   const bool use_p = s_use_p;
   const float rem = s_rem;
 
-  // per-thread contiguous runs of the chunk, scanned across the block
+  // the chunk's weights into LDS (coalesced loads)
   const int row_t = (w.mode == 2) ? S - 1 : w.a;
   const T* pt = tl + ((int64_t)r * S + row_t) * V;
   const T* pd = (w.mode == 0) ? dl + ((int64_t)r * (S - 1) + w.a) * V : nullptr;
   const int c0 = ch * chunk2, c1 = min(V, c0 + chunk2);
-  const int per = (c1 - c0 + kThreads - 1) / kThreads;
-  const int r0 = min(c1, c0 + tid * per), r1 = min(c1, r0 + per);
-  auto weight = [&](int i) -> float {
-    const float lt = ld1(pt + i);
-    if (use_p) return spec_p(lt, w, ct);
-    const float ld = pd ? ld1(pd + i) : 0.f;
-    return spec_weight(lt, ld, i, w, ct, cd);
-  };
+  for (int i = c0 + tid * VEC; i < c1; i += kThreads * VEC) {
+    float vt[VEC], vd[VEC];
+    VecLoad<T, VEC>::run(pt + i, vt);
+    if (pd) {
+      VecLoad<T, VEC>::run(pd + i, vd);
+    } else {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) vd[k] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k)
+      wl[i - c0 + k] = use_p ? spec_p(vt[k], w, ct) : spec_weight(vt[k], vd[k], i + k, w, ct, cd);
+  }
+  __syncthreads();
+
+  // per-thread contiguous runs of the chunk, scanned across the block
+  const int n = c1 - c0;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int r0 = min(n, tid * per), r1 = min(n, r0 + per);
   float s = 0.f;
-  for (int i = r0; i < r1; ++i) s += weight(i);
+  for (int i = r0; i < r1; ++i) s += wl[i];
   const float incl_w = wave_incl_scan(s);
   if (lane == 63) wsum[wv] = incl_w;
   const uint64_t posm = __ballot(s > 0.f);
@@ -383,16 +416,16 @@ __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
     int tok = -1, last = -1;
     float cum = excl;
     for (int i = r0; i < r1; ++i) {
-      const float wi = weight(i);
+      const float wi = wl[i];
       if (wi > 0.f) last = i;
       cum += wi;
       if (!last_positive && tok < 0 && cum > rem) tok = i;
     }
-    s_tok = (tok >= 0) ? tok : last;
+    s_tok = c0 + ((tok >= 0) ? tok : last);
   }
   __syncthreads();
   if (tid == 0) {
-    const int tok = (s_tok >= 0) ? s_tok : 0;
+    const int tok = (s_tok >= c0) ? s_tok : 0;
     out_tokens[(int64_t)r * S + w.a] = tok;
     next_anchor[r] = tok;
   }
@@ -418,7 +451,7 @@ hipError_t spec_launch(const int32_t* cand, const void* tl_, const void* dl_, co
                      cand, tl, dl, uni, prefix_len, S, V, stats, pl.n_chunks1, ct, cd, pl.chunk2,
                      pl.n_chunks2, csum, walk, accept_len, commit_len, out_tokens, new_seq_len);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((spec_pick_kernel<T>), dim3(B), dim3(kThreads), 0, st, tl, dl, uni, S, V, ct,
+  hipLaunchKernelGGL((spec_pick_kernel<T, VEC>), dim3(B), dim3(kThreads), 0, st, tl, dl, uni, S, V, ct,
                      cd, pl.chunk2, pl.n_chunks2, csum, walk, out_tokens, next_anchor);
   return hipGetLastError();
 }
@@ -439,7 +472,16 @@ SpecPlan plan_spec(int B, int S, int V, bool has_draft) {
     n = (V + chunk - 1) / chunk;
   };
   chunking(pl.rows, 2048, pl.chunk1, pl.n_chunks1);  // stats: ~2048 workgroups over all rows
+  const int rows_per_req = has_draft ? 2 * S - 1 : S;
+  while (pl.n_chunks1 > 1 && rows_per_req * pl.n_chunks1 > kMaxStatsPartials) {
+    pl.chunk1 += 64;  // fewer, longer chunks until one request's partials fit in LDS
+    pl.n_chunks1 = (V + pl.chunk1 - 1) / pl.chunk1;
+  }
   chunking(B, 1024, pl.chunk2, pl.n_chunks2);        // weight sums: ~1024 over the batch
+  if (pl.chunk2 > kMaxChunk2) {                      // the pick stages a chunk in LDS
+    pl.chunk2 = kMaxChunk2;
+    pl.n_chunks2 = (V + kMaxChunk2 - 1) / kMaxChunk2;  // <= 64 for V <= 64 * kMaxChunk2
+  }
   size_t off = 0;
   pl.off_stats = off;
   off += align256(sizeof(float2) * (size_t)pl.rows * pl.n_chunks1);

@@ -260,7 +260,7 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
  *   workspace      >= dflash_accept_sampling_workspace_bytes(batch, block_size,
  *                  vocab, draft_logits != NULL), 16-byte aligned
  * Arithmetic is fp32 with fixed-order sums (deterministic).  block_size 2..64;
- * logits_dtype F32 or BF16; temperatures finite and > 0 (draft_temperature is
+ * vocab <= 524288; logits_dtype F32 or BF16; temperatures finite and > 0 (draft_temperature is
  * read only with draft_logits).  NaN or +inf logits give unspecified tokens.
  */
 size_t dflash_accept_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab,

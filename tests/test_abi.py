@@ -148,7 +148,7 @@ def test_accept_sampling_argument_errors():
     assert call(B=0) == 0                       # nothing to do, no launch
     assert call(B=-1) == -1
     assert call(S=1) == -2 and call(S=65) == -2
-    assert call(V=0) == -1
+    assert call(V=0) == -1 and call(V=524289) == -2
     assert call(dt=dfl.FP8_E4M3) == -2
     assert call(Tt=0.0) == -1 and call(Tt=float("nan")) == -1
     assert call(Td=-1.0) == -1

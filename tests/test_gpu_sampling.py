@@ -131,6 +131,19 @@ def test_sampling_parity_batch32_full_vocab(with_draft):
     print(stats)
 
 
+def test_sampling_parity_many_requests_capped_chunks():
+    """Batch 200 at V = 151936: the pick chunks hit their 8192-logit cap (19
+    chunks per row instead of one per ~1024 / batch)."""
+    B, S, V = 200, 2, 151936
+    cand, tl, dl, u = synth.verify_inputs(B, S, V, seed=200, dtype=torch.bfloat16, device="cuda",
+                                          bump=22.0, bump_lo=13.0)
+    L = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for d in (None, dl):
+        g = run_gpu(cand, tl, u, L, 1.0, d, 1.0)
+        stats = check(g, run_oracle(cand, tl, u, L, 1.0, d, 1.0), cand, L)
+        assert stats["equal_draws"] >= 0.9 * stats["clear"], stats
+
+
 def test_sampling_misaligned_rows_take_scalar_path():
     """Logits that start 2 bytes past a 16-byte boundary run the scalar loads."""
     B, S, V = 4, 8, 2048
