@@ -41,16 +41,26 @@ GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
   GemmPlan p;
   p.fat = bf16 && M > 64;
   p.big = false;
-  if (p.fat && M > 192 && ((M + 255) / 256) * ((Ncols + 255) / 256) >= 256) {
-    // enough 256 x 256 tiles to fill the chip without splitting K (with 128
-    // rows or fewer the 128-row tiles of gemm_fat waste less)
+  if (p.fat && M > 192) {
+    // 256 x 256 tiles, one 512-thread workgroup per CU (~6 TFLOP/s each,
+    // several times the rate of gemm_fat's 256 x 128 tiles).  With fewer than
+    // 128 tiles K is split so that the grid reaches (but stays within) the
+    // 256 CUs, each split at least 512 deep; the split partials go through the
+    // same reduce-and-epilogue kernel as gemm_fat's.  (With 128 rows or fewer
+    // the 128-row tiles of gemm_fat waste less.)
     p.big = true;
     p.BM = 256;
     p.MB = 0;
     p.m_tiles = (M + 255) / 256;
     p.n_tiles = (Ncols + 255) / 256;
-    p.KS = 1;
-    p.Kc = K;
+    const int tiles = p.m_tiles * p.n_tiles;
+    int ks = tiles >= 128 ? 1 : 256 / tiles;
+    ks = ks < K / 512 ? ks : K / 512;
+    if (ks < 1) ks = 1;
+    int kc = (K + ks - 1) / ks;
+    kc = (kc + 31) / 32 * 32;
+    p.Kc = kc;
+    p.KS = (K + kc - 1) / kc;
     return p;
   }
   if (p.fat) {
@@ -96,7 +106,9 @@ GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
 
 size_t gemm_partial_floats(const GemmPlan& p) {
   if (p.KS <= 1) return 0;
-  return (size_t)p.KS * p.m_tiles * p.n_tiles * p.BM * BN;
+  // gemm_big's tiles are 256 wide: two 128-column partial tiles each
+  const size_t n128 = p.big ? 2 * (size_t)p.n_tiles : (size_t)p.n_tiles;
+  return (size_t)p.KS * p.m_tiles * n128 * p.BM * BN;
 }
 
 int logits_tiles(int V) { return (V + BN - 1) / BN; }
@@ -488,17 +500,22 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 
 template <class Epi>
 __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, int K, int m_tiles,
-                                                int n_tiles, int n_tiles128, Epi epi) {
+                                                int n_tiles, int n_tiles128, int KS, int Kc,
+                                                float* __restrict__ partial, Epi epi) {
   constexpr int SMEM = 2 * 128 * LDT * 4 > GB_NS * GB_STAGE * 2 ? 2 * 128 * LDT * 4
                                                                  : GB_NS * GB_STAGE * 2;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   bf16_t* const st0 = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, r16 = lane & 15, g4 = lane >> 4;
-  const int n_all = m_tiles * n_tiles;
+  // work item u = kb * tiles + t (K split slowest); XCD x (= workgroup id
+  // mod 8) takes a contiguous range of items
+  const int n_tile = m_tiles * n_tiles, n_all = n_tile * KS;
   const int per = (n_all + 7) / 8;
-  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (t >= n_all) return;  // padding of the last XCD's range
+  const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (u >= n_all) return;  // padding of the last XCD's range
+  const int kb = u / n_tile, t = u % n_tile;
+  const int k0 = kb * Kc, klen = imin(Kc, K - k0);
   const int first = (t / (FGM * n_tiles)) * FGM;
   const int gsz = imin(m_tiles - first, FGM);
   const int within = t % (FGM * n_tiles);
@@ -512,9 +529,11 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     const int row = (wave * 2 + v) * 16 + lane / 4;
-    ag[v] = asrc.A + (int64_t)block_row(imin(m0 + row, M - 1), asrc.S) * asrc.lda + (lane % 4) * 8;
+    ag[v] = asrc.A + (int64_t)block_row(imin(m0 + row, M - 1), asrc.S) * asrc.lda + (lane % 4) * 8 +
+            k0;
     const int s = wave * 2 + v;
-    bg[v] = epi.bslab(imin(2 * nt + s / 8, n_tiles128 - 1), s % 8) + lane * 8;
+    bg[v] = epi.bslab(imin(2 * nt + s / 8, n_tiles128 - 1), s % 8) + lane * 8 +
+            (int64_t)(k0 / 32) * kChunkElems;
   }
   auto issue = [&](bf16_t* stg, int c) {  // stage of K columns [32 c, 32 c + 32)
 #pragma unroll
@@ -544,7 +563,7 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  const int n_it = K / 32;
+  const int n_it = klen / 32;
   bf16_t* const st1 = st0 + GB_STAGE;
   bf16_t* const st2 = st1 + GB_STAGE;
   bf16_t* const st3 = st2 + GB_STAGE;
@@ -586,9 +605,28 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
           for (int e = 0; e < 4; ++e) tl[(i * 16 + g4 * 4 + e) * LDT + j * 16 + r16] = acc[i][j][e];
     }
     __syncthreads();
-    epi.prepare(128, m0 + 128 * h, M, tid);
-    epi.apply(tile0, 128, m0 + 128 * h, M, 2 * nt, tid);
-    epi.apply(tile1, 2 * nt + 1 < n_tiles128 ? 128 : 0, m0 + 128 * h, M, 2 * nt + 1, tid);
+    if (KS == 1) {
+      epi.prepare(128, m0 + 128 * h, M, tid);
+      epi.apply(tile0, 128, m0 + 128 * h, M, 2 * nt, tid);
+      epi.apply(tile1, 2 * nt + 1 < n_tiles128 ? 128 : 0, m0 + 128 * h, M, 2 * nt + 1, tid);
+    } else {
+      // split partial: rows [128 h, 128 h + 128) of the two 128-column tiles,
+      // in the reduce kernel's layout [(nt128 * m_tiles + mt) * KS + kb][256][128]
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int n128 = 2 * nt + q;
+        if (n128 >= n_tiles128) break;
+        const float* src = q ? tile1 : tile0;
+        float* dst = partial + ((int64_t)(n128 * m_tiles + mt) * KS + kb) * (256 * BN) +
+                     (int64_t)(128 * h) * BN;
+        for (int i = tid; i < 128 * BN / 4; i += 512) {
+          const int r = i / (BN / 4), c = (i % (BN / 4)) * 4;
+          *reinterpret_cast<float4*>(dst + r * BN + c) =
+              make_float4(src[r * LDT + c], src[r * LDT + c + 1], src[r * LDT + c + 2],
+                          src[r * LDT + c + 3]);
+        }
+      }
+    }
     __syncthreads();
   }
 }
@@ -1094,10 +1132,14 @@ static void launch_fat(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPl
 
 template <class Epi>
 static void launch_big(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPlan& p,
-                       int n_tiles128, const Epi& epi, hipStream_t st) {
-  const int grid = (p.m_tiles * p.n_tiles + 7) / 8 * 8;
+                       int n_tiles128, const Epi& epi, float* partial, hipStream_t st) {
+  const int grid = (p.m_tiles * p.n_tiles * p.KS + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_big<Epi>), dim3(grid), dim3(512), 0, st, asrc, M, K, p.m_tiles,
-                     p.n_tiles, n_tiles128, epi);
+                     p.n_tiles, n_tiles128, p.KS, p.Kc, partial, epi);
+  if (p.KS > 1)
+    hipLaunchKernelGGL((gemm_splitk_reduce<256, Epi>),
+                       dim3((unsigned)(n_tiles128 * p.m_tiles * (256 / RROWS))), dim3(256), 0, st,
+                       p.KS, p.m_tiles, M, (const float*)partial, epi);
 }
 
 template <typename T, class AS, class Epi>
@@ -1108,7 +1150,7 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
   if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     if (p.big) {
-      launch_big(asrc, M, K, p, (Ncols + BN - 1) / BN, epi, st);
+      launch_big(asrc, M, K, p, (Ncols + BN - 1) / BN, epi, ws.partial, st);
       return hipGetLastError();
     }
     if (p.fat) {
