@@ -896,6 +896,11 @@ __device__ __forceinline__ int* kv_block_flags() {
   __shared__ int f[8];
   return f;
 }
+// cache slot of each tile row, -1 when the row is not written
+__device__ __forceinline__ int32_t* kv_row_slot() {
+  __shared__ int32_t s[128];
+  return s;
+}
 
 template <typename T, typename KT> struct EpiKVInject {
   KVTargets tg; int H; int n_layers, nq, nkv, D; float eps; const float2* cs;
@@ -916,6 +921,7 @@ template <typename T, typename KT> struct EpiKVInject {
       const uint64_t b = __ballot(ok);
       if ((r & 15) == 0) kv_block_flags()[r / 16] = ((b >> (tid & 63 & ~15)) & 0xffffull) == 0xffffull;
     }
+    if (tid < rows) kv_row_slot()[tid] = row_written(m0 + tid, M) ? slots[m0 + tid] : -1;
     rs.fill(row_scale_lds(), rows, m0, M, tid);  // ends with a barrier
   }
   __device__ const T* bslab(int nt, int s) const {
@@ -939,34 +945,49 @@ template <typename T, typename KT> struct EpiKVInject {
         gk[hh][1] = Num<T>::to_f(g[lane + half]);
       }
     }
-    constexpr int G = 4;  // items per wave whose loads go out together
-    for (int ib = wave; ib < n_items; ib += nw * G) {
-      int32_t sl[G], vr[G];
-      float2 c[G];
-      int kind[G];  // 0 skip, 1 K row, 2 V row, 3 V block of 16 rows
-      // loads first, unconditionally (clamped rows), so that none waits for
-      // another's result; the decisions follow
+    // V heads of 16-row blocks of consecutive page-aligned slots: one (block,
+    // head) per wave, spread over the waves; lane = dimension, each writing a
+    // 16-slot run of its V^T page row
+    if (rows >= 16) {
+      for (int bi = wave; bi < (rows / 16) * HP; bi += nw) {
+        const int blk = bi / HP, hh = bi % HP, gh = nt * HP + hh, r = blk * 16;
+        if (gh >= n_layers * 2 * nkv || (gh % (2 * nkv)) < nkv || !bok[blk]) continue;
+        const int l = gh / (2 * nkv), head = gh % nkv;
+        const int32_t s0 = kv_row_slot()[r];
+        const int64_t page = s0 / P, off = s0 % P;
+        KT* base = static_cast<KT*>(tg.vc[l]) + ((page * nkv + head) * D) * P + off;
+        for (int d = lane; d < D; d += 64) {
+          float v[16];
 #pragma unroll
-      for (int u = 0; u < G; ++u) {
-        const int item = ib + nw * u;
-        const int m = imin(m0 + imin(item, n_items - 1) / HP, M - 1);
-        sl[u] = slots[m];
-        vr[u] = valid != nullptr ? valid[m / rpr] : rpr;
-        c[u] = lane < half ? cs[(int64_t)m * half + lane] : make_float2(0.f, 0.f);
+          for (int i = 0; i < 16; ++i) v[i] = t[(r + i) * LDT + hh * D + d] * srs[r + i];
+          store_run16(base + (int64_t)d * P, v);
+        }
       }
+    }
+    constexpr int G = 4;  // items per wave whose loads go out together
+    const int32_t* rsl = kv_row_slot();
+    for (int ib = wave; ib < n_items; ib += nw * G) {
+      int32_t sl[G];
+      float2 c[G];
+      int kind[G];  // 0 skip (or written with its 16-row block above), 1 K row, 2 V row
+      // decisions from LDS, then the (cos, sin) loads of every K row of the
+      // batch go out before any is used
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         const int item = ib + nw * u;
         const int r = item / HP, hh = item % HP, m = m0 + r, gh = nt * HP + hh;
         kind[u] = 0;
+        sl[u] = -1;
         if (item >= n_items || m >= M || gh >= n_layers * 2 * nkv) continue;
         const bool is_v = (gh % (2 * nkv)) >= nkv;
-        if (is_v && rows >= 16 && bok[r / 16]) {
-          kind[u] = (r % 16 == 0) ? 3 : 0;
-          continue;
-        }
-        const bool written = (m % rpr) < vr[u] && sl[u] >= 0 && sl[u] < num_slots;
-        if (written) kind[u] = is_v ? 2 : 1;
+        if (is_v && rows >= 16 && bok[r / 16]) continue;
+        sl[u] = rsl[r];
+        if (sl[u] >= 0) kind[u] = is_v ? 2 : 1;
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int m = m0 + (ib + nw * u) / HP;
+        c[u] = (kind[u] == 1 && lane < half) ? cs[(int64_t)m * half + lane] : make_float2(0.f, 0.f);
       }
 #pragma unroll
       for (int u = 0; u < G; ++u) {
@@ -975,17 +996,6 @@ template <typename T, typename KT> struct EpiKVInject {
         const int r = item / HP, hh = item % HP, gh = nt * HP + hh;
         const int l = gh / (2 * nkv), head = gh % nkv;
         const int64_t page = sl[u] / P, off = sl[u] % P;
-        if (kind[u] == 3) {
-          // the block's first row: this wave writes all 16 rows, lane = dim
-          KT* base = static_cast<KT*>(tg.vc[l]) + ((page * nkv + head) * D) * P + off;
-          for (int d = lane; d < D; d += 64) {
-            float v[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = t[(r + i) * LDT + hh * D + d] * srs[r + i];
-            store_run16(base + (int64_t)d * P, v);
-          }
-          continue;
-        }
         const bool act = lane < half;
         const float sc = srs[r];
         const float x0 = act ? t[r * LDT + hh * D + lane] * sc : 0.f;
