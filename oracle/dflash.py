@@ -54,8 +54,12 @@ def block_prep(anchor, prefix_len, page_table, block_size, mask_token_id, page_s
 
     For request r and block offset j: input id = anchor_r if j == 0 else the
     mask id; logical position = L_r + j; physical slot = the request's
-    position-to-slot mapping at that position, here a page table:
-    page_table[r][pos // P] * P + pos % P.
+    position-to-slot mapping at that position, here a page table read as a
+    ring: page_table[r][(pos // P) mod width] * P + pos % P (the identity
+    when the table covers every position; with a draft window the table
+    only needs the pages of the window and the block, which is the private
+    compact mapping windowed drafting uses: "Inside SGLang ...", section
+    "Who owns what?" of the startup walk-through).
     """
     anchor = np.asarray(anchor, np.int64)
     L = np.asarray(prefix_len, np.int64)
@@ -64,7 +68,8 @@ def block_prep(anchor, prefix_len, page_table, block_size, mask_token_id, page_s
     ids[:, 0] = anchor
     pos = L[:, None] + np.arange(S)[None, :]
     pt = np.asarray(page_table, np.int64)
-    slots = pt[np.arange(B)[:, None], pos // page_size] * page_size + pos % page_size
+    slots = pt[np.arange(B)[:, None], (pos // page_size) % pt.shape[1]] * page_size + \
+        pos % page_size
     return ids, pos, slots
 
 
@@ -120,8 +125,9 @@ def draft_block(cfg, W, cache, anchor, prefix_len, page_table, rope=True, reques
         h = rms(x; in_norm); q, k, v = h Wq^T, h Wk^T, h Wv^T
         q, k per head <- RoPE(rms(.; q_norm / k_norm), pos)
         o = attention of the block queries over the cached context keys at
-            logical positions [0, L_r) (window-limited on sliding layers) and
-            all S block keys, non-causal
+            logical positions [0, L_r) (window-limited on sliding layers; with
+            a draft window N only positions [L_r - N, L_r), on every layer)
+            and all S block keys, non-causal
         x += o Wo^T;  h2 = rms(x; post_norm);  x += (silu(h2 Wg^T) * h2 Wu^T) Wd^T
     Final: y = rms(x; final_norm) on rows 1..S-1 (the anchor row is not a
     prediction), logits = y W_lm^T with the target's lm_head, draft id =
@@ -160,8 +166,10 @@ def draft_block(cfg, W, cache, anchor, prefix_len, page_table, rope=True, reques
             lo = 0
             if W_l:
                 lo = max(0, int(L[r]) - W_l + 1)
+            if cfg.context_window:
+                lo = max(lo, int(L[r]) - cfg.context_window)
             cpos = np.arange(lo, int(L[r]), dtype=np.int64)
-            cslot = pt[r, cpos // P] * P + cpos % P
+            cslot = pt[r, (cpos // P) % pt.shape[1]] * P + cpos % P
             o[i] = block_attention(q[i], cache.k[l][cslot], cache.v[l][cslot], cpos,
                                    k[i], v[i], pos[r], W_l)
         x = x + o.reshape(b, S, nq * D) @ _f64(Lw["w_o"]).T

@@ -394,3 +394,73 @@ def test_draft_pass_matches_transformers_qwen3_layers(windowed):
         # transformers builds its RoPE frequency table in fp32 (relative error
         # ~1e-7); any structural difference would show at the 1e-1 scale
         assert np.allclose(logits[0].numpy(), o["logits"][r], rtol=1e-5, atol=1e-5)
+
+
+# ---------------------------------------------------------------- draft window
+def _windowed(cfg, n):
+    return dataclasses.replace(cfg, context_window=n)
+
+
+def test_draft_window_covering_the_context_changes_nothing():
+    cfg = SMALL_F32_D64
+    W, pt, npages = _setup(cfg, L=(45, 61))
+    cache = _ctx_cache(cfg, W, pt, npages, [45, 61])
+    a = oracle.draft_block(cfg, W, cache, [5, 6], [45, 61], pt)
+    b = oracle.draft_block(_windowed(cfg, 61), W, cache, [5, 6], [45, 61], pt)
+    assert np.array_equal(a["logits"], b["logits"])
+
+
+def test_draft_window_ring_table_equals_linear_table():
+    """A ring of R pages holding only the window's rows (logical page q in
+    physical page table[q mod R]) gives bit-identical logits to the full
+    linear table; rows before the window are NaN in the linear cache, so a
+    finite result also shows they are never read."""
+    N, L = 20, [45, 61]
+    cfg = _windowed(SMALL_F32_D64, N)
+    W, pt, npages = _setup(cfg, L=tuple(L))
+    lin = _ctx_cache(cfg, W, pt, npages, L)
+    S, P = cfg.block_size, cfg.page_size
+    R = (N + S - 1 + P - 1) // P + 1                  # pages spanned by window + block
+    rng = np.random.default_rng(0)
+    ring_pt = rng.permutation(2 * R)[:2 * R].reshape(2, R)
+    ring = oracle.OracleCache(cfg, 2 * R * P)
+    for r, l in enumerate(L):
+        for p in range(l - N, l):
+            src = pt[r, p // P] * P + p % P
+            dst = ring_pt[r, (p // P) % R] * P + p % P
+            for layer in range(cfg.n_layers):
+                ring.k[layer][dst] = lin.k[layer][src]
+                ring.v[layer][dst] = lin.v[layer][src]
+        for p in range(0, l - N):                    # poison what the window excludes
+            src = pt[r, p // P] * P + p % P
+            for layer in range(cfg.n_layers):
+                lin.k[layer][src] = np.nan
+                lin.v[layer][src] = np.nan
+    a = oracle.draft_block(cfg, W, lin, [5, 6], L, pt)
+    b = oracle.draft_block(cfg, W, ring, [5, 6], L, ring_pt)
+    assert np.isfinite(a["logits"]).all()
+    assert np.array_equal(a["logits"], b["logits"])
+    pos = np.array(L)[:, None] + np.arange(S)
+    assert np.array_equal(b["slots"], ring_pt[np.arange(2)[:, None], (pos // P) % R] * P + pos % P)
+
+
+def test_draft_window_equals_shifted_short_context():
+    """Attending to the last N rows of an L-row context equals attending to a
+    context of exactly those N rows re-injected at positions shifted by L - N
+    (RoPE sees only differences): the window means what it says."""
+    N, L = 24, 61
+    base = dataclasses.replace(SMALL_F32_D64, sliding_window=())
+    cfg = _windowed(base, N)
+    W, pt, npages = _setup(cfg, L=(L,))
+    f = synth.features(L, cfg, 5).numpy()
+    full = oracle.OracleCache(cfg, npages * 16)
+    pos = np.arange(L)
+    oracle.project_context(cfg, W, full, f, pos, pt[0, pos // 16] * 16 + pos % 16)
+    a = oracle.draft_block(cfg, W, full, [7], [L], pt)
+    short = oracle.OracleCache(base, npages * 16)
+    sp = np.arange(N)
+    oracle.project_context(base, W, short, f[L - N:], sp, pt[0, sp // 16] * 16 + sp % 16)
+    b = oracle.draft_block(base, W, short, [7], [N], pt)
+    assert np.allclose(a["logits"], b["logits"], rtol=1e-5, atol=1e-5)
+    c = oracle.draft_block(base, W, full, [7], [L], pt)
+    assert not np.allclose(a["logits"], c["logits"], rtol=1e-3, atol=1e-3)

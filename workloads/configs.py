@@ -36,6 +36,7 @@ class DFlashConfig:
     rope_theta: float = 1e6
     act_dtype: str = "bf16"                # "f32" | "bf16": weights, features, logits
     kv_dtype: str = "bf16"                 # "f32" | "bf16" | "fp8_e4m3"
+    context_window: int = 0                # draft window: last N context rows (0 = all)
 
     @property
     def feat_dim(self) -> int:
