@@ -49,6 +49,8 @@ def draft_pass_bytes(cfg, L):
         W = cfg.window(l)
         for Lr in L:
             keys = min(Lr, W - 1) if W else Lr
+            if cfg.context_window:
+                keys = min(keys, cfg.context_window)
             b += keys * nkv * D * 2 * kvb
     b += B * S * H * wb
     return b

@@ -42,7 +42,8 @@ class CConfig(ctypes.Structure):
                 ("page_size", ctypes.c_int32),
                 ("sliding_window", ctypes.c_int32 * MAX_LAYERS),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("act_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("context_window", ctypes.c_int32)]
 
 
 _LAYER_FIELDS = ["in_norm", "w_qkv", "q_norm", "k_norm", "w_o", "post_norm", "w_gate", "w_up",
@@ -147,6 +148,7 @@ def make_config(cfg) -> CConfig:
         c.sliding_window[l] = int(cfg.sliding_window[l]) if l < len(cfg.sliding_window) else 0
     c.rms_eps, c.rope_theta = float(cfg.rms_eps), float(cfg.rope_theta)
     c.act_dtype, c.kv_dtype = _DT_CODE[cfg.act_dtype], _DT_CODE[cfg.kv_dtype]
+    c.context_window = int(getattr(cfg, "context_window", 0))
     return c
 
 

@@ -70,6 +70,7 @@ dflash_status check_config(const dflash_config* c) {
     return fail(DFLASH_EINVAL, "rope_theta must be finite and > 0");
   for (int l = 0; l < c->n_layers; ++l)
     if (c->sliding_window[l] < 0) return fail(DFLASH_EINVAL, "negative sliding_window[%d]", l);
+  if (c->context_window < 0) return fail(DFLASH_EINVAL, "negative context_window");
   return DFLASH_OK;
 }
 
@@ -163,8 +164,10 @@ struct DraftWs {
 
 int layer_max_keys(const dflash_config* c, int l, int max_prefix) {
   const int W = c->sliding_window[l];
-  if (W > 0 && W - 1 < max_prefix) return W - 1;
-  return max_prefix;
+  int keys = max_prefix;
+  if (W > 0 && W - 1 < keys) keys = W - 1;
+  if (c->context_window > 0 && c->context_window < keys) keys = c->context_window;
+  return keys;
 }
 
 DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
@@ -384,7 +387,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     if ((e = launch_attention(dt, cfg->kv_dtype, D, L.q, L.kb, L.vb, cache->k[l], cache->v[l],
                               page_table, max_pages, cache->num_pages, prefix_len, max_prefix_len,
                               batch, S, nq, nkv, cfg->page_size, cfg->sliding_window[l],
-                              L.plans[l], L.o_part, L.ml_part, L.seg, L.o, st)) != hipSuccess)
+                              cfg->context_window, L.plans[l], L.o_part, L.ml_part, L.seg, L.o, st)) != hipSuccess)
       return hip_fail(e, "attention");
     if ((e = gemm_residual(dt, asrc_plain(L.o, nq * D), M, nq * D, W.w_o, H, L.x, L.ss, L.xg,
                            W.post_norm, L.gs, st)) != hipSuccess)

@@ -81,6 +81,7 @@ struct AttnArgs {
   const int32_t* pt; int max_pages; int64_t num_pages;
   const int32_t* prefix_len; int max_prefix;
   int B, S, G, nq, nkv, P, window, W;
+  int cwin;                            // draft window: last cwin context keys (0: all)
   float scale_log2;
   float* o_part; float2* ml_part;  // per partial slot: [64 rows][D], [64 rows]
   int4* seg;                       // per request: (units before it per head, units, U, -)
@@ -101,13 +102,21 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
-// Context length clamped as the kernels use it, and the units of a request
-// of that length.
+// Context length clamped as the kernels use it, the first context key any
+// block query sees (sliding window: keys i > L - W; draft window: the last
+// cwin keys), and the units of a request of that length.  Logical page q of a
+// request lives in physical page page_table[q mod max_pages] (a ring: the
+// identity when the table covers the whole prefix).
 __device__ __forceinline__ int clamped_len(const AttnArgs& a, int r) {
-  return imin(imax(a.prefix_len[r], 0), imin(a.max_prefix, a.max_pages * a.P));
+  return imin(imax(a.prefix_len[r], 0), a.max_prefix);
+}
+__device__ __forceinline__ int key_lo(const AttnArgs& a, int L) {
+  int lo = a.window > 0 ? L - a.window + 1 : 0;
+  if (a.cwin > 0) lo = imax(lo, L - a.cwin);
+  return imax(lo, 0);
 }
 __device__ __forceinline__ int units_of_len(const AttnArgs& a, int L) {
-  const int lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
+  const int lo = key_lo(a, L);
   const int a0 = lo & ~31;
   return 1 + (L > a0 ? (L - a0 + 31) / 32 : 0);
 }
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     for (int u = 0; u < SPB::PPT; ++u)
       rb[u] = gload16(piece_src<CT, D>(kp, vp, 16, tid + 256 * u));
   }
-  const int lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
+  const int lo = key_lo(a, L);
   const int a0 = lo & ~31;
   const bool has_blk = u0 == 0;
   const int t_first = imax(u0 - 1, 0);             // first context step
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     // filled: the loads issued below read step 0 unconditionally
     const int npages = (kbeg + 32 * imax(n_ctx, 1) - 1) / a.P - pfirst + 1;
     for (int i = tid; i < npages; i += 256) {
-      const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + (pfirst + i) % a.max_pages];
       pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
     }
   }
@@ -640,7 +649,7 @@ __global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
   }
-  const int lo = a.window > 0 ? imax(0, L - a.window + 1) : 0;
+  const int lo = key_lo(a, L);
   const int a0 = lo & ~31;
   const int blk = u0 == 0 ? 1 : 0;                 // the part starts with the block's keys
   const int t_first = imax(u0 - 1, 0);             // first context step
@@ -651,7 +660,7 @@ __global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs
   if (n_ctx > 0) {
     const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
     for (int i = tid; i < npages; i += 256) {
-      const int64_t page = a.pt[(int64_t)r * a.max_pages + imin(pfirst + i, a.max_pages - 1)];
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + (pfirst + i) % a.max_pages];
       pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
     }
   }
@@ -937,7 +946,8 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             const void* vblk, const void* kc, const void* vc,
                             const int32_t* page_table, int max_pages, int64_t num_pages,
                             const int32_t* prefix_len, int max_prefix, int B, int S, int nq,
-                            int nkv, int page_size, int window, const AttnPlan& plan,
+                            int nkv, int page_size, int window, int ctx_window,
+                            const AttnPlan& plan,
                             float* o_part, float2* ml_part, int4* seg, void* out,
                             hipStream_t st) {
   const bool dma = dt != DFLASH_F32 && kv_dt != DFLASH_FP8_E4M3;
@@ -947,6 +957,7 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
   a.pt = page_table; a.max_pages = max_pages; a.num_pages = num_pages;
   a.prefix_len = prefix_len; a.max_prefix = max_prefix;
   a.B = B; a.S = S; a.G = nq / nkv; a.nq = nq; a.nkv = nkv; a.P = page_size; a.window = window;
+  a.cwin = ctx_window;
   a.W = plan.n_launch;
   a.scale_log2 = LOG2E / sqrtf((float)D);
   a.o_part = o_part; a.ml_part = ml_part; a.seg = seg;

@@ -142,7 +142,8 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             const void* kc, const void* vc, const int32_t* page_table,
                             int max_pages, int64_t num_pages, const int32_t* prefix_len,
                             int max_prefix, int B,
-                            int S, int nq, int nkv, int page_size, int window, const AttnPlan& plan,
+                            int S, int nq, int nkv, int page_size, int window, int ctx_window,
+                            const AttnPlan& plan,
                             float* o_part, float2* ml_part, int4* seg, void* out, hipStream_t st);
 
 }  // namespace dflash

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void block_prep_kernel(
   int id = (j == 0) ? anchor[r] : mask_id;
   id = imin(imax(id, 0), V - 1);
   const int pos = prefix_len[r] + j;
-  const int pidx = imin(imax(pos / P, 0), max_pages - 1);
+  const int pidx = imax(pos / P, 0) % max_pages;  // the page table is a ring
   if (tid == 0) {
     if (block_ids != nullptr) block_ids[row] = (j == 0) ? anchor[r] : mask_id;
     positions[row] = pos;

@@ -79,6 +79,8 @@ typedef struct {
   float rope_theta;        /* neox (rotate-half) RoPE over the whole head_dim      */
   int32_t act_dtype;       /* dflash_dtype of weights, features and logits         */
   int32_t kv_dtype;        /* dflash_dtype of the draft K/V cache                  */
+  int32_t context_window;  /* draft window: the draft pass reads only the last      */
+                           /* context_window committed rows on every layer (0: all) */
 } dflash_config;
 
 /* Weights of one draft decoder layer, all of dtype act_dtype; the matrices
@@ -183,7 +185,15 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
  *
  * For request r with committed prefix L_r = prefix_len[r] and anchor token
  * anchor[r] the block is ids = [anchor, MASK x (S-1)] at logical positions
- * L_r .. L_r+S-1 and cache slots page_table[r][pos / P] * P + pos % P.
+ * L_r .. L_r+S-1 and cache slots page_table[r][(pos / P) mod max_pages] * P +
+ * pos % P: the page table is read as a ring, the identity when it covers the
+ * whole prefix.  With a draft window N (cfg->context_window) the context keys
+ * are those at positions [L_r - N, L_r) on every layer (also bounded by a
+ * sliding window), so the table needs only the pages that the window and the
+ * block span ("Inside SGLang ...", section "Who owns what?": windowed drafting
+ * keeps a private compact mapping); the caller keeps those positions'
+ * slots distinct (N + S + P - 1 <= max_pages * P suffices) and injects the
+ * committed rows at the slots this call returns.
  * x = embed[ids]; each layer applies q/k/v projection with per-head q/k
  * RMSNorm and RoPE, attention of the S block queries over the cached context
  * keys 0..L_r-1 (on a sliding layer with window W only keys i with
@@ -194,8 +204,9 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
  * draft token.  The block's own K/V are not stored.
  *
  *   anchor, prefix_len  [batch]
- *   page_table          [batch, max_pages]; entries up to page (L_r + S - 1) / P
- *                       must be valid pages of the cache
+ *   page_table          [batch, max_pages], read as a ring; every entry the
+ *                       window and the block reach (logical pages up to
+ *                       (L_r + S - 1) / P, mod max_pages) must be a valid page
  *   max_prefix_len      host upper bound of every prefix_len[r] (sizes the
  *                       split-KV grid; larger prefixes are truncated to it)
  *   block_ids           nullable [batch, S] out: [anchor, MASK, ...]

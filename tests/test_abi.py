@@ -42,8 +42,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_layout_matches_header():
-    # 11 int32, 16 windows, 2 floats, 2 int32
-    assert ctypes.sizeof(dfl.CConfig) == 4 * (11 + 16 + 2 + 2)
+    # 11 int32, 16 windows, 2 floats, 3 int32
+    assert ctypes.sizeof(dfl.CConfig) == 4 * (11 + 16 + 2 + 3)
     assert ctypes.sizeof(dfl.CWeights) == 8 * (5 + 9 * dfl.MAX_LAYERS)
     assert ctypes.sizeof(dfl.CKVCache) == 8 * (2 * dfl.MAX_LAYERS + 1)
 

@@ -19,6 +19,7 @@ Tolerances (floating point):
   draft pass then reads caches that differ by those single-code roundings;
   with identical caches the bf16 bound above holds).
 """
+import dataclasses
 import numpy as np
 import pytest
 import torch
@@ -301,3 +302,35 @@ def test_cycle_inject_draft_accept(name):
     assert rel.max() <= rel_tol
     sure = top2_margin(o2["logits"]) > m_tol
     assert np.array_equal(out2["candidates"].cpu().numpy()[:, 1:][sure], o2["draft_ids"][sure])
+
+
+# ---------------------------------------------------------------- draft window
+@pytest.mark.parametrize("name,window", [("small_bf16", 48), ("small_swa_fp8", 30),
+                                         ("small_f32_d64", 20)])
+def test_draft_block_window_ring_parity(name, window):
+    """Draft window N with the page table read as a ring of R pages per
+    request (prefixes up to several rings long, so positions wrap): every
+    layer reads only the last N context rows."""
+    wl = get_workload(name)
+    cfg = dataclasses.replace(wl.cfg, context_window=window)
+    wl = dataclasses.replace(wl, cfg=cfg)
+    S, P = cfg.block_size, cfg.page_size
+    R = (window + S - 1 + P - 1) // P + 1
+    _print(f"[draft window parity] {name} N={window} ring of {R} pages")
+    st = Setup(wl)
+    assert st.B * R <= st.num_pages and int(st.L.max()) > R * P
+    perm = torch.randperm(st.num_pages, generator=torch.Generator().manual_seed(window))
+    st.pt = perm[:st.B * R].view(st.B, R).to(torch.int32)
+    out = st.draft()
+    o = oracle.draft_block(cfg, st.np_W(), st.oracle_cache(), st.anchor.numpy(), st.L.numpy(),
+                           st.pt.numpy())
+    assert np.array_equal(out["positions"].cpu().numpy(), o["positions"])
+    assert np.array_equal(out["slots"].cpu().numpy(), o["slots"])
+    rel_tol, m_tol = tol(cfg)
+    gl = out["logits"].float().cpu().numpy()
+    rel = logits_row_rel_err(gl, o["logits"])
+    _print(f"  logits max rel err {rel.max():.3e}")
+    assert rel.max() <= rel_tol
+    sure = top2_margin(o["logits"]) > m_tol
+    cand = out["candidates"].cpu().numpy()
+    assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])

@@ -13,7 +13,7 @@ size of 3*hidden for the Kimi-shaped draft.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Optional, Tuple
 
 
@@ -127,6 +127,10 @@ WORKLOADS = {
     "kimi_k26_b8": Workload("kimi_k26_b8", KIMI_DRAFT, batch=16, ctx=(32768, 32768),
                             commit=(1, 8),
                             desc="Kimi-K2.6-DFlash-shaped draft, fp8 KV, batch 16, 32768 context"),
+    "kimi_k26_b8_w4096": Workload("kimi_k26_b8_w4096",
+                                  replace(KIMI_DRAFT, context_window=4096),
+                                  batch=16, ctx=(32768, 32768), commit=(1, 8),
+                                  desc="the Kimi-shaped workload with a 4096-row draft window"),
     # small parity workloads
     "small_bf16": Workload("small_bf16", SMALL_BF16, batch=3, ctx=(37, 301), commit=(1, 16),
                            inject_rows=0, seed=1),
