@@ -21,3 +21,4 @@ from .primitives import rms_norm, rope_neox, silu, softmax, block_attention  # n
 from .dflash import (block_prep, project_context, draft_block, accept,  # noqa: F401
                      OracleCache, speculative_decode)
 from .sampling import accept_sampling  # noqa: F401
+from . import selector  # noqa: F401

@@ -181,7 +181,7 @@ def draft_block(cfg, W, cache, anchor, prefix_len, page_table, rope=True, reques
     draft = np.argmax(logits, axis=-1)
     cand = np.concatenate([np.asarray(anchor, np.int64)[reqs][:, None], draft], axis=1)
     return {"block_ids": ids, "positions": pos, "slots": slots, "logits": logits,
-            "draft_ids": draft, "candidates": cand, "requests": reqs}
+            "draft_ids": draft, "candidates": cand, "requests": reqs, "hidden": y}
 
 
 def accept(candidates, posterior, prefix_len):
