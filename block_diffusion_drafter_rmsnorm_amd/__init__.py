@@ -60,6 +60,11 @@ class CWeights(ctypes.Structure):
                 ("final_norm", ctypes.c_void_p), ("layer", CLayerWeights * MAX_LAYERS)]
 
 
+class CSelector(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("w_h", ctypes.c_void_p),
+                ("rank", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
 class CKVCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p * MAX_LAYERS), ("v", ctypes.c_void_p * MAX_LAYERS),
                 ("num_pages", ctypes.c_int64)]
@@ -68,6 +73,7 @@ class CKVCache(ctypes.Structure):
 EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
             "dflash_accept_sampling_workspace_bytes", "dflash_accept_sampling",
+            "dflash_selector_workspace_bytes", "dflash_draft_block_selector",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_status_string", "dflash_last_error"]
@@ -100,6 +106,12 @@ def _load():
     lib.dflash_accept_sampling.argtypes = [P, P, P, I32, I32, F, F, P, P, I32, I32, P, P, P, P, P,
                                            P, SZ, P]
     lib.dflash_accept_sampling.restype = I32
+    selp = ctypes.POINTER(CSelector)
+    lib.dflash_selector_workspace_bytes.argtypes = [cfgp, selp, I32, I32]
+    lib.dflash_selector_workspace_bytes.restype = SZ
+    lib.dflash_draft_block_selector.argtypes = [cfgp, wp, kvp, selp, P, P, P, I32, I32, I32, P, P,
+                                                P, P, P, P, P, F, P, P, SZ, P]
+    lib.dflash_draft_block_selector.restype = I32
     lib.dflash_lm_head_workspace_bytes.argtypes = [cfgp, I32]
     lib.dflash_lm_head_workspace_bytes.restype = SZ
     lib.dflash_lm_head_argmax.argtypes = [cfgp, P, P, I32, P, P, P, SZ, P]
@@ -312,6 +324,42 @@ def dflash_accept_sampling(candidates: torch.Tensor, target_logits: torch.Tensor
         float(target_temperature), float(draft_temperature), _ptr(uniforms), _ptr(prefix_len),
         int(B), int(S), _ptr(accept_len), _ptr(commit_len), _ptr(out_tokens), _ptr(next_anchor),
         _ptr(new_seq_len), _ptr(ws), int(ws.numel()), _stream(stream)))
+
+
+class Selector:
+    """DFlash 2 selector weights: a, b [V, rank] (act dtype), w_h [rank, H]
+    (packed here, once).  The tensors are kept alive by this object."""
+
+    def __init__(self, a: torch.Tensor, b: torch.Tensor, w_h: torch.Tensor, top_k: int = 8):
+        self.a, self.b = a.contiguous(), b.contiguous()
+        self.w_h = dflash_pack_matrix(w_h.contiguous())
+        self.c = CSelector(self.a.data_ptr(), self.b.data_ptr(), self.w_h.data_ptr(),
+                           int(a.shape[1]), int(top_k))
+
+
+def selector_workspace_bytes(cfg, sel: "Selector", batch: int, max_prefix_len: int) -> int:
+    return int(_lib.dflash_selector_workspace_bytes(ctypes.byref(make_config(cfg)),
+                                                    ctypes.byref(sel.c), int(batch),
+                                                    int(max_prefix_len)))
+
+
+def dflash_draft_block_selector(cfg, weights: CWeights, cache: "KVCache", sel: "Selector",
+                                anchor: torch.Tensor, prefix_len: torch.Tensor,
+                                page_table: torch.Tensor, max_prefix_len: int,
+                                positions: torch.Tensor, slots: torch.Tensor,
+                                candidates: torch.Tensor, cand_ids: torch.Tensor,
+                                q_rows: torch.Tensor, ws: torch.Tensor,
+                                uniforms: Optional[torch.Tensor] = None, temperature: float = 1.0,
+                                block_ids: Optional[torch.Tensor] = None,
+                                logits: Optional[torch.Tensor] = None, stream=None):
+    c_cfg = make_config(cfg)
+    c_cache = cache.c_struct()
+    _check(_lib.dflash_draft_block_selector(
+        ctypes.byref(c_cfg), ctypes.byref(weights), ctypes.byref(c_cache), ctypes.byref(sel.c),
+        _ptr(anchor), _ptr(prefix_len), _ptr(page_table), int(page_table.shape[1]),
+        int(anchor.shape[0]), int(max_prefix_len), _ptr(block_ids), _ptr(positions), _ptr(slots),
+        _ptr(candidates), _ptr(cand_ids), _ptr(q_rows), _ptr(uniforms), float(temperature),
+        _ptr(logits), _ptr(ws), int(ws.numel()), _stream(stream)))
 
 
 def lm_head_workspace_bytes(cfg, rows: int) -> int:

@@ -338,7 +338,7 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
   return DFLASH_OK;
 }
 
-dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w,
+static dflash_status check_draft_args(const dflash_config* cfg, const dflash_weights* w,
                                  const dflash_kv_cache* cache, const int32_t* anchor,
                                  const int32_t* prefix_len, const int32_t* page_table,
                                  int32_t max_pages, int32_t batch, int32_t max_prefix_len,
@@ -360,10 +360,18 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     return fail(DFLASH_EINVAL, "anchor, prefix_len, page_table, positions, slots and candidates "
                                "must not be NULL");
   if (logits != nullptr && !aligned16(logits)) return fail(DFLASH_EINVAL, "logits not aligned");
-  const DraftWs L = layout_draft(cfg, batch, max_prefix_len, workspace);
-  if (workspace == nullptr || workspace_bytes < L.bytes)
-    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return DFLASH_OK;
+}
+
+// The backbone pass, the lm_head and the argmax (candidates 1..S-1), on a
+// workspace already carved by layout_draft.
+static dflash_status draft_core(const dflash_config* cfg, const dflash_weights* w,
+                                const dflash_kv_cache* cache, const int32_t* anchor,
+                                const int32_t* prefix_len, const int32_t* page_table,
+                                int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+                                int32_t* block_ids, int32_t* positions, int32_t* slots,
+                                int32_t* candidates, void* logits, const DraftWs& L,
+                                hipStream_t st) {
   const int dt = cfg->act_dtype, S = cfg->block_size, M = batch * S, M1 = batch * (S - 1);
   const int H = cfg->hidden, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, D = cfg->head_dim;
   const int I = cfg->inter;
@@ -405,6 +413,115 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   if ((e = launch_argmax_reduce(L.lm_part, M1, logits_tiles(cfg->vocab), S, candidates, st)) !=
       hipSuccess)
     return hip_fail(e, "argmax");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w,
+                                 const dflash_kv_cache* cache, const int32_t* anchor,
+                                 const int32_t* prefix_len, const int32_t* page_table,
+                                 int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+                                 int32_t* block_ids, int32_t* positions, int32_t* slots,
+                                 int32_t* candidates, void* logits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  dflash_status s = check_draft_args(cfg, w, cache, anchor, prefix_len, page_table, max_pages,
+                                     batch, max_prefix_len, block_ids, positions, slots,
+                                     candidates, logits, workspace, workspace_bytes, stream);
+  if (s != DFLASH_OK || batch == 0) return s;
+  const DraftWs L = layout_draft(cfg, batch, max_prefix_len, workspace);
+  if (workspace == nullptr || workspace_bytes < L.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  return draft_core(cfg, w, cache, anchor, prefix_len, page_table, max_pages, batch,
+                    max_prefix_len, block_ids, positions, slots, candidates, logits, L,
+                    static_cast<hipStream_t>(stream));
+}
+
+// Workspace of the selector stage, carved after the draft pass's.
+struct SelectorWs {
+  void* logits; float* pv; int* pi; float* unary; float* w; GemmScratch gs; size_t bytes;
+};
+static SelectorWs layout_selector(const dflash_config* c, const dflash_selector* sel, int B,
+                                  bool own_logits, void* base) {
+  Carver cv(base);
+  SelectorWs L;
+  const int M1 = B * (c->block_size - 1), K = sel->top_k, r = sel->rank;
+  const SelPlan pl = plan_selector(M1, c->vocab);
+  L.logits = own_logits ? cv.take((size_t)act_bytes(c->act_dtype) * M1 * c->vocab) : nullptr;
+  L.pv = (float*)cv.take(sizeof(float) * (size_t)M1 * pl.n_chunks * K);
+  L.pi = (int*)cv.take(sizeof(int) * (size_t)M1 * pl.n_chunks * K);
+  L.unary = (float*)cv.take(sizeof(float) * (size_t)M1 * K);
+  L.w = (float*)cv.take(sizeof(float) * (size_t)M1 * r);
+  const GemmPlan gp = plan_gemm(M1, r, c->hidden, c->act_dtype == DFLASH_BF16);
+  L.gs.partial_floats = gemm_partial_floats(gp);
+  L.gs.partial = (float*)cv.take(sizeof(float) * (L.gs.partial_floats > 0 ? L.gs.partial_floats : 1));
+  L.bytes = cv.off;
+  return L;
+}
+
+static dflash_status check_selector(const dflash_config* c, const dflash_selector* sel) {
+  if (sel == nullptr) return fail(DFLASH_EINVAL, "selector is NULL");
+  const int K = sel->top_k;
+  if (K != 1 && K != 2 && K != 4 && K != 8 && K != 16)
+    return fail(DFLASH_EUNSUPPORTED, "top_k %d (supported: 1, 2, 4, 8, 16)", K);
+  if (K > c->vocab) return fail(DFLASH_EINVAL, "top_k %d > vocab %d", K, c->vocab);
+  if (sel->rank < 1 || sel->rank > 256) return fail(DFLASH_EUNSUPPORTED, "rank %d outside 1..256",
+                                                    sel->rank);
+  REQUIRE_PTR(sel->a, "selector.a");
+  REQUIRE_PTR(sel->b, "selector.b");
+  REQUIRE_PTR(sel->w_h, "selector.w_h");
+  return DFLASH_OK;
+}
+
+size_t dflash_selector_workspace_bytes(const dflash_config* cfg, const dflash_selector* sel,
+                                       int32_t batch, int32_t max_prefix_len) {
+  if (check_config(cfg) != DFLASH_OK || sel == nullptr || batch <= 0 || max_prefix_len < 0 ||
+      sel->top_k < 1 || sel->top_k > 16 || sel->rank < 1 || sel->rank > 256)
+    return 0;
+  const size_t d = layout_draft(cfg, batch, max_prefix_len, nullptr).bytes;
+  return ((d + 255) & ~(size_t)255) + layout_selector(cfg, sel, batch, true, nullptr).bytes;
+}
+
+dflash_status dflash_draft_block_selector(
+    const dflash_config* cfg, const dflash_weights* w, const dflash_kv_cache* cache,
+    const dflash_selector* sel, const int32_t* anchor, const int32_t* prefix_len,
+    const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+    int32_t* block_ids, int32_t* positions, int32_t* slots, int32_t* candidates,
+    int32_t* cand_ids, float* q_rows, const float* uniforms, float temperature, void* logits,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  dflash_status s = check_draft_args(cfg, w, cache, anchor, prefix_len, page_table, max_pages,
+                                     batch, max_prefix_len, block_ids, positions, slots,
+                                     candidates, logits, workspace, workspace_bytes, stream);
+  if (s != DFLASH_OK || batch == 0) return s;
+  if ((s = check_selector(cfg, sel)) != DFLASH_OK) return s;
+  if (!cand_ids || !q_rows) return fail(DFLASH_EINVAL, "cand_ids and q_rows must not be NULL");
+  if (uniforms && (!(temperature > 0.f) || !isfinite(temperature)))
+    return fail(DFLASH_EINVAL, "temperature must be finite and > 0 when sampling");
+  const DraftWs L = layout_draft(cfg, batch, max_prefix_len, workspace);
+  const size_t d = (L.bytes + 255) & ~(size_t)255;
+  const SelectorWs SL = layout_selector(cfg, sel, batch, logits == nullptr,
+                                        workspace ? static_cast<char*>(workspace) + d : nullptr);
+  if (workspace == nullptr || workspace_bytes < d + SL.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, d + SL.bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* lg = logits ? logits : SL.logits;
+  if ((s = draft_core(cfg, w, cache, anchor, prefix_len, page_table, max_pages, batch,
+                      max_prefix_len, block_ids, positions, slots, candidates, lg, L, st)) !=
+      DFLASH_OK)
+    return s;
+  const int S = cfg->block_size, M1 = batch * (S - 1), K = sel->top_k;
+  hipError_t e;
+  // candidates and their unary logits from the logits just written
+  if ((e = launch_topk(cfg->act_dtype, lg, M1, cfg->vocab, K, plan_selector(M1, cfg->vocab),
+                       SL.pv, SL.pi, cand_ids, SL.unary, st)) != hipSuccess)
+    return hip_fail(e, "top-k");
+  // w_j = W_h y_j for the final-normed rows 1..S-1 (the norm applied by linearity)
+  if ((e = gemm_store_f32(cfg->act_dtype, asrc_normed(L.xg, cfg->hidden, L.ss, cfg->rms_eps, S),
+                          M1, cfg->hidden, sel->w_h, sel->rank, SL.w, nullptr, nullptr, nullptr,
+                          SL.gs, st)) != hipSuccess)
+    return hip_fail(e, "selector projection");
+  if ((e = launch_lattice_walk(cfg->act_dtype, cand_ids, SL.unary, SL.w, sel->a, sel->b, anchor,
+                               uniforms, uniforms ? temperature : 1.f, batch, S, K, sel->rank,
+                               cfg->vocab, candidates, q_rows, st)) != hipSuccess)
+    return hip_fail(e, "selector walk");
   return DFLASH_OK;
 }
 

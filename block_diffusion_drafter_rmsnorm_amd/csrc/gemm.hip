@@ -742,15 +742,19 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
 }
 
 template <typename T> struct EpiStoreF32 {
-  const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn;
-  __device__ void prepare(int, int, int, int) const {}
+  const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn; RowScale rs;
+  // rows of an RMSNorm-scaled A source are multiplied by 1/rms (1 for a plain source)
+  __device__ void prepare(int rows, int m0, int M, int tid) const {
+    rs.fill(row_scale_lds(), rows, m0, M, tid);
+  }
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
+    const float* srs = row_scale_lds();
     for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn, [&](int, int) { return 0.f; },
              [&](int r, int c, int m, int n, float) {
-               const float v = t[r * LDT + c];
+               const float v = t[r * LDT + c] * srs[r];
                if (out != nullptr) out[(int64_t)m * ldo + n] = v;
                return v;
              });
@@ -1193,11 +1197,11 @@ hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, in
                           hipStream_t st) {
   if (dt == DFLASH_BF16) {
     EpiStoreF32<bf16_t> e{(const bf16_t*)W, N, K, out, N, ss,
-                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next}};
+                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next}, row_scale(a)};
     return run_any<bf16_t>(a, M, K, N, e, ws, st);
   }
   EpiStoreF32<float> e{(const float*)W, N, K, out, N, ss,
-                       NextNorm<float>{(float*)xg, (const float*)g_next}};
+                       NextNorm<float>{(float*)xg, (const float*)g_next}, row_scale(a)};
   return run_any<float>(a, M, K, N, e, ws, st);
 }
 

@@ -127,6 +127,22 @@ hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const vo
                                   int32_t* out_tokens, int32_t* next_anchor,
                                   int32_t* new_seq_len, hipStream_t st);
 
+// ---- DFlash 2 candidate selector (selector.hip)
+struct SelPlan {
+  int chunk, n_chunks;  // vocabulary chunking of the top-K pass (n_chunks <= 64)
+};
+SelPlan plan_selector(int rows, int V);
+// top-K of rows x V logits (act dtype): per-chunk partials pv/pi [rows][n_chunks][K],
+// then cand [rows][K] ids and unary [rows][K] values; K in {1, 2, 4, 8, 16}
+hipError_t launch_topk(int dt, const void* logits, int rows, int V, int K, const SelPlan& pl,
+                       float* pv, int* pi, int32_t* cand, float* unary, hipStream_t st);
+// lattice of every (position, predecessor, candidate) and the walk: candidates
+// [B, S] = anchor + chosen tokens, q_rows [B, S-1, K]; uni nullable (greedy)
+hipError_t launch_lattice_walk(int dt, const int32_t* cand, const float* unary, const float* w,
+                               const void* A, const void* Bt, const int32_t* anchor,
+                               const float* uni, float temperature, int B, int S, int K, int r,
+                               int V, int32_t* candidates, float* q_rows, hipStream_t st);
+
 // ---- attention
 struct AttnPlan {
   int stages;      // LDS stages of the bf16-cache kernel (0: the register-staged kernel)

@@ -5,6 +5,7 @@
  * of a DFlash block-diffusion drafter runs on the GPU:
  *   dflash_project_context  context injection (target features -> draft K/V cache)
  *   dflash_draft_block      one non-causal draft pass over [anchor, MASK x (S-1)]
+ *   dflash_draft_block_selector  the same pass with the DFlash 2 candidate selector
  *   dflash_accept           greedy verify-accept, commit and logical crop
  *   dflash_accept_sampling  rejection-sampling verify-accept and commit
  *
@@ -285,6 +286,51 @@ dflash_status dflash_accept_sampling(const int32_t* candidates, const void* targ
                                      int32_t* commit_len, int32_t* out_tokens,
                                      int32_t* next_anchor, int32_t* new_seq_len, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * (2') One draft pass with the DFlash 2 candidate selector in place of the
+ * argmax ("Inside SGLang ...", section on DFlash 2: candidates, lattice, walk).
+ *
+ * Runs dflash_draft_block's backbone and lm_head, then, per drafted row j
+ * (block rows 1..S-1): the top_k tokens by logit (descending, ties to the
+ * lower id; NaN never wins) -> cand_ids[b, j, :] with their logits U; the
+ * lattice score(p, c) = U(c) + <a[p] * (w_h y_j), b[c]> for every predecessor
+ * p (the anchor for j = 0, else each candidate of row j - 1) and candidate c,
+ * y_j the row after the final RMSNorm; and the walk: from the anchor's row,
+ * the chosen candidate's row at the next position, taking the first maximum
+ * (uniforms NULL) or the smallest candidate whose running sum of
+ * softmax(row / temperature) exceeds uniforms[b, j].  q_rows[b, j, :] =
+ * softmax(row) (softmax(row / temperature) when sampling) of the row walked;
+ * candidates[b] = [anchor, chosen tokens].  The selector weights' values,
+ * top_k and rank are the caller's (the pages give none).
+ *
+ *   sel->a, sel->b  [vocab, rank] act_dtype;  sel->w_h [rank, hidden]
+ *                   fragment-packed (dflash_pack_matrix)
+ *   cand_ids        [batch, S-1, top_k] out;  q_rows [batch, S-1, top_k] f32 out
+ *   uniforms        nullable [batch, S-1] f32 draws in [0, 1)
+ *   logits          nullable [batch, S-1, vocab] out (kept in the workspace
+ *                   when NULL)
+ *   workspace       >= dflash_selector_workspace_bytes(cfg, sel, batch,
+ *                   max_prefix_len)
+ * top_k in {1, 2, 4, 8, 16}, rank 1..256; other arguments as
+ * dflash_draft_block.
+ */
+typedef struct {
+  const void* a;    /* [vocab, rank] predecessor table                         */
+  const void* b;    /* [vocab, rank] successor table                           */
+  const void* w_h;  /* [rank, hidden] projection of the hidden row, packed      */
+  int32_t rank;
+  int32_t top_k;
+} dflash_selector;
+size_t dflash_selector_workspace_bytes(const dflash_config* cfg, const dflash_selector* sel,
+                                       int32_t batch, int32_t max_prefix_len);
+dflash_status dflash_draft_block_selector(
+    const dflash_config* cfg, const dflash_weights* w, const dflash_kv_cache* cache,
+    const dflash_selector* sel, const int32_t* anchor, const int32_t* prefix_len,
+    const int32_t* page_table, int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+    int32_t* block_ids, int32_t* positions, int32_t* slots, int32_t* candidates,
+    int32_t* cand_ids, float* q_rows, const float* uniforms, float temperature, void* logits,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The draft-token selection step alone ("Inside SGLang ...", Step 4: the target

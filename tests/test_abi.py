@@ -160,3 +160,34 @@ def test_accept_sampling_argument_errors():
         dfl.accept_sampling_workspace_bytes(32, 16, 151936, True)
     assert dfl.accept_sampling_workspace_bytes(0, 16, 151936, True) == 0
     assert dfl.accept_sampling_workspace_bytes(4, 1, 100, True) == 0
+
+
+def test_selector_argument_errors():
+    """dflash_draft_block_selector rejects a missing or unsupported selector
+    before any launch (the draft arguments here pass their own checks)."""
+    lib = dfl.raw_lib()
+    cfg = dfl.make_config(TINY)
+    fake = 0x100000
+    w = dfl.CWeights()
+    for n in ("embed", "lm_head", "fc", "hidden_norm", "final_norm"):
+        setattr(w, n, fake)
+    for n in dfl._LAYER_FIELDS:
+        setattr(w.layer[0], n, fake)
+    kv = dfl.CKVCache()
+    kv.k[0] = kv.v[0] = fake
+    kv.num_pages = 8
+    F = ctypes.c_void_p(fake)
+
+    def call(sel, cand_ids=F):
+        return lib.dflash_draft_block_selector(
+            ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv),
+            ctypes.byref(sel) if sel is not None else None, F, F, F, 4, 1, 64, None, F, F, F,
+            cand_ids, F, None, 1.0, None, F, 1 << 30, None)
+
+    assert call(None) == -1
+    assert call(dfl.CSelector(fake, fake, fake, 64, 3)) == -2
+    assert call(dfl.CSelector(fake, fake, fake, 0, 8)) == -2
+    assert call(dfl.CSelector(None, fake, fake, 64, 8)) == -1
+    assert call(dfl.CSelector(fake, fake, fake, 64, 8), cand_ids=None) == -1
+    assert dfl.selector_workspace_bytes(TINY, type("S", (), {"c": dfl.CSelector(
+        fake, fake, fake, 64, 8)})(), 1, 64) > dfl.draft_workspace_bytes(TINY, 1, 64)

@@ -1,0 +1,126 @@
+"""GPU parity of the DFlash 2 candidate selector (dflash_draft_block_selector)
+against the fp64 oracle, through the C ABI.
+
+The oracle's selector reads the logits the GPU wrote (identical unary logits,
+so the candidate ids must match bit for bit) and its own fp64 final-normed
+rows for the compatibility term.  The GPU forms W_h y from the bf16 pass, so a
+lattice score differs from the oracle's by the bf16 error of the pass (the
+same ~1e-2 of scale as the logits); the walk is compared along the GPU's own
+path: wherever the oracle's row for the same predecessor has a top-2 gap above
+GAP, the GPU's choice must be the oracle's; q_rows must match the softmax of
+that row within QTOL.  With the compatibility switched off the selector must
+reproduce the plain draft pass exactly (same logits, same tie rule).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.selector import select
+from workloads import synth
+from workloads.configs import get_workload
+from tests.gpu_harness import Setup
+
+pytestmark = pytest.mark.gpu
+
+GAP = 0.05
+QTOL = 2e-2
+
+
+def dfl():
+    import block_diffusion_drafter_rmsnorm_amd as m
+    return m
+
+
+def _selector(cfg, r, K, seed, zero_a=False):
+    dt = synth._DT[cfg.act_dtype]
+    A = synth.normal((cfg.vocab, r), 0.3, seed, "sel_a", dt, "cuda")
+    if zero_a:
+        A.zero_()
+    Bt = synth.normal((cfg.vocab, r), 0.3, seed, "sel_b", dt, "cuda")
+    Wh = synth.normal((r, cfg.hidden), 0.02, seed, "sel_wh", dt, "cuda")
+    return A, Bt, Wh, dfl().Selector(A, Bt, Wh, K)
+
+
+def _run(st, sel, K, uniforms=None, T=1.0):
+    m = dfl()
+    cfg, B, S = st.cfg, st.B, st.S
+    mp = int(st.L.max())
+    ws = m.workspace(m.selector_workspace_bytes(cfg, sel, B, mp))
+    out = dict(positions=torch.empty((B, S), dtype=torch.int32, device="cuda"),
+               slots=torch.empty((B, S), dtype=torch.int32, device="cuda"),
+               candidates=torch.empty((B, S), dtype=torch.int32, device="cuda"),
+               cand_ids=torch.full((B, S - 1, K), -1, dtype=torch.int32, device="cuda"),
+               q_rows=torch.empty((B, S - 1, K), dtype=torch.float32, device="cuda"),
+               logits=torch.empty((B, S - 1, cfg.vocab), dtype=synth._DT[cfg.act_dtype],
+                                  device="cuda"))
+    m.dflash_draft_block_selector(cfg, st.c_weights(), st.cache, sel, st.anchor.cuda(),
+                                  st.L.cuda(), st.pt.cuda(), mp, out["positions"], out["slots"],
+                                  out["candidates"], out["cand_ids"], out["q_rows"], ws,
+                                  uniforms=uniforms, temperature=T, logits=out["logits"])
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "tiny_f32", "small_bf16_wide"])
+@pytest.mark.parametrize("K", [8, 4])
+def test_selector_parity(name, K):
+    wl = get_workload(name)
+    st = Setup(wl)
+    cfg, B, S = st.cfg, st.B, st.S
+    r = 64
+    A, Bt, Wh, sel = _selector(cfg, r, K, 7)
+    g = _run(st, sel, K)
+    d = oracle.draft_block(cfg, st.np_W(), st.oracle_cache(), st.anchor.numpy(), st.L.numpy(),
+                           st.pt.numpy())
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    o = select(f(g["logits"]), d["hidden"], st.anchor.numpy(), f(A), f(Bt), f(Wh), k=K)
+    cand = g["cand_ids"].numpy()
+    assert np.array_equal(cand, o["cand_ids"])            # identical logits -> identical ids
+    gc = g["candidates"].numpy()
+    assert np.array_equal(gc[:, 0], st.anchor.numpy())
+    n_clear = n_all = 0
+    for b in range(B):
+        p = 0
+        for j in range(S - 1):
+            row = o["score"][b, j, p]
+            k = int(np.nonzero(cand[b, j] == gc[b, 1 + j])[0][0])   # the GPU's choice
+            srt = np.sort(row)[::-1]
+            n_all += 1
+            if srt[0] - srt[1] > GAP:
+                n_clear += 1
+                assert k == int(np.argmax(row)), (b, j, k, row)
+            q = np.exp(row - row.max())
+            q /= q.sum()
+            assert np.allclose(g["q_rows"].numpy()[b, j], q, atol=QTOL), (b, j)
+            p = k
+    assert n_clear >= 0.7 * n_all, (n_clear, n_all)
+
+
+def test_selector_without_compatibility_is_the_plain_draft():
+    st = Setup(get_workload("small_bf16"))
+    K = 8
+    _, _, _, sel = _selector(st.cfg, 64, K, 3, zero_a=True)
+    g = _run(st, sel, K)
+    plain = st.draft()
+    assert np.array_equal(g["candidates"].numpy(), plain["candidates"].cpu().numpy())
+    assert torch.equal(g["logits"], plain["logits"].cpu())
+    assert np.array_equal(g["cand_ids"].numpy()[:, :, 0], plain["candidates"].cpu().numpy()[:, 1:])
+
+
+def test_selector_sampled_walk_draws_from_its_q_rows():
+    st = Setup(get_workload("small_bf16_wide"))
+    K, T = 8, 0.8
+    _, _, _, sel = _selector(st.cfg, 64, K, 5)
+    B, S = st.B, st.S
+    u = torch.rand(B, S - 1, generator=torch.Generator("cuda").manual_seed(4), device="cuda")
+    g = _run(st, sel, K, uniforms=u, T=T)
+    u = u.cpu().numpy().astype(np.float64)
+    cand, gc, q = g["cand_ids"].numpy(), g["candidates"].numpy(), g["q_rows"].numpy()
+    assert np.allclose(q.sum(-1), 1.0, atol=1e-5)
+    for b in range(B):
+        for j in range(S - 1):
+            k = int(np.nonzero(cand[b, j] == gc[b, 1 + j])[0][0])
+            c = np.cumsum(q[b, j].astype(np.float64))
+            lo = c[k - 1] if k > 0 else 0.0
+            assert lo - 1e-5 <= u[b, j] and (u[b, j] < c[k] + 1e-5 or k == K - 1), (b, j, k)
