@@ -210,6 +210,9 @@ def main():
     # [B, S, V], the draft pass's own logits [B, S-1, V] as the proposal q
     sv = sampling_verify(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, c_cfg,
                          c_cache, timed, max(args.steps, 10), dev)
+    # the same pass with the DFlash 2 candidate selector (top-8, rank 64)
+    sel = selector_pass(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, timed,
+                        args.steps, dev, ms_draft)
 
     if args.copy_probe:
         # a plain copy of known size: under a counter-collection run its
@@ -258,6 +261,7 @@ def main():
                      "bytes_per_launch": lm_bytes,
                      "avg_launch_us": round(lm_avg_s * 1e6, 2)},
         "sampling_verify": sv,
+        "selector_pass": sel,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -301,6 +305,33 @@ def sampling_verify(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix,
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "mean_commit": round(float(outs[1].float().mean()), 3)}
     return res
+
+
+def selector_pass(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, timed, n, dev,
+                  ms_plain):
+    """dflash_draft_block_selector at the workload's batch: the pass plus top-k,
+    the W_h projection, the lattice and the walk (synthetic selector weights)."""
+    import torch
+    B, S, K, r = wl.batch, cfg.block_size, 8, 64
+    dt = synth._DT[cfg.act_dtype]
+    A = synth.normal((cfg.vocab, r), 0.3, wl.seed, "sel_a", dt, dev)
+    Bt = synth.normal((cfg.vocab, r), 0.3, wl.seed, "sel_b", dt, dev)
+    Wh = synth.normal((r, cfg.hidden), 0.02, wl.seed, "sel_wh", dt, dev)
+    sel = dfl.Selector(A, Bt, Wh, K)
+    ws = dfl.workspace(dfl.selector_workspace_bytes(cfg, sel, B, max_prefix))
+    pos = torch.empty((B, S), dtype=torch.int32, device=dev)
+    slots, cand = torch.empty_like(pos), torch.empty_like(pos)
+    cids = torch.empty((B, S - 1, K), dtype=torch.int32, device=dev)
+    q = torch.empty((B, S - 1, K), dtype=torch.float32, device=dev)
+
+    def call():
+        dfl.dflash_draft_block_selector(cfg, cw, cache, sel, anchor, Ld, ptd, max_prefix, pos,
+                                        slots, cand, cids, q, ws)
+    call()
+    ms = timed(call, n)
+    return {"ms": round(ms, 4), "blocks_per_s": round(B / (ms * 1e-3), 2),
+            "overhead_us_vs_argmax_pass": round((ms - ms_plain) * 1e3, 1), "top_k": K,
+            "rank": r}
 
 
 def cpu_baseline(cfg, wl, L, W_dev):

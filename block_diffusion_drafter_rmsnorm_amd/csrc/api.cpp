@@ -463,8 +463,9 @@ static dflash_status check_selector(const dflash_config* c, const dflash_selecto
   if (K != 1 && K != 2 && K != 4 && K != 8 && K != 16)
     return fail(DFLASH_EUNSUPPORTED, "top_k %d (supported: 1, 2, 4, 8, 16)", K);
   if (K > c->vocab) return fail(DFLASH_EINVAL, "top_k %d > vocab %d", K, c->vocab);
-  if (sel->rank < 1 || sel->rank > 256) return fail(DFLASH_EUNSUPPORTED, "rank %d outside 1..256",
-                                                    sel->rank);
+  if (sel->rank != 16 && sel->rank != 32 && sel->rank != 64 && sel->rank != 128)
+    return fail(DFLASH_EUNSUPPORTED, "rank %d (supported: 16, 32, 64, 128)", sel->rank);
+  if (c->vocab > 524288) return fail(DFLASH_EUNSUPPORTED, "vocab %d > 524288", c->vocab);
   REQUIRE_PTR(sel->a, "selector.a");
   REQUIRE_PTR(sel->b, "selector.b");
   REQUIRE_PTR(sel->w_h, "selector.w_h");
@@ -474,7 +475,7 @@ static dflash_status check_selector(const dflash_config* c, const dflash_selecto
 size_t dflash_selector_workspace_bytes(const dflash_config* cfg, const dflash_selector* sel,
                                        int32_t batch, int32_t max_prefix_len) {
   if (check_config(cfg) != DFLASH_OK || sel == nullptr || batch <= 0 || max_prefix_len < 0 ||
-      sel->top_k < 1 || sel->top_k > 16 || sel->rank < 1 || sel->rank > 256)
+      sel->top_k < 1 || sel->top_k > 16 || sel->rank < 1 || sel->rank > 128)
     return 0;
   const size_t d = layout_draft(cfg, batch, max_prefix_len, nullptr).bytes;
   return ((d + 255) & ~(size_t)255) + layout_selector(cfg, sel, batch, true, nullptr).bytes;

@@ -13,8 +13,8 @@
 //               predecessor: greedy first maximum or an inverse-CDF draw from
 //               softmax(row / T); q_rows = that softmax.
 //
-// Kernels: topk_chunk_kernel (grid rows x chunks: a sorted register list per
-// thread, then K rounds of block argmax over the lists' heads in LDS),
+// Kernels: topk_chunk_kernel (grid rows x chunks of <= 8192 logits staged in
+// LDS, K rounds of block argmax each strictly after the previous winner),
 // topk_merge_kernel (one wave per row over the <= 64 chunk lists), and
 // lattice_walk_kernel (one workgroup per request: every (position,
 // predecessor, candidate) score in parallel, then the walk).
@@ -29,6 +29,7 @@ namespace {
 constexpr int kT = 256;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNoIdx = 0x7fffffff;
+constexpr int kMaxChunk = 8192;  // logits of one top-K chunk (32 KB of LDS)
 
 // (value, index) order of the candidates: larger value first, then lower index
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
@@ -39,6 +40,23 @@ template <typename T> __device__ __forceinline__ float ldf(const T* p);
 template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ldf<bf16_t>(const bf16_t* p) {
   return bf16_to_f32(p->bits);
+}
+
+// Eight consecutive values as fp32 (16-byte loads for bf16, two for fp32).
+__device__ __forceinline__ void ld8(const bf16_t* p, float* v) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = __uint_as_float(u[k] << 16);
+    v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void ld8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 // Block-wide best (value, index) of one entry per thread; every thread gets it.
@@ -68,61 +86,56 @@ __device__ __forceinline__ void block_best(float& v, int& i, float* rv, int* ri)
 }
 
 // ---------------------------------------------------------------- top-K
-template <typename T, int K>
+// One workgroup per (row, chunk of at most kMaxChunk logits): the chunk is
+// staged in LDS as fp32 (16-byte loads when VEC8: rows on 16-byte boundaries,
+// V a multiple of 8), then K rounds each take the block's best element that
+// comes strictly after the previous round's winner in the (value, index)
+// order.  Every thread does the same work in every round (no divergent
+// insertion); NaN is never taken.
+template <typename T, int K, bool VEC8>
 __global__ __launch_bounds__(kT) void topk_chunk_kernel(const T* __restrict__ logits, int V,
                                                         int chunk, int n_chunks,
                                                         float* __restrict__ pv,
                                                         int* __restrict__ pi) {
   const int row = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const T* x = logits + (int64_t)row * V;
-  const int c0 = c * chunk, c1 = min(V, c0 + chunk);
-  float bv[K];
-  int bi[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    bv[k] = kNegInf;
-    bi[k] = kNoIdx;
-  }
-  for (int i = c0 + tid; i < c1; i += kT) {
-    float cv = ldf(x + i);
-    int ci = i;
-    if (!better(cv, ci, bv[K - 1], bi[K - 1])) continue;
-    // sorted insertion by compare-and-swap down the list (static indices)
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-      if (better(cv, ci, bv[k], bi[k])) {
-        const float tv = bv[k];
-        const int ti = bi[k];
-        bv[k] = cv;
-        bi[k] = ci;
-        cv = tv;
-        ci = ti;
-      }
-  }
-  __shared__ float lv[kT * K];
-  __shared__ int li[kT * K];
+  const int c0 = c * chunk, n = min(V, c0 + chunk) - c0;
+  __shared__ float xs[kMaxChunk];
   __shared__ float rv[kT / 64];
   __shared__ int ri[kT / 64];
+  if (VEC8) {
+    for (int e = tid * 8; e < n; e += kT * 8) {
+      float v[8];
+      ld8(x + c0 + e, v);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    lv[tid * K + k] = bv[k];
-    li[tid * K + k] = bi[k];
+      for (int u = 0; u < 8; ++u) xs[e + u] = v[u];
+    }
+  } else {
+    for (int e = tid; e < n; e += kT) xs[e] = ldf(x + c0 + e);
   }
   __syncthreads();
-  int ptr = 0;
+  float prev_v = __builtin_huge_valf();
+  int prev_i = -1;
   float* ov = pv + ((int64_t)row * n_chunks + c) * K;
   int* oi = pi + ((int64_t)row * n_chunks + c) * K;
   for (int k = 0; k < K; ++k) {
-    const float hv = ptr < K ? lv[tid * K + ptr] : kNegInf;
-    const int hi = ptr < K ? li[tid * K + ptr] : kNoIdx;
-    float v = hv;
-    int i = hi;
-    block_best(v, i, rv, ri);
-    if (hi == i && i != kNoIdx) ++ptr;  // indices are unique: one thread advances
-    if (tid == 0) {
-      ov[k] = v;
-      oi[k] = i;
+    float bv = kNegInf;
+    int bi = kNoIdx;
+    for (int e = tid; e < n; e += kT) {
+      const float v = xs[e];
+      const int i = c0 + e;
+      if (better(prev_v, prev_i, v, i) && better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
     }
+    block_best(bv, bi, rv, ri);
+    if (tid == 0) {
+      ov[k] = bv;
+      oi[k] = bi;
+    }
+    prev_v = bv;
+    prev_i = bi;
   }
 }
 
@@ -167,15 +180,20 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict_
 
 // ---------------------------------------------------------------- lattice + walk
 // grid (B); 256 threads.  J = S - 1 drafted positions, r = rank (multiple of 8).
-template <typename T>
+template <typename T, int R>
 __global__ __launch_bounds__(kT) void lattice_walk_kernel(
     const int32_t* __restrict__ cand, const float* __restrict__ unary,
     const float* __restrict__ w, const T* __restrict__ A, const T* __restrict__ Bt,
     const int32_t* __restrict__ anchor, const float* __restrict__ uni, float temperature,
-    int S, int K, int r, int V, int32_t* __restrict__ candidates, float* __restrict__ q_rows) {
+    int S, int K, int V, int32_t* __restrict__ candidates, float* __restrict__ q_rows) {
+  constexpr int r = R;
   const int b = blockIdx.x, tid = threadIdx.x, J = S - 1;
-  extern __shared__ float score[];  // [J][K][K]
+  extern __shared__ float score[];  // [J][K][K], then this request's w rows [J][r]
   const int n = J * K * K;
+  float* ws = score + n;
+  for (int e = tid; e < J * r; e += kT) ws[e] = w[(int64_t)b * J * r + e];
+  __syncthreads();
+
   const int32_t* cb = cand + (int64_t)b * J * K;
   const float* ub = unary + (int64_t)b * J * K;
   const int a0 = min(max(anchor[b], 0), V - 1);
@@ -189,9 +207,17 @@ __global__ __launch_bounds__(kT) void lattice_walk_kernel(
     const int c = min(max(cb[j * K + k], 0), V - 1);
     const T* ar = A + (int64_t)pred * r;
     const T* br = Bt + (int64_t)c * r;
-    const float* wr = w + ((int64_t)b * J + j) * r;
+    const float* wr = ws + j * r;
+    // both rows' loads go out together (R / 8 of each), then the sum in order
+    float av[R], bv[R];
+#pragma unroll
+    for (int e = 0; e < R; e += 8) {
+      ld8(ar + e, av + e);
+      ld8(br + e, bv + e);
+    }
     float s = 0.f;
-    for (int e = 0; e < r; ++e) s += ldf(ar + e) * wr[e] * ldf(br + e);
+#pragma unroll
+    for (int e = 0; e < R; ++e) s += av[e] * wr[e] * bv[e];
     score[t] = ub[j * K + k] + s;
   }
   __syncthreads();
@@ -236,15 +262,26 @@ __global__ __launch_bounds__(kT) void lattice_walk_kernel(
   }
 }
 
+template <typename T, int K>
+void topk_chunks(const void* logits, int rows, int V, const SelPlan& pl, float* pv, int* pi,
+                 hipStream_t st) {
+  const bool vec8 = V % 8 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+  const T* x = static_cast<const T*>(logits);
+  if (vec8)
+    hipLaunchKernelGGL((topk_chunk_kernel<T, K, true>), dim3(rows, pl.n_chunks), dim3(kT), 0, st,
+                       x, V, pl.chunk, pl.n_chunks, pv, pi);
+  else
+    hipLaunchKernelGGL((topk_chunk_kernel<T, K, false>), dim3(rows, pl.n_chunks), dim3(kT), 0,
+                       st, x, V, pl.chunk, pl.n_chunks, pv, pi);
+}
+
 template <int K>
 hipError_t topk_launch(int dt, const void* logits, int rows, int V, const SelPlan& pl, float* pv,
                        int* pi, int32_t* cand, float* unary, hipStream_t st) {
   if (dt == DFLASH_BF16)
-    hipLaunchKernelGGL((topk_chunk_kernel<bf16_t, K>), dim3(rows, pl.n_chunks), dim3(kT), 0, st,
-                       static_cast<const bf16_t*>(logits), V, pl.chunk, pl.n_chunks, pv, pi);
+    topk_chunks<bf16_t, K>(logits, rows, V, pl, pv, pi, st);
   else
-    hipLaunchKernelGGL((topk_chunk_kernel<float, K>), dim3(rows, pl.n_chunks), dim3(kT), 0, st,
-                       static_cast<const float*>(logits), V, pl.chunk, pl.n_chunks, pv, pi);
+    topk_chunks<float, K>(logits, rows, V, pl, pv, pi, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((topk_merge_kernel<K>), dim3(rows), dim3(64), 0, st, pv, pi, pl.n_chunks, V,
@@ -256,9 +293,10 @@ hipError_t topk_launch(int dt, const void* logits, int rows, int V, const SelPla
 
 SelPlan plan_selector(int rows, int V) {
   SelPlan pl{};
-  int want = (1024 + rows - 1) / rows;
+  int want = (2048 + rows - 1) / rows;
   want = want < 1 ? 1 : (want > 64 ? 64 : want);
   pl.chunk = ((V + want - 1) / want + 63) / 64 * 64;
+  if (pl.chunk > kMaxChunk) pl.chunk = kMaxChunk;  // V <= 64 * kMaxChunk keeps n_chunks <= 64
   pl.n_chunks = (V + pl.chunk - 1) / pl.chunk;
   return pl;
 }
@@ -276,21 +314,46 @@ hipError_t launch_topk(int dt, const void* logits, int rows, int V, int K, const
   }
 }
 
+template <typename T, int R>
+static void lattice_launch(const int32_t* cand, const float* unary, const float* w, const void* A,
+                           const void* Bt, const int32_t* anchor, const float* uni,
+                           float temperature, int B, int S, int K, int V, int32_t* candidates,
+                           float* q_rows, hipStream_t st) {
+  const size_t lds = sizeof(float) * ((size_t)(S - 1) * K * K + (size_t)(S - 1) * R);
+  hipLaunchKernelGGL((lattice_walk_kernel<T, R>), dim3(B), dim3(kT), lds, st, cand, unary, w,
+                     static_cast<const T*>(A), static_cast<const T*>(Bt), anchor, uni,
+                     temperature, S, K, V, candidates, q_rows);
+}
+
+template <typename T>
+static hipError_t lattice_rank(int r, const int32_t* cand, const float* unary, const float* w,
+                               const void* A, const void* Bt, const int32_t* anchor,
+                               const float* uni, float temperature, int B, int S, int K, int V,
+                               int32_t* candidates, float* q_rows, hipStream_t st) {
+  switch (r) {
+    case 16: lattice_launch<T, 16>(cand, unary, w, A, Bt, anchor, uni, temperature, B, S, K, V,
+                                   candidates, q_rows, st); break;
+    case 32: lattice_launch<T, 32>(cand, unary, w, A, Bt, anchor, uni, temperature, B, S, K, V,
+                                   candidates, q_rows, st); break;
+    case 64: lattice_launch<T, 64>(cand, unary, w, A, Bt, anchor, uni, temperature, B, S, K, V,
+                                   candidates, q_rows, st); break;
+    case 128: lattice_launch<T, 128>(cand, unary, w, A, Bt, anchor, uni, temperature, B, S, K, V,
+                                     candidates, q_rows, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_lattice_walk(int dt, const int32_t* cand, const float* unary, const float* w,
                                const void* A, const void* Bt, const int32_t* anchor,
                                const float* uni, float temperature, int B, int S, int K, int r,
                                int V, int32_t* candidates, float* q_rows, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  const size_t lds = sizeof(float) * (size_t)(S - 1) * K * K;
   if (dt == DFLASH_BF16)
-    hipLaunchKernelGGL((lattice_walk_kernel<bf16_t>), dim3(B), dim3(kT), lds, st, cand, unary, w,
-                       static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(Bt), anchor, uni,
-                       temperature, S, K, r, V, candidates, q_rows);
-  else
-    hipLaunchKernelGGL((lattice_walk_kernel<float>), dim3(B), dim3(kT), lds, st, cand, unary, w,
-                       static_cast<const float*>(A), static_cast<const float*>(Bt), anchor, uni,
-                       temperature, S, K, r, V, candidates, q_rows);
-  return hipGetLastError();
+    return lattice_rank<bf16_t>(r, cand, unary, w, A, Bt, anchor, uni, temperature, B, S, K, V,
+                                candidates, q_rows, st);
+  return lattice_rank<float>(r, cand, unary, w, A, Bt, anchor, uni, temperature, B, S, K, V,
+                             candidates, q_rows, st);
 }
 
 }  // namespace dflash

@@ -312,7 +312,8 @@ dflash_status dflash_accept_sampling(const int32_t* candidates, const void* targ
  *                   when NULL)
  *   workspace       >= dflash_selector_workspace_bytes(cfg, sel, batch,
  *                   max_prefix_len)
- * top_k in {1, 2, 4, 8, 16}, rank 1..256; other arguments as
+ * top_k in {1, 2, 4, 8, 16}, rank in {16, 32, 64, 128}, vocab <= 524288; other
+ * arguments as
  * dflash_draft_block.
  */
 typedef struct {
