@@ -19,7 +19,9 @@ Readings where the section is silent (each also applied by the GPU path):
   after reading candidates[j], i.e. the one that verifies d_{j+1} (the same
   one-position shift as the greedy verify of Step 6).
 * q_j = softmax(draft_logits[j] / T_d) when draft logits are given (row j
-  proposed d_{j+1}); otherwise the point mass on d_{j+1}.
+  proposed d_{j+1}); q_j = draft_probs[j] when a proposal distribution is
+  given directly (the DFlash 2 selector's realised q rows, scattered over the
+  vocabulary as the section describes); otherwise the point mass on d_{j+1}.
 * The random draws are inputs: uniforms[r, j] in [0, 1) for j < S - 1 is the
   acceptance draw of d_{j+1} ("accept iff u * q(y) < p(y)", the event
   u < min(1, p/q) written without a division); uniforms[r, S - 1] is the one
@@ -57,12 +59,13 @@ def _inverse_cdf(w, u):
 
 
 def accept_sampling(candidates, target_logits, prefix_len, uniforms, target_temperature,
-                    draft_logits=None, draft_temperature=1.0):
+                    draft_logits=None, draft_temperature=1.0, draft_probs=None):
     """Rejection-sampling verify and commit for a batch of blocks.
 
     candidates    [B, S]     [anchor, d_1 .. d_{S-1}]
     target_logits [B, S, V]  row j: the target's logits after reading candidates[j]
     draft_logits  [B, S-1, V] or None (argmax proposals: q is a point mass)
+    draft_probs   [B, S-1, V] or None: q itself (takes precedence over draft_logits)
     uniforms      [B, S]     draws in [0, 1): acceptance draws, then the token draw
     Returns the greedy accept's outputs (accept_len, commit_len, out_tokens,
     next_anchor, new_seq_len) plus, per request, what a checker needs to judge
@@ -78,6 +81,7 @@ def accept_sampling(candidates, target_logits, prefix_len, uniforms, target_temp
     B, S = cand.shape
     Tt = float(target_temperature)
     dl = None if draft_logits is None else np.asarray(draft_logits, np.float64)
+    dq = None if draft_probs is None else np.asarray(draft_probs, np.float64)
     Td = float(draft_temperature)
 
     acc = np.zeros(B, np.int64)
@@ -91,7 +95,9 @@ def accept_sampling(candidates, target_logits, prefix_len, uniforms, target_temp
         while a < S - 1:
             y = cand[r, a + 1]
             p = _softmax(tl[r, a] / Tt)
-            if dl is None:
+            if dq is not None:
+                q = dq[r, a]
+            elif dl is None:
                 q = np.zeros_like(p)
                 q[y] = 1.0
             else:

@@ -180,3 +180,35 @@ def test_output_invariants():
         assert r["out_tokens"][i, a[i]] == r["next_anchor"][i]
         assert np.all(r["out_tokens"][i, c[i]:] == 0)
     assert len(set(a.tolist())) > 3              # a spread of accept lengths
+
+
+def test_sparse_proposal_is_lossless_and_matches_dense_forms():
+    """q given directly as a distribution over a few candidates (the DFlash 2
+    selector's q rows scattered over the vocabulary): the first emitted token
+    still follows p; a point-mass q given this way equals the argmax-draft
+    mode; q == p given this way accepts every draft."""
+    rng = np.random.default_rng(8)
+    n, V = 30000, 5
+    p = _softmax(P_LOGITS)
+    qs = np.array([0.0, 0.6, 0.0, 0.4, 0.0])          # support on two candidates
+    cand = np.zeros((n, 2), np.int64)
+    cand[:, 1] = rng.choice(V, size=n, p=qs)
+    tl = np.broadcast_to(P_LOGITS, (n, 2, V))
+    dq = np.broadcast_to(qs, (n, 1, V))
+    u = rng.random((n, 2))
+    r = oracle.accept_sampling(cand, tl, np.zeros(n), u, 1.0, draft_probs=dq)
+    assert _chi2(np.bincount(r["out_tokens"][:, 0], minlength=V), p) < CHI2_4DF_1EM4
+    B, S = 40, 5
+    tl2 = rng.normal(0, 1.5, (B, S, V))
+    c2 = rng.integers(0, V, (B, S))
+    u2 = rng.random((B, S))
+    pm = np.zeros((B, S - 1, V))
+    pm[np.arange(B)[:, None], np.arange(S - 1)[None, :], c2[:, 1:]] = 1.0
+    a = oracle.accept_sampling(c2, tl2, np.zeros(B), u2, 1.0, draft_probs=pm)
+    b = oracle.accept_sampling(c2, tl2, np.zeros(B), u2, 1.0)
+    for k in ("accept_len", "out_tokens"):
+        assert np.array_equal(a[k], b[k])
+    pe = np.exp(tl2[:, :S - 1] - tl2[:, :S - 1].max(-1, keepdims=True))
+    pe /= pe.sum(-1, keepdims=True)
+    full = oracle.accept_sampling(c2, tl2, np.zeros(B), u2, 1.0, draft_probs=pe)
+    assert np.all(full["accept_len"] == S - 1)
