@@ -74,6 +74,7 @@ EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
             "dflash_accept_sampling_workspace_bytes", "dflash_accept_sampling",
             "dflash_selector_workspace_bytes", "dflash_draft_block_selector",
+            "dflash_accept_sampling_sparse",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_status_string", "dflash_last_error"]
@@ -106,6 +107,9 @@ def _load():
     lib.dflash_accept_sampling.argtypes = [P, P, P, I32, I32, F, F, P, P, I32, I32, P, P, P, P, P,
                                            P, SZ, P]
     lib.dflash_accept_sampling.restype = I32
+    lib.dflash_accept_sampling_sparse.argtypes = [P, P, I32, I32, F, P, P, I32, P, P, I32, I32, P,
+                                                  P, P, P, P, P, SZ, P]
+    lib.dflash_accept_sampling_sparse.restype = I32
     selp = ctypes.POINTER(CSelector)
     lib.dflash_selector_workspace_bytes.argtypes = [cfgp, selp, I32, I32]
     lib.dflash_selector_workspace_bytes.restype = SZ
@@ -360,6 +364,27 @@ def dflash_draft_block_selector(cfg, weights: CWeights, cache: "KVCache", sel: "
         int(anchor.shape[0]), int(max_prefix_len), _ptr(block_ids), _ptr(positions), _ptr(slots),
         _ptr(candidates), _ptr(cand_ids), _ptr(q_rows), _ptr(uniforms), float(temperature),
         _ptr(logits), _ptr(ws), int(ws.numel()), _stream(stream)))
+
+
+def dflash_accept_sampling_sparse(candidates: torch.Tensor, target_logits: torch.Tensor,
+                                  q_ids: torch.Tensor, q_probs: torch.Tensor,
+                                  uniforms: torch.Tensor, prefix_len: torch.Tensor,
+                                  accept_len: torch.Tensor, commit_len: torch.Tensor,
+                                  out_tokens: torch.Tensor, next_anchor: torch.Tensor,
+                                  new_seq_len: torch.Tensor, ws: torch.Tensor,
+                                  target_temperature: float = 1.0, stream=None):
+    """q_ids / q_probs [B, S-1, K]: the selector's cand_ids and q_rows; ws from
+    workspace(accept_sampling_workspace_bytes(B, S, V, False))."""
+    B, S = candidates.shape
+    dt = _LOGITS_DT.get(target_logits.dtype)
+    if dt is None:
+        raise DFlashError(-2, f"logits dtype {target_logits.dtype} (supported: f32, bf16)")
+    _check(_lib.dflash_accept_sampling_sparse(
+        _ptr(candidates), _ptr(target_logits), dt, int(target_logits.shape[-1]),
+        float(target_temperature), _ptr(q_ids), _ptr(q_probs), int(q_ids.shape[-1]),
+        _ptr(uniforms), _ptr(prefix_len), int(B), int(S), _ptr(accept_len), _ptr(commit_len),
+        _ptr(out_tokens), _ptr(next_anchor), _ptr(new_seq_len), _ptr(ws), int(ws.numel()),
+        _stream(stream)))
 
 
 def lm_head_workspace_bytes(cfg, rows: int) -> int:

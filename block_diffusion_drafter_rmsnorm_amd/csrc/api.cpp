@@ -435,6 +435,45 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
                     static_cast<hipStream_t>(stream));
 }
 
+dflash_status dflash_accept_sampling_sparse(
+    const int32_t* candidates, const void* target_logits, int32_t logits_dtype, int32_t vocab,
+    float target_temperature, const int32_t* q_ids, const float* q_probs, int32_t q_k,
+    const float* uniforms, const int32_t* prefix_len, int32_t batch, int32_t block_size,
+    int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens, int32_t* next_anchor,
+    int32_t* new_seq_len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(DFLASH_EINVAL, "batch %d < 0", batch);
+  if (block_size < 2 || block_size > 64)
+    return fail(DFLASH_EUNSUPPORTED, "block_size %d outside 2..64", block_size);
+  if (vocab <= 0) return fail(DFLASH_EINVAL, "vocab %d <= 0", vocab);
+  if (vocab > 524288) return fail(DFLASH_EUNSUPPORTED, "vocab %d > 524288", vocab);
+  if (q_k < 1 || q_k > 16) return fail(DFLASH_EUNSUPPORTED, "q_k %d outside 1..16", q_k);
+  if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16)
+    return fail(DFLASH_EUNSUPPORTED, "logits_dtype %d (supported: F32, BF16)", logits_dtype);
+  if (!(target_temperature > 0.f) || !isfinite(target_temperature))
+    return fail(DFLASH_EINVAL, "target_temperature must be finite and > 0");
+  if ((int64_t)batch * (2 * block_size - 1) > (int64_t)1 << 30)
+    return fail(DFLASH_EUNSUPPORTED, "batch %d too large", batch);
+  if (batch == 0) return DFLASH_OK;
+  if (!candidates || !target_logits || !q_ids || !q_probs || !uniforms || !prefix_len ||
+      !accept_len || !commit_len || !out_tokens || !next_anchor || !new_seq_len)
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  const SpecPlan pl = plan_spec(batch, block_size, vocab, false);
+  if (workspace == nullptr || workspace_bytes < pl.bytes)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.bytes);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
+  const int esz = logits_dtype == DFLASH_BF16 ? 2 : 4;
+  int vec = 16 / esz;
+  if (vocab % vec || !aligned16(target_logits)) vec = 1;
+  const float ct = (float)(1.4426950408889634 / (double)target_temperature);
+  hipError_t e = launch_accept_sampling(logits_dtype, vec, candidates, target_logits, nullptr,
+                                        q_ids, q_probs, q_k, uniforms, prefix_len, batch,
+                                        block_size, vocab, ct, 0.f, pl, workspace, accept_len,
+                                        commit_len, out_tokens, next_anchor, new_seq_len,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "accept_sampling_sparse");
+  return DFLASH_OK;
+}
+
 // Workspace of the selector stage, carved after the draft pass's.
 struct SelectorWs {
   void* logits; float* pv; int* pi; float* unary; float* w; GemmScratch gs; size_t bytes;
@@ -618,7 +657,8 @@ dflash_status dflash_accept_sampling(const int32_t* candidates, const void* targ
   const float ct = (float)(log2e / (double)target_temperature);
   const float cd = draft_logits ? (float)(log2e / (double)draft_temperature) : 0.f;
   hipError_t e = launch_accept_sampling(logits_dtype, vec, candidates, target_logits, draft_logits,
-                                        uniforms, prefix_len, batch, block_size, vocab, ct, cd, pl,
+                                        nullptr, nullptr, 0, uniforms, prefix_len, batch,
+                                        block_size, vocab, ct, cd, pl,
                                         workspace, accept_len, commit_len, out_tokens,
                                         next_anchor, new_seq_len,
                                         static_cast<hipStream_t>(stream));

@@ -120,12 +120,14 @@ struct SpecPlan {
 };
 SpecPlan plan_spec(int B, int S, int V, bool has_draft);
 // vec: 8 (bf16) / 4 (f32) for 16-byte loads, else 1; ct, cd = log2(e) / temperature
+// q_ids / q_probs (nullable, [B, S-1, q_k]): the proposal given as q_k (id,
+// probability) pairs per drafted row instead of draft logits or a point mass
 hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const void* tl,
-                                  const void* dl, const float* uni, const int32_t* prefix_len,
-                                  int B, int S, int V, float ct, float cd, const SpecPlan& pl,
-                                  void* ws, int32_t* accept_len, int32_t* commit_len,
-                                  int32_t* out_tokens, int32_t* next_anchor,
-                                  int32_t* new_seq_len, hipStream_t st);
+                                  const void* dl, const int32_t* q_ids, const float* q_probs,
+                                  int q_k, const float* uni, const int32_t* prefix_len, int B,
+                                  int S, int V, float ct, float cd, const SpecPlan& pl, void* ws,
+                                  int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                                  int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st);
 
 // ---- DFlash 2 candidate selector (selector.hip)
 struct SelPlan {

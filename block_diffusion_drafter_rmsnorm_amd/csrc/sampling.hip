@@ -38,7 +38,8 @@ struct SpecWalk {
   float md, izd;  // the same for the draft row (mode 0)
   int a;          // accepted drafts
   int y;          // rejected draft token (mode 1)
-  int mode;       // 0: [p - q]_+ with q from draft logits, 1: [p - point mass]_+, 2: p (bonus)
+  int mode;       // 0: [p - q]_+ with q from draft logits, 1: [p - point mass]_+, 2: p (bonus),
+                  // 3: [p - q]_+ with q given as K (id, probability) pairs
   int pad;
 };
 
@@ -102,14 +103,29 @@ __device__ __forceinline__ void lse_add(float& m, float& s, const float* v, floa
   for (int k = 0; k < VEC; ++k) s += exp2f((v[k] - m) * sc);
 }
 
+// A proposal given directly as K (id, probability) pairs per drafted row (the
+// DFlash 2 selector's realised q rows); K == 0: absent.
+struct SparseQ {
+  const int32_t* ids;
+  const float* probs;
+  int K;
+};
+
 // Weight of token i in the row the final token is drawn from.  One function
-// for the chunk sums and the pick so both evaluate the same expression.
+// for the chunk sums and the pick so both evaluate the same expression; sid /
+// sp hold the rejected row's K pairs (mode 3).
 __device__ __forceinline__ float spec_weight(float lt, float ld, int i, const SpecWalk& w,
-                                             float ct, float cd) {
+                                             float ct, float cd, const int* sid = nullptr,
+                                             const float* sp = nullptr, int sk = 0) {
 #pragma clang fp contract(off)
   const float pt = exp2f((lt - w.mt) * ct) * w.izt;
   if (w.mode == 2) return pt;
   if (w.mode == 1) return (i == w.y) ? fmaxf(pt - 1.f, 0.f) : pt;
+  if (w.mode == 3) {
+    float q = 0.f;
+    for (int k = 0; k < sk; ++k) q += (sid[k] == i) ? sp[k] : 0.f;
+    return fmaxf(pt - q, 0.f);
+  }
   const float qt = exp2f((ld - w.md) * cd) * w.izd;
   return fmaxf(pt - qt, 0.f);
 }
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void spec_walk_kernel(
     const float* __restrict__ uni, const int32_t* __restrict__ prefix_len, int S, int V,
     const float2* __restrict__ stats, int n_chunks1, float ct, float cd, int chunk2,
     int n_chunks2, float2* __restrict__ csum, SpecWalk* __restrict__ walk, int32_t* accept_len,
-    int32_t* commit_len, int32_t* out_tokens, int32_t* new_seq_len) {
+    int32_t* commit_len, int32_t* out_tokens, int32_t* new_seq_len, SparseQ sq) {
   const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int B = gridDim.x;
   const bool has_draft = dl != nullptr;
@@ -233,6 +249,10 @@ __global__ __launch_bounds__(kThreads) void spec_walk_kernel(
         if (has_draft) {
           const float ld = ld1(dl + ((int64_t)r * (S - 1) + tid) * V + y);
           q = exp2f((ld - st_d[tid].x) * cd) * st_d[tid].y;
+        } else if (sq.K > 0) {
+          const int64_t qr = ((int64_t)r * (S - 1) + tid) * sq.K;
+          q = 0.f;
+          for (int k = 0; k < sq.K; ++k) q += (sq.ids[qr + k] == y) ? sq.probs[qr + k] : 0.f;
         }
         reject = !(uni[(int64_t)r * S + tid] * q < p);
       }
@@ -251,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void spec_walk_kernel(
         w.md = 0.f;
         w.izd = 0.f;
       } else {
-        w.mode = has_draft ? 0 : 1;
+        w.mode = has_draft ? 0 : (sq.K > 0 ? 3 : 1);
         w.y = y;
         w.mt = st_t[a].x;
         w.izt = st_t[a].y;
@@ -263,6 +283,13 @@ __global__ __launch_bounds__(kThreads) void spec_walk_kernel(
   }
   __syncthreads();
   const SpecWalk w = sw;
+  __shared__ int s_id[16];
+  __shared__ float s_p[16];
+  if (w.mode == 3 && tid < sq.K) {
+    s_id[tid] = sq.ids[((int64_t)r * (S - 1) + w.a) * sq.K + tid];
+    s_p[tid] = sq.probs[((int64_t)r * (S - 1) + w.a) * sq.K + tid];
+  }
+  __syncthreads();
 
   // weights of this chunk of the row the token is drawn from
   const int row_t = (w.mode == 2) ? S - 1 : w.a;
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void spec_walk_kernel(
     }
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-      sw_ += spec_weight(vt[k], vd[k], i + k, w, ct, cd);
+      sw_ += spec_weight(vt[k], vd[k], i + k, w, ct, cd, s_id, s_p, sq.K);
       sp += spec_p(vt[k], w, ct);
     }
   }
@@ -318,7 +345,7 @@ template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
     const T* __restrict__ tl, const T* __restrict__ dl, const float* __restrict__ uni, int S,
     int V, float ct, float cd, int chunk2, int n_chunks2, const float2* __restrict__ csum,
-    const SpecWalk* __restrict__ walk, int32_t* out_tokens, int32_t* next_anchor) {
+    const SpecWalk* __restrict__ walk, int32_t* out_tokens, int32_t* next_anchor, SparseQ sq) {
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const SpecWalk w = walk[r];
   __shared__ float wl[kMaxChunk2];
@@ -357,6 +384,12 @@ __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
       s_rem = rem;
     }
   }
+  __shared__ int s_id[16];
+  __shared__ float s_p[16];
+  if (w.mode == 3 && tid < sq.K) {
+    s_id[tid] = sq.ids[((int64_t)r * (S - 1) + w.a) * sq.K + tid];
+    s_p[tid] = sq.probs[((int64_t)r * (S - 1) + w.a) * sq.K + tid];
+  }
   __syncthreads();
   const int ch = s_chunk;
   const bool use_p = s_use_p;
@@ -378,7 +411,8 @@ __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
     }
 #pragma unroll
     for (int k = 0; k < VEC; ++k)
-      wl[i - c0 + k] = use_p ? spec_p(vt[k], w, ct) : spec_weight(vt[k], vd[k], i + k, w, ct, cd);
+      wl[i - c0 + k] = use_p ? spec_p(vt[k], w, ct)
+                             : spec_weight(vt[k], vd[k], i + k, w, ct, cd, s_id, s_p, sq.K);
   }
   __syncthreads();
 
@@ -432,7 +466,8 @@ __global__ __launch_bounds__(kThreads) void spec_pick_kernel(
 }
 
 template <typename T, int VEC>
-hipError_t spec_launch(const int32_t* cand, const void* tl_, const void* dl_, const float* uni,
+hipError_t spec_launch(const SparseQ& sq, const int32_t* cand, const void* tl_, const void* dl_,
+                       const float* uni,
                        const int32_t* prefix_len, int B, int S, int V, float ct, float cd,
                        const SpecPlan& pl, void* ws, int32_t* accept_len, int32_t* commit_len,
                        int32_t* out_tokens, int32_t* next_anchor, int32_t* new_seq_len,
@@ -449,10 +484,10 @@ hipError_t spec_launch(const int32_t* cand, const void* tl_, const void* dl_, co
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((spec_walk_kernel<T, VEC>), dim3(B, pl.n_chunks2), dim3(kThreads), 0, st,
                      cand, tl, dl, uni, prefix_len, S, V, stats, pl.n_chunks1, ct, cd, pl.chunk2,
-                     pl.n_chunks2, csum, walk, accept_len, commit_len, out_tokens, new_seq_len);
+                     pl.n_chunks2, csum, walk, accept_len, commit_len, out_tokens, new_seq_len, sq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((spec_pick_kernel<T, VEC>), dim3(B), dim3(kThreads), 0, st, tl, dl, uni, S, V, ct,
-                     cd, pl.chunk2, pl.n_chunks2, csum, walk, out_tokens, next_anchor);
+                     cd, pl.chunk2, pl.n_chunks2, csum, walk, out_tokens, next_anchor, sq);
   return hipGetLastError();
 }
 
@@ -494,26 +529,27 @@ SpecPlan plan_spec(int B, int S, int V, bool has_draft) {
 }
 
 hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const void* tl,
-                                  const void* dl, const float* uni, const int32_t* prefix_len,
-                                  int B, int S, int V, float ct, float cd, const SpecPlan& pl,
-                                  void* ws, int32_t* accept_len, int32_t* commit_len,
-                                  int32_t* out_tokens, int32_t* next_anchor,
-                                  int32_t* new_seq_len, hipStream_t st) {
+                                  const void* dl, const int32_t* q_ids, const float* q_probs,
+                                  int q_k, const float* uni, const int32_t* prefix_len, int B,
+                                  int S, int V, float ct, float cd, const SpecPlan& pl, void* ws,
+                                  int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                                  int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st) {
   if (B <= 0) return hipSuccess;
+  const SparseQ sq{q_ids, q_probs, q_ids != nullptr ? q_k : 0};
   if (dt == DFLASH_BF16) {
     if (vec > 1)
-      return spec_launch<bf16_t, 8>(cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
+      return spec_launch<bf16_t, 8>(sq, cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
                                     accept_len, commit_len, out_tokens, next_anchor, new_seq_len,
                                     st);
-    return spec_launch<bf16_t, 1>(cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
+    return spec_launch<bf16_t, 1>(sq, cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
                                   accept_len, commit_len, out_tokens, next_anchor, new_seq_len,
                                   st);
   }
   if (vec > 1)
-    return spec_launch<float, 4>(cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
+    return spec_launch<float, 4>(sq, cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
                                  accept_len, commit_len, out_tokens, next_anchor, new_seq_len, st);
-  return spec_launch<float, 1>(cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws, accept_len,
-                               commit_len, out_tokens, next_anchor, new_seq_len, st);
+  return spec_launch<float, 1>(sq, cand, tl, dl, uni, prefix_len, B, S, V, ct, cd, pl, ws,
+                               accept_len, commit_len, out_tokens, next_anchor, new_seq_len, st);
 }
 
 }  // namespace dflash

@@ -8,6 +8,7 @@
  *   dflash_draft_block_selector  the same pass with the DFlash 2 candidate selector
  *   dflash_accept           greedy verify-accept, commit and logical crop
  *   dflash_accept_sampling  rejection-sampling verify-accept and commit
+ *   dflash_accept_sampling_sparse  the same with the selector's sparse q rows
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory unless its name starts with
@@ -286,6 +287,24 @@ dflash_status dflash_accept_sampling(const int32_t* candidates, const void* targ
                                      int32_t* commit_len, int32_t* out_tokens,
                                      int32_t* next_anchor, int32_t* new_seq_len, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * (3'') Rejection-sampling verify with the proposal given as q_k (id,
+ * probability) pairs per drafted row: the DFlash 2 selector's cand_ids and
+ * q_rows ("Inside SGLang ...", section on sampling with the proposal
+ * distribution the walk used: the selector's q rows, not the unary
+ * distribution).  q_j(t) = the probability paired with t in row j (0 for a
+ * token not listed); everything else as dflash_accept_sampling.
+ *   q_ids    [batch, block_size - 1, q_k] int32;  q_probs [batch, block_size - 1, q_k] f32
+ *   workspace >= dflash_accept_sampling_workspace_bytes(batch, block_size, vocab, 0)
+ * q_k 1..16.
+ */
+dflash_status dflash_accept_sampling_sparse(
+    const int32_t* candidates, const void* target_logits, int32_t logits_dtype, int32_t vocab,
+    float target_temperature, const int32_t* q_ids, const float* q_probs, int32_t q_k,
+    const float* uniforms, const int32_t* prefix_len, int32_t batch, int32_t block_size,
+    int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens, int32_t* next_anchor,
+    int32_t* new_seq_len, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * (2') One draft pass with the DFlash 2 candidate selector in place of the

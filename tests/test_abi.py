@@ -191,3 +191,18 @@ def test_selector_argument_errors():
     assert call(dfl.CSelector(fake, fake, fake, 64, 8), cand_ids=None) == -1
     assert dfl.selector_workspace_bytes(TINY, type("S", (), {"c": dfl.CSelector(
         fake, fake, fake, 64, 8)})(), 1, 64) > dfl.draft_workspace_bytes(TINY, 1, 64)
+
+
+def test_accept_sampling_sparse_argument_errors():
+    lib = dfl.raw_lib()
+    F = ctypes.c_void_p(0x100000)
+
+    def call(B=2, S=4, V=1000, k=8, T=1.0, qi=F, wsb=1 << 30):
+        return lib.dflash_accept_sampling_sparse(F, F, dfl.BF16, V, T, qi, F, k, F, F, B, S, F, F,
+                                                 F, F, F, F, wsb, None)
+
+    assert call(B=0) == 0
+    assert call(k=0) == -2 and call(k=17) == -2
+    assert call(S=65) == -2 and call(V=524289) == -2
+    assert call(T=0.0) == -1 and call(qi=None) == -1
+    assert call(wsb=16) == -3

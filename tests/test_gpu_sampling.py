@@ -226,3 +226,89 @@ def test_sampling_is_lossless_on_gpu():
     counts = np.bincount(g["out_tokens"][:, 0], minlength=V)
     chi2 = float(np.sum((counts - B * p) ** 2 / (B * p)))
     assert chi2 < 23.51, (counts, B * p)     # 4 degrees of freedom, p = 1e-4
+
+
+def _sparse_q(cand, V, K, seed):
+    """Per drafted row K distinct ids (the drafted token among them) with
+    Dirichlet probabilities: a stand-in for the selector's q rows."""
+    rng = np.random.default_rng(seed)
+    c = cand.cpu().numpy()
+    B, S = c.shape
+    ids = np.zeros((B, S - 1, K), np.int32)
+    probs = rng.dirichlet(np.ones(K), size=(B, S - 1)).astype(np.float32)
+    for b in range(B):
+        for j in range(S - 1):
+            others = rng.choice(np.setdiff1d(np.arange(V), [c[b, j + 1]]), K - 1, replace=False)
+            row = np.concatenate([[c[b, j + 1]], others])
+            ids[b, j] = rng.permutation(row)
+    dense = np.zeros((B, S - 1, V))
+    np.put_along_axis(dense, ids.astype(np.int64), probs.astype(np.float64), axis=-1)
+    return torch.from_numpy(ids).cuda(), torch.from_numpy(probs).cuda(), dense
+
+
+def _run_sparse(cand, tl, qi, qp, u, L, Tt=1.0):
+    m = dfl()
+    B, S = cand.shape
+    V = tl.shape[-1]
+    outs = [torch.full((B,), -7, dtype=torch.int32, device="cuda") for _ in range(4)]
+    out_tok = torch.full((B, S), -7, dtype=torch.int32, device="cuda")
+    ws = m.workspace(m.accept_sampling_workspace_bytes(B, S, V, False))
+    m.dflash_accept_sampling_sparse(cand, tl, qi, qp, u, L, outs[0], outs[1], out_tok, outs[2],
+                                    outs[3], ws, target_temperature=Tt)
+    torch.cuda.synchronize()
+    names = ["accept_len", "commit_len", "next_anchor", "new_seq_len"]
+    r = {n: o.cpu().numpy().astype(np.int64) for n, o in zip(names, outs)}
+    r["out_tokens"] = out_tok.cpu().numpy().astype(np.int64)
+    return r
+
+
+@pytest.mark.parametrize("shape,dtype", [((9, 8, 1000), torch.float32), ((6, 16, 4096), torch.bfloat16),
+                                         ((4, 16, 151936), torch.bfloat16)])
+def test_sampling_sparse_q_parity(shape, dtype):
+    B, S, V = shape
+    cand, tl, _, u = synth.verify_inputs(B, S, V, seed=B + S, dtype=dtype, device="cuda",
+                                         bump=22.0 if V > 10000 else 12.0,
+                                         bump_lo=13.0 if V > 10000 else 0.0)
+    L = synth.randint(0, 5000, (B,), 5, "verify_L", "cuda").to(torch.int32)
+    qi, qp, dense = _sparse_q(cand, V, 8, B * S)
+    g = _run_sparse(cand, tl, qi, qp, u, L, 0.9)
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    o = oracle.accept_sampling(cand.cpu().numpy(), f(tl), L.cpu().numpy(), f(u), 0.9,
+                               draft_probs=dense)
+    check(g, o, cand, L, max_ambiguous=0.25)
+
+
+def test_selector_then_sparse_verify():
+    """The DFlash 2 path end to end on the GPU: the selector's candidates and
+    q rows feed the sparse sampled verify; the oracle verifies the same
+    candidates with the q rows scattered over the vocabulary."""
+    from tests.gpu_harness import Setup
+    from workloads.configs import get_workload
+    m = dfl()
+    st = Setup(get_workload("small_bf16"))
+    cfg, B, S, K = st.cfg, st.B, st.S, 8
+    dt = synth._DT[cfg.act_dtype]
+    sel = m.Selector(synth.normal((cfg.vocab, 64), 0.3, 1, "sel_a", dt, "cuda"),
+                     synth.normal((cfg.vocab, 64), 0.3, 1, "sel_b", dt, "cuda"),
+                     synth.normal((64, cfg.hidden), 0.02, 1, "sel_wh", dt, "cuda"), K)
+    mp = int(st.L.max())
+    ws = m.workspace(m.selector_workspace_bytes(cfg, sel, B, mp))
+    pos = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    slots, cand = torch.empty_like(pos), torch.empty_like(pos)
+    cids = torch.empty((B, S - 1, K), dtype=torch.int32, device="cuda")
+    q = torch.empty((B, S - 1, K), dtype=torch.float32, device="cuda")
+    u_sel = torch.rand(B, S - 1, generator=torch.Generator("cuda").manual_seed(2), device="cuda")
+    m.dflash_draft_block_selector(cfg, st.c_weights(), st.cache, sel, st.anchor.cuda(),
+                                  st.L.cuda(), st.pt.cuda(), mp, pos, slots, cand, cids, q, ws,
+                                  uniforms=u_sel, temperature=1.0)
+    tl = synth.normal((B, S, cfg.vocab), 2.0, 9, "sel_target", torch.float32, "cuda")
+    u = torch.rand(B, S, generator=torch.Generator("cuda").manual_seed(3), device="cuda")
+    L = st.L.cuda()
+    g = _run_sparse(cand, tl, cids, q, u, L)
+    dense = np.zeros((B, S - 1, cfg.vocab))
+    np.put_along_axis(dense, cids.cpu().numpy().astype(np.int64),
+                      q.cpu().numpy().astype(np.float64), axis=-1)
+    o = oracle.accept_sampling(cand.cpu().numpy(), tl.cpu().numpy().astype(np.float64),
+                               st.L.numpy(), u.cpu().numpy().astype(np.float64), 1.0,
+                               draft_probs=dense)
+    check(g, o, cand, L, max_ambiguous=0.34)
