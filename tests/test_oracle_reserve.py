@@ -54,7 +54,8 @@ def test_reserve_order_and_shortage():
     assert pt2[0, :2].tolist() == [9, 8] and pt2[1, :2].tolist() == [7, 6]
     assert pt2[2, :3].tolist() == [5, 4, 3]
     # a shortage stops at the first request that does not fit
-    pt3, n3, s3, top3, st3 = reserve([10, 100, 5], 4, 16, pt, n, stack, 4)
+    wide = np.full((3, 8), -1)                         # rows wide enough for 7 pages
+    pt3, n3, s3, top3, st3 = reserve([10, 100, 5], 4, 16, wide, n, stack, 4)
     assert st3 == 1 and n3.tolist() == [2, 0, 0] and top3 == 2
     # a row too short for the reservation
     pt4, n4, s4, top4, st4 = reserve([10, 200], 4, 16, pt, n, stack, 10)
