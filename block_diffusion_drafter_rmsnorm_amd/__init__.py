@@ -74,7 +74,7 @@ EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
             "dflash_accept_sampling_workspace_bytes", "dflash_accept_sampling",
             "dflash_selector_workspace_bytes", "dflash_draft_block_selector",
-            "dflash_accept_sampling_sparse",
+            "dflash_accept_sampling_sparse", "dflash_reserve_pages", "dflash_release_pages",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_status_string", "dflash_last_error"]
@@ -110,6 +110,10 @@ def _load():
     lib.dflash_accept_sampling_sparse.argtypes = [P, P, I32, I32, F, P, P, I32, P, P, I32, I32, P,
                                                   P, P, P, P, P, SZ, P]
     lib.dflash_accept_sampling_sparse.restype = I32
+    lib.dflash_reserve_pages.argtypes = [P, I32, I32, I32, P, I32, P, P, I32, P, P, P]
+    lib.dflash_reserve_pages.restype = I32
+    lib.dflash_release_pages.argtypes = [P, I32, P, I32, P, P, I32, P, P]
+    lib.dflash_release_pages.restype = I32
     selp = ctypes.POINTER(CSelector)
     lib.dflash_selector_workspace_bytes.argtypes = [cfgp, selp, I32, I32]
     lib.dflash_selector_workspace_bytes.restype = SZ
@@ -385,6 +389,23 @@ def dflash_accept_sampling_sparse(candidates: torch.Tensor, target_logits: torch
         _ptr(uniforms), _ptr(prefix_len), int(B), int(S), _ptr(accept_len), _ptr(commit_len),
         _ptr(out_tokens), _ptr(next_anchor), _ptr(new_seq_len), _ptr(ws), int(ws.numel()),
         _stream(stream)))
+
+
+def dflash_reserve_pages(seq_len: torch.Tensor, block_size: int, page_size: int,
+                         page_table: torch.Tensor, n_pages: torch.Tensor,
+                         free_pages: torch.Tensor, free_count: torch.Tensor,
+                         status: torch.Tensor, stream=None):
+    _check(_lib.dflash_reserve_pages(_ptr(seq_len), int(seq_len.shape[0]), int(block_size),
+                                     int(page_size), _ptr(page_table), int(page_table.shape[1]),
+                                     _ptr(n_pages), _ptr(free_pages), int(free_pages.numel()),
+                                     _ptr(free_count), _ptr(status), _stream(stream)))
+
+
+def dflash_release_pages(mask: torch.Tensor, page_table: torch.Tensor, n_pages: torch.Tensor,
+                         free_pages: torch.Tensor, free_count: torch.Tensor, stream=None):
+    _check(_lib.dflash_release_pages(_ptr(mask), int(mask.shape[0]), _ptr(page_table),
+                                     int(page_table.shape[1]), _ptr(n_pages), _ptr(free_pages),
+                                     int(free_pages.numel()), _ptr(free_count), _stream(stream)))
 
 
 def lm_head_workspace_bytes(cfg, rows: int) -> int:

@@ -474,6 +474,36 @@ dflash_status dflash_accept_sampling_sparse(
   return DFLASH_OK;
 }
 
+dflash_status dflash_reserve_pages(const int32_t* seq_len, int32_t batch, int32_t block_size,
+                                   int32_t page_size, int32_t* page_table, int32_t max_pages,
+                                   int32_t* n_pages, const int32_t* free_pages,
+                                   int32_t free_capacity, int32_t* free_count, int32_t* status,
+                                   void* stream) {
+  if (batch < 0 || block_size < 1 || page_size < 1 || max_pages < 1 || free_capacity < 0)
+    return fail(DFLASH_EINVAL, "batch, block_size, page_size, max_pages or capacity out of range");
+  if (!seq_len || !page_table || !n_pages || !free_pages || !free_count || !status)
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  hipError_t e = launch_reserve(seq_len, batch, block_size, page_size, page_table, max_pages,
+                                n_pages, free_pages, free_capacity, free_count, status,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reserve");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_release_pages(const int32_t* mask, int32_t batch, const int32_t* page_table,
+                                   int32_t max_pages, int32_t* n_pages, int32_t* free_pages,
+                                   int32_t free_capacity, int32_t* free_count, void* stream) {
+  if (batch < 0 || max_pages < 1 || free_capacity < 0)
+    return fail(DFLASH_EINVAL, "batch, max_pages or capacity out of range");
+  if (batch == 0) return DFLASH_OK;
+  if (!mask || !page_table || !n_pages || !free_pages || !free_count)
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  hipError_t e = launch_release(mask, batch, page_table, max_pages, n_pages, free_pages,
+                                free_capacity, free_count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "release");
+  return DFLASH_OK;
+}
+
 // Workspace of the selector stage, carved after the draft pass's.
 struct SelectorWs {
   void* logits; float* pv; int* pi; float* unary; float* w; GemmScratch gs; size_t bytes;

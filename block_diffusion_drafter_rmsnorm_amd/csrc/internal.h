@@ -129,6 +129,14 @@ hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const vo
                                   int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
                                   int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st);
 
+// ---- cache reservation (reserve.hip)
+hipError_t launch_reserve(const int32_t* seq_len, int B, int S, int P, int32_t* pt, int max_pages,
+                          int32_t* n_pages, const int32_t* free_pages, int capacity,
+                          int32_t* free_count, int32_t* status, hipStream_t st);
+hipError_t launch_release(const int32_t* mask, int B, const int32_t* pt, int max_pages,
+                          int32_t* n_pages, int32_t* free_pages, int capacity, int32_t* free_count,
+                          hipStream_t st);
+
 // ---- DFlash 2 candidate selector (selector.hip)
 struct SelPlan {
   int chunk, n_chunks;  // vocabulary chunking of the top-K pass (n_chunks <= 64)

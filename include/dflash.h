@@ -9,6 +9,7 @@
  *   dflash_accept           greedy verify-accept, commit and logical crop
  *   dflash_accept_sampling  rejection-sampling verify-accept and commit
  *   dflash_accept_sampling_sparse  the same with the selector's sparse q rows
+ *   dflash_reserve_pages / dflash_release_pages  page reservation on the device
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory unless its name starts with
@@ -305,6 +306,36 @@ dflash_status dflash_accept_sampling_sparse(
     const float* uniforms, const int32_t* prefix_len, int32_t batch, int32_t block_size,
     int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens, int32_t* next_anchor,
     int32_t* new_seq_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Cache reservation before acceptance is known ("Inside SGLang ...", Step 2:
+ * a 2 x block_size page-aligned headroom beyond the committed prefix;
+ * allocation is not acceptance; the overlap section and the Spec V2 PR: the
+ * next step plans from the lengths the GPU published).  Enqueued after
+ * dflash_accept on the same stream, it reads the new_seq_len that call wrote.
+ *
+ * For each request r in batch order: need = ceil((seq_len[r] + 2 * block_size)
+ * / page_size) pages; the pages it lacks (need - n_pages[r]) are popped from
+ * the top of the free stack (free_pages[free_count - 1], then below) and
+ * appended to page_table[r] from entry n_pages[r]; n_pages[r] = need.  The
+ * first request whose shortfall exceeds the stack (status 1) or whose need
+ * exceeds max_pages (status 2) is left as it is, and so is every later one.
+ *   seq_len     [batch]   committed lengths (device)
+ *   page_table  [batch, max_pages]; n_pages [batch]: pages each row holds
+ *   free_pages  [free_capacity] stack of free physical pages; free_count [1]
+ *   status      [1] out: 0 served, 1 out of pages, 2 row too short
+ * Reservations never shrink or move a page.  dflash_release_pages pushes the
+ * pages of every request with mask[r] != 0 back (batch order, row order) and
+ * sets its n_pages to 0.  Deterministic; one workgroup; no workspace.
+ */
+dflash_status dflash_reserve_pages(const int32_t* seq_len, int32_t batch, int32_t block_size,
+                                   int32_t page_size, int32_t* page_table, int32_t max_pages,
+                                   int32_t* n_pages, const int32_t* free_pages,
+                                   int32_t free_capacity, int32_t* free_count, int32_t* status,
+                                   void* stream);
+dflash_status dflash_release_pages(const int32_t* mask, int32_t batch, const int32_t* page_table,
+                                   int32_t max_pages, int32_t* n_pages, int32_t* free_pages,
+                                   int32_t free_capacity, int32_t* free_count, void* stream);
 
 /*
  * (2') One draft pass with the DFlash 2 candidate selector in place of the
