@@ -506,17 +506,14 @@ dflash_status dflash_release_pages(const int32_t* mask, int32_t batch, const int
 
 // Workspace of the selector stage, carved after the draft pass's.
 struct SelectorWs {
-  void* logits; float* pv; int* pi; float* unary; float* w; GemmScratch gs; size_t bytes;
+  void* logits; float* unary; float* w; GemmScratch gs; size_t bytes;
 };
 static SelectorWs layout_selector(const dflash_config* c, const dflash_selector* sel, int B,
                                   bool own_logits, void* base) {
   Carver cv(base);
   SelectorWs L;
   const int M1 = B * (c->block_size - 1), K = sel->top_k, r = sel->rank;
-  const SelPlan pl = plan_selector(M1, c->vocab);
   L.logits = own_logits ? cv.take((size_t)act_bytes(c->act_dtype) * M1 * c->vocab) : nullptr;
-  L.pv = (float*)cv.take(sizeof(float) * (size_t)M1 * pl.n_chunks * K);
-  L.pi = (int*)cv.take(sizeof(int) * (size_t)M1 * pl.n_chunks * K);
   L.unary = (float*)cv.take(sizeof(float) * (size_t)M1 * K);
   L.w = (float*)cv.take(sizeof(float) * (size_t)M1 * r);
   const GemmPlan gp = plan_gemm(M1, r, c->hidden, c->act_dtype == DFLASH_BF16);
@@ -579,9 +576,10 @@ dflash_status dflash_draft_block_selector(
     return s;
   const int S = cfg->block_size, M1 = batch * (S - 1), K = sel->top_k;
   hipError_t e;
-  // candidates and their unary logits from the logits just written
-  if ((e = launch_topk(cfg->act_dtype, lg, M1, cfg->vocab, K, plan_selector(M1, cfg->vocab),
-                       SL.pv, SL.pi, cand_ids, SL.unary, st)) != hipSuccess)
+  // candidates and their unary logits from the logits just written and the
+  // lm_head's per-tile argmax partials
+  if ((e = launch_topk(cfg->act_dtype, lg, L.lm_part, M1, cfg->vocab, K, cand_ids, SL.unary,
+                       st)) != hipSuccess)
     return hip_fail(e, "top-k");
   // w_j = W_h y_j for the final-normed rows 1..S-1 (the norm applied by linearity)
   if ((e = gemm_store_f32(cfg->act_dtype, asrc_normed(L.xg, cfg->hidden, L.ss, cfg->rms_eps, S),

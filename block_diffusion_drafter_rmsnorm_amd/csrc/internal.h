@@ -138,14 +138,11 @@ hipError_t launch_release(const int32_t* mask, int B, const int32_t* pt, int max
                           hipStream_t st);
 
 // ---- DFlash 2 candidate selector (selector.hip)
-struct SelPlan {
-  int chunk, n_chunks;  // vocabulary chunking of the top-K pass (n_chunks <= 64)
-};
-SelPlan plan_selector(int rows, int V);
-// top-K of rows x V logits (act dtype): per-chunk partials pv/pi [rows][n_chunks][K],
-// then cand [rows][K] ids and unary [rows][K] values; K in {1, 2, 4, 8, 16}
-hipError_t launch_topk(int dt, const void* logits, int rows, int V, int K, const SelPlan& pl,
-                       float* pv, int* pi, int32_t* cand, float* unary, hipStream_t st);
+// top-K (K in {1, 2, 4, 8, 16}) of rows x V logits (act dtype) from the
+// lm_head's per-128-column argmax partials part [rows][ceil(V / 128)]:
+// cand [rows][K] ids, unary [rows][K] values
+hipError_t launch_topk(int dt, const void* logits, const float2* part, int rows, int V, int K,
+                       int32_t* cand, float* unary, hipStream_t st);
 // lattice of every (position, predecessor, candidate) and the walk: candidates
 // [B, S] = anchor + chosen tokens, q_rows [B, S-1, K]; uni nullable (greedy)
 hipError_t launch_lattice_walk(int dt, const int32_t* cand, const float* unary, const float* w,

@@ -13,11 +13,12 @@
 //               predecessor: greedy first maximum or an inverse-CDF draw from
 //               softmax(row / T); q_rows = that softmax.
 //
-// Kernels: topk_chunk_kernel (grid rows x chunks of <= 8192 logits staged in
-// LDS, K rounds of block argmax each strictly after the previous winner),
-// topk_merge_kernel (one wave per row over the <= 64 chunk lists), and
+// Kernels: topk_tiles_kernel (one workgroup per row: only the 128-column
+// tiles whose lm_head argmax partial reaches the K-th largest tile maximum can
+// hold a candidate; their logits are searched by rounds of block argmax), and
 // lattice_walk_kernel (one workgroup per request: every (position,
-// predecessor, candidate) score in parallel, then the walk).
+// predecessor, candidate) score in parallel, then the walk on one wave, a lane
+// per candidate slot).
 #include <math.h>
 
 #include "common.cuh"
@@ -29,7 +30,6 @@ namespace {
 constexpr int kT = 256;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNoIdx = 0x7fffffff;
-constexpr int kMaxChunk = 8192;  // logits of one top-K chunk (32 KB of LDS)
 
 // (value, index) order of the candidates: larger value first, then lower index
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
@@ -59,122 +59,227 @@ __device__ __forceinline__ void ld8(const float* p, float* v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Block-wide best (value, index) of one entry per thread; every thread gets it.
-__device__ __forceinline__ void block_best(float& v, int& i, float* rv, int* ri) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(i, o, 64);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    rv[threadIdx.x >> 6] = v;
-    ri[threadIdx.x >> 6] = i;
-  }
-  __syncthreads();
-  v = rv[0];
-  i = ri[0];
-  for (int w = 1; w < kT / 64; ++w)
-    if (better(rv[w], ri[w], v, i)) {
-      v = rv[w];
-      i = ri[w];
-    }
+// ---------------------------------------------------------------- top-K
+// Wave reductions on DPP moves (ALU latency, no LDS crossbar): quad
+// permutations 1032 and 2301, the half-row and row mirrors combine each row of
+// 16 lanes; row broadcasts of lanes 15 (into rows 1 and 3) and 31 (into rows
+// 2 and 3) finish in lane 63, which readlane hands to every lane.  A lane a
+// move leaves out keeps old.  Every lane of the wave must be active.
+constexpr int kQuad1032 = 0xB1, kQuad2301 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143, kRowShr = 0x110;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
 }
 
-// ---------------------------------------------------------------- top-K
-// One workgroup per (row, chunk of at most kMaxChunk logits): the chunk is
-// staged in LDS as fp32 (16-byte loads when VEC8: rows on 16-byte boundaries,
-// V a multiple of 8), then K rounds each take the block's best element that
-// comes strictly after the previous round's winner in the (value, index)
-// order.  Every thread does the same work in every round (no divergent
-// insertion); NaN is never taken.
-template <typename T, int K, bool VEC8>
-__global__ __launch_bounds__(kT) void topk_chunk_kernel(const T* __restrict__ logits, int V,
-                                                        int chunk, int n_chunks,
-                                                        float* __restrict__ pv,
-                                                        int* __restrict__ pi) {
-  const int row = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const T* x = logits + (int64_t)row * V;
-  const int c0 = c * chunk, n = min(V, c0 + chunk) - c0;
-  __shared__ float xs[kMaxChunk];
-  __shared__ float rv[kT / 64];
-  __shared__ int ri[kT / 64];
-  if (VEC8) {
-    for (int e = tid * 8; e < n; e += kT * 8) {
-      float v[8];
-      ld8(x + c0 + e, v);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) xs[e + u] = v[u];
-    }
-  } else {
-    for (int e = tid; e < n; e += kT) xs[e] = ldf(x + c0 + e);
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  const float ov = __int_as_float(dpp<CTRL, ROWS>(__float_as_int(v), __float_as_int(v)));
+  const int oi = dpp<CTRL, ROWS>(i, i);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
   }
-  __syncthreads();
-  float prev_v = __builtin_huge_valf();
-  int prev_i = -1;
-  float* ov = pv + ((int64_t)row * n_chunks + c) * K;
-  int* oi = pi + ((int64_t)row * n_chunks + c) * K;
+}
+
+// Wave-wide best (value, index) in (value, lower index) order; every lane gets
+// it.  Values must not be NaN (the order is then total, so any combining
+// order gives the same result).
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+  best_step<kQuad1032, 0xf>(v, i);
+  best_step<kQuad2301, 0xf>(v, i);
+  best_step<kHalfMirror, 0xf>(v, i);
+  best_step<kMirror, 0xf>(v, i);
+  best_step<kBcast15, 0xa>(v, i);
+  best_step<kBcast31, 0xc>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float add_step(float s) {
+  return s + __int_as_float(dpp<CTRL, ROWS>(0, __float_as_int(s)));
+}
+
+// Wave-wide sum in a fixed order; every lane gets it.
+__device__ __forceinline__ float wave_sum(float s) {
+  s = add_step<kQuad1032, 0xf>(s);
+  s = add_step<kQuad2301, 0xf>(s);
+  s = add_step<kHalfMirror, 0xf>(s);
+  s = add_step<kMirror, 0xf>(s);
+  s = add_step<kBcast15, 0xa>(s);
+  s = add_step<kBcast31, 0xc>(s);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
+}
+
+// Inclusive prefix sum over the 16 lanes of each row (row shifts by 1, 2, 4, 8;
+// a lane whose source falls before its row adds 0).
+__device__ __forceinline__ float row_incl_scan(float c) {
+  c = add_step<kRowShr + 1, 0xf>(c);
+  c = add_step<kRowShr + 2, 0xf>(c);
+  c = add_step<kRowShr + 4, 0xf>(c);
+  c = add_step<kRowShr + 8, 0xf>(c);
+  return c;
+}
+
+// One workgroup per row, from the lm_head's per-128-column argmax partials.
+// K tiles whose maxima all reach t hold K distinct logits >= t, so t bounds
+// the row's K-th largest logit from below and only tiles whose maximum reaches
+// t can hold a top-K logit.  t is the K-th largest tile maximum (each wave
+// takes the K largest of its share, then the 4 K are merged).  The logits of
+// the qualifying tiles are read in batches of 32 tiles, 16 per thread in
+// registers (the loads issued together); each wave finds the K best of its
+// share and the running list by K rounds of wave argmax, each strictly after
+// the previous winner in (value, index) order, and one wave merges the 4 K
+// results into the running list.
+constexpr int kMaxTiles = 4096;  // 128-column tiles of a row (vocab <= 524288)
+
+// The K best of one register array per lane (plus one extra entry), strictly
+// after nothing, by K rounds of wave argmax; lane 0 writes round k to ov/oi.
+template <int K, int N>
+__device__ __forceinline__ void wave_topk(const float (&v)[N], const int (&ix)[N], float xv,
+                                          int xi, float* ov, int* oi) {
+  float pv = __builtin_huge_valf();
+  int pi = -1;
   for (int k = 0; k < K; ++k) {
     float bv = kNegInf;
     int bi = kNoIdx;
-    for (int e = tid; e < n; e += kT) {
-      const float v = xs[e];
-      const int i = c0 + e;
-      if (better(prev_v, prev_i, v, i) && better(v, i, bv, bi)) {
-        bv = v;
-        bi = i;
-      }
+    if (better(pv, pi, xv, xi)) {
+      bv = xv;
+      bi = xi;
     }
-    block_best(bv, bi, rv, ri);
-    if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (better(pv, pi, v[i], ix[i]) && better(v[i], ix[i], bv, bi)) {
+        bv = v[i];
+        bi = ix[i];
+      }
+    wave_best(bv, bi);
+    if ((threadIdx.x & 63) == 0) {
       ov[k] = bv;
       oi[k] = bi;
     }
-    prev_v = bv;
-    prev_i = bi;
+    pv = bv;
+    pi = bi;
   }
 }
 
-// One wave per row: lane l holds chunk l's sorted list (n_chunks <= 64).
-template <int K>
-__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ pv,
-                                                        const int* __restrict__ pi,
-                                                        int n_chunks, int V,
-                                                        int32_t* __restrict__ cand,
+template <typename T, int K>
+__global__ __launch_bounds__(kT) void topk_tiles_kernel(const T* __restrict__ logits,
+                                                        const float2* __restrict__ part, int V,
+                                                        int n_tiles, int32_t* __restrict__ cand,
                                                         float* __restrict__ unary) {
-  const int row = blockIdx.x, lane = threadIdx.x;
-  __shared__ float lv[64 * K];
-  __shared__ int li[64 * K];
-  for (int e = lane; e < 64 * K; e += 64) {
-    const int l = e / K;
-    lv[e] = l < n_chunks ? pv[((int64_t)row * n_chunks + l) * K + e % K] : kNegInf;
-    li[e] = l < n_chunks ? pi[((int64_t)row * n_chunks + l) * K + e % K] : kNoIdx;
-  }
-  __syncthreads();
-  int ptr = 0;
-  for (int k = 0; k < K; ++k) {
-    const float hv = ptr < K ? lv[lane * K + ptr] : kNegInf;
-    const int hi = ptr < K ? li[lane * K + ptr] : kNoIdx;
-    float v = hv;
-    int i = hi;
+  constexpr int NW = kT / 64;
+  constexpr int TPT = kMaxTiles / kT;  // tile maxima per thread
+  constexpr int TPB = 32;              // qualifying tiles per batch
+  constexpr int EPT = TPB * 128 / kT;  // logits per thread per batch
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int qt[kMaxTiles];
+  __shared__ float wv[NW * K];
+  __shared__ int wi[NW * K];
+  __shared__ float lv[K];
+  __shared__ int li[K];
+  __shared__ int wc[NW];
+  // tile maxima: tile tid + i * kT in register i (never NaN: the partials map
+  // NaN to -inf); absent tiles carry no index
+  float tm[TPT];
+  int ti[TPT];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(v, o, 64);
-      const int oi = __shfl_xor(i, o, 64);
-      if (better(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
+  for (int i = 0; i < TPT; ++i) {
+    const int t = tid + i * kT;
+    tm[i] = t < n_tiles ? part[(int64_t)row * n_tiles + t].x : kNegInf;
+    ti[i] = t < n_tiles ? t : kNoIdx;
+  }
+  wave_topk<K>(tm, ti, kNegInf, kNoIdx, wv + wave * K, wi + wave * K);
+  __syncthreads();
+  float thr;
+  {  // every wave merges the NW * K <= 64 entries (one per lane) the same way
+    const float ev = lane < NW * K ? wv[lane] : kNegInf;
+    const int ei = lane < NW * K ? wi[lane] : kNoIdx;
+    float pv = __builtin_huge_valf();
+    int pi = -1;
+    for (int k = 0; k < K; ++k) {
+      float bv = kNegInf;
+      int bi = kNoIdx;
+      if (better(pv, pi, ev, ei)) {
+        bv = ev;
+        bi = ei;
+      }
+      wave_best(bv, bi);
+      pv = bv;
+      pi = bi;
+    }
+    thr = pi == kNoIdx ? kNegInf : pv;  // fewer than K tiles: every tile qualifies
+  }
+  // qualifying tiles: a count per thread, a block scan, then each thread's own
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) cnt += (ti[i] != kNoIdx && tm[i] >= thr) ? 1 : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();  // wv / wi are read above before the batches rewrite them
+  if (lane == 63) wc[wave] = incl;
+  __syncthreads();
+  int off = incl - cnt, nq = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) off += wc[w];
+    nq += wc[w];
+  }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+    if (ti[i] != kNoIdx && tm[i] >= thr) qt[off++] = ti[i];
+  __syncthreads();
+  // batches of qualifying tiles: logit e = tid + i * kT of the batch is column
+  // (tid & 127) of the batch's tile 2 i + (tid >> 7)
+  int n_list = 0;
+  for (int b0 = 0; b0 < nq; b0 += TPB) {
+    const int nb = min(TPB, nq - b0);
+    float v[EPT];
+    int ix[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int slot = 2 * i + (tid >> 7);
+      const int col = slot < nb ? qt[b0 + slot] * 128 + (tid & 127) : V;
+      v[i] = col < V ? ldf(logits + (int64_t)row * V + col) : kNegInf;
+      ix[i] = col < V ? col : kNoIdx;
+    }
+    const bool has_list = tid < K && tid < n_list;
+    wave_topk<K>(v, ix, has_list ? lv[tid] : kNegInf, has_list ? li[tid] : kNoIdx,
+                 wv + wave * K, wi + wave * K);
+    __syncthreads();
+    if (wave == 0) {  // merge the waves' lists (NW * K <= 64 entries, one per lane)
+      const float ev = lane < NW * K ? wv[lane] : kNegInf;
+      const int ei = lane < NW * K ? wi[lane] : kNoIdx;
+      float pv = __builtin_huge_valf();
+      int pi = -1;
+      for (int k = 0; k < K; ++k) {
+        float bv = kNegInf;
+        int bi = kNoIdx;
+        if (better(pv, pi, ev, ei)) {
+          bv = ev;
+          bi = ei;
+        }
+        wave_best(bv, bi);
+        if (lane == 0) {
+          lv[k] = bv;
+          li[k] = bi;
+        }
+        pv = bv;
+        pi = bi;
       }
     }
-    if (hi == i && i != kNoIdx) ++ptr;
-    if (lane == 0) {
-      cand[(int64_t)row * K + k] = (i >= 0 && i < V) ? i : 0;
-      unary[(int64_t)row * K + k] = v;
-    }
+    n_list = K;
+    __syncthreads();
+  }
+  if (tid < K) {
+    const int i = li[tid];
+    cand[(int64_t)row * K + tid] = (i >= 0 && i < V) ? i : 0;
+    unary[(int64_t)row * K + tid] = lv[tid];
   }
 }
 
@@ -221,95 +326,58 @@ __global__ __launch_bounds__(kT) void lattice_walk_kernel(
     score[t] = ub[j * K + k] + s;
   }
   __syncthreads();
-  if (tid != 0) return;
-  const float invT = 1.0f / temperature;
-  candidates[(int64_t)b * S] = anchor[b];
+  // the walk, on the first wave: lane k < K holds candidate slot k of the row
+  if (tid >= 64) return;
+  const int lane = tid;
+  const float sc = uni ? 1.0f / temperature : 1.f;
+  if (lane == 0) candidates[(int64_t)b * S] = anchor[b];
   int p = 0;
   for (int j = 0; j < J; ++j) {
-    const float* row = score + (j * K + p) * K;
-    float m = kNegInf;
-    int best = 0;
-    for (int k = 0; k < K; ++k)
-      if (row[k] > m) {  // first maximum
-        m = row[k];
-        best = k;
-      }
-    const float mt = m * (uni ? invT : 1.f);
-    float sum = 0.f;
-    float* q = q_rows + ((int64_t)b * J + j) * K;
-    for (int k = 0; k < K; ++k) {
-      const float e = expf(row[k] * (uni ? invT : 1.f) - mt);
-      q[k] = e;
-      sum += e;
-    }
-    const float inv = 1.0f / sum;
-    for (int k = 0; k < K; ++k) q[k] *= inv;
+    const float v = lane < K ? score[(j * K + p) * K + lane] : kNegInf;
+    // greedy: the first maximum (NaN never wins)
+    float m = v == v ? v : kNegInf;
+    int best = lane < K ? lane : kNoIdx;
+    wave_best(m, best);
+    const float e = lane < K ? expf(v * sc - m * sc) : 0.f;
+    const float q = e * (1.0f / wave_sum(e));
+    if (lane < K) q_rows[((int64_t)b * J + j) * K + lane] = q;
     int pick = best;
     if (uni) {
+      // inverse CDF: the first slot whose running sum of q exceeds the draw
       const float x = uni[(int64_t)b * J + j];
-      float cum = 0.f;
-      pick = K - 1;
-      for (int k = 0; k < K; ++k) {
-        cum += q[k];
-        if (cum > x) {
-          pick = k;
-          break;
-        }
-      }
+      const float c = row_incl_scan(q);  // K <= 16: the candidates sit in row 0
+      const uint64_t hit = __ballot(lane < K && c > x);
+      pick = hit ? __ffsll((unsigned long long)hit) - 1 : K - 1;
     }
-    candidates[(int64_t)b * S + 1 + j] = cb[j * K + pick];
+    if (lane == 0) candidates[(int64_t)b * S + 1 + j] = cb[j * K + pick];
     p = pick;
   }
 }
 
-template <typename T, int K>
-void topk_chunks(const void* logits, int rows, int V, const SelPlan& pl, float* pv, int* pi,
-                 hipStream_t st) {
-  const bool vec8 = V % 8 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
-  const T* x = static_cast<const T*>(logits);
-  if (vec8)
-    hipLaunchKernelGGL((topk_chunk_kernel<T, K, true>), dim3(rows, pl.n_chunks), dim3(kT), 0, st,
-                       x, V, pl.chunk, pl.n_chunks, pv, pi);
-  else
-    hipLaunchKernelGGL((topk_chunk_kernel<T, K, false>), dim3(rows, pl.n_chunks), dim3(kT), 0,
-                       st, x, V, pl.chunk, pl.n_chunks, pv, pi);
-}
-
 template <int K>
-hipError_t topk_launch(int dt, const void* logits, int rows, int V, const SelPlan& pl, float* pv,
-                       int* pi, int32_t* cand, float* unary, hipStream_t st) {
+hipError_t topk_launch(int dt, const void* logits, const float2* part, int rows, int V,
+                       int32_t* cand, float* unary, hipStream_t st) {
+  const int nt = logits_tiles(V);
   if (dt == DFLASH_BF16)
-    topk_chunks<bf16_t, K>(logits, rows, V, pl, pv, pi, st);
+    hipLaunchKernelGGL((topk_tiles_kernel<bf16_t, K>), dim3(rows), dim3(kT), 0, st,
+                       static_cast<const bf16_t*>(logits), part, V, nt, cand, unary);
   else
-    topk_chunks<float, K>(logits, rows, V, pl, pv, pi, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_merge_kernel<K>), dim3(rows), dim3(64), 0, st, pv, pi, pl.n_chunks, V,
-                     cand, unary);
+    hipLaunchKernelGGL((topk_tiles_kernel<float, K>), dim3(rows), dim3(kT), 0, st,
+                       static_cast<const float*>(logits), part, V, nt, cand, unary);
   return hipGetLastError();
 }
 
 }  // namespace
 
-SelPlan plan_selector(int rows, int V) {
-  SelPlan pl{};
-  int want = (2048 + rows - 1) / rows;
-  want = want < 1 ? 1 : (want > 64 ? 64 : want);
-  pl.chunk = ((V + want - 1) / want + 63) / 64 * 64;
-  if (pl.chunk > kMaxChunk) pl.chunk = kMaxChunk;  // V <= 64 * kMaxChunk keeps n_chunks <= 64
-  pl.n_chunks = (V + pl.chunk - 1) / pl.chunk;
-  return pl;
-}
-
-hipError_t launch_topk(int dt, const void* logits, int rows, int V, int K, const SelPlan& pl,
-                       float* pv, int* pi, int32_t* cand, float* unary, hipStream_t st) {
+hipError_t launch_topk(int dt, const void* logits, const float2* part, int rows, int V, int K,
+                       int32_t* cand, float* unary, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   switch (K) {
-    case 1: return topk_launch<1>(dt, logits, rows, V, pl, pv, pi, cand, unary, st);
-    case 2: return topk_launch<2>(dt, logits, rows, V, pl, pv, pi, cand, unary, st);
-    case 4: return topk_launch<4>(dt, logits, rows, V, pl, pv, pi, cand, unary, st);
-    case 8: return topk_launch<8>(dt, logits, rows, V, pl, pv, pi, cand, unary, st);
-    case 16: return topk_launch<16>(dt, logits, rows, V, pl, pv, pi, cand, unary, st);
+    case 1: return topk_launch<1>(dt, logits, part, rows, V, cand, unary, st);
+    case 2: return topk_launch<2>(dt, logits, part, rows, V, cand, unary, st);
+    case 4: return topk_launch<4>(dt, logits, part, rows, V, cand, unary, st);
+    case 8: return topk_launch<8>(dt, logits, part, rows, V, cand, unary, st);
+    case 16: return topk_launch<16>(dt, logits, part, rows, V, cand, unary, st);
     default: return hipErrorInvalidValue;
   }
 }

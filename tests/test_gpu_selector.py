@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.selector import select
+from oracle.selector import select, top_k
 from workloads import synth
 from workloads.configs import get_workload
 from tests.gpu_harness import Setup
@@ -124,3 +124,35 @@ def test_selector_sampled_walk_draws_from_its_q_rows():
             c = np.cumsum(q[b, j].astype(np.float64))
             lo = c[k - 1] if k > 0 else 0.0
             assert lo - 1e-5 <= u[b, j] and (u[b, j] < c[k] + 1e-5 or k == K - 1), (b, j, k)
+
+
+@pytest.mark.parametrize("name,K", [("small_bf16_vocab", 16), ("small_bf16", 4)])
+def test_selector_topk_ties_across_tiles(name, K):
+    """lm_head rows repeat with period 7, so every 128-column tile holds the same
+    maximum and each logit value recurs across the whole vocabulary: every tile
+    qualifies for the search, and the candidates must be the lowest ids of the
+    largest values, in the oracle's (value, lower id) order."""
+    st = Setup(get_workload(name))
+    W = st.W["lm_head"]
+    V = st.cfg.vocab
+    W.copy_(W[:7].repeat((V + 6) // 7, 1)[:V])
+    _, _, _, sel = _selector(st.cfg, 32, K, 9)
+    g = _run(st, sel, K)
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    lg = f(g["logits"])
+    ids = top_k(lg, K)[0]
+    assert np.array_equal(g["cand_ids"].numpy(), ids)
+    # the case is what it claims: the K-th candidate ties the first in most rows
+    top = np.take_along_axis(lg, ids, -1)
+    assert np.mean(top[..., 0] == top[..., K - 1]) > 0.5
+
+
+def test_selector_parity_wide_vocab():
+    """A vocabulary of 257 tiles with a ragged last tile, K = 16."""
+    st = Setup(get_workload("small_bf16_vocab"))
+    K = 16
+    A, Bt, Wh, sel = _selector(st.cfg, 32, K, 11)
+    g = _run(st, sel, K)
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    ids, _ = top_k(f(g["logits"]), K)
+    assert np.array_equal(g["cand_ids"].numpy(), ids)
