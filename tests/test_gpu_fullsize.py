@@ -257,3 +257,59 @@ def test_fullsize_kimi_fp8_sliding():
     slots = torch.cat([_slots_of(st.pt, r, pos.view(B, S)[r].long(), st.P) for r in range(B)])
     _check_inject(st, feats, pos.to(torch.int32), slots, commit, B, S, list(range(0, B * S, 5)))
     st.free()
+
+
+def test_fullsize_kimi_draft_window():
+    """The Kimi-shaped pass with a 4096-row draft window over 32768-row
+    prefixes: every layer's attention reads only the last 4096 context rows."""
+    st = Setup("kimi_k26_b8_w4096")
+    assert st.cfg.context_window == 4096 and int(st.L.min()) > 4096
+    _check_draft(st, [3])
+    st.free()
+
+
+def test_fullsize_selector_qwen3_8b_b16():
+    """The DFlash 2 selector at the benchmark's shape and settings (top-8,
+    rank 64): candidate ids from the GPU's logits bit-exact against the
+    oracle's top-k; the walk's decisions checked where the oracle's row (its
+    fp64 final-normed hidden row) has a top-2 gap above 0.05, q_rows within
+    2e-2 of the oracle's softmax."""
+    from oracle.selector import select
+    st = Setup("qwen3_8b_b16")
+    m = dfl()
+    cfg, B, S = st.cfg, st.B, st.S
+    K, r, s = 8, 64, st.wl.seed
+    dt = synth._DT[cfg.act_dtype]
+    A = synth.normal((cfg.vocab, r), 0.3, s, "sel_a", dt, "cuda")
+    Bt = synth.normal((cfg.vocab, r), 0.3, s, "sel_b", dt, "cuda")
+    Wh = synth.normal((r, cfg.hidden), 0.02, s, "sel_wh", dt, "cuda")
+    sel = m.Selector(A, Bt, Wh, K)
+    mp = int(st.L.max())
+    ws = m.workspace(m.selector_workspace_bytes(cfg, sel, B, mp))
+    o32 = lambda *shape: torch.empty(shape, dtype=torch.int32, device="cuda")  # noqa: E731
+    pos, slots, cand, cids = o32(B, S), o32(B, S), o32(B, S), o32(B, S - 1, K)
+    q = torch.empty((B, S - 1, K), dtype=torch.float32, device="cuda")
+    lg = torch.empty((B, S - 1, cfg.vocab), dtype=dt, device="cuda")
+    m.dflash_draft_block_selector(cfg, st.cw, st.cache, sel, st.anchor.cuda(), st.L.cuda(),
+                                  st.pt.cuda(), mp, pos, slots, cand, cids, q, ws, logits=lg)
+    torch.cuda.synchronize()
+    d = oracle.draft_block(cfg, oracle_weights(st.W), st.oracle_cache(), st.anchor.numpy(),
+                           st.L.numpy(), st.pt.numpy(), requests=[0])
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    o = select(f(lg)[:1], d["hidden"], st.anchor.numpy()[:1], f(A), f(Bt), f(Wh), k=K)
+    ci, gc, gq = cids.cpu().numpy()[:1], cand.cpu().numpy()[:1], q.cpu().numpy()[:1]
+    assert np.array_equal(ci, o["cand_ids"])
+    p, n_clear = 0, 0
+    for j in range(S - 1):
+        row = o["score"][0, j, p]
+        k = int(np.nonzero(ci[0, j] == gc[0, 1 + j])[0][0])
+        srt = np.sort(row)[::-1]
+        if srt[0] - srt[1] > 0.05:
+            n_clear += 1
+            assert k == int(np.argmax(row)), (j, k, row)
+        e = np.exp(row - row.max())
+        assert np.allclose(gq[0, j], e / e.sum(), atol=2e-2), j
+        p = k
+    _print(f"[fullsize selector] walk decisions checked on {n_clear}/{S - 1} positions")
+    assert n_clear >= (S - 1) // 2
+    st.free()
