@@ -126,13 +126,19 @@ __device__ __forceinline__ float row_incl_scan(float c) {
 // One workgroup per row, from the lm_head's per-128-column argmax partials.
 // K tiles whose maxima all reach t hold K distinct logits >= t, so t bounds
 // the row's K-th largest logit from below and only tiles whose maximum reaches
-// t can hold a top-K logit.  t is the K-th largest tile maximum (each wave
-// takes the K largest of its share, then the 4 K are merged).  The logits of
-// the qualifying tiles are read in batches of 32 tiles, 16 per thread in
-// registers (the loads issued together); each wave finds the K best of its
-// share and the running list by K rounds of wave argmax, each strictly after
-// the previous winner in (value, index) order, and one wave merges the 4 K
-// results into the running list.
+// t can hold a top-K logit, and only their logits that reach t.
+//   t: each thread's largest tile maximum, ranked within its wave: the
+//   lane maximum of rank K-1 bounds t from below (K distinct tiles reach it),
+//   and the largest of the 4 waves' bounds selects the candidate tiles; when
+//   they are at most 64, ranking them gives t exactly.
+//   top-K: the logits of the qualifying tiles (16 per thread in registers, the
+//   loads issued together) that reach t; when they are at most 64, one wave
+//   ranks them and rank k is candidate k.
+// Ranks count the entries before one in (value desc, index asc) order, so they
+// are distinct and the result is the plain top-K with ties to the lower id.
+// When a set is larger (ties over many tiles), the same result comes from K
+// rounds of wave argmax (each strictly after the previous winner) over the
+// tiles, then over batches of 32 qualifying tiles with a running list.
 constexpr int kMaxTiles = 4096;  // 128-column tiles of a row (vocab <= 524288)
 
 // The K best of one register array per lane (plus one extra entry), strictly
@@ -165,6 +171,45 @@ __device__ __forceinline__ void wave_topk(const float (&v)[N], const int (&ix)[N
   }
 }
 
+// Rank of (v, i) among the n (value, index bits) entries of an LDS list.
+// Reads go out 8 at a time: the list must hold n rounded up to 8 entries
+// (the ones past n are not counted).
+__device__ __forceinline__ int rank_in(const float2* list, int n, float v, int i) {
+  int r = 0;
+  for (int j0 = 0; j0 < n; j0 += 8) {
+    float2 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = list[j0 + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      r += (j0 + u < n && better(o[u].x, __float_as_int(o[u].y), v, i)) ? 1 : 0;
+  }
+  return r;
+}
+
+// This thread's offset for cnt entries in thread order, and the block total.
+// All threads call it; it begins with a barrier (earlier readers of tmp are
+// done) and ends with one (every count is in).
+__device__ __forceinline__ int block_offset(int cnt, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int off = incl - cnt;
+  total = 0;
+  for (int w = 0; w < kT / 64; ++w) {
+    if (w < wave) off += tmp[w];
+    total += tmp[w];
+  }
+  return off;
+}
+
 template <typename T, int K>
 __global__ __launch_bounds__(kT) void topk_tiles_kernel(const T* __restrict__ logits,
                                                         const float2* __restrict__ part, int V,
@@ -174,6 +219,7 @@ __global__ __launch_bounds__(kT) void topk_tiles_kernel(const T* __restrict__ lo
   constexpr int TPT = kMaxTiles / kT;  // tile maxima per thread
   constexpr int TPB = 32;              // qualifying tiles per batch
   constexpr int EPT = TPB * 128 / kT;  // logits per thread per batch
+  constexpr int kRankCap = 64;         // largest set ranked in one pass
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int qt[kMaxTiles];
   __shared__ float wv[NW * K];
@@ -181,6 +227,8 @@ __global__ __launch_bounds__(kT) void topk_tiles_kernel(const T* __restrict__ lo
   __shared__ float lv[K];
   __shared__ int li[K];
   __shared__ int wc[NW];
+  __shared__ float2 cl[kT];  // lane maxima, then candidate tiles, then candidate logits
+  __shared__ float2 bw[NW];
   // tile maxima: tile tid + i * kT in register i (never NaN: the partials map
   // NaN to -inf); absent tiles carry no index
   float tm[TPT];
@@ -191,10 +239,47 @@ __global__ __launch_bounds__(kT) void topk_tiles_kernel(const T* __restrict__ lo
     tm[i] = t < n_tiles ? part[(int64_t)row * n_tiles + t].x : kNegInf;
     ti[i] = t < n_tiles ? t : kNoIdx;
   }
-  wave_topk<K>(tm, ti, kNegInf, kNoIdx, wv + wave * K, wi + wave * K);
+  // lower bound of t: per wave, the lane maximum of rank K - 1
+  float mv = kNegInf;
+  int mi = kNoIdx;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+    if (better(tm[i], ti[i], mv, mi)) {
+      mv = tm[i];
+      mi = ti[i];
+    }
+  cl[tid] = make_float2(mv, __int_as_float(mi));
+  if (lane == 0) bw[wave] = make_float2(kNegInf, __int_as_float(kNoIdx));
+  __syncthreads();
+  if (mi != kNoIdx && rank_in(cl + wave * 64, 64, mv, mi) == K - 1)
+    bw[wave] = make_float2(mv, __int_as_float(mi));
+  __syncthreads();
+  float lb = kNegInf;
+  for (int w = 0; w < NW; ++w) lb = fmaxf(lb, bw[w].x);
+  // candidate tiles (maxima >= lb): at least K of them
+  int cnt0 = 0;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) cnt0 += (ti[i] != kNoIdx && tm[i] >= lb) ? 1 : 0;
+  int nc;
+  int off0 = block_offset(cnt0, wc, nc);
+  if (nc <= kRankCap) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+      if (ti[i] != kNoIdx && tm[i] >= lb) cl[off0++] = make_float2(tm[i], __int_as_float(ti[i]));
+  }
   __syncthreads();
   float thr;
-  {  // every wave merges the NW * K <= 64 entries (one per lane) the same way
+  if (nc <= kRankCap) {
+    // every wave ranks the candidates the same way: rank K - 1 is t (fewer
+    // than K tiles: no bound, every tile qualifies)
+    const float2 me = lane < nc ? cl[lane] : make_float2(kNegInf, __int_as_float(kNoIdx));
+    const bool at = lane < nc && rank_in(cl, nc, me.x, __float_as_int(me.y)) == K - 1;
+    const uint64_t hit = __ballot(at);
+    thr = hit ? __shfl(me.x, __ffsll((unsigned long long)hit) - 1, 64) : kNegInf;
+  } else {
+    wave_topk<K>(tm, ti, kNegInf, kNoIdx, wv + wave * K, wi + wave * K);
+    __syncthreads();
+    // every wave merges the NW * K <= 64 entries (one per lane) the same way
     const float ev = lane < NW * K ? wv[lane] : kNegInf;
     const int ei = lane < NW * K ? wi[lane] : kNoIdx;
     float pv = __builtin_huge_valf();
@@ -234,8 +319,51 @@ __global__ __launch_bounds__(kT) void topk_tiles_kernel(const T* __restrict__ lo
   for (int i = 0; i < TPT; ++i)
     if (ti[i] != kNoIdx && tm[i] >= thr) qt[off++] = ti[i];
   __syncthreads();
-  // batches of qualifying tiles: logit e = tid + i * kT of the batch is column
-  // (tid & 127) of the batch's tile 2 i + (tid >> 7)
+  // logit e = tid + i * kT of a batch of qualifying tiles is column (tid & 127)
+  // of the batch's tile 2 i + (tid >> 7)
+  if (nq <= TPB) {
+    float v[EPT];
+    int ix[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int slot = 2 * i + (tid >> 7);
+      const int col = slot < nq ? qt[slot] * 128 + (tid & 127) : V;
+      v[i] = col < V ? ldf(logits + (int64_t)row * V + col) : kNegInf;
+      ix[i] = col < V ? col : kNoIdx;
+    }
+    // only logits that reach t can be among the K largest (NaN never does)
+    int cnt1 = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) cnt1 += (ix[i] != kNoIdx && v[i] >= thr) ? 1 : 0;
+    int ne;
+    int off1 = block_offset(cnt1, wc, ne);
+    if (ne <= kRankCap) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if (ix[i] != kNoIdx && v[i] >= thr) cl[off1++] = make_float2(v[i], __int_as_float(ix[i]));
+      if (tid < K) {
+        lv[tid] = kNegInf;
+        li[tid] = kNoIdx;
+      }
+      __syncthreads();
+      if (wave == 0 && lane < ne) {
+        const float2 me = cl[lane];
+        const int rk = rank_in(cl, ne, me.x, __float_as_int(me.y));
+        if (rk < K) {
+          lv[rk] = me.x;
+          li[rk] = __float_as_int(me.y);
+        }
+      }
+      __syncthreads();
+      if (tid < K) {
+        const int i = li[tid];
+        cand[(int64_t)row * K + tid] = (i >= 0 && i < V) ? i : 0;
+        unary[(int64_t)row * K + tid] = lv[tid];
+      }
+      return;
+    }
+  }
+  // batches of at most 32 qualifying tiles with a running list
   int n_list = 0;
   for (int b0 = 0; b0 < nq; b0 += TPB) {
     const int nb = min(TPB, nq - b0);
@@ -293,13 +421,19 @@ __global__ __launch_bounds__(kT) void lattice_walk_kernel(
     int S, int K, int V, int32_t* __restrict__ candidates, float* __restrict__ q_rows) {
   constexpr int r = R;
   const int b = blockIdx.x, tid = threadIdx.x, J = S - 1;
-  extern __shared__ float score[];  // [J][K][K], then this request's w rows [J][r]
+  // LDS: score [J][K][K], this request's w rows [J][r], its candidate ids
+  // [J][K] and its uniforms [J] (the walk then reads no global memory)
+  extern __shared__ float score[];
   const int n = J * K * K;
   float* ws = score + n;
+  int* cb = reinterpret_cast<int*>(ws + J * r);
+  float* us = reinterpret_cast<float*>(cb + J * K);
   for (int e = tid; e < J * r; e += kT) ws[e] = w[(int64_t)b * J * r + e];
+  for (int e = tid; e < J * K; e += kT) cb[e] = cand[(int64_t)b * J * K + e];
+  if (uni != nullptr)
+    for (int e = tid; e < J; e += kT) us[e] = uni[(int64_t)b * J + e];
   __syncthreads();
 
-  const int32_t* cb = cand + (int64_t)b * J * K;
   const float* ub = unary + (int64_t)b * J * K;
   const int a0 = min(max(anchor[b], 0), V - 1);
   for (int t = tid; t < n; t += kT) {
@@ -344,7 +478,7 @@ __global__ __launch_bounds__(kT) void lattice_walk_kernel(
     int pick = best;
     if (uni) {
       // inverse CDF: the first slot whose running sum of q exceeds the draw
-      const float x = uni[(int64_t)b * J + j];
+      const float x = us[j];
       const float c = row_incl_scan(q);  // K <= 16: the candidates sit in row 0
       const uint64_t hit = __ballot(lane < K && c > x);
       pick = hit ? __ffsll((unsigned long long)hit) - 1 : K - 1;
@@ -387,7 +521,8 @@ static void lattice_launch(const int32_t* cand, const float* unary, const float*
                            const void* Bt, const int32_t* anchor, const float* uni,
                            float temperature, int B, int S, int K, int V, int32_t* candidates,
                            float* q_rows, hipStream_t st) {
-  const size_t lds = sizeof(float) * ((size_t)(S - 1) * K * K + (size_t)(S - 1) * R);
+  const size_t lds = sizeof(float) * ((size_t)(S - 1) * K * K + (size_t)(S - 1) * R) +
+                     sizeof(int) * (size_t)(S - 1) * K + sizeof(float) * (size_t)(S - 1);
   hipLaunchKernelGGL((lattice_walk_kernel<T, R>), dim3(B), dim3(kT), lds, st, cand, unary, w,
                      static_cast<const T*>(A), static_cast<const T*>(Bt), anchor, uni,
                      temperature, S, K, V, candidates, q_rows);

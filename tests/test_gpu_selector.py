@@ -156,3 +156,24 @@ def test_selector_parity_wide_vocab():
     f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     ids, _ = top_k(f(g["logits"]), K)
     assert np.array_equal(g["cand_ids"].numpy(), ids)
+
+
+def test_selector_topk_many_ties_in_few_tiles():
+    """lm_head rows 0..255 (two tiles) all equal one row, the rest scaled by
+    0.01: in every drafted row whose shared logit is positive, few tiles
+    qualify but they hold 256 logits tied at the top, more than one ranking
+    pass takes; the candidates must still be the oracle's (the lowest ids)."""
+    st = Setup(get_workload("small_bf16_vocab"))
+    W = st.W["lm_head"]
+    row0 = W[0].clone()
+    W.mul_(0.01)
+    W[:256] = row0
+    K = 16
+    _, _, _, sel = _selector(st.cfg, 32, K, 13)
+    g = _run(st, sel, K)
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    lg = f(g["logits"])
+    ids = top_k(lg, K)[0]
+    assert np.array_equal(g["cand_ids"].numpy(), ids)
+    tied = (lg == lg.max(-1, keepdims=True)).sum(-1)
+    assert (tied >= 256).sum() >= 5, tied      # the case occurs in several rows
