@@ -636,6 +636,17 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
 // loads issued before the adds); the two halves are then added in a fixed
 // order, so the result does not depend on timing.
 constexpr int RROWS = 4;
+
+// An epilogue with kPrefetch has fetch(), which loads the inputs its apply()
+// reads for one row per wave (rows <= the workgroup's waves), and apply_pre(),
+// which takes them: the reduce issues fetch() while the partials are in flight.
+template <class E, class = void> struct HasPrefetch {
+  static constexpr bool value = false;
+};
+template <class E> struct HasPrefetch<E, decltype((void)E::kPrefetch)> {
+  static constexpr bool value = E::kPrefetch;
+};
+
 template <int TROWS, class Epi>
 __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, int M,
                                                           const float* __restrict__ partial,
@@ -651,7 +662,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
   const int row = i4 / (BN / 4), c = (i4 % (BN / 4)) * 4;
   const float* p = partial + (int64_t)tix * KS * tile_elems + (int64_t)(rb * RROWS + row) * BN + c;
   // the loads of (up to) the first 32 splits go out first; the epilogue's
-  // own inputs (row scales) are fetched while they are in flight
+  // own inputs (row scales, residual rows) are fetched while they are in flight
   constexpr int QB = 16;
   float4 v[QB];
 #pragma unroll
@@ -659,6 +670,8 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
     v[u] = (h + 2 * u < KS) ? *reinterpret_cast<const float4*>(p + (int64_t)(h + 2 * u) * tile_elems)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
   epi.prepare(RROWS, mt * TROWS + rb * RROWS, M, tid);
+  float pre[4];
+  if constexpr (HasPrefetch<Epi>::value) epi.fetch(RROWS, mt * TROWS + rb * RROWS, M, nt, tid, pre);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int u = 0; u < QB; ++u) {
@@ -685,7 +698,10 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
     t[3] = s.w + o.w;
   }
   __syncthreads();
-  epi.apply(tile, RROWS, mt * TROWS + rb * RROWS, M, nt, tid);
+  if constexpr (HasPrefetch<Epi>::value)
+    epi.apply_pre(tile, RROWS, mt * TROWS + rb * RROWS, M, nt, tid, pre);
+  else
+    epi.apply(tile, RROWS, mt * TROWS + rb * RROWS, M, nt, tid);
 }
 
 // ---------------------------------------------------------------- epilogues
@@ -693,17 +709,18 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce(int KS, int m_tiles, i
 // Row-wise pass over a [rows, 128] fp32 tile (one wave per row, two columns per
 // lane); f returns the value stored for (row, col), whose squares are summed
 // into the row's partial sum of squares over the tile when ss != null.
+// gpre: the next norm's gains at the lane's two columns, already loaded (or null).
 template <typename T, typename FL, typename F>
 __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N, int tid,
                                          float* ss, int n_ss, const NextNorm<T>& nn, FL&& in,
-                                         F&& f) {
+                                         F&& f, const float* gpre = nullptr) {
   const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
   float gn[2] = {0.f, 0.f};  // the next norm's gain at this lane's two columns
   if (nn.xg != nullptr) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int n = nt * BN + lane + 64 * h;
-      gn[h] = n < N ? Num<T>::to_f(nn.g[n]) : 0.f;
+      gn[h] = gpre != nullptr ? gpre[h] : (n < N ? Num<T>::to_f(nn.g[n]) : 0.f);
     }
   }
   // rows in groups of 4 per wave: the group's input loads go out before any
@@ -775,6 +792,29 @@ template <typename T> struct EpiResidual {
                x[(int64_t)m * N + n] = v;
                return v;
              });
+  }
+  // pre = the residual at row m0 + wave, columns nt * BN + lane (+ 64), then
+  // the next norm's gains there (for_rows reads exactly these when rows <= waves)
+  static constexpr bool kPrefetch = true;
+  __device__ void fetch(int rows, int m0, int M, int nt, int tid, float (&pre)[4]) const {
+    const int lane = tid & 63, wave = tid >> 6, m = m0 + wave;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = nt * BN + lane + 64 * h;
+      pre[h] = (wave < rows && m < M && n < N) ? x[(int64_t)m * N + n] : 0.f;
+      pre[2 + h] = (nn.xg != nullptr && n < N) ? Num<T>::to_f(nn.g[n]) : 0.f;
+    }
+  }
+  __device__ void apply_pre(const float* t, int rows, int m0, int M, int nt, int tid,
+                            const float (&pre)[4]) const {
+    for_rows(rows, m0, M, nt, N, tid, ss, ss_tiles(N), nn,
+             [&](int, int n) { return n - nt * BN >= 64 ? pre[1] : pre[0]; },
+             [&](int r, int c, int m, int n, float res) {
+               const float v = res + t[r * LDT + c];
+               x[(int64_t)m * N + n] = v;
+               return v;
+             },
+             pre + 2);
   }
 };
 
