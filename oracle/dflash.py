@@ -216,6 +216,23 @@ def accept(candidates, posterior, prefix_len):
             "next_anchor": bonus, "new_seq_len": L + commit}
 
 
+def greedy_posterior(target_logits):
+    """The target's greedy token at every verified position ("Inside SGLang
+    ...", Step 6: the verify forward's logits give the target's choice after
+    each block position): the first index among equal maxima over the
+    vocabulary.  Reading: a NaN logit never wins (it counts as -inf, so a row
+    of only NaN and -inf gives index 0).  target_logits [..., V] -> [...]."""
+    x = np.asarray(target_logits, np.float64)
+    x = np.where(np.isnan(x), -np.inf, x)
+    return np.argmax(x, axis=-1)
+
+
+def accept_logits(candidates, target_logits, prefix_len):
+    """Greedy verify-accept reading the target's logits [B, S, V] instead of
+    its greedy ids: accept() against greedy_posterior(target_logits)."""
+    return accept(candidates, greedy_posterior(target_logits), prefix_len)
+
+
 def speculative_decode(cfg, W, num_slots, page_table, prompt_tokens, max_new,
                        target_next, target_feat):
     """The decode loop for one request with a stand-in target (CSDN article,

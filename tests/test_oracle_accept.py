@@ -117,3 +117,38 @@ def test_kv_bytes_per_token_kimi():
     g = GOLD["kv_bytes_per_token"]
     assert KIMI_DRAFT.n_layers == g["layers"] and KIMI_DRAFT.n_kv_heads == g["kv_heads"]
     assert KIMI_DRAFT.kv_bytes_per_token == g["bytes"]
+
+
+def test_greedy_posterior_ties_and_nan():
+    """First index among equal maxima; NaN never wins; a row of only NaN and
+    -inf gives index 0."""
+    x = np.array([[0.5, 2.0, 2.0, -1.0],
+                  [np.nan, 0.0, np.nan, 0.0],
+                  [np.nan, np.nan, np.nan, np.nan],
+                  [-np.inf, np.nan, -np.inf, -np.inf],
+                  [-3.0, -2.0, -2.5, np.inf]])
+    assert oracle.greedy_posterior(x).tolist() == [1, 1, 0, 0, 3]
+
+
+@pytest.mark.parametrize("S", [2, 5, 16])
+def test_accept_logits_reproduces_planted_posteriors(S):
+    """Logits that put one clear maximum on a planted posterior id per position
+    (every other logit below it) give that posterior, so the commit lengths
+    planted through the candidates come back exactly."""
+    rng = np.random.default_rng(S)
+    B, V = 40, 97
+    post = rng.integers(0, V, (B, S))
+    commit = rng.integers(1, S + 1, B)
+    cand = rng.integers(0, V, (B, S))
+    for r in range(B):
+        c = commit[r]
+        cand[r, 1:c] = post[r, :c - 1]
+        if c < S and cand[r, c] == post[r, c - 1]:
+            cand[r, c] = (post[r, c - 1] + 1) % V
+    logits = -np.abs(rng.normal(0, 1, (B, S, V))) - 0.01
+    logits[np.arange(B)[:, None], np.arange(S)[None, :], post] = rng.uniform(0, 3, (B, S))
+    L = rng.integers(0, 1000, B)
+    out = oracle.accept_logits(cand, logits, L)
+    assert np.array_equal(out["commit_len"], commit)
+    assert np.array_equal(out["next_anchor"], post[np.arange(B), commit - 1])
+    assert np.array_equal(out["new_seq_len"], L + commit)
