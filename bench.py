@@ -210,6 +210,8 @@ def main():
     # [B, S, V], the draft pass's own logits [B, S-1, V] as the proposal q
     sv = sampling_verify(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, c_cfg,
                          c_cache, timed, max(args.steps, 10), dev)
+    # greedy accept reading the target's logits [B, S, V] (fused argmax)
+    al = accept_from_logits(dfl, synth, cfg, wl, Ld, timed, max(args.steps, 10), dev)
     # the same pass with the DFlash 2 candidate selector (top-8, rank 64)
     sel = selector_pass(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, timed,
                         args.steps, dev, ms_draft)
@@ -261,6 +263,7 @@ def main():
                      "bytes_per_launch": lm_bytes,
                      "avg_launch_us": round(lm_avg_s * 1e6, 2)},
         "sampling_verify": sv,
+        "accept_logits": al,
         "selector_pass": sel,
         "cpu_baseline": None,
     }
@@ -305,6 +308,31 @@ def sampling_verify(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix,
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "mean_commit": round(float(outs[1].float().mean()), 3)}
     return res
+
+
+def accept_from_logits(dfl, synth, cfg, wl, Ld, timed, n, dev):
+    """Time dflash_accept_logits at the workload's batch on synthetic target
+    logits [B, S, V].  Algorithmic bytes: every logit read once, plus ids and
+    outputs."""
+    import torch
+    B, S, V = wl.batch, cfg.block_size, cfg.vocab
+    dt = synth._DT[cfg.act_dtype]
+    vc, tl, _, _ = synth.verify_inputs(B, S, V, wl.seed, dtype=dt, device=dev, bump=22.0,
+                                       bump_lo=13.0)
+    outs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
+    ot = torch.empty((B, S), dtype=torch.int32, device=dev)
+    ws = dfl.workspace(dfl.accept_logits_workspace_bytes(B, S, V))
+
+    def call():
+        dfl.dflash_accept_logits(vc, tl, Ld, outs[0], outs[1], ot, outs[2], outs[3], ws)
+    call()
+    ms = timed(call, n)
+    esz = 2 if cfg.act_dtype == "bf16" else 4
+    nbytes = B * S * V * esz + B * S * 8 + B * 20
+    return {"us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mean_commit": round(float(outs[1].float().mean()), 3)}
 
 
 def selector_pass(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, timed, n, dev,

@@ -72,6 +72,7 @@ class CKVCache(ctypes.Structure):
 
 EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
+            "dflash_accept_logits_workspace_bytes", "dflash_accept_logits",
             "dflash_accept_sampling_workspace_bytes", "dflash_accept_sampling",
             "dflash_selector_workspace_bytes", "dflash_draft_block_selector",
             "dflash_accept_sampling_sparse", "dflash_reserve_pages", "dflash_release_pages",
@@ -101,6 +102,10 @@ def _load():
     lib.dflash_draft_block.restype = I32
     lib.dflash_accept.argtypes = [P, P, P, I32, I32, P, P, P, P, P, P]
     lib.dflash_accept.restype = I32
+    lib.dflash_accept_logits_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.dflash_accept_logits_workspace_bytes.restype = SZ
+    lib.dflash_accept_logits.argtypes = [P, P, I32, I32, P, I32, I32, P, P, P, P, P, P, SZ, P]
+    lib.dflash_accept_logits.restype = I32
     lib.dflash_accept_sampling_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.dflash_accept_sampling_workspace_bytes.restype = SZ
     F = ctypes.c_float
@@ -308,6 +313,28 @@ def accept_sampling_workspace_bytes(batch: int, block_size: int, vocab: int,
 
 
 _LOGITS_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def accept_logits_workspace_bytes(batch: int, block_size: int, vocab: int) -> int:
+    return int(_lib.dflash_accept_logits_workspace_bytes(int(batch), int(block_size), int(vocab)))
+
+
+def dflash_accept_logits(candidates: torch.Tensor, target_logits: torch.Tensor,
+                         prefix_len: torch.Tensor, accept_len: torch.Tensor,
+                         commit_len: torch.Tensor, out_tokens: torch.Tensor,
+                         next_anchor: torch.Tensor, new_seq_len: torch.Tensor, ws: torch.Tensor,
+                         stream=None):
+    """Greedy accept against the argmax of target_logits [B, S, V] (f32 or bf16);
+    ws from workspace(accept_logits_workspace_bytes())."""
+    B, S = candidates.shape
+    V = int(target_logits.shape[-1])
+    dt = _LOGITS_DT.get(target_logits.dtype)
+    if dt is None:
+        raise DFlashError(-2, f"logits dtype {target_logits.dtype} (supported: f32, bf16)")
+    _check(_lib.dflash_accept_logits(
+        _ptr(candidates), _ptr(target_logits), dt, V, _ptr(prefix_len), int(B), int(S),
+        _ptr(accept_len), _ptr(commit_len), _ptr(out_tokens), _ptr(next_anchor),
+        _ptr(new_seq_len), _ptr(ws), int(ws.numel()), _stream(stream)))
 
 
 def dflash_accept_sampling(candidates: torch.Tensor, target_logits: torch.Tensor,

@@ -640,6 +640,45 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
   return DFLASH_OK;
 }
 
+size_t dflash_accept_logits_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab) {
+  if (batch <= 0 || block_size < 2 || block_size > 64 || vocab <= 0 || vocab > 524288) return 0;
+  return sizeof(float2) * (size_t)batch * block_size * accept_logits_chunks(vocab);
+}
+
+dflash_status dflash_accept_logits(const int32_t* candidates, const void* target_logits,
+                                   int32_t logits_dtype, int32_t vocab,
+                                   const int32_t* prefix_len, int32_t batch, int32_t block_size,
+                                   int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                                   int32_t* next_anchor, int32_t* new_seq_len, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(DFLASH_EINVAL, "batch %d < 0", batch);
+  if (block_size < 2 || block_size > 64)
+    return fail(DFLASH_EUNSUPPORTED, "block_size %d outside 2..64", block_size);
+  if (vocab <= 0) return fail(DFLASH_EINVAL, "vocab %d <= 0", vocab);
+  if (vocab > 524288) return fail(DFLASH_EUNSUPPORTED, "vocab %d > 524288", vocab);
+  if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16)
+    return fail(DFLASH_EUNSUPPORTED, "logits_dtype %d (supported: F32, BF16)", logits_dtype);
+  if ((int64_t)batch * block_size > (int64_t)1 << 24)
+    return fail(DFLASH_EUNSUPPORTED, "batch %d too large", batch);
+  if (batch == 0) return DFLASH_OK;
+  if (!candidates || !target_logits || !prefix_len || !accept_len || !commit_len || !out_tokens ||
+      !next_anchor || !new_seq_len)
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  const size_t need = dflash_accept_logits_workspace_bytes(batch, block_size, vocab);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
+  // 16-byte loads when every run of 8 columns starts on a 16-byte boundary
+  const bool vec = vocab % 8 == 0 && aligned16(target_logits);
+  hipError_t e = launch_accept_logits(logits_dtype, target_logits, vocab, vec, candidates,
+                                      prefix_len, batch, block_size,
+                                      static_cast<float2*>(workspace), accept_len, commit_len,
+                                      out_tokens, next_anchor, new_seq_len,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "accept from logits");
+  return DFLASH_OK;
+}
+
 size_t dflash_accept_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab,
                                               int32_t has_draft_logits) {
   if (batch <= 0 || block_size < 2 || block_size > 64 || vocab <= 0 || vocab > 524288) return 0;

@@ -108,6 +108,15 @@ hipError_t launch_argmax_reduce(const float2* part, int M, int n_tiles, int S, i
 hipError_t launch_accept(const int32_t* cand, const int32_t* post, const int32_t* prefix_len, int B,
                          int S, int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
                          int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st);
+// greedy accept from target logits [B, S, V] (dt F32 or BF16): chunked row
+// argmax into part [B * S * accept_logits_chunks(V)], then the accept; vec:
+// every run of 8 columns starts on a 16-byte boundary (V % 8 == 0 and an
+// aligned base)
+int accept_logits_chunks(int V);
+hipError_t launch_accept_logits(int dt, const void* logits, int V, bool vec, const int32_t* cand,
+                                const int32_t* prefix_len, int B, int S, float2* part,
+                                int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                                int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st);
 
 // ---- rejection-sampling verify (sampling.hip)
 // Vocabulary chunking and workspace layout: stats partials (max, sum) per

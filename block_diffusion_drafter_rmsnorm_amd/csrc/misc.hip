@@ -201,4 +201,143 @@ hipError_t launch_accept(const int32_t* cand, const int32_t* post, const int32_t
   return hipGetLastError();
 }
 
+// ---- greedy accept from the target's logits ("Inside SGLang ...", Step 6:
+// the target's choice after each block position is the argmax of its verify
+// logits).  Row argmax in chunks of 16384 columns, one workgroup per (row,
+// chunk): 256 threads x 8 runs of 8 consecutive columns (one 16-byte load per
+// run of bf16, two of fp32; every load of the chunk issued before any compare,
+// kept raw until then); NaN counts as -inf, ties go to the lower column.
+// part[row * n_chunks + chunk] = (max, column bits).
+template <typename T> struct ArgRuns {
+  static constexpr int RUNS = 8;
+  static constexpr int CHUNK = 256 * 8 * RUNS;  // columns per workgroup
+};
+
+__device__ __forceinline__ bool arg_better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void row_argmax_kernel(const T* __restrict__ x, int V,
+                                                         int n_chunks, float2* __restrict__ part) {
+  constexpr int RUNS = ArgRuns<T>::RUNS, CHUNK = ArgRuns<T>::CHUNK;
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int row = blockIdx.x / n_chunks, ch = blockIdx.x % n_chunks, tid = threadIdx.x;
+  const T* xr = x + (int64_t)row * V;
+  const int c0 = ch * CHUNK;
+  Raw8<T> raw[RUNS];
+#pragma unroll
+  for (int i = 0; i < RUNS; ++i) {
+    const int col = c0 + (i * 256 + tid) * 8;
+    if (VEC && col + 8 <= V) raw[i].load(xr + col);
+  }
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < RUNS; ++i) {
+    const int col = c0 + (i * 256 + tid) * 8;
+    float v[8];
+    if (VEC && col + 8 <= V) {
+      raw[i].to_f(v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = col + k < V ? Num<T>::to_f(xr[col + k]) : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float val = v[k] == v[k] ? v[k] : -INFINITY;
+      if (col + k < V && arg_better(val, col + k, bv, bi)) {
+        bv = val;
+        bi = col + k;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (arg_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if ((tid & 63) == 0) {
+    rv[tid >> 6] = bv;
+    ri[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (arg_better(rv[w], ri[w], bv, bi)) {
+        bv = rv[w];
+        bi = ri[w];
+      }
+    part[blockIdx.x] = make_float2(bv, __int_as_float(bi));
+  }
+}
+
+// One wave per request: lane j < S merges row j's chunk partials in chunk
+// order (the target's greedy token after position j); the first mismatch
+// between d_{j+1} and that token (a ballot) ends the accepted prefix.
+__global__ __launch_bounds__(64) void accept_logits_kernel(
+    const int32_t* __restrict__ cand, const float2* __restrict__ part, int n_chunks,
+    const int32_t* __restrict__ prefix_len, int S, int32_t* accept_len, int32_t* commit_len,
+    int32_t* out_tokens, int32_t* next_anchor, int32_t* new_seq_len) {
+  const int r = blockIdx.x, j = threadIdx.x;
+  int post = 0;
+  if (j < S) {
+    const float2* p = part + ((int64_t)r * S + j) * n_chunks;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float2 q = p[c];
+      if (arg_better(q.x, __float_as_int(q.y), bv, bi)) {
+        bv = q.x;
+        bi = __float_as_int(q.y);
+      }
+    }
+    post = bi;
+  }
+  const int32_t* c = cand + (int64_t)r * S;
+  const uint64_t mism = __ballot(j < S - 1 && c[j < S - 1 ? j + 1 : 0] != post);
+  const int a = mism ? __ffsll((unsigned long long)mism) - 1 : S - 1;
+  const int pa = __shfl(post, a, 64);
+  if (j < S) out_tokens[(int64_t)r * S + j] = j < a ? c[j + 1] : (j == a ? pa : 0);
+  if (j == 0) {
+    accept_len[r] = a;
+    commit_len[r] = a + 1;
+    next_anchor[r] = pa;
+    new_seq_len[r] = prefix_len[r] + a + 1;
+  }
+}
+
+int accept_logits_chunks(int V) {
+  return (V + ArgRuns<float>::CHUNK - 1) / ArgRuns<float>::CHUNK;
+}
+
+hipError_t launch_accept_logits(int dt, const void* logits, int V, bool vec, const int32_t* cand,
+                                const int32_t* prefix_len, int B, int S, float2* part,
+                                int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                                int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  const int chunk = dt == DFLASH_BF16 ? ArgRuns<bf16_t>::CHUNK : ArgRuns<float>::CHUNK;
+  const int nc = (V + chunk - 1) / chunk;
+  const dim3 grid((unsigned)((int64_t)B * S * nc));
+  if (dt == DFLASH_BF16) {
+    const bf16_t* x = static_cast<const bf16_t*>(logits);
+    if (vec) hipLaunchKernelGGL((row_argmax_kernel<bf16_t, true>), grid, dim3(256), 0, st, x, V, nc, part);
+    else hipLaunchKernelGGL((row_argmax_kernel<bf16_t, false>), grid, dim3(256), 0, st, x, V, nc, part);
+  } else {
+    const float* x = static_cast<const float*>(logits);
+    if (vec) hipLaunchKernelGGL((row_argmax_kernel<float, true>), grid, dim3(256), 0, st, x, V, nc, part);
+    else hipLaunchKernelGGL((row_argmax_kernel<float, false>), grid, dim3(256), 0, st, x, V, nc, part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_logits_kernel, dim3(B), dim3(64), 0, st, cand, part, nc, prefix_len, S,
+                     accept_len, commit_len, out_tokens, next_anchor, new_seq_len);
+  return hipGetLastError();
+}
+
 }  // namespace dflash

@@ -247,6 +247,27 @@ dflash_status dflash_accept(const int32_t* candidates, const int32_t* posterior,
                             int32_t* next_anchor, int32_t* new_seq_len, void* stream);
 
 /*
+ * (3a) Greedy verify-accept reading the target's logits ("Inside SGLang ...",
+ * Step 6: the verify forward's logits give the target's greedy choice after
+ * each block position): posterior[r, j] = the first index among the largest
+ * values of target_logits[r, j] (a NaN logit never wins), then exactly
+ * dflash_accept.  The argmax runs on the GPU in chunks of 16384 columns.
+ *   candidates     [batch, block_size]
+ *   target_logits  [batch, block_size, vocab] logits_dtype (F32 or BF16)
+ *   prefix_len and the outputs as dflash_accept
+ *   workspace      >= dflash_accept_logits_workspace_bytes(batch, block_size,
+ *                  vocab), 16-byte aligned
+ * Bit-exact integer results; block_size 2..64; vocab <= 524288.
+ */
+size_t dflash_accept_logits_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab);
+dflash_status dflash_accept_logits(const int32_t* candidates, const void* target_logits,
+                                   int32_t logits_dtype, int32_t vocab,
+                                   const int32_t* prefix_len, int32_t batch, int32_t block_size,
+                                   int32_t* accept_len, int32_t* commit_len, int32_t* out_tokens,
+                                   int32_t* next_anchor, int32_t* new_seq_len, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * (3') Rejection-sampling verify-accept and commit ("Inside SGLang ...", the
  * section on sampling with the proposal distribution the drafter used, and
  * Step 6 for the outputs; CSDN DFlash article, SGLang flow step 7: non-greedy

@@ -193,6 +193,28 @@ def test_selector_argument_errors():
         fake, fake, fake, 64, 8)})(), 1, 64) > dfl.draft_workspace_bytes(TINY, 1, 64)
 
 
+def test_accept_logits_argument_errors():
+    """Host-visible errors of dflash_accept_logits come back before any launch
+    (every call below fails a check, or has nothing to do)."""
+    lib = dfl.raw_lib()
+    F = ctypes.c_void_p(0x100000)
+
+    def call(B=2, S=4, V=1000, dt=dfl.BF16, cand=F, ws=F, wsb=1 << 30):
+        return lib.dflash_accept_logits(cand, F, dt, V, F, B, S, F, F, F, F, F, ws, wsb, None)
+
+    assert call(B=0) == 0
+    assert call(B=-1) == -1
+    assert call(S=1) == -2 and call(S=65) == -2
+    assert call(V=0) == -1 and call(V=524289) == -2
+    assert call(dt=dfl.FP8_E4M3) == -2
+    assert call(cand=None) == -1
+    assert call(wsb=16) == -3 and b"workspace" in lib.dflash_last_error()
+    assert call(ws=ctypes.c_void_p(0x100004)) == -1
+    # one (max, index) partial per row and 16384-column chunk
+    assert dfl.accept_logits_workspace_bytes(32, 16, 151936) == 8 * 32 * 16 * 10
+    assert dfl.accept_logits_workspace_bytes(0, 16, 151936) == 0
+
+
 def test_accept_sampling_sparse_argument_errors():
     lib = dfl.raw_lib()
     F = ctypes.c_void_p(0x100000)

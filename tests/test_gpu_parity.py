@@ -67,6 +67,68 @@ def test_accept_bitexact(S):
     assert np.array_equal(o["commit_len"][B // 4:], commit[B // 4:].numpy())
 
 
+def _accept_logits_case(B, S, V, dtype, seed, ties=False, nan_rows=0, offset=0):
+    """Seeded target logits (torch generator on the host), candidates planted
+    from the oracle's posterior so every commit length 1..S occurs, and the
+    GPU's five outputs compared with oracle.accept_logits element by element."""
+    m = dfl()
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((B, S, V), generator=g) * 3.0
+    if ties:                                   # few distinct values: ties across chunks
+        x = torch.round(x)
+    if nan_rows:
+        x.view(B * S, V)[:nan_rows, ::3] = float("nan")
+        x.view(B * S, V)[nan_rows:2 * nan_rows] = float("nan")   # rows of NaN only
+    x = x.to(dtype)
+    post = oracle.greedy_posterior(x.float().numpy())
+    commit = torch.randint(1, S + 1, (B,), generator=g).numpy()
+    cand = torch.randint(0, V, (B, S), generator=g, dtype=torch.int32).numpy()
+    for r in range(B):
+        c = commit[r]
+        cand[r, 1:c] = post[r, :c - 1]
+        if c < S and cand[r, c] == post[r, c - 1]:
+            cand[r, c] = (post[r, c - 1] + 1) % V
+    L = torch.randint(0, 100000, (B,), generator=g, dtype=torch.int32)
+    # an offset view makes the rows start off a 16-byte boundary
+    buf = torch.empty(B * S * V + offset, dtype=dtype, device="cuda")
+    xd = buf[offset:].view(B, S, V)
+    xd.copy_(x.cuda())
+    outs = [torch.full((B,), -7, dtype=torch.int32, device="cuda") for _ in range(4)]
+    out_tok = torch.full((B, S), -7, dtype=torch.int32, device="cuda")
+    ws = m.workspace(m.accept_logits_workspace_bytes(B, S, V))
+    m.dflash_accept_logits(torch.from_numpy(cand).cuda(), xd, L.cuda(), outs[0], outs[1], out_tok,
+                           outs[2], outs[3], ws)
+    torch.cuda.synchronize()
+    o = oracle.accept_logits(cand, x.float().numpy(), L.numpy())
+    assert np.array_equal(outs[0].cpu().numpy(), o["accept_len"])
+    assert np.array_equal(outs[1].cpu().numpy(), o["commit_len"])
+    assert np.array_equal(out_tok.cpu().numpy(), o["out_tokens"])
+    assert np.array_equal(outs[2].cpu().numpy(), o["next_anchor"])
+    assert np.array_equal(outs[3].cpu().numpy(), o["new_seq_len"])
+    assert np.array_equal(o["commit_len"], commit)
+    return o
+
+
+@pytest.mark.parametrize("B,S,V,dtype", [(7, 4, 1000, torch.float32), (3, 16, 4096, torch.bfloat16),
+                                         (5, 2, 1003, torch.bfloat16), (2, 64, 20000, torch.float32),
+                                         (4, 8, 40001, torch.bfloat16)])
+def test_accept_logits_bitexact(B, S, V, dtype):
+    _accept_logits_case(B, S, V, dtype, seed=B * 1000 + S)
+
+
+def test_accept_logits_ties_nan_and_misaligned_rows():
+    # rounded logits tie within and across 16384-column chunks; NaN never wins
+    _accept_logits_case(6, 8, 50000, torch.bfloat16, seed=5, ties=True, nan_rows=4)
+    # rows that start off a 16-byte boundary take the element-wise loads
+    _accept_logits_case(5, 4, 8192, torch.bfloat16, seed=6, offset=3)
+    _accept_logits_case(5, 4, 8192, torch.float32, seed=7, offset=1, ties=True)
+
+
+def test_accept_logits_full_size():
+    """The batch-32, block-16, vocabulary-151936 shape in bf16."""
+    _accept_logits_case(32, 16, 151936, torch.bfloat16, seed=11)
+
+
 # ---------------------------------------------------------------- weight packing
 def _packed_reference(w):
     """The packed layout written out from its definition: record l of chunk c
