@@ -170,6 +170,22 @@ def main():
     ms_draft = timed(draft, args.steps)
     log(f"[bench] step {ms_step:.3f} ms, draft pass {ms_draft:.3f} ms")
 
+    # spread of single draft passes: an event pair around each call (the mean
+    # above is the back-to-back figure; these include one event gap each)
+    def per_call(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    one = per_call(draft, max(args.steps, 20))
+    pct = lambda q: round(one[min(len(one) - 1, int(q * len(one)))], 4)  # noqa: E731
+
     # dominant kernel: lm_head GEMM + argmax partials over the B*(S-1) rows,
     # timed alone on the same shapes: back-to-back calls between two events on
     # the stream they run on (the launch is the GEMM plus the ~5 us second
@@ -249,7 +265,9 @@ def main():
                        "drafted_tokens_per_s": round(B * (S - 1) / (ms_draft * 1e-3), 1),
                        "algorithmic_bytes": pass_bytes,
                        "hbm_gbs": round(pass_bytes / (ms_draft * 1e-3) / 1e9, 1),
-                       "hbm_frac": round(pass_bytes / (ms_draft * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                       "hbm_frac": round(pass_bytes / (ms_draft * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "single_call_ms": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9),
+                                          "calls": len(one)}},
         "context_injection": {"rows": T, "ms": round(ms_inj, 4),
                               "context_tokens_per_s": round(T / (ms_inj * 1e-3), 1),
                               "tflops": round(inj_flops / (ms_inj * 1e-3) / 1e12, 2),
