@@ -33,7 +33,18 @@ def plant(cand, commit, rand_ids, V):
     return torch.where(fix, (cnext + 1) % V, post).to(torch.int32)
 
 
-def test_device_resident_cycles_match_oracle():
+def logits_for(post, noise):
+    """Target logits whose greedy choice is `post`: seeded values below 0 and
+    1.0 at the planted id of every position (test plumbing, either device)."""
+    x = noise.to(post.device).clone()
+    x.scatter_(2, post.long()[..., None], 1.0)
+    return x
+
+
+@pytest.mark.parametrize("via_logits", [False, True])
+def test_device_resident_cycles_match_oracle(via_logits):
+    """via_logits: the accept reads the target's logits [B, S, V]
+    (dflash_accept_logits / oracle.accept_logits) instead of its greedy ids."""
     import block_diffusion_drafter_rmsnorm_amd as m
     wl = dataclasses.replace(get_workload("tiny_f32"), batch=3, ctx=(40, 70))
     cfg = wl.cfg
@@ -47,6 +58,8 @@ def test_device_resident_cycles_match_oracle():
     commits = [torch.tensor(rng.integers(1, S + 1, B), dtype=torch.int32) for _ in range(cycles)]
     rand_ids = [synth.randint(0, V - 1, (B, S), c, "loop_post") for c in range(cycles)]
     feats = [synth.features(B * S, cfg, 100 + c) for c in range(cycles)]
+    noise = [-torch.rand((B, S, V), generator=torch.Generator().manual_seed(50 + c)) - 0.01
+             for c in range(cycles)]
     max_prefix = int(L0.max()) + cycles * S
 
     # ---------------------------------------------------------------- GPU
@@ -61,6 +74,7 @@ def test_device_resident_cycles_match_oracle():
     cw = st.c_weights()
     dws = m.workspace(m.draft_workspace_bytes(cfg, B, max_prefix))
     cws = m.workspace(m.context_workspace_bytes(cfg, B * S))
+    aws = m.workspace(m.accept_logits_workspace_bytes(B, S, V))
     rec = []
     for c in range(cycles):
         pos = torch.empty((B, S), dtype=torch.int32, device=dev)
@@ -69,7 +83,11 @@ def test_device_resident_cycles_match_oracle():
         post = plant(cand, commits[c], rand_ids[c], V)
         acc = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(4)]
         out = torch.empty((B, S), dtype=torch.int32, device=dev)
-        m.dflash_accept(cand, post, Ld, acc[0], acc[1], out, acc[2], acc[3])
+        if via_logits:
+            m.dflash_accept_logits(cand, logits_for(post, noise[c]), Ld, acc[0], acc[1], out,
+                                   acc[2], acc[3], aws)
+        else:
+            m.dflash_accept(cand, post, Ld, acc[0], acc[1], out, acc[2], acc[3])
         m.dflash_project_context(cfg, cw, st.cache, feats[c].to(dev), pos.view(-1),
                                  slots.view(-1), acc[1], B, S, cws)
         m.dflash_reserve_pages(acc[3], S, P, pt, npg, stack, top, status)
@@ -96,7 +114,11 @@ def test_device_resident_cycles_match_oracle():
         gcand, gout, gcommit, gL = (t.cpu().numpy() for t in rec[c])
         assert np.array_equal(gcand, d["candidates"]), c
         post = plant(torch.from_numpy(d["candidates"]), commits[c], rand_ids[c], V).numpy()
-        a = oracle.accept(d["candidates"], post, L)
+        if via_logits:
+            a = oracle.accept_logits(d["candidates"],
+                                     logits_for(torch.from_numpy(post), noise[c]).numpy(), L)
+        else:
+            a = oracle.accept(d["candidates"], post, L)
         assert np.array_equal(gout, a["out_tokens"]) and np.array_equal(gL, a["new_seq_len"])
         assert np.array_equal(gcommit, commits[c].numpy())
         oracle.project_context(cfg, W, oc, feats[c].numpy(), d["positions"].ravel(),
