@@ -16,6 +16,18 @@ from workloads.configs import TINY, SMALL_F32_D64
 from tests.helpers import np_weights
 
 
+def _hf_window_visible(q_pos, k_pos, window):
+    """Visibility of key positions to query positions under transformers' own
+    sliding-window rule (masking_utils.sliding_window_overlay, the overlay its
+    sliding-window causal masks are built from), evaluated elementwise: an
+    independent statement of the window boundary, not the oracle's."""
+    from transformers.masking_utils import sliding_window_overlay
+    keep = sliding_window_overlay(int(window))
+    qp = torch.as_tensor(np.asarray(q_pos, np.int64))[:, None]
+    kp = torch.as_tensor(np.asarray(k_pos, np.int64))[None, :]
+    return keep(0, 0, qp, kp)
+
+
 # ---------------------------------------------------------------- primitives
 def test_rms_norm_matches_torch():
     rng = np.random.default_rng(0)
@@ -68,7 +80,7 @@ def test_block_attention_matches_torch_sdpa(window):
     vals = vals.repeat_interleave(nq // nkv, 0)
     mask = torch.ones(S, n + S, dtype=torch.bool)
     if window:
-        mask[:, :n] = torch.from_numpy((qpos[:, None] - cpos[None, :]) < window)
+        mask[:, :n] = _hf_window_visible(qpos, cpos, window)
     ref = Fnn.scaled_dot_product_attention(torch.from_numpy(q).permute(1, 0, 2), keys, vals,
                                            attn_mask=mask, is_causal=False)
     assert np.allclose(o, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
@@ -99,6 +111,72 @@ def test_block_attention_bruteforce_loops():
             tot = sum(e)
             ref = sum((ei / tot) * v for ei, v in zip(e, vs))
             assert np.allclose(o[j, h], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 5, 12])
+def test_block_attention_window_boundary_keys(window):
+    """The window boundary itself: with zero queries every visible key gets
+    the same weight, and one-hot values read back which keys were visible.
+    For the query at position p the context key at p - W must be invisible and
+    the one at p - W + 1 visible (transformers' sliding_window_overlay); every
+    other key agrees with that overlay too."""
+    S, nq, nkv, D, n = 3, 2, 1, 40, 30
+    cpos = np.arange(n) + 7
+    qpos = np.arange(S) + n + 7
+    q = np.zeros((S, nq, D))
+    kc = np.zeros((n, nkv, D))
+    kb = np.zeros((S, nkv, D))
+    vc = np.zeros((n, nkv, D))
+    vb = np.zeros((S, nkv, D))
+    for i in range(n):
+        vc[i, 0, i] = 1.0
+    for j in range(S):
+        vb[j, 0, n + j] = 1.0
+    o = block_attention(q, kc, vc, cpos, kb, vb, qpos, window)
+    hf = _hf_window_visible(qpos, cpos, window).numpy()
+    for j in range(S):
+        seen = o[j, 0, :n] > 0
+        assert np.array_equal(seen, hf[j])
+        assert np.all(o[j, 0, n:n + S] > 0)          # every block key, always
+        p = qpos[j]
+        i_out, i_in = p - window - cpos[0], p - window + 1 - cpos[0]
+        if 0 <= i_out < n:
+            assert not seen[i_out]
+        if 0 <= i_in < n:
+            assert seen[i_in]
+        assert np.isclose(o[j, 0].sum(), 1.0, rtol=1e-12)
+
+
+def test_draft_window_boundary_rows():
+    """At the draft-pass level, on a sliding layer placed first (so that what
+    the anchor row sees there reaches every drafted row through the block keys
+    of the next layer): the cached rows before position L - W + 1 are never
+    read (NaN there leaves the logits unchanged), and the row at L - W + 1 is
+    read (changing it changes the logits)."""
+    Wwin = 33
+    cfg = dataclasses.replace(SMALL_F32_D64, sliding_window=(Wwin, 0))
+    Lr = 61
+    W, pt, npages = _setup(cfg, L=(Lr,))
+    cache = _ctx_cache(cfg, W, pt, npages, [Lr])
+    base = oracle.draft_block(cfg, W, cache, [5], [Lr], pt)["logits"]
+    P = cfg.page_size
+
+    def slot(i):
+        return pt[0, i // P] * P + i % P
+
+    first = Lr - Wwin + 1
+    poisoned = oracle.OracleCache(cfg, npages * P)
+    for l in range(cfg.n_layers):
+        poisoned.k[l][:] = cache.k[l]
+        poisoned.v[l][:] = cache.v[l]
+    for i in range(first):
+        poisoned.k[0][slot(i)] = np.nan
+        poisoned.v[0][slot(i)] = np.nan
+    got = oracle.draft_block(cfg, W, poisoned, [5], [Lr], pt)["logits"]
+    assert np.array_equal(got, base)
+    poisoned.v[0][slot(first)] *= -3.0
+    moved = oracle.draft_block(cfg, W, poisoned, [5], [Lr], pt)["logits"]
+    assert np.max(np.abs(moved - base)) > 1e-9
 
 
 # ---------------------------------------------------------------- fixtures
@@ -384,8 +462,7 @@ def test_draft_pass_matches_transformers_qwen3_layers(windowed):
                 mask = torch.zeros(1, 1, S, L[r] + S, dtype=torch.float64)
                 Wl = cfg.window(l)
                 if Wl:
-                    qp = torch.arange(L[r], L[r] + S)[:, None]
-                    vis = (qp - torch.arange(L[r])[None, :]) < Wl
+                    vis = _hf_window_visible(np.arange(L[r], L[r] + S), np.arange(L[r]), Wl)
                     mask[0, 0, :, :L[r]] = torch.where(vis, 0.0, float("-inf"))
                 out = lay(x, attention_mask=mask, position_ids=pos, past_key_values=kv,
                           use_cache=True, position_embeddings=pe)
