@@ -78,6 +78,7 @@ EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_accept_sampling_sparse", "dflash_reserve_pages", "dflash_release_pages",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
+            "dflash_draft_block_noalloc_limit", "dflash_draft_block_noalloc",
             "dflash_status_string", "dflash_last_error"]
 
 
@@ -100,6 +101,11 @@ def _load():
     lib.dflash_draft_block.argtypes = [cfgp, wp, kvp, P, P, P, I32, I32, I32, P, P, P, P, P, P,
                                        SZ, P]
     lib.dflash_draft_block.restype = I32
+    lib.dflash_draft_block_noalloc_limit.argtypes = []
+    lib.dflash_draft_block_noalloc_limit.restype = SZ
+    lib.dflash_draft_block_noalloc.argtypes = [cfgp, wp, kvp, P, P, P, I32, I32, I32, P, P, P, P,
+                                               P, P]
+    lib.dflash_draft_block_noalloc.restype = I32
     lib.dflash_accept.argtypes = [P, P, P, I32, I32, P, P, P, P, P, P]
     lib.dflash_accept.restype = I32
     lib.dflash_accept_logits_workspace_bytes.argtypes = [I32, I32, I32]
@@ -295,6 +301,27 @@ def dflash_draft_block(cfg, weights: CWeights, cache: KVCache, anchor: torch.Ten
         _ptr(prefix_len), _ptr(page_table), int(page_table.shape[1]), int(anchor.shape[0]),
         int(max_prefix_len), _ptr(block_ids), _ptr(positions), _ptr(slots), _ptr(candidates),
         _ptr(logits), _ptr(ws), int(ws.numel()), _stream(stream)))
+
+
+def draft_block_noalloc_limit() -> int:
+    return int(_lib.dflash_draft_block_noalloc_limit())
+
+
+def dflash_draft_block_noalloc(cfg, weights: CWeights, cache: KVCache, anchor: torch.Tensor,
+                               prefix_len: torch.Tensor, page_table: torch.Tensor,
+                               max_prefix_len: int, positions: torch.Tensor, slots: torch.Tensor,
+                               candidates: torch.Tensor, block_ids: Optional[torch.Tensor] = None,
+                               logits: Optional[torch.Tensor] = None, stream=None,
+                               c_cfg: Optional[CConfig] = None,
+                               c_cache: Optional[CKVCache] = None):
+    """dflash_draft_block on the library's fixed scratch array (no workspace argument)."""
+    c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
+    c_cache = c_cache if c_cache is not None else cache.c_struct()
+    _check(_lib.dflash_draft_block_noalloc(
+        ctypes.byref(c_cfg), ctypes.byref(weights), ctypes.byref(c_cache), _ptr(anchor),
+        _ptr(prefix_len), _ptr(page_table), int(page_table.shape[1]), int(anchor.shape[0]),
+        int(max_prefix_len), _ptr(block_ids), _ptr(positions), _ptr(slots), _ptr(candidates),
+        _ptr(logits), _stream(stream)))
 
 
 def dflash_accept(candidates: torch.Tensor, posterior: torch.Tensor, prefix_len: torch.Tensor,

@@ -227,6 +227,10 @@ LmHeadWs layout_lm_head(const dflash_config* c, int rows, void* ws) {
 
 }  // namespace
 
+namespace dflash {
+dflash_status set_error(dflash_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace dflash
+
 extern "C" {
 
 const char* dflash_status_string(dflash_status s) {

@@ -178,4 +178,7 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             const AttnPlan& plan,
                             float* o_part, float2* ml_part, int4* seg, void* out, hipStream_t st);
 
+// Record msg as the calling thread's last error (dflash_last_error) and return s.
+dflash_status set_error(dflash_status s, const char* msg);
+
 }  // namespace dflash

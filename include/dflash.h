@@ -6,6 +6,7 @@
  *   dflash_project_context  context injection (target features -> draft K/V cache)
  *   dflash_draft_block      one non-causal draft pass over [anchor, MASK x (S-1)]
  *   dflash_draft_block_selector  the same pass with the DFlash 2 candidate selector
+ *   dflash_draft_block_noalloc   the draft pass on a fixed in-library scratch array
  *   dflash_accept           greedy verify-accept, commit and logical crop
  *   dflash_accept_sampling  rejection-sampling verify-accept and commit
  *   dflash_accept_sampling_sparse  the same with the selector's sparse q rows
@@ -15,7 +16,8 @@
  *   - Every pointer argument is DEVICE memory unless its name starts with
  *     host_.  The caller owns every buffer (weights, cache, page table,
  *     inputs, outputs, workspace); the library never allocates or frees
- *     device memory and keeps no state between calls.
+ *     device memory and keeps no state between calls (one exception:
+ *     dflash_draft_block_noalloc's fixed scratch array, below).
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream).  Results are ready when the stream is.
  *   - Failures come back as a dflash_status; nothing throws across the ABI.
@@ -227,6 +229,30 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
                                  int32_t* block_ids, int32_t* positions, int32_t* slots,
                                  int32_t* candidates, void* logits, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * (2-noalloc) dflash_draft_block for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as dflash_draft_block
+ * except that the workspace is a fixed device array inside the library
+ * (dflash_draft_block_noalloc_limit() bytes, 64 MiB; one copy per GPU, held
+ * until the process ends).  The caller still passes every input and output.
+ *   - A call whose dflash_draft_workspace_bytes(cfg, batch, max_prefix_len)
+ *     exceeds the limit returns DFLASH_EWORKSPACE before any HIP call.
+ *   - The first call on a device looks up that device's copy of the array
+ *     (the current device, hipGetDevice); nothing is allocated, then or later.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, or threads) race and give wrong
+ *     results.  Calls ordered on one stream are safe.  Nothing in the array
+ *     needs to start at zero: each call writes every scratch value it reads.
+ */
+size_t dflash_draft_block_noalloc_limit(void);
+dflash_status dflash_draft_block_noalloc(const dflash_config* cfg, const dflash_weights* w,
+                                         const dflash_kv_cache* cache, const int32_t* anchor,
+                                         const int32_t* prefix_len, const int32_t* page_table,
+                                         int32_t max_pages, int32_t batch, int32_t max_prefix_len,
+                                         int32_t* block_ids, int32_t* positions, int32_t* slots,
+                                         int32_t* candidates, void* logits, void* stream);
 
 /*
  * (3) Greedy verify-accept and commit ("Inside SGLang ...", Step 6 and Step 7;

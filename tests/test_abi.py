@@ -228,3 +228,26 @@ def test_accept_sampling_sparse_argument_errors():
     assert call(S=65) == -2 and call(V=524289) == -2
     assert call(T=0.0) == -1 and call(qi=None) == -1
     assert call(wsb=16) == -3
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """The fixed-scratch draft pass refuses a call whose workspace exceeds its
+    array, with DFLASH_EWORKSPACE and a message, before any HIP call."""
+    lib = dfl.raw_lib()
+    limit = dfl.draft_block_noalloc_limit()
+    assert limit == 64 << 20
+    need = dfl.draft_workspace_bytes(QWEN3_8B_DRAFT, 32, 8192)
+    assert need > limit
+    fake = ctypes.c_void_p(0x100000)
+    c = dfl.make_config(QWEN3_8B_DRAFT)
+    w, kv = dfl.CWeights(), dfl.CKVCache()
+    st = lib.dflash_draft_block_noalloc(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), fake,
+                                        fake, fake, 600, 32, 8192, None, fake, fake, fake, None,
+                                        None)
+    assert st == -3
+    assert b"scratch" in lib.dflash_last_error()
+    bad = dfl.make_config(dataclasses.replace(TINY, head_dim=96))
+    st = lib.dflash_draft_block_noalloc(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(kv),
+                                        fake, fake, fake, 4, 1, 64, None, fake, fake, fake, None,
+                                        None)
+    assert st == -1
