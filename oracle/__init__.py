@@ -22,3 +22,4 @@ from .dflash import (block_prep, project_context, draft_block, accept,  # noqa: 
                      greedy_posterior, accept_logits, OracleCache, speculative_decode)
 from .sampling import accept_sampling  # noqa: F401
 from . import selector  # noqa: F401
+from . import relay  # noqa: F401
