@@ -70,6 +70,12 @@ class CKVCache(ctypes.Structure):
                 ("num_pages", ctypes.c_int64)]
 
 
+class CRequestPool(ctypes.Structure):
+    _fields_ = [("anchor", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("n_pages", ctypes.c_void_p),
+                ("capacity", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+
+
 EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_project_context", "dflash_draft_block", "dflash_accept",
             "dflash_accept_logits_workspace_bytes", "dflash_accept_logits",
@@ -79,6 +85,7 @@ EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_lm_head_workspace_bytes", "dflash_lm_head_argmax",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_draft_block_noalloc_limit", "dflash_draft_block_noalloc",
+            "dflash_relay_resolve", "dflash_relay_stash",
             "dflash_status_string", "dflash_last_error"]
 
 
@@ -125,6 +132,11 @@ def _load():
     lib.dflash_reserve_pages.restype = I32
     lib.dflash_release_pages.argtypes = [P, I32, P, I32, P, P, I32, P, P]
     lib.dflash_release_pages.restype = I32
+    poolp = ctypes.POINTER(CRequestPool)
+    lib.dflash_relay_resolve.argtypes = [poolp, P, I32, P, P, P, P, P]
+    lib.dflash_relay_resolve.restype = I32
+    lib.dflash_relay_stash.argtypes = [poolp, P, I32, P, P, P, P, P]
+    lib.dflash_relay_stash.restype = I32
     selp = ctypes.POINTER(CSelector)
     lib.dflash_selector_workspace_bytes.argtypes = [cfgp, selp, I32, I32]
     lib.dflash_selector_workspace_bytes.restype = SZ
@@ -479,3 +491,33 @@ def dflash_lm_head_argmax(cfg, lm_head: torch.Tensor, hidden: torch.Tensor, ids:
 def raw_lib():
     """The ctypes library handle (for ABI tests)."""
     return _lib
+
+
+def make_request_pool(anchor: torch.Tensor, seq_len: torch.Tensor,
+                      page_table: Optional[torch.Tensor] = None,
+                      n_pages: Optional[torch.Tensor] = None) -> CRequestPool:
+    """C request-pool table over int32 device tensors [capacity] (page_table
+    [capacity, max_pages]); the caller keeps the tensors alive."""
+    p = CRequestPool()
+    p.anchor, p.seq_len = anchor.data_ptr(), seq_len.data_ptr()
+    p.page_table = None if page_table is None else page_table.data_ptr()
+    p.n_pages = None if n_pages is None else n_pages.data_ptr()
+    p.capacity = int(anchor.shape[0])
+    p.max_pages = 0 if page_table is None else int(page_table.shape[1])
+    return p
+
+
+def dflash_relay_resolve(pool: CRequestPool, req_slots: torch.Tensor, anchor: torch.Tensor,
+                         prefix_len: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+                         n_pages: Optional[torch.Tensor] = None, stream=None):
+    _check(_lib.dflash_relay_resolve(ctypes.byref(pool), _ptr(req_slots), int(req_slots.shape[0]),
+                                     _ptr(anchor), _ptr(prefix_len), _ptr(page_table),
+                                     _ptr(n_pages), _stream(stream)))
+
+
+def dflash_relay_stash(pool: CRequestPool, req_slots: torch.Tensor, next_anchor: torch.Tensor,
+                       new_seq_len: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+                       n_pages: Optional[torch.Tensor] = None, stream=None):
+    _check(_lib.dflash_relay_stash(ctypes.byref(pool), _ptr(req_slots), int(req_slots.shape[0]),
+                                   _ptr(next_anchor), _ptr(new_seq_len), _ptr(page_table),
+                                   _ptr(n_pages), _stream(stream)))

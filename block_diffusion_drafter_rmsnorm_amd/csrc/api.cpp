@@ -478,6 +478,48 @@ dflash_status dflash_accept_sampling_sparse(
   return DFLASH_OK;
 }
 
+static dflash_status relay(bool stash, const dflash_request_pool* pool, const int32_t* req_slots,
+                           int32_t batch, const int32_t* anchor, const int32_t* len,
+                           const int32_t* pt, const int32_t* np, void* stream) {
+  if (pool == nullptr) return fail(DFLASH_EINVAL, "pool is NULL");
+  if (batch < 0 || pool->capacity < 0 || pool->max_pages < 0)
+    return fail(DFLASH_EINVAL, "negative batch, capacity or max_pages");
+  if ((int64_t)pool->capacity * pool->max_pages > ((int64_t)1 << 40))
+    return fail(DFLASH_EINVAL, "pool too large");
+  const void* pairs[4][2] = {{pool->anchor, anchor}, {pool->seq_len, len},
+                             {pool->page_table, pt}, {pool->n_pages, np}};
+  const char* names[4] = {"anchor", "seq_len", "page_table", "n_pages"};
+  for (int i = 0; i < 4; ++i)
+    if ((pairs[i][0] == nullptr) != (pairs[i][1] == nullptr))
+      return fail(DFLASH_EINVAL, "%s: the pool and the batch array must both be given or both NULL",
+                  names[i]);
+  if (pt != nullptr && pool->max_pages == 0)
+    return fail(DFLASH_EINVAL, "page_table given with max_pages 0");
+  if (batch == 0) return DFLASH_OK;
+  if (req_slots == nullptr) return fail(DFLASH_EINVAL, "req_slots is NULL");
+  hipError_t e = launch_relay(stash, req_slots, batch, pool->capacity, pool->max_pages,
+                              pool->anchor, pool->seq_len, pool->page_table, pool->n_pages,
+                              const_cast<int32_t*>(anchor), const_cast<int32_t*>(len),
+                              const_cast<int32_t*>(pt), const_cast<int32_t*>(np),
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, stash ? "relay stash" : "relay resolve");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_relay_resolve(const dflash_request_pool* pool, const int32_t* req_slots,
+                                   int32_t batch, int32_t* anchor, int32_t* prefix_len,
+                                   int32_t* page_table, int32_t* n_pages, void* stream) {
+  return relay(false, pool, req_slots, batch, anchor, prefix_len, page_table, n_pages, stream);
+}
+
+dflash_status dflash_relay_stash(const dflash_request_pool* pool, const int32_t* req_slots,
+                                 int32_t batch, const int32_t* next_anchor,
+                                 const int32_t* new_seq_len, const int32_t* page_table,
+                                 const int32_t* n_pages, void* stream) {
+  return relay(true, pool, req_slots, batch, next_anchor, new_seq_len, page_table, n_pages,
+               stream);
+}
+
 dflash_status dflash_reserve_pages(const int32_t* seq_len, int32_t batch, int32_t block_size,
                                    int32_t page_size, int32_t* page_table, int32_t max_pages,
                                    int32_t* n_pages, const int32_t* free_pages,

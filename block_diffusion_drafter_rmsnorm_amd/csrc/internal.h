@@ -142,6 +142,12 @@ hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const vo
 hipError_t launch_reserve(const int32_t* seq_len, int B, int S, int P, int32_t* pt, int max_pages,
                           int32_t* n_pages, const int32_t* free_pages, int capacity,
                           int32_t* free_count, int32_t* status, hipStream_t st);
+// request-pool relay: stash = batch rows -> pool slots, else pool slots -> batch
+// rows; any of the four fields may be NULL on both sides (not copied)
+hipError_t launch_relay(bool stash, const int32_t* slots, int B, int capacity, int max_pages,
+                        int32_t* p_anchor, int32_t* p_len, int32_t* p_pt, int32_t* p_np,
+                        int32_t* anchor, int32_t* len, int32_t* pt, int32_t* np,
+                        hipStream_t st);
 hipError_t launch_release(const int32_t* mask, int B, const int32_t* pt, int max_pages,
                           int32_t* n_pages, int32_t* free_pages, int capacity, int32_t* free_count,
                           hipStream_t st);

@@ -128,7 +128,66 @@ __global__ __launch_bounds__(kT) void release_kernel(const int32_t* __restrict__
   if (tid == 0) free_count[0] = top;
 }
 
+// Relay of per-request decode state through request-pool slots ("Inside
+// SGLang ...", section "Back in the scheduler: GPU continuation and CPU
+// output": the relay is indexed by request-pool slots, so the batch can be
+// filtered or merged between iterations).  One workgroup per batch row; the
+// page-table row is copied with consecutive threads on consecutive entries.
+// resolve: pool slot slots[b] -> batch row b (a slot outside the pool gives
+// anchor 0, length 0, no pages and a row of -1); stash: batch row b -> pool
+// slot slots[b] (a slot outside the pool is skipped).
+__global__ __launch_bounds__(kT) void relay_resolve_kernel(
+    const int32_t* __restrict__ slots, int capacity, int max_pages,
+    const int32_t* __restrict__ p_anchor, const int32_t* __restrict__ p_len,
+    const int32_t* __restrict__ p_pt, const int32_t* __restrict__ p_np,
+    int32_t* __restrict__ anchor, int32_t* __restrict__ len, int32_t* __restrict__ pt,
+    int32_t* __restrict__ np) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int s = slots[b];
+  const bool ok = s >= 0 && s < capacity;
+  if (tid == 0) {
+    if (anchor != nullptr) anchor[b] = ok ? p_anchor[s] : 0;
+    if (len != nullptr) len[b] = ok ? p_len[s] : 0;
+    if (np != nullptr) np[b] = ok ? p_np[s] : 0;
+  }
+  if (pt != nullptr)
+    for (int i = tid; i < max_pages; i += kT)
+      pt[(int64_t)b * max_pages + i] = ok ? p_pt[(int64_t)s * max_pages + i] : -1;
+}
+
+__global__ __launch_bounds__(kT) void relay_stash_kernel(
+    const int32_t* __restrict__ slots, int capacity, int max_pages,
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ len,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ np,
+    int32_t* __restrict__ p_anchor, int32_t* __restrict__ p_len, int32_t* __restrict__ p_pt,
+    int32_t* __restrict__ p_np) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int s = slots[b];
+  if (s < 0 || s >= capacity) return;
+  if (tid == 0) {
+    if (anchor != nullptr) p_anchor[s] = anchor[b];
+    if (len != nullptr) p_len[s] = len[b];
+    if (np != nullptr) p_np[s] = np[b];
+  }
+  if (pt != nullptr)
+    for (int i = tid; i < max_pages; i += kT)
+      p_pt[(int64_t)s * max_pages + i] = pt[(int64_t)b * max_pages + i];
+}
+
 }  // namespace
+
+hipError_t launch_relay(bool stash, const int32_t* slots, int B, int capacity, int max_pages,
+                        int32_t* p_anchor, int32_t* p_len, int32_t* p_pt, int32_t* p_np,
+                        int32_t* anchor, int32_t* len, int32_t* pt, int32_t* np,
+                        hipStream_t st) {
+  if (stash)
+    hipLaunchKernelGGL(relay_stash_kernel, dim3(B), dim3(kT), 0, st, slots, capacity, max_pages,
+                       anchor, len, pt, np, p_anchor, p_len, p_pt, p_np);
+  else
+    hipLaunchKernelGGL(relay_resolve_kernel, dim3(B), dim3(kT), 0, st, slots, capacity,
+                       max_pages, p_anchor, p_len, p_pt, p_np, anchor, len, pt, np);
+  return hipGetLastError();
+}
 
 hipError_t launch_reserve(const int32_t* seq_len, int B, int S, int P, int32_t* pt, int max_pages,
                           int32_t* n_pages, const int32_t* free_pages, int capacity,

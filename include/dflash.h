@@ -11,6 +11,7 @@
  *   dflash_accept_sampling  rejection-sampling verify-accept and commit
  *   dflash_accept_sampling_sparse  the same with the selector's sparse q rows
  *   dflash_reserve_pages / dflash_release_pages  page reservation on the device
+ *   dflash_relay_resolve / dflash_relay_stash  decode state by request-pool slot
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is DEVICE memory unless its name starts with
@@ -371,6 +372,9 @@ dflash_status dflash_accept_sampling_sparse(
  *   page_table  [batch, max_pages]; n_pages [batch]: pages each row holds
  *   free_pages  [free_capacity] stack of free physical pages; free_count [1]
  *   status      [1] out: 0 served, 1 out of pages, 2 row too short
+ * Rows are linear (logical page i in entry i): a request read through a draft
+ * window keeps a fixed ring of pages (dflash_draft_block) and is not passed
+ * here, since its need grows past any ring (status 2).
  * Reservations never shrink or move a page.  dflash_release_pages pushes the
  * pages of every request with mask[r] != 0 back (batch order, row order) and
  * sets its n_pages to 0.  Deterministic; one workgroup; no workspace.
@@ -383,6 +387,50 @@ dflash_status dflash_reserve_pages(const int32_t* seq_len, int32_t batch, int32_
 dflash_status dflash_release_pages(const int32_t* mask, int32_t batch, const int32_t* page_table,
                                    int32_t max_pages, int32_t* n_pages, int32_t* free_pages,
                                    int32_t free_capacity, int32_t* free_count, void* stream);
+
+/*
+ * Relay of per-request decode state through a request pool ("Inside SGLang
+ * ...", section "Back in the scheduler: GPU continuation and CPU output":
+ * before the worker, the previous iteration's anchor and lengths are gathered
+ * for the current request rows; after it, the lengths and the next anchor are
+ * stashed; the relay is indexed by request-pool slots, so the batch can be
+ * filtered or merged between iterations without the old row order).
+ *
+ * The pool holds, per slot, the request's next anchor, committed length, and
+ * its page-table row with the count of pages it holds (the reservation
+ * travels with the request).  A batch is req_slots[batch]: distinct pool
+ * slots, in the order of the batch rows (device memory, so the next
+ * iteration's composition can be written without a host round trip).
+ *   dflash_relay_resolve  batch row b <- pool slot req_slots[b]: anchor,
+ *                         prefix_len, page_table[b, :], n_pages (a slot
+ *                         outside [0, capacity) gives 0, 0, a row of -1, 0)
+ *   dflash_relay_stash    pool slot req_slots[b] <- batch row b: next_anchor,
+ *                         new_seq_len, page_table[b, :], n_pages (a slot
+ *                         outside the pool is skipped; every other slot is
+ *                         left as it is)
+ * Typical cycle, all on one stream: resolve -> dflash_draft_block -> accept
+ * -> dflash_reserve_pages (on the batch rows) -> stash -> dflash_project_context
+ * of the committed rows.  Batch-side page_table rows have the pool's
+ * max_pages entries.  Each of the four fields is copied when both its pool
+ * array and its batch array are non-NULL and skipped when both are NULL
+ * (DFLASH_EINVAL otherwise).  Duplicate slots in one stash are the caller's
+ * error (unspecified which row lands).  Bit-exact integer copies; no workspace.
+ */
+typedef struct {
+  int32_t* anchor;      /* [capacity] next anchor                                */
+  int32_t* seq_len;     /* [capacity] committed length                           */
+  int32_t* page_table;  /* [capacity, max_pages] physical pages in logical order */
+  int32_t* n_pages;     /* [capacity] pages held                                 */
+  int32_t capacity;
+  int32_t max_pages;
+} dflash_request_pool;
+dflash_status dflash_relay_resolve(const dflash_request_pool* pool, const int32_t* req_slots,
+                                   int32_t batch, int32_t* anchor, int32_t* prefix_len,
+                                   int32_t* page_table, int32_t* n_pages, void* stream);
+dflash_status dflash_relay_stash(const dflash_request_pool* pool, const int32_t* req_slots,
+                                 int32_t batch, const int32_t* next_anchor,
+                                 const int32_t* new_seq_len, const int32_t* page_table,
+                                 const int32_t* n_pages, void* stream);
 
 /*
  * (2') One draft pass with the DFlash 2 candidate selector in place of the

@@ -251,3 +251,23 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
                                         fake, fake, fake, 4, 1, 64, None, fake, fake, fake, None,
                                         None)
     assert st == -1
+
+
+def test_relay_argument_errors():
+    """Host-visible relay errors come back before any launch: a field given on
+    one side only, negative sizes, a NULL pool."""
+    lib = dfl.raw_lib()
+    fake = ctypes.c_void_p(0x100000)
+    p = dfl.CRequestPool()
+    p.anchor, p.seq_len, p.capacity, p.max_pages = 0x100000, 0x100000, 4, 0
+    assert lib.dflash_relay_resolve(None, fake, 2, fake, fake, None, None, None) == -1
+    # page_table on the batch side but not in the pool
+    assert lib.dflash_relay_resolve(ctypes.byref(p), fake, 2, fake, fake, fake, None, None) == -1
+    assert b"page_table" in lib.dflash_last_error()
+    assert lib.dflash_relay_stash(ctypes.byref(p), fake, -1, fake, fake, None, None, None) == -1
+    # n_pages in the pool but not on the batch side
+    p.n_pages = 0x100000
+    assert lib.dflash_relay_stash(ctypes.byref(p), fake, 2, fake, fake, None, None, None) == -1
+    # an empty batch is a no-op
+    p.n_pages = None
+    assert lib.dflash_relay_stash(ctypes.byref(p), None, 0, fake, fake, None, None, None) == 0
