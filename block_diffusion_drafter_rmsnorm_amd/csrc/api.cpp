@@ -144,7 +144,7 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   // the last chunk of a call can be any size up to `chunk`: take the worst case
   size_t pf = 0;
   for (int m = 1; m <= M; ++m) {
-    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim, c->act_dtype == DFLASH_BF16),
+    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim, c->act_dtype == DFLASH_BF16, 1),
                             plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim, c->hidden,
                                       c->act_dtype == DFLASH_BF16)};
     for (const GemmPlan& p : ps)
@@ -197,9 +197,9 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   L.seg = (int4*)cv.take(sizeof(int4) * (size_t)B);
   L.lm_part = (float2*)cv.take(sizeof(float2) * (size_t)M1 * logits_tiles(c->vocab));
   const bool bf = c->act_dtype == DFLASH_BF16;
-  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H, bf), plan_gemm(M, H, nq * D, bf),
-                         plan_gemm(M, ((I + 63) / 64) * 128, H, bf), plan_gemm(M, H, I, bf),
-                         plan_gemm(M1, c->vocab, H, bf)};
+  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H, bf), plan_gemm(M, H, nq * D, bf, 1),
+                         plan_gemm(M, ((I + 63) / 64) * 128, H, bf, 2), plan_gemm(M, H, I, bf, 1),
+                         plan_gemm(M1, c->vocab, H, bf, 8)};
   size_t pf = 0;
   for (const GemmPlan& p : ps)
     if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
@@ -217,7 +217,7 @@ LmHeadWs layout_lm_head(const dflash_config* c, int rows, void* ws) {
   Carver cv(ws);
   LmHeadWs L;
   L.part = (float2*)cv.take(sizeof(float2) * (size_t)rows * logits_tiles(c->vocab));
-  const GemmPlan p = plan_gemm(rows, c->vocab, c->hidden, c->act_dtype == DFLASH_BF16);
+  const GemmPlan p = plan_gemm(rows, c->vocab, c->hidden, c->act_dtype == DFLASH_BF16, 8);
   const size_t pf = gemm_partial_floats(p);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
@@ -562,7 +562,7 @@ static SelectorWs layout_selector(const dflash_config* c, const dflash_selector*
   L.logits = own_logits ? cv.take((size_t)act_bytes(c->act_dtype) * M1 * c->vocab) : nullptr;
   L.unary = (float*)cv.take(sizeof(float) * (size_t)M1 * K);
   L.w = (float*)cv.take(sizeof(float) * (size_t)M1 * r);
-  const GemmPlan gp = plan_gemm(M1, r, c->hidden, c->act_dtype == DFLASH_BF16);
+  const GemmPlan gp = plan_gemm(M1, r, c->hidden, c->act_dtype == DFLASH_BF16, 1);
   L.gs.partial_floats = gemm_partial_floats(gp);
   L.gs.partial = (float*)cv.take(sizeof(float) * (L.gs.partial_floats > 0 ? L.gs.partial_floats : 1));
   L.bytes = cv.off;

@@ -37,8 +37,34 @@ __host__ __device__ __forceinline__ int64_t slab_elems(int K) {
   return (int64_t)(K / 32) * kChunkElems;
 }
 
-GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16) {
+GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow) {
   GemmPlan p;
+  p.rows = false;
+  p.NSL = p.NW = p.kw = 0;
+  // (128-column tiles: up to 32 rows, so the per-wave partial tiles fit in LDS)
+  if (narrow > 0 && M <= (narrow == 8 ? 32 : 64)) {
+    // narrow tiles: one or two slabs per workgroup (two for SwiGLU: a gate
+    // slab and its up slab); the waves split K so that the grid holds ~4096+
+    // waves (16 per workgroup when the groups are few, else 8; fp32: 8)
+    p.rows = true;
+    p.fat = p.big = false;
+    p.NSL = narrow;
+    p.MB = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    p.BM = 16 * p.MB;
+    p.m_tiles = (M + p.BM - 1) / p.BM;
+    p.n_tiles = (Ncols + 16 * p.NSL - 1) / (16 * p.NSL);
+    // NSL 8 (the lm_head's 128-column argmax tiles): 16 waves = 4 slab pairs x
+    // 4 K splits, so that even a partial last round of workgroups keeps
+    // thousands of waves streaming
+    p.NW = (bf16 && (p.NSL == 8 || (p.NSL == 1 && p.n_tiles < 512))) ? 16 : 8;
+    const int nsw = p.NSL > 2 ? 2 : p.NSL;       // slabs per wave (gemm_rows' NSW)
+    const int ksplit = p.NW / (p.NSL / nsw);      // waves per slab group
+    int kw = (K + ksplit - 1) / ksplit;
+    p.kw = (kw + 31) / 32 * 32;
+    p.KS = 1;
+    p.Kc = K;
+    return p;
+  }
   p.fat = bf16 && M > 64;
   p.big = false;
   if (p.fat && M > 192) {
@@ -149,35 +175,89 @@ struct RowScale {
   float eps;
   int S;
   // 1/rms of the tile's rows m0 .. m0+rows-1 into out[] (LDS), one wave per row
-  // (lanes load the row's partial sums in parallel, summed in a fixed tree;
-  // a wave issues the loads of 8 rows before it sums any).
-  // Called by all threads of the workgroup; ends with a barrier.
+  // (the row's partial sums spread over the lanes, all of a batch of G rows'
+  // loads issued before any is summed; each lane adds its values in a fixed
+  // order, then a fixed wave tree).  Called by all threads of the workgroup;
+  // ends with a barrier.
   __device__ __forceinline__ void fill(float* out, int rows, int m0, int M, int tid) const {
     const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
-    constexpr int G = 8;
+    if (ss == nullptr) {
+      for (int r = tid; r < rows; r += (int)blockDim.x) out[r] = 1.0f;
+      __syncthreads();
+      return;
+    }
+    constexpr int G = 4;  // rows per wave batch
+    constexpr int Q = 8;  // partials per lane held at once (n_ss <= 512 in one pass)
     for (int r0 = wave; r0 < rows; r0 += nw * G) {
-      float acc[G];
+      float v[G][Q];
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         const int r = r0 + nw * u;
         const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
-        acc[u] = (ss != nullptr && r < rows && lane < n_ss) ? p[lane] : 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const int t = lane + 64 * q;
+          v[u][q] = (r < rows && t < n_ss) ? p[t] : 0.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         const int r = r0 + nw * u;
         if (r >= rows) break;
-        float v = 1.0f;
-        if (ss != nullptr) {
-          const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
-          for (int t = lane + 64; t < n_ss; t += 64) acc[u] += p[t];
-          v = 1.0f / sqrtf(wave_sum(acc[u]) / (float)H + eps);
-        }
-        if (lane == 0) out[r] = v;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) acc += v[u][q];
+        const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+        for (int t = lane + 64 * Q; t < n_ss; t += 64) acc += p[t];
+        const float inv = 1.0f / sqrtf(wave_sum(acc) / (float)H + eps);
+        if (lane == 0) out[r] = inv;
       }
     }
     __syncthreads();
   }
+  // 1/rms of rows first, first + step, ... (< rows) into out[] (LDS), by the
+  // calling wave alone and without a barrier (the caller's next barrier
+  // publishes them): gemm_rows computes its row scales while its first weight
+  // loads are in flight.
+  __device__ __forceinline__ void fill_rows(float* out, int rows, int m0, int M, int first,
+                                            int step, int lane) const {
+    constexpr int G = 4;  // rows whose loads go out together
+    constexpr int Q = 8;
+    for (int r0 = first; r0 < rows; r0 += step * G) {
+      float v[G][Q];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int r = r0 + step * u;
+        const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          v[u][q] = (ss != nullptr && r < rows && lane + 64 * q < n_ss) ? p[lane + 64 * q] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int r = r0 + step * u;
+        if (r >= rows) break;
+        float inv = 1.0f;
+        if (ss != nullptr) {
+          const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < Q; ++q) acc += v[u][q];
+          for (int t = lane + 64 * Q; t < n_ss; t += 64) acc += p[t];
+          inv = 1.0f / sqrtf(wave_sum(acc) / (float)H + eps);
+        }
+        if (lane == 0) out[r] = inv;
+      }
+    }
+  }
+
+};
+
+// Values a narrow epilogue loads for its (up to) two items per thread before
+// the K loop: the residual and the next norm's gain at the item's column.
+struct NarrowPre {
+  float x[2];
+  float g[2];
 };
 
 // 1/rms of the rows of the tile an epilogue works on: filled by the
@@ -200,12 +280,12 @@ template <typename T> struct NextNorm {
 // record of each chunk of its two slabs (B) and the matching 8 K elements
 // 32 c + 8 (l / 16) .. of its A rows.  The K loop double-buffers steps in
 // registers so the next step's weight loads are in flight during the MFMAs.
-template <typename T, int MB, class ASrc> struct Step64 {
-  Frag<T> a0[MB], a1[MB], b0[2], b1[2];
+template <typename T, int MB, class ASrc, int NSL = 2> struct Step64 {
+  Frag<T> a0[MB], a1[MB], b0[NSL], b1[NSL];
   __device__ __forceinline__ void load(const ASrc& asrc, const typename ASrc::template State<MB>& as,
                                        const T* const* bp, int c, int g4) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NSL; ++nb) {
       load_frag(b0[nb], bp[nb] + (int64_t)c * kChunkElems);
       load_frag(b1[nb], bp[nb] + (int64_t)(c + 1) * kChunkElems);
     }
@@ -215,11 +295,11 @@ template <typename T, int MB, class ASrc> struct Step64 {
       asrc.template load<MB>(a1[mb], as, mb, c * 32 + 32 + g4 * 8);
     }
   }
-  __device__ __forceinline__ void mma_into(f32x4 (&acc)[MB][2]) const {
+  __device__ __forceinline__ void mma_into(f32x4 (&acc)[MB][NSL]) const {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NSL; ++nb) {
         mma(acc[mb][nb], a0[mb], b0[nb]);
         mma(acc[mb][nb], a1[mb], b1[nb]);
       }
@@ -312,6 +392,174 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         mine[(mb * 16 + g4 * 4 + i) * BN + wave * 32 + nb * 16 + r16] = acc[mb][nb][i];
+}
+
+// ---------------------------------------------------------------- narrow tiles
+// Weight streaming for up to 64 rows with the K split inside the workgroup: a
+// workgroup owns NSL packed slabs (16 NSL output columns, its column group g)
+// over the whole K; its NW waves stream disjoint contiguous K ranges of all
+// NSL slabs (wave w: [w kw, w kw + kw)), each into its own accumulators,
+// through a ring of NB register buffers.  The NW partial tiles are then summed
+// in LDS in wave order -- a fixed order, so the result does not depend on
+// timing -- and the epilogue runs in the same kernel: no partial tiles in HBM
+// and no second kernel.  The K ranges depend only on (Ncols, K), so a row's
+// bits do not depend on how many rows share the call.
+//
+// Narrow epilogue interface: nslab(n0) = the packed slab holding output
+// columns [n0, n0 + 16) of the epilogue's column space; nprepare() as
+// prepare(); napply(tile, ldt, rows, m0, M, n0, ncols, tid) over columns
+// [n0, n0 + ncols) with ncols a multiple of 16.
+template <typename T, int MB, int NSL, int NSW, int NW, int NB, int MINW, bool ILV, class ASrc,
+          class Epi>
+__global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int K, int kw,
+                                                           int m_tiles, Epi epi) {
+  constexpr int TR = 16 * MB, TC = 16 * NSL;
+  constexpr int LDR = TC + 4;  // padded row of the summed tile (floats)
+  constexpr int WC = 16 * NSW;  // columns of one wave's partial tile
+  constexpr int NG = NSL / NSW;  // slab groups; wave = ks * NG + group
+  constexpr int KSPL = NW / NG;  // K splits
+  static_assert(NSL % NSW == 0 && NW % NG == 0, "waves cover slab groups x K splits");
+  static_assert(NSL != 1 || TR * NSL <= 8 * NW, "narrow_rows handles two items per thread");
+  __shared__ float red[NW * TR * WC];
+  __shared__ float tile[TR * LDR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mt = (int)blockIdx.x % m_tiles, g = (int)blockIdx.x / m_tiles;
+  const int m0 = mt * TR, n0 = g * TC;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int sg = wave % NG, ksp = wave / NG;
+  const int k0 = imin(K, ksp * kw), k1 = imin(K, k0 + kw);
+
+  const T* bp[NSW];  // this lane's record in chunk 0 of each of the wave's slabs
+#pragma unroll
+  for (int s = 0; s < NSW; ++s) bp[s] = epi.nslab(n0 + 16 * (sg * NSW + s)) + lane * 8;
+  typename ASrc::template State<MB> as;
+  asrc.template setup<MB>(as, m0, M, r16);
+
+  f32x4 acc[MB][NSW];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) acc[mb][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ILV: the K splits interleave by 64-wide step (split ksp takes steps ksp,
+  // ksp + KSPL, ...), so the waves of a slab group read one contiguous run of
+  // the slabs at a time; else split ksp takes the contiguous range [k0, k1).
+  int c = k0 / 32;  // chunk index (k0, k1 are multiples of 32)
+  const bool odd = ILV ? ((K & 32) && ksp == 0) : ((k1 - k0) & 32);
+  if (ILV) c = K / 32 - 1;  // the odd last chunk (split 0)
+  if (odd) {  // a single chunk first when the range is not a multiple of 64
+    Frag<T> b0[NSW];
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) load_frag(b0[s], bp[s] + (int64_t)c * kChunkElems);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      Frag<T> a0;
+      asrc.template load<MB>(a0, as, mb, c * 32 + g4 * 8);
+#pragma unroll
+      for (int s = 0; s < NSW; ++s) mma(acc[mb][s], a0, b0[s]);
+    }
+    ++c;
+  }
+  const int n64 = ILV ? (K / 64 > ksp ? (K / 64 - ksp + KSPL - 1) / KSPL : 0) : (k1 / 32 - c) / 2;
+  auto chunk_of = [&](int st) { return ILV ? 2 * (ksp + st * KSPL) : c + 2 * st; };
+  Step64<T, MB, ASrc, NSW> buf[NB];
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b)
+    if (b < n64) buf[b].load(asrc, as, bp, chunk_of(b), g4);
+  // while those loads are in flight: the row scales of the epilogue (one wave
+  // per row; published by the barrier after the partial tiles) and the values
+  // the epilogue reads (residual, gains)
+  epi.nrow_scale(row_scale_lds(), TR, m0, M, wave, NW, lane);
+  NarrowPre pre;
+  epi.nfetch(pre, TR, m0, M, n0, TC, tid);
+  for (int i = 0; i < n64; i += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int st = i + b, nxt = st + NB - 1;
+      if (st < n64) {
+        if (nxt < n64) buf[(b + NB - 1) % NB].load(asrc, as, bp, chunk_of(nxt), g4);
+        buf[b].mma_into(acc);
+      }
+    }
+  }
+  // this wave's partial tile, then the sum over the K splits in split order
+  float* mine = red + wave * (TR * WC);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int s = 0; s < NSW; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[(mb * 16 + g4 * 4 + i) * WC + s * 16 + r16] = acc[mb][s][i];
+  __syncthreads();
+  for (int e = tid; e < TR * TC; e += NW * 64) {
+    const int r = e / TC, cc = e % TC, grp = cc / WC;
+    const float* src = red + (grp * TR + r) * WC + cc % WC;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < KSPL; ++k) v += src[k * NG * TR * WC];
+    tile[r * LDR + cc] = v;
+  }
+  __syncthreads();
+  epi.napply(tile, LDR, TR, m0, M, n0, TC, tid, pre);
+}
+
+// Row pass of a narrow epilogue: item (row r, 16-column group q) goes to a
+// 16-lane group, lane i = column 16 q + i; every lane of a wave runs the same
+// iterations (the 16-lane reductions are wave-uniform), at most two items per
+// thread (rows x groups <= 8 x waves).  narrow_item() gives the thread's item j
+// (the same for the prefetch before the K loop and the pass after it).
+// f(r, c, m, n, j) returns the value stored for tile (r, c) = output (m, n);
+// its squares are summed per 16-column group into ss (nullable) and v *
+// pre.g[j] (the next norm's gain at n) is written to xg.
+struct NarrowItem {
+  bool in;       // an item of the tile (the wave-uniform part of the bound)
+  bool act;      // ... and inside the output
+  int r, c, m, n;
+};
+__device__ __forceinline__ NarrowItem narrow_item(int j, int rows, int m0, int M, int n0,
+                                                  int ncols, int N, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
+  const int ng = ncols / 16, items = rows * ng;
+  const int b = wave * 4 + j * nw * 4, it = b + (lane >> 4);
+  NarrowItem t;
+  t.in = b < items;
+  t.r = it / ng;
+  t.c = (it % ng) * 16 + (lane & 15);
+  t.m = m0 + t.r;
+  t.n = n0 + t.c;
+  t.act = it < items && t.m < M && t.n < N;
+  return t;
+}
+template <typename T, typename F>
+__device__ __forceinline__ void narrow_rows(int rows, int m0, int M, int n0, int ncols, int N,
+                                            int tid, float* ss, int n_ss, const NextNorm<T>& nn,
+                                            const NarrowPre& pre, F&& f) {
+  const int lane = tid & 63;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const NarrowItem t = narrow_item(j, rows, m0, M, n0, ncols, N, tid);
+    if (!t.in) break;
+    float v = 0.f;
+    if (t.act) {
+      v = f(t.r, t.c, t.m, t.n, j);
+      if (nn.xg != nullptr) nn.xg[(int64_t)t.m * N + t.n] = Num<T>::from_f(v * pre.g[j]);
+    }
+    if (ss != nullptr) {
+      const float q = row16_sum(t.act ? v * v : 0.f);
+      if ((lane & 15) == 0 && t.act) ss[(int64_t)t.m * n_ss + t.n / 16] = q;
+    }
+  }
+}
+// The next norm's gains (and with x != null the residual) at a thread's items.
+template <typename T>
+__device__ __forceinline__ void narrow_fetch(NarrowPre& pre, const float* x, const T* g, int rows,
+                                             int m0, int M, int n0, int ncols, int N, int tid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const NarrowItem t = narrow_item(j, rows, m0, M, n0, ncols, N, tid);
+    pre.x[j] = (x != nullptr && t.act) ? x[(int64_t)t.m * N + t.n] : 0.f;
+    pre.g[j] = (g != nullptr && t.act) ? Num<T>::to_f(g[t.n]) : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------- tiled kernel
@@ -740,19 +988,25 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
       const int r = r0 + nw * u, m = m0 + r;
       if (r >= rows) break;
       if (m >= M) continue;
-      float acc = 0.f;
+      float sq[2] = {0.f, 0.f};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = lane + 64 * h, n = nt * BN + c;
         if (n < N) {
           const float v = f(r, c, m, n, iv[u][h]);
-          acc += v * v;
+          sq[h] = v * v;
           if (nn.xg != nullptr) nn.xg[(int64_t)m * N + n] = Num<T>::from_f(v * gn[h]);
         }
       }
       if (ss != nullptr) {
-        acc = wave_sum(acc);
-        if (lane == 0) ss[(int64_t)m * n_ss + nt] = acc;
+        // per 16-column group: lanes 16 q .. 16 q + 15 hold columns 16 q + i
+        // (h = 0) and 64 + 16 q + i (h = 1) of the tile
+        const float s0 = row16_sum(sq[0]), s1 = row16_sum(sq[1]);
+        if ((lane & 15) == 0) {
+          const int t0 = nt * (BN / 16) + (lane >> 4), t1 = t0 + 4;
+          if (t0 < n_ss) ss[(int64_t)m * n_ss + t0] = s0;
+          if (t1 < n_ss) ss[(int64_t)m * n_ss + t1] = s1;
+        }
       }
     }
   }
@@ -760,6 +1014,7 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
 
 template <typename T> struct EpiStoreF32 {
   const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn; RowScale rs;
+  static constexpr int kNarrow = 1;
   // rows of an RMSNorm-scaled A source are multiplied by 1/rms (1 for a plain source)
   __device__ void prepare(int rows, int m0, int M, int tid) const {
     rs.fill(row_scale_lds(), rows, m0, M, tid);
@@ -776,10 +1031,34 @@ template <typename T> struct EpiStoreF32 {
                return v;
              });
   }
+  // narrow tiles (gemm_rows)
+  __device__ const T* nslab(int n0) const {
+    return W + (int64_t)(imin(n0, N - 1) / 16) * slab_elems(K);
+  }
+  __device__ void nrow_scale(float* srs, int rows, int m0, int M, int wave, int nw,
+                             int lane) const {
+    rs.fill_rows(srs, rows, m0, M, wave, nw, lane);
+  }
+  __device__ void nfetch(NarrowPre& pre, int rows, int m0, int M, int n0, int ncols,
+                         int tid) const {
+    narrow_fetch<T>(pre, nullptr, nn.xg != nullptr ? nn.g : nullptr, rows, m0, M, n0, ncols, N,
+                    tid);
+  }
+  __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int ncols,
+                         int tid, const NarrowPre& pre) const {
+    const float* srs = row_scale_lds();
+    narrow_rows(rows, m0, M, n0, ncols, N, tid, ss, ss_tiles(N), nn, pre,
+                [&](int r, int c, int m, int n, int) {
+                  const float v = t[r * ldt + c] * srs[r];
+                  if (out != nullptr) out[(int64_t)m * ldo + n] = v;
+                  return v;
+                });
+  }
 };
 
 template <typename T> struct EpiResidual {
   const T* W; int N; int K; float* x; float* ss; NextNorm<T> nn;
+  static constexpr int kNarrow = 1;
   __device__ void prepare(int, int, int, int) const {}
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
@@ -792,6 +1071,24 @@ template <typename T> struct EpiResidual {
                x[(int64_t)m * N + n] = v;
                return v;
              });
+  }
+  // narrow tiles (gemm_rows)
+  __device__ const T* nslab(int n0) const {
+    return W + (int64_t)(imin(n0, N - 1) / 16) * slab_elems(K);
+  }
+  __device__ void nrow_scale(float*, int, int, int, int, int, int) const {}
+  __device__ void nfetch(NarrowPre& pre, int rows, int m0, int M, int n0, int ncols,
+                         int tid) const {
+    narrow_fetch<T>(pre, x, nn.xg != nullptr ? nn.g : nullptr, rows, m0, M, n0, ncols, N, tid);
+  }
+  __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int ncols,
+                         int tid, const NarrowPre& pre) const {
+    narrow_rows(rows, m0, M, n0, ncols, N, tid, ss, ss_tiles(N), nn, pre,
+                [&](int r, int c, int m, int n, int j) {
+                  const float v = pre.x[j] + t[r * ldt + c];
+                  x[(int64_t)m * N + n] = v;
+                  return v;
+                });
   }
   // pre = the residual at row m0 + wave, columns nt * BN + lane (+ 64), then
   // the next norm's gains there (for_rows reads exactly these when rows <= waves)
@@ -821,6 +1118,7 @@ template <typename T> struct EpiResidual {
 // Tile columns 0..63 are gate rows nt*64.., columns 64..127 the matching up rows.
 template <typename T> struct EpiSiluMul {
   const T* Wg; const T* Wu; int I; int K; T* act; RowScale rs;
+  static constexpr int kNarrow = 2;
   __device__ void prepare(int rows, int m0, int M, int tid) const {
     rs.fill(row_scale_lds(), rows, m0, M, tid);
   }
@@ -835,6 +1133,31 @@ template <typename T> struct EpiSiluMul {
       if (m < M && n < I) {
         const float sc = srs[r];
         const float g = t[r * LDT + c] * sc, u = t[r * LDT + 64 + c] * sc;
+        act[(int64_t)m * I + n] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
+      }
+    }
+  }
+  // narrow tiles (gemm_rows): the column space is blocks of 32, [16 gate
+  // rows | the 16 matching up rows] for output columns 16 b .. 16 b + 15
+  __device__ const T* nslab(int n0) const {
+    const int o = imin((n0 / 32) * 16, I - 1);
+    return ((n0 & 16) ? Wu : Wg) + (int64_t)(o / 16) * slab_elems(K);
+  }
+  __device__ void nrow_scale(float* srs, int rows, int m0, int M, int wave, int nw,
+                             int lane) const {
+    rs.fill_rows(srs, rows, m0, M, wave, nw, lane);
+  }
+  __device__ void nfetch(NarrowPre&, int, int, int, int, int, int) const {}
+  __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int ncols,
+                         int tid, const NarrowPre&) const {
+    const float* srs = row_scale_lds();
+    const int half = ncols / 2;
+    for (int idx = tid; idx < rows * half; idx += (int)blockDim.x) {
+      const int r = idx / half, j = idx % half, pb = j / 16, i = j % 16;
+      const int m = m0 + r, n = n0 / 2 + j;
+      if (m < M && n < I) {
+        const float sc = srs[r];
+        const float g = t[r * ldt + 32 * pb + i] * sc, u = t[r * ldt + 32 * pb + 16 + i] * sc;
         act[(int64_t)m * I + n] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
       }
     }
@@ -1075,6 +1398,19 @@ template <typename T, typename KT> struct EpiKVInject {
 // then the (max, first index) of every row over the slice.
 template <typename T> struct EpiLogits {
   const T* W; int V; int H; T* logits; float2* part; int n_tiles; RowScale rs;
+  static constexpr int kNarrow = 8;  // 128-column tiles: one argmax partial each
+  __device__ const T* nslab(int n0) const {
+    return W + (int64_t)(imin(n0, V - 1) / 16) * slab_elems(H);
+  }
+  __device__ void nrow_scale(float* srs, int rows, int m0, int M, int wave, int nw,
+                             int lane) const {
+    rs.fill_rows(srs, rows, m0, M, wave, nw, lane);
+  }
+  __device__ void nfetch(NarrowPre&, int, int, int, int, int, int) const {}
+  __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int,
+                         int tid, const NarrowPre&) const {
+    apply_ld(t, ldt, rows, m0, M, n0 / BN, tid);
+  }
   __device__ void prepare(int rows, int m0, int M, int tid) const {
     rs.fill(row_scale_lds(), rows, m0, M, tid);
   }
@@ -1082,6 +1418,10 @@ template <typename T> struct EpiLogits {
     return W + (int64_t)(imin(nt * BN + 16 * s, V - 1) / 16) * slab_elems(H);
   }
   __device__ void apply(const float* t, int rows, int m0, int M, int nt, int tid) const {
+    apply_ld(t, LDT, rows, m0, M, nt, tid);
+  }
+  __device__ void apply_ld(const float* t, int ldt, int rows, int m0, int M, int nt,
+                           int tid) const {
     const float* srs = row_scale_lds();
     const int lane = tid & 63, wave = tid >> 6;
     for (int r = wave; r < rows; r += (int)(blockDim.x >> 6)) {
@@ -1094,7 +1434,7 @@ template <typename T> struct EpiLogits {
       for (int h = 0; h < 2; ++h) {
         const int c = lane + 64 * h, n = nt * BN + c;
         if (n < V) {
-          const T tv = Num<T>::from_f(t[r * LDT + c] * sc);
+          const T tv = Num<T>::from_f(t[r * ldt + c] * sc);
           if (logits != nullptr) logits[(int64_t)m * V + n] = tv;
           float v = Num<T>::to_f(tv);
           if (!(v == v)) v = -INFINITY;
@@ -1196,11 +1536,75 @@ static void launch_big(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPl
                        p.KS, p.m_tiles, M, (const float*)partial, epi);
 }
 
+// Slabs per workgroup of an epilogue that runs on narrow tiles (0: it needs
+// whole 128-column tiles).
+template <class E, class = void> struct NarrowSlabs {
+  static constexpr int value = 0;
+};
+template <class E> struct NarrowSlabs<E, decltype((void)E::kNarrow)> {
+  static constexpr int value = E::kNarrow;
+};
+
+// K splits of gemm_rows interleaved by 64-wide step (else contiguous ranges).
+constexpr bool kRowsInterleave = true;
+
+// Register ring depth and occupancy of gemm_rows: bf16 kernels are held to
+// four waves per SIMD (<= 128 VGPRs: one 16-wave or two 8-wave workgroups per
+// CU), fp32 ones to two; the ring takes what the accumulators and addresses
+// leave.  (The second launch-bounds argument is the minimum waves per SIMD.)
+template <typename T, int MB, int NSL, int NW, class AS, class Epi>
+static void launch_rows_cfg(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
+                            hipStream_t st) {
+  constexpr int NSW = NSL > 2 ? 2 : NSL;  // slabs per wave
+  constexpr int STEP = (MB + NSW) * 2 * (sizeof(T) == 2 ? 4 : 8);
+  constexpr int FIXED = MB * NSW * 4 + 32;  // accumulators, addresses, indices, prefetch
+  // four waves per SIMD where a two-step ring fits in 128 VGPRs (always for
+  // 16-wave workgroups), else three (168)
+  constexpr int MINW = sizeof(T) == 2 ? ((NW == 16 || 2 * STEP + FIXED <= 128) ? 4 : 3) : 2;
+  constexpr int BUDGET = (MINW == 4 ? 128 : (MINW == 3 ? 168 : 256)) - FIXED;
+  constexpr int NB0 = BUDGET / STEP;
+  constexpr int NB = NB0 < 1 ? 1 : (NB0 > 4 ? 4 : NB0);
+  hipLaunchKernelGGL((gemm_rows<T, MB, NSL, NSW, NW, NB, MINW, kRowsInterleave, AS, Epi>),
+                     dim3((unsigned)(p.n_tiles * p.m_tiles)), dim3(NW * 64), 0, st, asrc, M, K,
+                     p.kw, p.m_tiles, epi);
+}
+template <typename T, int NSL, class AS, class Epi>
+static void launch_rows(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
+                        hipStream_t st) {
+  if constexpr (NSL == 8) {  // up to 32 rows (plan_gemm)
+    constexpr int NW = sizeof(T) == 2 ? 16 : 8;
+    if (p.MB == 1) launch_rows_cfg<T, 1, NSL, NW>(asrc, M, K, p, epi, st);
+    else launch_rows_cfg<T, 2, NSL, NW>(asrc, M, K, p, epi, st);
+    return;
+  }
+  if constexpr (sizeof(T) == 2 && NSL == 1) {
+    if (p.NW == 16) {
+      switch (p.MB) {
+        case 1: launch_rows_cfg<T, 1, NSL, 16>(asrc, M, K, p, epi, st); return;
+        case 2: launch_rows_cfg<T, 2, NSL, 16>(asrc, M, K, p, epi, st); return;
+        default: launch_rows_cfg<T, 4, NSL, 16>(asrc, M, K, p, epi, st); return;
+      }
+    }
+  }
+  switch (p.MB) {
+    case 1: launch_rows_cfg<T, 1, NSL, 8>(asrc, M, K, p, epi, st); return;
+    case 2: launch_rows_cfg<T, 2, NSL, 8>(asrc, M, K, p, epi, st); return;
+    default: launch_rows_cfg<T, 4, NSL, 8>(asrc, M, K, p, epi, st); return;
+  }
+}
+
 template <typename T, class AS, class Epi>
 static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& epi,
                            const GemmScratch& ws, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  const GemmPlan p = plan_gemm(M, Ncols, K, sizeof(T) == 2);
+  constexpr int NAR = NarrowSlabs<Epi>::value;
+  const GemmPlan p = plan_gemm(M, Ncols, K, sizeof(T) == 2, NAR);
+  if constexpr (NAR > 0) {
+    if (p.rows) {
+      launch_rows<T, NAR>(asrc, M, K, p, epi, st);
+      return hipGetLastError();
+    }
+  }
   if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     if (p.big) {

@@ -18,6 +18,10 @@ struct GemmScratch {
 // Launch geometry of a GEMM C[M, Ncols] = A[M, K] W^T: the weight-streaming
 // kernel (M <= 64, or fp32) or the LDS-tiled kernel (bf16, M > 64).
 struct GemmPlan {
+  bool rows;     // narrow tiles, K split inside the workgroup (gemm_rows; M <= 64)
+  int NSL;       //   packed 16-column slabs per workgroup (1 or 2)
+  int NW;        //   waves per workgroup (8 or 16), each streaming kw of K
+  int kw;
   bool fat;      // LDS-tiled kernel
   bool big;      // 256 x 256 tiles, no split K (n_tiles counts 256 columns)
   int BM;        // rows per tile (16 MB for the streaming kernel; 128 or 256)
@@ -27,7 +31,10 @@ struct GemmPlan {
   int KS;        // split-K factor
   int Kc;        // K elements per split
 };
-GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16);
+// narrow: slabs per workgroup when the epilogue runs on narrow tiles (1 for
+// store and residual, 2 for SwiGLU's gate/up pairs; 0: it needs 128-column
+// tiles), so that up to 64 rows take gemm_rows (no split-K partials)
+GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow = 0);
 size_t gemm_partial_floats(const GemmPlan& p);
 
 struct KVTargets {
@@ -40,7 +47,7 @@ struct KVTargets {
 // A operand of a GEMM: rows of T with row stride lda.  S_skip > 0 maps GEMM row
 // m to A row (m / (S-1)) * S + m % (S-1) + 1.  When ss != null the A rows are
 // x * g of an RMSNorm and each output row is scaled by 1/rms(x), from the sums
-// of squares ss[row * n_ss + t] of columns [128 t, 128 t + 128) of x (width H).
+// of squares ss[row * n_ss + t] of columns [16 t, 16 t + 16) of x (width H).
 struct ASrc {
   const void* a;
   int64_t lda;
@@ -54,10 +61,11 @@ inline ASrc asrc_plain(const void* a, int64_t lda, int S_skip = 0) {
   return ASrc{a, lda, nullptr, 0, 0, 0.f, S_skip};
 }
 inline ASrc asrc_normed(const void* xg, int H, const float* ss, float eps, int S_skip = 0) {
-  return ASrc{xg, H, ss, (H + 127) / 128, H, eps, S_skip};
+  return ASrc{xg, H, ss, (H + 15) / 16, H, eps, S_skip};
 }
-// 128-column tiles of a row (the granularity of the row sums of squares)
-__host__ __device__ inline int ss_tiles(int H) { return (H + 127) / 128; }
+// 16-column groups of a row: the granularity of the row sums of squares (one
+// packed weight slab of output columns, the narrowest tile a GEMM writes)
+__host__ __device__ inline int ss_tiles(int H) { return (H + 15) / 16; }
 
 // y = A W^T: out[M, N] fp32 (nullable), per-128-column row sums of squares of y
 // into ss (nullable) and xg = y * g_next rounded to the act dtype (nullable)

@@ -132,6 +132,16 @@ def top2_margin(orc):
     return s[..., -1] - s[..., -2]
 
 
+def argmax_checked_rows(orc, margin):
+    """Rows whose oracle top-2 margin exceeds `margin` on the scale the logits
+    tolerance is stated on (a fraction of the row's max |oracle logit|): a
+    path within a relative error bound e of that scale can reorder any two
+    logits closer than 2 e of it, so its argmax must agree wherever the
+    margin exceeds 2 e (5e-2 > 2 x 2e-2 for bf16; 1e-3 > 2 x 1e-4 for fp32)."""
+    o = np.asarray(orc, np.float64)
+    return top2_margin(o) > margin * np.max(np.abs(o), axis=-1)
+
+
 def e4m3_spacing(x):
     """Distance between adjacent E4M3 values around |x|."""
     a = np.abs(np.asarray(x, np.float64))

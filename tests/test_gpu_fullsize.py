@@ -17,7 +17,7 @@ import oracle
 from oracle.formats import e4m3_decode
 from workloads import synth
 from workloads.configs import get_workload
-from tests.gpu_harness import dfl, logits_row_rel_err, top2_margin, e4m3_spacing
+from tests.gpu_harness import dfl, logits_row_rel_err, argmax_checked_rows, e4m3_spacing
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -139,12 +139,22 @@ def _check_draft(st, reqs):
     assert np.array_equal(out["slots"].cpu().numpy(), o["slots"])
     gl = out["logits"].float().cpu().numpy()[reqs]
     rel = logits_row_rel_err(gl, o["logits"])
-    sure = top2_margin(o["logits"]) > 5e-2
+    sure = argmax_checked_rows(o["logits"], 5e-2)
     cand = out["candidates"].cpu().numpy()[reqs]
     _print(f"  logits max rel err {rel.max():.3e}; argmax checked on {sure.sum()}/{sure.size} rows")
+    for b, j in zip(*np.nonzero(cand[:, 1:] != o["draft_ids"])):
+        ol = o["logits"][b, j]
+        top = np.argsort(-ol)[:2]
+        g_id = cand[b, j + 1]
+        _print(f"  row ({reqs[b]}, {j + 1}): gpu {g_id} (oracle {ol[g_id]:.5f}, gpu "
+               f"{gl[b, j, g_id]:.5f}); oracle top-2 {top.tolist()} {ol[top].round(5).tolist()} "
+               f"(gpu {gl[b, j, top].round(5).tolist()}); row max |oracle| "
+               f"{np.abs(ol).max():.4f}, max |gpu - oracle| {np.abs(gl[b, j] - ol).max():.5f}")
     assert rel.max() <= 2e-2
     assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
     assert np.array_equal(cand[:, 0], st.anchor.numpy()[reqs])
+    # the GPU's ids are the argmax of its own stored logits (first index on ties)
+    assert np.array_equal(cand[:, 1:], np.argmax(gl, axis=-1))
 
 
 def _check_inject(st, feats, pos, slots, valid, n_req, rpr, sample_rows):

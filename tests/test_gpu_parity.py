@@ -6,9 +6,14 @@ fp32 caches.  Integers bit-exact; floating point within the tolerances below.
 Tolerances (floating point):
 * bf16 models: logits max|gpu - oracle| / max|oracle| per row <= 2e-2, and the
   draft id must equal the oracle's argmax wherever the oracle's top-2 margin
-  exceeds 5e-2; injected K/V per (slot, head) max|gpu - oracle| /
-  max|oracle| <= 2e-2.
-* fp32 models: 1e-4 relative, argmax agreement where the margin exceeds 1e-3.
+  exceeds 5e-2 on the same scale (5e-2 x max|oracle| of the row: within the
+  2e-2 bound two logits can swap only if they are closer than 4e-2 of it);
+  injected K/V per (slot, head) max|gpu - oracle| / max|oracle| <= 2e-2.
+* fp32 models: 1e-4 relative, argmax agreement where the margin exceeds 1e-3
+  of the row's max |oracle logit|.
+* every row: the draft id is the argmax (first index among equal maxima) of
+  the GPU's own stored logits, bit-exactly -- the integer decision taken in
+  the kernel's precision.
 * fp8 caches: every stored value within one E4M3 step (at that magnitude)
   plus the bf16-class allowance 2e-2 * max|oracle| of its head, and at least
   90% of codes identical: the two sides round slightly different values (the
@@ -27,7 +32,7 @@ import torch
 import oracle
 from workloads import synth
 from workloads.configs import get_workload
-from tests.gpu_harness import Setup, logits_row_rel_err, top2_margin, e4m3_spacing, dfl
+from tests.gpu_harness import Setup, logits_row_rel_err, argmax_checked_rows, e4m3_spacing, dfl
 
 pytestmark = pytest.mark.gpu
 
@@ -178,8 +183,7 @@ def test_draft_block_parity(name):
     rel = logits_row_rel_err(gl, o["logits"])
     _print(f"  logits max rel err {rel.max():.3e}")
     assert rel.max() <= rel_tol
-    margin = top2_margin(o["logits"])
-    sure = margin > m_tol
+    sure = argmax_checked_rows(o["logits"], m_tol)
     assert sure.mean() > 0.3
     assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
     # the GPU's ids are the argmax of its own logits (first index on ties)
@@ -362,7 +366,7 @@ def test_cycle_inject_draft_accept(name):
     rel = logits_row_rel_err(out2["logits"].float().cpu().numpy(), o2["logits"])
     _print(f"  cycle-2 logits max rel err {rel.max():.3e}")
     assert rel.max() <= rel_tol
-    sure = top2_margin(o2["logits"]) > m_tol
+    sure = argmax_checked_rows(o2["logits"], m_tol)
     assert np.array_equal(out2["candidates"].cpu().numpy()[:, 1:][sure], o2["draft_ids"][sure])
 
 
@@ -393,6 +397,6 @@ def test_draft_block_window_ring_parity(name, window):
     rel = logits_row_rel_err(gl, o["logits"])
     _print(f"  logits max rel err {rel.max():.3e}")
     assert rel.max() <= rel_tol
-    sure = top2_margin(o["logits"]) > m_tol
+    sure = argmax_checked_rows(o["logits"], m_tol)
     cand = out["candidates"].cpu().numpy()
     assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
