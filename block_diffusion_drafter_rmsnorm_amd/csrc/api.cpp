@@ -158,7 +158,8 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
 
 struct DraftWs {
   float* x; float* ss; void* xg; void* act; void* q; void* kb; void* vb; void* o; float2* cs;
-  float* o_part; float2* ml_part; int4* seg; float2* lm_part; GemmScratch gs; size_t bytes;
+  float* o_part; float2* ml_part; int4* seg; float2* lm_part; float* qkv_raw; GemmScratch gs;
+  size_t bytes;
   AttnPlan plans[DFLASH_MAX_LAYERS];
 };
 
@@ -196,8 +197,14 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   L.ml_part = (float2*)cv.take(sizeof(float2) * max_launch * 64);
   L.seg = (int4*)cv.take(sizeof(int4) * (size_t)B);
   L.lm_part = (float2*)cv.take(sizeof(float2) * (size_t)M1 * logits_tiles(c->vocab));
+  // fp32 q/k/v of the narrow QKV GEMM (up to 64 block rows)
+  L.qkv_raw = M <= 64 ? (float*)cv.take(sizeof(float) * (size_t)qkv_k_splits((nq + 2 * nkv) * D) *
+                                         M * (nq + 2 * nkv) * D)
+                      : nullptr;
   const bool bf = c->act_dtype == DFLASH_BF16;
-  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H, bf), plan_gemm(M, H, nq * D, bf, 1),
+  const GemmPlan ps[] = {plan_gemm(M, (nq + 2 * nkv) * D, H, bf, M <= 64 ? qkv_slabs() : 0,
+                                   qkv_k_splits((nq + 2 * nkv) * D)),
+                         plan_gemm(M, H, nq * D, bf, 1),
                          plan_gemm(M, ((I + 63) / 64) * 128, H, bf, 2), plan_gemm(M, H, I, bf, 1),
                          plan_gemm(M1, c->vocab, H, bf, 8)};
   size_t pf = 0;
@@ -394,7 +401,7 @@ static dflash_status draft_core(const dflash_config* cfg, const dflash_weights* 
     const dflash_layer_weights& W = w->layer[l];
     const void* g_after = (l + 1 < cfg->n_layers) ? w->layer[l + 1].in_norm : w->final_norm;
     if ((e = gemm_qkv(dt, xin, M, H, W.w_qkv, W.q_norm, W.k_norm, nq, nkv, D, eps, L.cs, L.q, L.kb,
-                      L.vb, S, L.gs, st)) != hipSuccess)
+                      L.vb, S, L.qkv_raw, L.gs, st)) != hipSuccess)
       return hip_fail(e, "qkv gemm");
     if ((e = launch_attention(dt, cfg->kv_dtype, D, L.q, L.kb, L.vb, cache->k[l], cache->v[l],
                               page_table, max_pages, cache->num_pages, prefix_len, max_prefix_len,

@@ -52,8 +52,29 @@ constexpr int kDeepSteps = 8;                       // workgroup size of the dee
 //   grows (in multiples of 256) so that no range exceeds kMaxSteps units.
 AttnPlan plan_attention(int max_keys, int B, int nkv, bool dma) {
   AttnPlan p;
+  p.kps = 0;
   const int64_t units_max = 1 + ((int64_t)(max_keys > 0 ? max_keys : 0) + 31 + 31) / 32;
   const int64_t u_max = units_max * B * nkv;
+  if (dma && (int64_t)B * nkv <= 64) {
+    // Few segments (small batches): kps workgroups per segment, none crossing
+    // a segment, at most 256 in all unless a part would exceed kMaxSteps, and
+    // at least ~2 context steps each.  The split is by the context length
+    // the host bounds (max_prefix), so every workgroup knows its key range
+    // before any length arrives (aligned kernel).
+    const int segs = B * nkv;
+    const int64_t ctx = units_max - 1;
+    int64_t k = kCUs / segs;
+    if (k > (ctx + 1) / 2) k = (ctx + 1) / 2;
+    const int64_t kmin = (ctx + kMaxSteps - 2) / (kMaxSteps - 1);
+    if (k < kmin) k = kmin;
+    if (k < 1) k = 1;
+    p.kps = (int)k;
+    p.stages = kDeepSteps;
+    p.n_launch = (int)(segs * k);
+    p.n_partials = p.n_launch;
+    p.fits = true;
+    return p;
+  }
   int64_t W;
   if (dma && u_max <= (int64_t)kDeepSteps * kCUs) {
     // at most one workgroup per CU, with at least ~5 steps each: fewer
@@ -82,6 +103,7 @@ struct AttnArgs {
   const int32_t* prefix_len; int max_prefix;
   int B, S, G, nq, nkv, P, window, W;
   int cwin;                            // draft window: last cwin context keys (0: all)
+  int kps;                             // aligned partition: workgroups per segment (0: by bytes)
   float scale_log2;
   float* o_part; float2* ml_part;  // per partial slot: [64 rows][D], [64 rows]
   int4* seg;                       // per request: (units before it per head, units, U, -)
@@ -616,62 +638,28 @@ template <int DPW, int K> __device__ __forceinline__ void attn_wait_steps(int la
   }
 }
 
+// One part of a segment on the bf16 cache: the block's own keys (when blk)
+// and n_ctx context steps from kbeg, staged NS deep straight from global
+// memory into LDS, then this wave's unnormalised O^T and (m, l) per query row
+// at partial slot `base`.  The page list (physical page of logical page
+// pfirst + i in pages[i]) and Q are in place; every wave of the workgroup
+// calls it.
 template <int D, int NS>
-__global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs a) {
+__device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L, int lo, int blk,
+                                         int n_ctx, int kbeg, int kend, int pfirst,
+                                         const int* pages, bf16_t (*stg_s)[64 * D],
+                                         const Frag<bf16_t> (&qf)[D / 32], int64_t base) {
   using CT = bf16_t;
-  constexpr int STAGE = 64 * D;       // elements of one staged step
   constexpr int OPW = D / 64;         // K (and V) DMAs per wave per step
   constexpr int DPW = 2 * OPW;        // DMAs per wave per step
-  __shared__ int pages[kMaxChunkPages];
-  __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
-  __shared__ int red[12];
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, r16 = lane & 15,
             g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
   const bool qlive = wave * 16 < R;
   const int rho = imin(wave * 16 + r16, R - 1);
   const int jrow = rho % S;
-  const UnitTable tab = unit_table(a, red);
-  write_seg_table(a, tab);
-  const int64_t x_end = range_start((int64_t)blockIdx.x + 1, tab.U, a.W);
-  for (int64_t x = range_start(blockIdx.x, tab.U, a.W); x < x_end;) {
-  const SegPos sp = find_segment(a, tab, x, red);
-  const int g = sp.g, r = sp.r, L = sp.L;
-  const int u0 = (int)(x - sp.start);
-  const int u1 = (int)((x_end < sp.start + sp.units ? x_end : sp.start + sp.units) - sp.start);
-  const int64_t base = ((int64_t)blockIdx.x + r * a.nkv + g) * 64;  // partial slot w + s
-  x = sp.start + u1;
-  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
-  Frag<CT> qf[D / 32];
-  {
-    const int hl = rho / S;
-    const CT* qp = static_cast<const CT*>(a.q) + ((int64_t)(r * S + jrow) * a.nq + g * a.G + hl) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
-  }
-  const int lo = key_lo(a, L);
-  const int a0 = lo & ~31;
-  const int blk = u0 == 0 ? 1 : 0;                 // the part starts with the block's keys
-  const int t_first = imax(u0 - 1, 0);             // first context step
-  const int n_ctx = u1 - 1 - t_first;              // context steps of the part
-  const int kbeg = a0 + 32 * t_first;
-  const int kend = imin(L, kbeg + 32 * n_ctx);
-  const int pfirst = kbeg / a.P;
-  if (n_ctx > 0) {
-    const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
-    for (int i = tid; i < npages; i += 256) {
-      const int64_t page = a.pt[(int64_t)r * a.max_pages + (pfirst + i) % a.max_pages];
-      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
-    }
-  }
-  // every load the compiler issued (Q, page table) is complete from here on,
-  // and it knows so: it does not wait again, behind the DMAs, before the
-  // first use of Q
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  lds_barrier();
-
-  // Steps: the first part of a segment starts with the block's own keys
-  // (one 16-key page, both halves pointing at it), then the context steps.
+  // Steps: the block's own keys first (one 16-key page, both halves pointing
+  // at it) when blk, then the context steps.
   const int n_seq = n_ctx + blk;
   const CT* kc = static_cast<const CT*>(a.kc);
   const CT* vc = static_cast<const CT*>(a.vc);
@@ -827,9 +815,133 @@ __global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs
           make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
     if (g4 == 0) a.ml_part[base + wave * 16 + r16] = make_float2(mq, lq);
   }
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs a) {
+  using CT = bf16_t;
+  constexpr int STAGE = 64 * D;       // elements of one staged step
+  constexpr int OPW = D / 64;         // K (and V) DMAs per wave per step
+  constexpr int DPW = 2 * OPW;        // DMAs per wave per step
+  __shared__ int pages[kMaxChunkPages];
+  __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
+  __shared__ int red[12];
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, r16 = lane & 15,
+            g4 = lane >> 4;
+  const int S = a.S, R = a.G * S;
+  const bool qlive = wave * 16 < R;
+  const int rho = imin(wave * 16 + r16, R - 1);
+  const int jrow = rho % S;
+  const UnitTable tab = unit_table(a, red);
+  write_seg_table(a, tab);
+  const int64_t x_end = range_start((int64_t)blockIdx.x + 1, tab.U, a.W);
+  for (int64_t x = range_start(blockIdx.x, tab.U, a.W); x < x_end;) {
+  const SegPos sp = find_segment(a, tab, x, red);
+  const int g = sp.g, r = sp.r, L = sp.L;
+  const int u0 = (int)(x - sp.start);
+  const int u1 = (int)((x_end < sp.start + sp.units ? x_end : sp.start + sp.units) - sp.start);
+  const int64_t base = ((int64_t)blockIdx.x + r * a.nkv + g) * 64;  // partial slot w + s
+  x = sp.start + u1;
+  // Q^T (B operand): query r16 of this wave's block, dims ks*32 + g4*8 .. +8
+  Frag<CT> qf[D / 32];
+  {
+    const int hl = rho / S;
+    const CT* qp = static_cast<const CT*>(a.q) + ((int64_t)(r * S + jrow) * a.nq + g * a.G + hl) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
+  }
+  const int lo = key_lo(a, L);
+  const int a0 = lo & ~31;
+  const int blk = u0 == 0 ? 1 : 0;                 // the part starts with the block's keys
+  const int t_first = imax(u0 - 1, 0);             // first context step
+  const int n_ctx = u1 - 1 - t_first;              // context steps of the part
+  const int kbeg = a0 + 32 * t_first;
+  const int kend = imin(L, kbeg + 32 * n_ctx);
+  const int pfirst = kbeg / a.P;
+  if (n_ctx > 0) {
+    const int npages = (kbeg + 32 * n_ctx - 1) / a.P - pfirst + 1;
+    for (int i = tid; i < npages; i += 256) {
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + (pfirst + i) % a.max_pages];
+      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
+    }
+  }
+  // every load the compiler issued (Q, page table) is complete from here on,
+  // and it knows so: it does not wait again, behind the DMAs, before the
+  // first use of Q
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  lds_barrier();
+
+  dma_part<D, NS>(a, r, g, L, lo, blk, n_ctx, kbeg, kend, pfirst, pages, stg_s, qf, base);
   // the next part reuses the stage buffers and the page list
   __syncthreads();
   }
+}
+
+// Aligned partition (few segments): workgroup w takes part w % kps of
+// segment w / kps = (request r, kv head g): the segment's context steps are
+// cut into kps equal parts (part 0 also takes the block's own keys), so no
+// workgroup crosses a segment and each writes exactly one partial, at slot w.
+// The cut is computed from max_prefix first, so the page-table entries of the
+// part go out together with Q and the request's length; only when the length
+// differs from max_prefix is the part recomputed and its page list reloaded.
+struct PartGeom {
+  int lo, blk, n_ctx, kbeg, kend, pfirst, npages;
+};
+__device__ __forceinline__ PartGeom part_geom(const AttnArgs& a, int L, int part) {
+  PartGeom q;
+  q.lo = key_lo(a, L);
+  const int a0 = q.lo & ~31;
+  const int steps = L > a0 ? (L - a0 + 31) / 32 : 0;
+  const int t0 = (int)((int64_t)part * steps / a.kps);
+  const int t1 = (int)((int64_t)(part + 1) * steps / a.kps);
+  q.blk = part == 0 ? 1 : 0;
+  q.n_ctx = t1 - t0;
+  q.kbeg = a0 + 32 * t0;
+  q.kend = imin(L, q.kbeg + 32 * q.n_ctx);
+  q.pfirst = q.kbeg / a.P;
+  q.npages = q.n_ctx > 0 ? (q.kbeg + 32 * q.n_ctx - 1) / a.P - q.pfirst + 1 : 0;
+  return q;
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(256, 1) void attn_dma_aligned(AttnArgs a) {
+  using CT = bf16_t;
+  constexpr int STAGE = 64 * D;
+  __shared__ int pages[kMaxChunkPages];
+  __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4;
+  const int S = a.S, R = a.G * S;
+  const int rho = imin(wave * 16 + (lane & 15), R - 1);
+  const int jrow = rho % S;
+  const int seg = (int)blockIdx.x / a.kps, part = (int)blockIdx.x % a.kps;
+  const int r = seg / a.nkv, g = seg % a.nkv;
+  // the request's length, Q and the page entries of the part as if the
+  // length were max_prefix, all in flight together
+  const int L = clamped_len(a, r);
+  Frag<CT> qf[D / 32];
+  {
+    const int hl = rho / S;
+    const CT* qp = static_cast<const CT*>(a.q) + ((int64_t)(r * S + jrow) * a.nq + g * a.G + hl) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) load_frag(qf[ks], qp + ks * 32 + g4 * 8);
+  }
+  auto load_pages = [&](const PartGeom& q) {
+    for (int i = tid; i < q.npages; i += 256) {
+      const int64_t page = a.pt[(int64_t)r * a.max_pages + (q.pfirst + i) % a.max_pages];
+      pages[i] = (int)(page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page));
+    }
+  };
+  PartGeom q = part_geom(a, a.max_prefix, part);
+  load_pages(q);
+  if (L != a.max_prefix) {  // wave-uniform (one request per workgroup)
+    q = part_geom(a, L, part);
+    lds_barrier();          // every wave is done with the first list
+    load_pages(q);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the page list are in
+  lds_barrier();
+  dma_part<D, NS>(a, r, g, L, q.lo, q.blk, q.n_ctx, q.kbeg, q.kend, q.pfirst, pages, stg_s, qf,
+                  (int64_t)blockIdx.x * 64);
 }
 
 // Combine the partials of one query row: one wave per row.  A partial in
@@ -848,15 +960,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __res
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.B * a.nkv * R) return;
   const int rho = row % R, g = (row / R) % a.nkv, r = row / (R * a.nkv);
-  // the workgroups whose ranges meet segment s = (r, g); that of workgroup
-  // w is written at partial slot w + s
-  const int4 sg = a.seg[r];
-  const int64_t U = sg.z, s0 = ((int64_t)sg.x * a.nkv + (int64_t)g * sg.y);
-  const int w_lo = range_owner(s0, U, a.W), w_hi = range_owner(s0 + sg.y - 1, U, a.W);
-  const int n = w_hi - w_lo + 1;
-  auto prow = [&](int s) { return ((int64_t)w_lo + s + r * a.nkv + g) * 64 + rho; };
+  // the workgroups whose ranges meet segment s = (r, g): with the aligned
+  // partition parts kps s .. kps s + kps - 1 (each at its own slot, every one
+  // written); otherwise those of the byte ranges, workgroup w's at slot w + s
+  int w_lo, n;
+  int64_t U = 0;
+  if (a.kps > 0) {
+    w_lo = (r * a.nkv + g) * a.kps;
+    n = a.kps;
+  } else {
+    const int4 sg = a.seg[r];
+    U = sg.z;
+    const int64_t s0 = ((int64_t)sg.x * a.nkv + (int64_t)g * sg.y);
+    w_lo = range_owner(s0, U, a.W);
+    n = range_owner(s0 + sg.y - 1, U, a.W) - w_lo + 1;
+  }
+  const int slot_off = a.kps > 0 ? 0 : r * a.nkv + g;
+  auto prow = [&](int s) { return ((int64_t)w_lo + s + slot_off) * 64 + rho; };
   // with U < W some ranges are empty: those workgroups wrote nothing
   auto has_range = [&](int s) {
+    if (a.kps > 0) return true;
     const int64_t w = (int64_t)w_lo + s;
     return range_start(w + 1, U, a.W) > range_start(w, U, a.W);
   };
@@ -927,7 +1050,9 @@ template <typename CT, typename KT, int D>
 static hipError_t run_attn(const AttnArgs& a, const AttnPlan& plan, void* out, hipStream_t st) {
   const dim3 grid((unsigned)plan.n_launch);
   if constexpr (std::is_same<CT, bf16_t>::value && std::is_same<KT, bf16_t>::value) {
-    if (plan.stages == kDeepSteps)
+    if (plan.kps > 0)
+      hipLaunchKernelGGL((attn_dma_aligned<D, kDeepSteps>), grid, dim3(256), 0, st, a);
+    else if (plan.stages == kDeepSteps)
       hipLaunchKernelGGL((attn_dma_kernel<D, kDeepSteps>), grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((attn_dma_kernel<D, 3>), grid, dim3(256), 0, st, a);
@@ -958,6 +1083,7 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
   a.prefix_len = prefix_len; a.max_prefix = max_prefix;
   a.B = B; a.S = S; a.G = nq / nkv; a.nq = nq; a.nkv = nkv; a.P = page_size; a.window = window;
   a.cwin = ctx_window;
+  a.kps = plan.kps;
   a.W = plan.n_launch;
   a.scale_log2 = LOG2E / sqrtf((float)D);
   a.o_part = o_part; a.ml_part = ml_part; a.seg = seg;

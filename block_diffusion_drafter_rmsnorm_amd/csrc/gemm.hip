@@ -37,10 +37,17 @@ __host__ __device__ __forceinline__ int64_t slab_elems(int K) {
   return (int64_t)(K / 32) * kChunkElems;
 }
 
-GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow) {
+// The narrow QKV GEMM (its consumer adds K-range partials): target workgroup
+// count, slabs per workgroup (and per wave), waves per workgroup.
+constexpr int kQkvUnits = 768;  // target workgroups of the narrow QKV GEMM
+constexpr int kQkvSlabs = 2;    // its slabs per workgroup (and per wave)
+constexpr int kQkvWaves = 4;    // its waves per workgroup
+
+GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow, int ksw) {
   GemmPlan p;
   p.rows = false;
   p.NSL = p.NW = p.kw = 0;
+  p.KSW = 1;
   // (128-column tiles: up to 32 rows, so the per-wave partial tiles fit in LDS)
   if (narrow > 0 && M <= (narrow == 8 ? 32 : 64)) {
     // narrow tiles: one or two slabs per workgroup (two for SwiGLU: a gate
@@ -53,14 +60,18 @@ GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow) {
     p.BM = 16 * p.MB;
     p.m_tiles = (M + p.BM - 1) / p.BM;
     p.n_tiles = (Ncols + 16 * p.NSL - 1) / (16 * p.NSL);
-    // NSL 8 (the lm_head's 128-column argmax tiles): 16 waves = 4 slab pairs x
-    // 4 K splits, so that even a partial last round of workgroups keeps
-    // thousands of waves streaming
-    p.NW = (bf16 && (p.NSL == 8 || (p.NSL == 1 && p.n_tiles < 512))) ? 16 : 8;
-    const int nsw = p.NSL > 2 ? 2 : p.NSL;       // slabs per wave (gemm_rows' NSW)
-    const int ksplit = p.NW / (p.NSL / nsw);      // waves per slab group
-    int kw = (K + ksplit - 1) / ksplit;
-    p.kw = (kw + 31) / 32 * 32;
+    // waves per workgroup: 16 when the tiles fit one round of 16 waves per CU
+    // (4096 waves on the chip), else 8; the lm_head's 128-column tiles take 8
+    // = 4 slab pairs x 2 K splits.  fp32: 8.
+    if (!bf16) p.NW = 8;
+    else if (p.NSL == 8) p.NW = 8;
+    else if (ksw > 1) p.NW = kQkvWaves;  // the QKV store split over workgroups
+    else if (p.NSL == 1) p.NW = p.n_tiles <= 256 ? 16 : 8;  // (narrow_rows: <= 8 x NW items)
+    else p.NW = 8;  // (gate/up: 8 measured faster than 4)
+    // K ranges across workgroups (ksw > 1 only for epilogues whose consumer
+    // sums the partials): kw = the K of each range, a multiple of 64
+    p.KSW = ksw > 1 ? ksw : 1;
+    p.kw = ((K + p.KSW - 1) / p.KSW + 63) / 64 * 64;
     p.KS = 1;
     p.Kc = K;
     return p;
@@ -139,6 +150,15 @@ size_t gemm_partial_floats(const GemmPlan& p) {
 
 int logits_tiles(int V) { return (V + BN - 1) / BN; }
 
+// K ranges of the narrow QKV GEMM across workgroups: enough that the
+// workgroups come to ~kQkvUnits, at most 4.
+int qkv_slabs() { return kQkvSlabs; }
+int qkv_k_splits(int ncols) {
+  const int slabs = (ncols + 15) / 16;
+  int k = (kQkvUnits * kQkvSlabs + slabs - 1) / slabs;
+  return k < 1 ? 1 : (k > 4 ? 4 : k);
+}
+
 // ---------------------------------------------------------------- A sources
 // A rows as stored (T).  With S > 0 GEMM row m reads A row
 // (m / (S-1)) * S + m % (S-1) + 1 (rows 1..S-1 of every block: lm_head skips
@@ -215,10 +235,44 @@ struct RowScale {
     }
     __syncthreads();
   }
+  // Rows first and first + step of a wave's rows (below): their partial sums
+  // loaded into registers before the K loop, consumed after it (no wait in
+  // between, so the loop's weight loads stay in flight).
+  __device__ __forceinline__ void pre_rows(float (&v)[2][8], int rows, int m0, int M, int first,
+                                           int step, int lane) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = first + step * u;
+      const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[u][q] = (ss != nullptr && r < rows && lane + 64 * q < n_ss) ? p[lane + 64 * q] : 0.f;
+    }
+  }
+  __device__ __forceinline__ void finish_rows(const float (&v)[2][8], float* out, int rows,
+                                              int m0, int M, int first, int step,
+                                              int lane) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = first + step * u;
+      if (r >= rows) break;
+      float inv = 1.0f;
+      if (ss != nullptr) {
+        const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc += v[u][q];
+        for (int t = lane + 64 * 8; t < n_ss; t += 64) acc += p[t];
+        inv = 1.0f / sqrtf(wave_sum(acc) / (float)H + eps);
+      }
+      if (lane == 0) out[r] = inv;
+    }
+    // rows beyond two per wave
+    fill_rows(out, rows, m0, M, first + 2 * step, step, lane);
+  }
   // 1/rms of rows first, first + step, ... (< rows) into out[] (LDS), by the
   // calling wave alone and without a barrier (the caller's next barrier
-  // publishes them): gemm_rows computes its row scales while its first weight
-  // loads are in flight.
+  // publishes them).
   __device__ __forceinline__ void fill_rows(float* out, int rows, int m0, int M, int first,
                                             int step, int lane) const {
     constexpr int G = 4;  // rows whose loads go out together
@@ -254,10 +308,13 @@ struct RowScale {
 };
 
 // Values a narrow epilogue loads for its (up to) two items per thread before
-// the K loop: the residual and the next norm's gain at the item's column.
+// the K loop: the residual and the next norm's gain at the item's column, and
+// the first 8 x 64 per-16-column sums of squares of (up to) two of the rows
+// whose 1/rms this wave computes after the loop.
 struct NarrowPre {
   float x[2];
   float g[2];
+  float ss[2][8];
 };
 
 // 1/rms of the rows of the tile an epilogue works on: filled by the
@@ -409,25 +466,27 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
 // columns [n0, n0 + 16) of the epilogue's column space; nprepare() as
 // prepare(); napply(tile, ldt, rows, m0, M, n0, ncols, tid) over columns
 // [n0, n0 + ncols) with ncols a multiple of 16.
-template <typename T, int MB, int NSL, int NSW, int NW, int NB, int MINW, bool ILV, class ASrc,
-          class Epi>
-__global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int K, int kw,
-                                                           int m_tiles, Epi epi) {
+template <typename T, int MB, int NSL, int NSW, int NW, int NB, int MINW, class ASrc, class Epi>
+__global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int K, int kq_len,
+                                                           int ksw, int m_tiles, Epi epi_all) {
   constexpr int TR = 16 * MB, TC = 16 * NSL;
   constexpr int LDR = TC + 4;  // padded row of the summed tile (floats)
   constexpr int WC = 16 * NSW;  // columns of one wave's partial tile
   constexpr int NG = NSL / NSW;  // slab groups; wave = ks * NG + group
   constexpr int KSPL = NW / NG;  // K splits
   static_assert(NSL % NSW == 0 && NW % NG == 0, "waves cover slab groups x K splits");
-  static_assert(NSL != 1 || TR * NSL <= 8 * NW, "narrow_rows handles two items per thread");
   __shared__ float red[NW * TR * WC];
   __shared__ float tile[TR * LDR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mt = (int)blockIdx.x % m_tiles, g = (int)blockIdx.x / m_tiles;
+  const int kq = (int)blockIdx.x % ksw, rest = (int)blockIdx.x / ksw;
+  const int mt = rest % m_tiles, g = rest / m_tiles;
   const int m0 = mt * TR, n0 = g * TC;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int sg = wave % NG, ksp = wave / NG;
-  const int k0 = imin(K, ksp * kw), k1 = imin(K, k0 + kw);
+  // this workgroup's K range [kr0, kr1) (ksw > 1: one of ksw ranges, each
+  // written as its own partial by the epilogue, for a consumer that sums them)
+  const int kr0 = imin(K, kq * kq_len), kr1 = imin(K, kr0 + kq_len);
+  const Epi epi = epi_all.nsplit(kq);
 
   const T* bp[NSW];  // this lane's record in chunk 0 of each of the wave's slabs
 #pragma unroll
@@ -441,13 +500,13 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
 #pragma unroll
     for (int s = 0; s < NSW; ++s) acc[mb][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ILV: the K splits interleave by 64-wide step (split ksp takes steps ksp,
-  // ksp + KSPL, ...), so the waves of a slab group read one contiguous run of
-  // the slabs at a time; else split ksp takes the contiguous range [k0, k1).
-  int c = k0 / 32;  // chunk index (k0, k1 are multiples of 32)
-  const bool odd = ILV ? ((K & 32) && ksp == 0) : ((k1 - k0) & 32);
-  if (ILV) c = K / 32 - 1;  // the odd last chunk (split 0)
-  if (odd) {  // a single chunk first when the range is not a multiple of 64
+  // The waves' K splits interleave by 64-wide step (split ksp takes steps
+  // ksp, ksp + KSPL, ... of the range), so the waves of a slab group read one
+  // contiguous run of the slabs at a time; an odd last 32-chunk goes to split 0.
+  const int c0 = kr0 / 32;  // first chunk (kr0, kr1 are multiples of 32)
+  const int steps = (kr1 - kr0) / 64;
+  if (((kr1 - kr0) & 32) && ksp == 0) {  // the odd chunk
+    const int c = kr1 / 32 - 1;
     Frag<T> b0[NSW];
 #pragma unroll
     for (int s = 0; s < NSW; ++s) load_frag(b0[s], bp[s] + (int64_t)c * kChunkElems);
@@ -458,20 +517,18 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
 #pragma unroll
       for (int s = 0; s < NSW; ++s) mma(acc[mb][s], a0, b0[s]);
     }
-    ++c;
   }
-  const int n64 = ILV ? (K / 64 > ksp ? (K / 64 - ksp + KSPL - 1) / KSPL : 0) : (k1 / 32 - c) / 2;
-  auto chunk_of = [&](int st) { return ILV ? 2 * (ksp + st * KSPL) : c + 2 * st; };
+  const int n64 = steps > ksp ? (steps - ksp + KSPL - 1) / KSPL : 0;
+  auto chunk_of = [&](int st) { return c0 + 2 * (ksp + st * KSPL); };
   Step64<T, MB, ASrc, NSW> buf[NB];
 #pragma unroll
   for (int b = 0; b < NB - 1; ++b)
     if (b < n64) buf[b].load(asrc, as, bp, chunk_of(b), g4);
-  // while those loads are in flight: the row scales of the epilogue (one wave
-  // per row; published by the barrier after the partial tiles) and the values
-  // the epilogue reads (residual, gains)
-  epi.nrow_scale(row_scale_lds(), TR, m0, M, wave, NW, lane);
+  // while those loads are in flight: the loads of what the epilogue reads
+  // (residual, gains) and of the sums of squares behind the row scales
   NarrowPre pre;
   epi.nfetch(pre, TR, m0, M, n0, TC, tid);
+  epi.nrow_pre(pre, TR, m0, M, wave, NW, lane);
   for (int i = 0; i < n64; i += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -482,7 +539,10 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
       }
     }
   }
-  // this wave's partial tile, then the sum over the K splits in split order
+  // the row scales of the epilogue (one wave per row; published by the
+  // barrier below), this wave's partial tile, then the sum over the K splits
+  // in split order
+  epi.nrow_fin(pre, row_scale_lds(), TR, m0, M, wave, NW, lane);
   float* mine = red + wave * (TR * WC);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -500,14 +560,16 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
     tile[r * LDR + cc] = v;
   }
   __syncthreads();
-  epi.napply(tile, LDR, TR, m0, M, n0, TC, tid, pre);
+  constexpr int J = (TR * NSL + 4 * NW - 1) / (4 * NW);  // epilogue items per thread
+  epi.template napply<J>(tile, LDR, TR, m0, M, n0, TC, tid, pre);
 }
 
 // Row pass of a narrow epilogue: item (row r, 16-column group q) goes to a
 // 16-lane group, lane i = column 16 q + i; every lane of a wave runs the same
-// iterations (the 16-lane reductions are wave-uniform), at most two items per
-// thread (rows x groups <= 8 x waves).  narrow_item() gives the thread's item j
-// (the same for the prefetch before the K loop and the pass after it).
+// iterations (the 16-lane reductions are wave-uniform), J items per thread
+// (rows x groups <= 4 x waves x J).  narrow_item() gives the thread's item j
+// (the same for the prefetch before the K loop, which covers j < 2, and the
+// pass after it).
 // f(r, c, m, n, j) returns the value stored for tile (r, c) = output (m, n);
 // its squares are summed per 16-column group into ss (nullable) and v *
 // pre.g[j] (the next norm's gain at n) is written to xg.
@@ -530,19 +592,23 @@ __device__ __forceinline__ NarrowItem narrow_item(int j, int rows, int m0, int M
   t.act = it < items && t.m < M && t.n < N;
   return t;
 }
-template <typename T, typename F>
+template <int J, typename T, typename F>
 __device__ __forceinline__ void narrow_rows(int rows, int m0, int M, int n0, int ncols, int N,
                                             int tid, float* ss, int n_ss, const NextNorm<T>& nn,
                                             const NarrowPre& pre, F&& f) {
   const int lane = tid & 63;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < J; ++j) {
     const NarrowItem t = narrow_item(j, rows, m0, M, n0, ncols, N, tid);
     if (!t.in) break;
     float v = 0.f;
     if (t.act) {
       v = f(t.r, t.c, t.m, t.n, j);
-      if (nn.xg != nullptr) nn.xg[(int64_t)t.m * N + t.n] = Num<T>::from_f(v * pre.g[j]);
+      if (nn.xg != nullptr) {
+        // the gain prefetched for the first two items, loaded for later ones
+        const float gj = j < 2 ? pre.g[j < 2 ? j : 0] : Num<T>::to_f(nn.g[t.n]);
+        nn.xg[(int64_t)t.m * N + t.n] = Num<T>::from_f(v * gj);
+      }
     }
     if (ss != nullptr) {
       const float q = row16_sum(t.act ? v * v : 0.f);
@@ -1014,7 +1080,14 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
 
 template <typename T> struct EpiStoreF32 {
   const T* W; int N; int K; float* out; int ldo; float* ss; NextNorm<T> nn; RowScale rs;
+  int64_t split_stride;  // elements between the partials of K ranges (gemm_rows ksw > 1)
   static constexpr int kNarrow = 1;
+  static constexpr bool kRowScale = true;
+  __device__ EpiStoreF32 nsplit(int kq) const {
+    EpiStoreF32 e = *this;
+    if (kq > 0) e.out += kq * split_stride;
+    return e;
+  }
   // rows of an RMSNorm-scaled A source are multiplied by 1/rms (1 for a plain source)
   __device__ void prepare(int rows, int m0, int M, int tid) const {
     rs.fill(row_scale_lds(), rows, m0, M, tid);
@@ -1035,20 +1108,25 @@ template <typename T> struct EpiStoreF32 {
   __device__ const T* nslab(int n0) const {
     return W + (int64_t)(imin(n0, N - 1) / 16) * slab_elems(K);
   }
-  __device__ void nrow_scale(float* srs, int rows, int m0, int M, int wave, int nw,
-                             int lane) const {
-    rs.fill_rows(srs, rows, m0, M, wave, nw, lane);
+  __device__ void nrow_pre(NarrowPre& pre, int rows, int m0, int M, int wave, int nw,
+                           int lane) const {
+    rs.pre_rows(pre.ss, rows, m0, M, wave, nw, lane);
+  }
+  __device__ void nrow_fin(const NarrowPre& pre, float* srs, int rows, int m0, int M, int wave,
+                           int nw, int lane) const {
+    rs.finish_rows(pre.ss, srs, rows, m0, M, wave, nw, lane);
   }
   __device__ void nfetch(NarrowPre& pre, int rows, int m0, int M, int n0, int ncols,
                          int tid) const {
     narrow_fetch<T>(pre, nullptr, nn.xg != nullptr ? nn.g : nullptr, rows, m0, M, n0, ncols, N,
                     tid);
   }
+  template <int J>
   __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int ncols,
                          int tid, const NarrowPre& pre) const {
     const float* srs = row_scale_lds();
-    narrow_rows(rows, m0, M, n0, ncols, N, tid, ss, ss_tiles(N), nn, pre,
-                [&](int r, int c, int m, int n, int) {
+    narrow_rows<J>(rows, m0, M, n0, ncols, N, tid, ss, ss_tiles(N), nn, pre,
+                   [&](int r, int c, int m, int n, int) {
                   const float v = t[r * ldt + c] * srs[r];
                   if (out != nullptr) out[(int64_t)m * ldo + n] = v;
                   return v;
@@ -1056,9 +1134,22 @@ template <typename T> struct EpiStoreF32 {
   }
 };
 
+// The QKV store of the narrow path: EpiStoreF32 on kQkvSlabs slabs per
+// workgroup (its consumer adds the K-range partials).
+template <typename T> struct EpiQKVStore : EpiStoreF32<T> {
+  static constexpr int kNarrow = kQkvSlabs;
+  __device__ EpiQKVStore nsplit(int kq) const {
+    EpiQKVStore e = *this;
+    if (kq > 0) e.out += kq * this->split_stride;
+    return e;
+  }
+};
+
 template <typename T> struct EpiResidual {
   const T* W; int N; int K; float* x; float* ss; NextNorm<T> nn;
   static constexpr int kNarrow = 1;
+  static constexpr bool kRowScale = false;
+  __device__ EpiResidual nsplit(int) const { return *this; }
   __device__ void prepare(int, int, int, int) const {}
   __device__ const T* bslab(int nt, int s) const {
     return W + (int64_t)(imin(nt * BN + 16 * s, N - 1) / 16) * slab_elems(K);
@@ -1076,16 +1167,20 @@ template <typename T> struct EpiResidual {
   __device__ const T* nslab(int n0) const {
     return W + (int64_t)(imin(n0, N - 1) / 16) * slab_elems(K);
   }
-  __device__ void nrow_scale(float*, int, int, int, int, int, int) const {}
+  __device__ void nrow_pre(NarrowPre&, int, int, int, int, int, int) const {}
+  __device__ void nrow_fin(const NarrowPre&, float*, int, int, int, int, int, int) const {}
   __device__ void nfetch(NarrowPre& pre, int rows, int m0, int M, int n0, int ncols,
                          int tid) const {
     narrow_fetch<T>(pre, x, nn.xg != nullptr ? nn.g : nullptr, rows, m0, M, n0, ncols, N, tid);
   }
+  template <int J>
   __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int ncols,
                          int tid, const NarrowPre& pre) const {
-    narrow_rows(rows, m0, M, n0, ncols, N, tid, ss, ss_tiles(N), nn, pre,
-                [&](int r, int c, int m, int n, int j) {
-                  const float v = pre.x[j] + t[r * ldt + c];
+    narrow_rows<J>(rows, m0, M, n0, ncols, N, tid, ss, ss_tiles(N), nn, pre,
+                   [&](int r, int c, int m, int n, int j) {
+                  // the residual prefetched for the first two items, loaded for later ones
+                  const float res = j < 2 ? pre.x[j < 2 ? j : 0] : x[(int64_t)m * N + n];
+                  const float v = res + t[r * ldt + c];
                   x[(int64_t)m * N + n] = v;
                   return v;
                 });
@@ -1119,6 +1214,8 @@ template <typename T> struct EpiResidual {
 template <typename T> struct EpiSiluMul {
   const T* Wg; const T* Wu; int I; int K; T* act; RowScale rs;
   static constexpr int kNarrow = 2;
+  static constexpr bool kRowScale = true;
+  __device__ EpiSiluMul nsplit(int) const { return *this; }
   __device__ void prepare(int rows, int m0, int M, int tid) const {
     rs.fill(row_scale_lds(), rows, m0, M, tid);
   }
@@ -1143,11 +1240,16 @@ template <typename T> struct EpiSiluMul {
     const int o = imin((n0 / 32) * 16, I - 1);
     return ((n0 & 16) ? Wu : Wg) + (int64_t)(o / 16) * slab_elems(K);
   }
-  __device__ void nrow_scale(float* srs, int rows, int m0, int M, int wave, int nw,
-                             int lane) const {
-    rs.fill_rows(srs, rows, m0, M, wave, nw, lane);
+  __device__ void nrow_pre(NarrowPre& pre, int rows, int m0, int M, int wave, int nw,
+                           int lane) const {
+    rs.pre_rows(pre.ss, rows, m0, M, wave, nw, lane);
+  }
+  __device__ void nrow_fin(const NarrowPre& pre, float* srs, int rows, int m0, int M, int wave,
+                           int nw, int lane) const {
+    rs.finish_rows(pre.ss, srs, rows, m0, M, wave, nw, lane);
   }
   __device__ void nfetch(NarrowPre&, int, int, int, int, int, int) const {}
+  template <int J>
   __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int ncols,
                          int tid, const NarrowPre&) const {
     const float* srs = row_scale_lds();
@@ -1399,14 +1501,21 @@ template <typename T, typename KT> struct EpiKVInject {
 template <typename T> struct EpiLogits {
   const T* W; int V; int H; T* logits; float2* part; int n_tiles; RowScale rs;
   static constexpr int kNarrow = 8;  // 128-column tiles: one argmax partial each
+  static constexpr bool kRowScale = true;
+  __device__ EpiLogits nsplit(int) const { return *this; }
   __device__ const T* nslab(int n0) const {
     return W + (int64_t)(imin(n0, V - 1) / 16) * slab_elems(H);
   }
-  __device__ void nrow_scale(float* srs, int rows, int m0, int M, int wave, int nw,
-                             int lane) const {
-    rs.fill_rows(srs, rows, m0, M, wave, nw, lane);
+  __device__ void nrow_pre(NarrowPre& pre, int rows, int m0, int M, int wave, int nw,
+                           int lane) const {
+    rs.pre_rows(pre.ss, rows, m0, M, wave, nw, lane);
+  }
+  __device__ void nrow_fin(const NarrowPre& pre, float* srs, int rows, int m0, int M, int wave,
+                           int nw, int lane) const {
+    rs.finish_rows(pre.ss, srs, rows, m0, M, wave, nw, lane);
   }
   __device__ void nfetch(NarrowPre&, int, int, int, int, int, int) const {}
+  template <int J>
   __device__ void napply(const float* t, int ldt, int rows, int m0, int M, int n0, int,
                          int tid, const NarrowPre&) const {
     apply_ld(t, ldt, rows, m0, M, n0 / BN, tid);
@@ -1545,9 +1654,6 @@ template <class E> struct NarrowSlabs<E, decltype((void)E::kNarrow)> {
   static constexpr int value = E::kNarrow;
 };
 
-// K splits of gemm_rows interleaved by 64-wide step (else contiguous ranges).
-constexpr bool kRowsInterleave = true;
-
 // Register ring depth and occupancy of gemm_rows: bf16 kernels are held to
 // four waves per SIMD (<= 128 VGPRs: one 16-wave or two 8-wave workgroups per
 // CU), fp32 ones to two; the ring takes what the accumulators and addresses
@@ -1557,48 +1663,51 @@ static void launch_rows_cfg(const AS& asrc, int M, int K, const GemmPlan& p, con
                             hipStream_t st) {
   constexpr int NSW = NSL > 2 ? 2 : NSL;  // slabs per wave
   constexpr int STEP = (MB + NSW) * 2 * (sizeof(T) == 2 ? 4 : 8);
-  constexpr int FIXED = MB * NSW * 4 + 32;  // accumulators, addresses, indices, prefetch
+  // accumulators, addresses, indices, prefetch (+16 for the prefetched sums of
+  // squares of an epilogue that applies a row scale)
+  constexpr int FIXED = MB * NSW * 4 + 32 + (Epi::kRowScale ? 16 : 0);
   // four waves per SIMD where a two-step ring fits in 128 VGPRs (always for
   // 16-wave workgroups), else three (168)
   constexpr int MINW = sizeof(T) == 2 ? ((NW == 16 || 2 * STEP + FIXED <= 128) ? 4 : 3) : 2;
   constexpr int BUDGET = (MINW == 4 ? 128 : (MINW == 3 ? 168 : 256)) - FIXED;
   constexpr int NB0 = BUDGET / STEP;
-  constexpr int NB = NB0 < 1 ? 1 : (NB0 > 4 ? 4 : NB0);
-  hipLaunchKernelGGL((gemm_rows<T, MB, NSL, NSW, NW, NB, MINW, kRowsInterleave, AS, Epi>),
-                     dim3((unsigned)(p.n_tiles * p.m_tiles)), dim3(NW * 64), 0, st, asrc, M, K,
-                     p.kw, p.m_tiles, epi);
+  constexpr int NB = NB0 < 1 ? 1 : (NB0 > 6 ? 6 : NB0);
+  hipLaunchKernelGGL((gemm_rows<T, MB, NSL, NSW, NW, NB, MINW, AS, Epi>),
+                     dim3((unsigned)(p.n_tiles * p.m_tiles * p.KSW)), dim3(NW * 64), 0, st, asrc,
+                     M, K, p.kw, p.KSW, p.m_tiles, epi);
+}
+template <typename T, int NSL, int NW, class AS, class Epi>
+static void launch_rows_mb(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
+                           hipStream_t st) {
+  if constexpr (NSL == 8) {  // up to 32 rows (plan_gemm)
+    if (p.MB == 1) launch_rows_cfg<T, 1, NSL, NW>(asrc, M, K, p, epi, st);
+    else launch_rows_cfg<T, 2, NSL, NW>(asrc, M, K, p, epi, st);
+  } else {
+    switch (p.MB) {
+      case 1: launch_rows_cfg<T, 1, NSL, NW>(asrc, M, K, p, epi, st); return;
+      case 2: launch_rows_cfg<T, 2, NSL, NW>(asrc, M, K, p, epi, st); return;
+      default: launch_rows_cfg<T, 4, NSL, NW>(asrc, M, K, p, epi, st); return;
+    }
+  }
 }
 template <typename T, int NSL, class AS, class Epi>
 static void launch_rows(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
                         hipStream_t st) {
-  if constexpr (NSL == 8) {  // up to 32 rows (plan_gemm)
-    constexpr int NW = sizeof(T) == 2 ? 16 : 8;
-    if (p.MB == 1) launch_rows_cfg<T, 1, NSL, NW>(asrc, M, K, p, epi, st);
-    else launch_rows_cfg<T, 2, NSL, NW>(asrc, M, K, p, epi, st);
-    return;
-  }
   if constexpr (sizeof(T) == 2 && NSL == 1) {
-    if (p.NW == 16) {
-      switch (p.MB) {
-        case 1: launch_rows_cfg<T, 1, NSL, 16>(asrc, M, K, p, epi, st); return;
-        case 2: launch_rows_cfg<T, 2, NSL, 16>(asrc, M, K, p, epi, st); return;
-        default: launch_rows_cfg<T, 4, NSL, 16>(asrc, M, K, p, epi, st); return;
-      }
-    }
+    if (p.NW == 16) return launch_rows_mb<T, NSL, 16>(asrc, M, K, p, epi, st);
   }
-  switch (p.MB) {
-    case 1: launch_rows_cfg<T, 1, NSL, 8>(asrc, M, K, p, epi, st); return;
-    case 2: launch_rows_cfg<T, 2, NSL, 8>(asrc, M, K, p, epi, st); return;
-    default: launch_rows_cfg<T, 4, NSL, 8>(asrc, M, K, p, epi, st); return;
+  if constexpr (sizeof(T) == 2 && NSL == 2) {
+    if (p.NW == 4) return launch_rows_mb<T, NSL, 4>(asrc, M, K, p, epi, st);
   }
+  launch_rows_mb<T, NSL, 8>(asrc, M, K, p, epi, st);
 }
 
 template <typename T, class AS, class Epi>
 static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& epi,
-                           const GemmScratch& ws, hipStream_t st) {
+                           const GemmScratch& ws, hipStream_t st, int ksw = 1) {
   if (M <= 0) return hipSuccess;
   constexpr int NAR = NarrowSlabs<Epi>::value;
-  const GemmPlan p = plan_gemm(M, Ncols, K, sizeof(T) == 2, NAR);
+  const GemmPlan p = plan_gemm(M, Ncols, K, sizeof(T) == 2, NAR, ksw);
   if constexpr (NAR > 0) {
     if (p.rows) {
       launch_rows<T, NAR>(asrc, M, K, p, epi, st);
@@ -1627,9 +1736,9 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
 
 template <typename T, class Epi>
 static hipError_t run_any(const ASrc& a, int M, int K, int Ncols, const Epi& epi,
-                          const GemmScratch& ws, hipStream_t st) {
+                          const GemmScratch& ws, hipStream_t st, int ksw = 1) {
   const ASrcPlain<T> s{static_cast<const T*>(a.a), a.lda, a.S_skip};
-  return run_gemm<T>(s, M, K, Ncols, epi, ws, st);
+  return run_gemm<T>(s, M, K, Ncols, epi, ws, st, ksw);
 }
 
 static RowScale row_scale(const ASrc& a) {
@@ -1673,10 +1782,89 @@ hipError_t gemm_silu_mul(int dt, const ASrc& a, int M, int K, const void* Wg, co
   return run_any<float>(a, M, K, ncols, e, ws, st);
 }
 
+// Per-head q/k RMSNorm + RoPE of the block rows from the fp32 q/k/v the
+// narrow QKV GEMM wrote (raw [M][(nq + 2 nkv) D], input RMSNorm applied), into
+// the layouts attention reads: one wave per (row, head); the same arithmetic as
+// EpiQKV on the same fp32 values.
+template <typename T>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(
+    const float* __restrict__ raw, int ksw, int M, int nq, int nkv, int D,
+    const T* __restrict__ qn, const T* __restrict__ kn, float eps, const float2* __restrict__ cs,
+    T* __restrict__ q, T* __restrict__ kblk, T* __restrict__ vblk, int S) {
+  const int lane = threadIdx.x & 63, HH = nq + 2 * nkv, half = D / 2;
+  const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (item >= M * HH) return;  // wave-uniform
+  const int m = item / HH, gh = item % HH, rq = m / S, j = m % S;
+  const bool act = lane < half;
+  // the ksw K-range partials of the GEMM, added in range order
+  const int64_t pstride = (int64_t)M * HH * D;
+  const float* src = raw + (int64_t)m * HH * D + (int64_t)gh * D;
+  float p0[4], p1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    p0[k] = (act && k < ksw) ? src[k * pstride + lane] : 0.f;
+    p1[k] = (act && k < ksw) ? src[k * pstride + lane + half] : 0.f;
+  }
+  float x0 = p0[0], x1 = p1[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    x0 += p0[k];
+    x1 += p1[k];
+  }
+  float o0 = x0, o1 = x1;
+  if (gh < nq) {
+    norm_rope_pair<T>(x0, x1, lane, D, act, qn, eps, cs + (int64_t)m * half, o0, o1);
+    T* dst = q + ((int64_t)m * nq + gh) * D;
+    if (act) {
+      dst[lane] = Num<T>::from_f(o0);
+      dst[lane + half] = Num<T>::from_f(o1);
+    }
+  } else if (gh < nq + nkv) {
+    norm_rope_pair<T>(x0, x1, lane, D, act, kn, eps, cs + (int64_t)m * half, o0, o1);
+    T* dst = kblk + (((int64_t)rq * nkv + (gh - nq)) * 16 + j) * D;
+    if (act) {
+      dst[lane] = Num<T>::from_f(o0);
+      dst[lane + half] = Num<T>::from_f(o1);
+    }
+  } else {
+    T* dst = vblk + ((int64_t)rq * nkv + (gh - nq - nkv)) * D * 16 + j;
+    if (act) {
+      dst[(int64_t)lane * 16] = Num<T>::from_f(o0);
+      dst[(int64_t)(lane + half) * 16] = Num<T>::from_f(o1);
+    }
+  }
+}
+
 hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const void* qn,
                     const void* kn, int nq, int nkv, int D, float eps, const float2* cs, void* q,
-                    void* k, void* v, int S, const GemmScratch& ws, hipStream_t st) {
+                    void* k, void* v, int S, float* raw, const GemmScratch& ws, hipStream_t st) {
   const int ncols = (nq + 2 * nkv) * D;
+  if (raw != nullptr && M <= 64) {
+    // narrow GEMM into fp32 raw (input RMSNorm applied; K split over ksw
+    // workgroups so that the CUs stream equal shares), then the per-head norms
+    // and RoPE in a second small kernel that adds the partials: the GEMM needs
+    // no whole heads
+    const int ksw = qkv_k_splits(ncols);
+    const int64_t pstride = (int64_t)M * ncols;
+    const unsigned grid = (unsigned)((M * (nq + 2 * nkv) + 3) / 4);
+    hipError_t e;
+    if (dt == DFLASH_BF16) {
+      EpiQKVStore<bf16_t> ep{{(const bf16_t*)Wqkv, ncols, H, raw, ncols, nullptr,
+                              NextNorm<bf16_t>{nullptr, nullptr}, row_scale(a), pstride}};
+      if ((e = run_any<bf16_t>(a, M, H, ncols, ep, ws, st, ksw)) != hipSuccess) return e;
+      hipLaunchKernelGGL(qk_norm_rope_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, raw, ksw, M,
+                         nq, nkv, D, (const bf16_t*)qn, (const bf16_t*)kn, eps, cs, (bf16_t*)q,
+                         (bf16_t*)k, (bf16_t*)v, S);
+    } else {
+      EpiQKVStore<float> ep{{(const float*)Wqkv, ncols, H, raw, ncols, nullptr,
+                             NextNorm<float>{nullptr, nullptr}, row_scale(a), pstride}};
+      if ((e = run_any<float>(a, M, H, ncols, ep, ws, st, ksw)) != hipSuccess) return e;
+      hipLaunchKernelGGL(qk_norm_rope_kernel<float>, dim3(grid), dim3(256), 0, st, raw, ksw, M,
+                         nq, nkv, D, (const float*)qn, (const float*)kn, eps, cs, (float*)q,
+                         (float*)k, (float*)v, S);
+    }
+    return hipGetLastError();
+  }
   if (dt == DFLASH_BF16) {
     EpiQKV<bf16_t> e{(const bf16_t*)Wqkv, H, nq, nkv, D, (const bf16_t*)qn, (const bf16_t*)kn,
                      eps, cs, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, row_scale(a), S};

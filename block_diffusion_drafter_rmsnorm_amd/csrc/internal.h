@@ -21,7 +21,8 @@ struct GemmPlan {
   bool rows;     // narrow tiles, K split inside the workgroup (gemm_rows; M <= 64)
   int NSL;       //   packed 16-column slabs per workgroup (1 or 2)
   int NW;        //   waves per workgroup (8 or 16), each streaming kw of K
-  int kw;
+  int kw;       //   K of each workgroup's range (a multiple of 64)
+  int KSW;       //   K ranges across workgroups (1 unless the caller adds partials)
   bool fat;      // LDS-tiled kernel
   bool big;      // 256 x 256 tiles, no split K (n_tiles counts 256 columns)
   int BM;        // rows per tile (16 MB for the streaming kernel; 128 or 256)
@@ -34,7 +35,12 @@ struct GemmPlan {
 // narrow: slabs per workgroup when the epilogue runs on narrow tiles (1 for
 // store and residual, 2 for SwiGLU's gate/up pairs; 0: it needs 128-column
 // tiles), so that up to 64 rows take gemm_rows (no split-K partials)
-GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow = 0);
+// ksw: K ranges across workgroups, each written as its own partial (narrow
+// epilogues whose consumer adds them: the QKV store)
+GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow = 0, int ksw = 1);
+// K ranges of the narrow QKV GEMM (its fp32 output holds that many partials)
+int qkv_k_splits(int ncols);
+int qkv_slabs();  // slabs per workgroup of the narrow QKV GEMM
 size_t gemm_partial_floats(const GemmPlan& p);
 
 struct KVTargets {
@@ -84,10 +90,13 @@ hipError_t gemm_residual(int dt, const ASrc& a, int M, int K, const void* W, int
 hipError_t gemm_silu_mul(int dt, const ASrc& a, int M, int K, const void* Wg, const void* Wu,
                          int I, void* act, const GemmScratch& ws, hipStream_t st);
 // q/k/v of the block rows with per-head RMSNorm + RoPE on q and k; q -> [M, nq, D],
-// k -> kblk [B][nkv][16][D], v -> vblk [B][nkv][D][16] (block row j = m % S)
+// k -> kblk [B][nkv][16][D], v -> vblk [B][nkv][D][16] (block row j = m % S).
+// raw (nullable, [M][(nq + 2 nkv) D] fp32): with M <= 64 the GEMM runs on
+// narrow tiles into raw and a second kernel applies the per-head norms.
 hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const void* qn,
                     const void* kn, int nq, int nkv, int D, float eps, const float2* cs, void* q,
-                    void* kblk, void* vblk, int S, const GemmScratch& ws, hipStream_t st);
+                    void* kblk, void* vblk, int S, float* raw, const GemmScratch& ws,
+                    hipStream_t st);
 // stacked K/V of all layers for context rows -> paged cache
 hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
@@ -179,6 +188,7 @@ struct AttnPlan {
   int n_launch;    // workgroups W (a multiple of 256)
   int n_partials;  // (O, m, l) partial slots: W + B * nkv
   bool fits;       // the unit count fits the kernels' 32-bit bookkeeping
+  int kps;         // aligned partition (few segments): workgroups per segment; 0: by bytes
 };
 // max_keys: the most context keys a request sees on the layer; dma: the cache
 // and compute types are bf16 (the direct-to-LDS kernel runs).
