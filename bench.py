@@ -71,7 +71,7 @@ def profiled_traffic(workload):
             vals[k.strip()] = v.strip()
     csrc = os.path.join(ROOT, "block_diffusion_drafter_rmsnorm_amd", "csrc")
     sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
-                                  for f in ("gemm.hip", "common.cuh"))).hexdigest()
+                                  for f in ("gemm.hip", "common.h"))).hexdigest()
     if vals.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in vals:
         return None
     return int(float(vals["traffic_bytes_per_launch"]))

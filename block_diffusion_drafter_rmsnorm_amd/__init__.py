@@ -17,7 +17,9 @@ from typing import Dict, List, Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdflash.so")
+# DFLASH_LIBRARY selects another build of the same sources (the tests load the
+# host-sanitized one through it); by default the in-tree library.
+LIB_PATH = os.environ.get("DFLASH_LIBRARY") or os.path.join(_HERE, "libdflash.so")
 MAX_LAYERS = 16
 
 F32, BF16, FP8_E4M3 = 0, 1, 2

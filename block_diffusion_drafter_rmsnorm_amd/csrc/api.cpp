@@ -141,15 +141,25 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   L.cs = (float2*)cv.take(sizeof(float2) * M * (c->head_dim / 2));
   L.cg = cv.take((size_t)act_bytes(c->act_dtype) * M * c->hidden);
   L.ss = (float*)cv.take(sizeof(float) * (size_t)M * ss_tiles(c->hidden));
-  // the last chunk of a call can be any size up to `chunk`: take the worst case
+  // the last chunk of a call can be any size up to `chunk`: take the worst
+  // case over row counts.  A plan depends on the row count only through its
+  // kernel and its number of row tiles, so one count per (kernel, tile count)
+  // covers every case: the streaming kernel's 16 / 32 / 64-row tiles, the
+  // 128- and 256-row tiles of the tiled kernels (bf16), 64-row tiles beyond
+  // 64 rows (fp32).
+  const bool bf = c->act_dtype == DFLASH_BF16;
   size_t pf = 0;
-  for (int m = 1; m <= M; ++m) {
-    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim, c->act_dtype == DFLASH_BF16, 1),
-                            plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim, c->hidden,
-                                      c->act_dtype == DFLASH_BF16)};
+  auto probe = [&](int m) {
+    if (m < 1 || m > M) return;
+    const GemmPlan ps[2] = {plan_gemm(m, c->hidden, c->feat_dim, bf, 1),
+                            plan_gemm(m, c->n_layers * 2 * c->n_kv_heads * c->head_dim,
+                                      c->hidden, bf)};
     for (const GemmPlan& p : ps)
       if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
-  }
+  };
+  for (int m : {16, 32, 64, 128, 192}) probe(m);
+  for (int t = 1; (int64_t)(t - 1) * (bf ? 256 : 64) < M; ++t) probe(t * (bf ? 256 : 64));
+  probe(M);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
   L.bytes = cv.off;
@@ -307,11 +317,9 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
   if (feat_row_stride < cfg->feat_dim || feat_row_stride % 8)
     return fail(DFLASH_EINVAL, "feat_row_stride %lld must be >= feat_dim and a multiple of 8",
                 (long long)feat_row_stride);
-  int64_t chunk = inject_chunk_rows(T);
-  if (valid_rows != nullptr) {
-    if (rows_per_req > kInjectChunk) chunk = rows_per_req;
-    else chunk = (chunk / rows_per_req) * rows_per_req;
-  }
+  // chunks of up to kInjectChunk rows: a chunk may start or end inside a
+  // request (the K/V epilogue finds each row's request from its grid row)
+  const int64_t chunk = inject_chunk_rows(T);
   const ContextWs L = layout_context(cfg, chunk, workspace);
   if (workspace == nullptr || workspace_bytes < L.bytes)
     return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
@@ -338,12 +346,11 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
                             cfg->hidden, nullptr, L.ss, L.cg, w->hidden_norm, L.gs, st)) !=
         hipSuccess)
       return hip_fail(e, "fc gemm");
-    const int32_t* vr = valid_rows ? valid_rows + t0 / rows_per_req : nullptr;
     const ASrc cin = asrc_normed(L.cg, cfg->hidden, L.ss, cfg->rms_eps);
     if ((e = gemm_kv_inject(dt, cfg->kv_dtype, cin, M, cfg->hidden, tg, cfg->n_layers,
                             cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, L.cs,
-                            slots + t0, vr, rows_per_req > 0 ? rows_per_req : 1, cfg->page_size,
-                            cache->num_pages, L.gs, st)) != hipSuccess)
+                            slots + t0, valid_rows, rows_per_req > 0 ? rows_per_req : 1, t0,
+                            cfg->page_size, cache->num_pages, L.gs, st)) != hipSuccess)
       return hip_fail(e, "kv inject gemm");
   }
   return DFLASH_OK;

@@ -22,7 +22,7 @@
 // and fp32 caches go through registers.
 #include <type_traits>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace dflash {
@@ -620,8 +620,16 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 // for every one in flight before each LDS read); the kernel waits for them.
 __device__ __forceinline__ void attn_dma16(const void* g, const void* lds_wave_base) {
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
-               : "memory", "m0");
+  // m0 (the LDS base of the copy) is saved and restored inside the block, so
+  // whatever the surrounding code keeps in m0 survives; the copy reads m0 when
+  // it issues (the compiler's own code for these copies rewrites m0 right
+  // after each one)
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
 }
 template <int N> __device__ __forceinline__ void attn_wait_vmcnt() {
   static_assert(N <= 63, "vmcnt holds 6 bits");
@@ -821,15 +829,12 @@ template <int D, int NS>
 __global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs a) {
   using CT = bf16_t;
   constexpr int STAGE = 64 * D;       // elements of one staged step
-  constexpr int OPW = D / 64;         // K (and V) DMAs per wave per step
-  constexpr int DPW = 2 * OPW;        // DMAs per wave per step
   __shared__ int pages[kMaxChunkPages];
   __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
   __shared__ int red[12];
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, r16 = lane & 15,
             g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
-  const bool qlive = wave * 16 < R;
   const int rho = imin(wave * 16 + r16, R - 1);
   const int jrow = rho % S;
   const UnitTable tab = unit_table(a, red);

@@ -23,7 +23,7 @@
 // for the q/k RMSNorm + RoPE of the QKV and K/V-injection epilogues, paired
 // gate/up columns for SwiGLU, a 128-wide vocabulary slice for the argmax
 // partials of lm_head, the next RMSNorm's inputs.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace dflash {
@@ -805,8 +805,16 @@ constexpr int GB_NS = 4;
 // barrier that precedes the reads.
 __device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
-               : "memory", "m0");
+  // m0 (the LDS base of the copy) is saved and restored inside the block, so
+  // whatever the surrounding code keeps in m0 survives; the copy reads m0 when
+  // it issues (the compiler's own code for these copies rewrites m0 right
+  // after each one)
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -1374,9 +1382,11 @@ __device__ __forceinline__ int32_t* kv_row_slot() {
 template <typename T, typename KT> struct EpiKVInject {
   KVTargets tg; int H; int n_layers, nq, nkv, D; float eps; const float2* cs;
   const int32_t* slots; const int32_t* valid; int rpr; int P; int64_t num_slots; RowScale rs;
+  int64_t row0;  // grid row of GEMM row 0 (the chunk's first row): request (row0 + m) / rpr
   __device__ bool row_written(int m, int M) const {
     if (m >= M) return false;
-    if (valid != nullptr && (m % rpr) >= valid[m / rpr]) return false;
+    const int64_t t = row0 + m;
+    if (valid != nullptr && (int)(t % rpr) >= valid[t / rpr]) return false;
     const int64_t slot = slots[m];
     return slot >= 0 && slot < num_slots;  // outside the pool: never written
   }
@@ -1878,22 +1888,22 @@ hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const
 hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
                           const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
-                          int page_size, int64_t num_pages, const GemmScratch& ws,
+                          int64_t row0, int page_size, int64_t num_pages, const GemmScratch& ws,
                           hipStream_t st) {
   const int64_t ns = num_pages * page_size;
   const int ncols = n_layers * 2 * nkv * D;
   if (dt == DFLASH_BF16) {
     if (kv_dt == DFLASH_FP8_E4M3) {
       EpiKVInject<bf16_t, fp8_t> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,
-                                   rows_per_req, page_size, ns, row_scale(a)};
+                                   rows_per_req, page_size, ns, row_scale(a), row0};
       return run_any<bf16_t>(a, M, H, ncols, e, ws, st);
     }
     EpiKVInject<bf16_t, bf16_t> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,
-                                  rows_per_req, page_size, ns, row_scale(a)};
+                                  rows_per_req, page_size, ns, row_scale(a), row0};
     return run_any<bf16_t>(a, M, H, ncols, e, ws, st);
   }
   EpiKVInject<float, float> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,
-                              rows_per_req, page_size, ns, row_scale(a)};
+                              rows_per_req, page_size, ns, row_scale(a), row0};
   return run_any<float>(a, M, H, ncols, e, ws, st);
 }
 

@@ -97,11 +97,13 @@ hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const
                     const void* kn, int nq, int nkv, int D, float eps, const float2* cs, void* q,
                     void* kblk, void* vblk, int S, float* raw, const GemmScratch& ws,
                     hipStream_t st);
-// stacked K/V of all layers for context rows -> paged cache
+// stacked K/V of all layers for context rows -> paged cache.  GEMM row m is
+// row row0 + m of the [n_req, rows_per_req] grid (valid_rows indexed by grid
+// request; slots by GEMM row).
 hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
                           const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
-                          int page_size, int64_t num_pages, const GemmScratch& ws,
+                          int64_t row0, int page_size, int64_t num_pages, const GemmScratch& ws,
                           hipStream_t st);
 // logits[M, V] (nullable) and per-tile argmax partials (value, index) [M, n_tiles]
 hipError_t gemm_logits(int dt, const ASrc& a, int M, int H, const void* Wlm, int V, void* logits,

@@ -1,7 +1,7 @@
 // Small kernels of the draft/accept path: block preparation with the embedding
 // gather and the RoPE table, row RMSNorm, the second argmax stage and greedy
 // accept.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace dflash {

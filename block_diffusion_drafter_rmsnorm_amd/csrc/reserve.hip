@@ -12,7 +12,7 @@
 // or whose row is too short (status 2) stops the pass for it and every later
 // request.  One workgroup walks the batch in chunks of 256 requests with a
 // block scan of the shortfalls, so the assignment is deterministic.
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace dflash {

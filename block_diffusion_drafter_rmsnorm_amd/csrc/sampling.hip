@@ -21,7 +21,7 @@
 //      per-thread runs over LDS finds the token.
 #include <math.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace dflash {

@@ -21,7 +21,7 @@
 // per candidate slot).
 #include <math.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace dflash {

@@ -287,6 +287,43 @@ def test_project_context_large_tiles():
             assert err.max() <= 2e-2
 
 
+def test_project_context_prefix_valid_longer_than_a_chunk():
+    """A prefix-valid grid whose requests are longer than the 8192-row
+    injection chunk (3 x 9000 rows, valid 8193 / 0 / 9000), with the workspace
+    the query returns for all rows: chunks start and end inside requests.
+    Rows past a request's valid prefix keep their old cache values; sampled
+    live rows (around every chunk boundary too) match the oracle."""
+    wl = get_workload("small_bf16")
+    cfg = wl.cfg
+    n_req, rpr = 3, 9000
+    T = n_req * rpr
+    _print(f"[inject prefix-valid long] {n_req} x {rpr}")
+    st = Setup(wl, extra_tokens=T)
+    feats, pos, slots, _ = _inject_case(st, T, 555)
+    valid = torch.tensor([8193, 0, 9000], dtype=torch.int32)
+    before = st.oracle_cache()
+    st.inject(feats, pos, slots, valid, n_req, rpr)
+    live = (np.arange(T) % rpr) < np.repeat(valid.numpy(), rpr)
+    dead = slots.numpy()[~live]
+    rows = np.arange(0, T, 53)
+    edges = np.array([8190, 8191, 8192, 8193, 9000 + 8191, 18000 + 8191, 18000 + 8192, T - 1])
+    rows = np.unique(np.concatenate([rows, edges]))
+    rows = rows[live[rows]]
+    o_cache = oracle.OracleCache(cfg, st.num_pages * cfg.page_size)
+    oracle.project_context(cfg, st.np_W(), o_cache, feats[rows].float().numpy(),
+                           pos.numpy()[rows], slots.numpy()[rows])
+    sl = slots.numpy()[rows]
+    for l in range(cfg.n_layers):
+        for kind, pool, opool, bpool in (("k", st.cache.k[l], o_cache.k[l], before.k[l]),
+                                         ("v", st.cache.v[l], o_cache.v[l], before.v[l])):
+            got = st._pool_values(pool, transposed=(kind == "v"))
+            assert np.array_equal(got[dead], bpool[dead]), (l, kind)
+            g, o = got[sl], opool[sl]
+            err = np.max(np.abs(g - o), axis=-1) / np.max(np.abs(o), axis=-1)
+            _print(f"  layer {l} {kind}: {len(rows)} sampled rows, max rel err {err.max():.3e}")
+            assert err.max() <= 2e-2
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "small_swa_fp8", "tiny_f32"])
 def test_project_context_chunked_equals_once_and_idempotent(name):
     """Injecting rows in several calls of at most 64 rows gives the same bits

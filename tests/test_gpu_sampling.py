@@ -7,8 +7,8 @@ comparison is in two tiers:
 * requests whose decisions all clear the fp32 error bound (relative gap
   |u q(y) - p(y)| / max(u q(y), p(y)) above DEC_TOL, from the oracle) must
   match the oracle exactly in accept_len, commit_len, new_seq_len and every
-  surviving draft in out_tokens; at most 1%
-  of the requests may fall inside the bound, and those are checked only for
+  surviving draft in out_tokens; at most 1/32 of the requests (none below
+  batch 32) may fall inside the bound, and those are checked only for
   well-formed outputs;
 * the drawn token (correction or bonus) must be a valid inverse-CDF result
   under the oracle's fp64 weights up to CDF_TOL (running sum before it at most
@@ -76,6 +76,7 @@ def check(g, o, cand, L, max_ambiguous=0.01):
         assert g["out_tokens"][r, a[r]] == g["next_anchor"][r]
         assert np.all(g["out_tokens"][r, a[r] + 1:] == 0)
     clear = o["margin"] > DEC_TOL
+    print(f"  {int(np.sum(~clear))} of {B} requests with a decision within {DEC_TOL:g}", flush=True)
     assert np.mean(~clear) <= max_ambiguous, f"{np.sum(~clear)} of {B} decisions within tolerance"
     for k in ("accept_len", "commit_len", "new_seq_len"):
         assert np.array_equal(g[k][clear], o[k][clear]), k
@@ -108,7 +109,7 @@ def test_sampling_parity_small(dtype, with_draft, shape):
     Tt, Td = (0.8, 1.2) if with_draft else (1.0, 1.0)
     g = run_gpu(cand, tl, u, L, Tt, dl, Td)
     o = run_oracle(cand, tl, u, L, Tt, dl, Td)
-    check(g, o, cand, L, max_ambiguous=0.2 if B < 10 else 0.01)
+    check(g, o, cand, L, max_ambiguous=1 / 32)
 
 
 @pytest.mark.parametrize("with_draft", [False, True])
@@ -155,7 +156,7 @@ def test_sampling_misaligned_rows_take_scalar_path():
     g1 = run_gpu(cand, tl_mis, u, L)
     g2 = run_gpu(cand, tl, u, L)
     o = run_oracle(cand, tl, u, L)
-    check(g1, o, cand, L, max_ambiguous=0.25)
+    check(g1, o, cand, L, max_ambiguous=1 / 32)
     for k in g1:
         assert np.array_equal(g1[k][o["margin"] > DEC_TOL], g2[k][o["margin"] > DEC_TOL]), k
 
@@ -275,7 +276,7 @@ def test_sampling_sparse_q_parity(shape, dtype):
     f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     o = oracle.accept_sampling(cand.cpu().numpy(), f(tl), L.cpu().numpy(), f(u), 0.9,
                                draft_probs=dense)
-    check(g, o, cand, L, max_ambiguous=0.25)
+    check(g, o, cand, L, max_ambiguous=1 / 32)
 
 
 def test_selector_then_sparse_verify():
@@ -311,4 +312,4 @@ def test_selector_then_sparse_verify():
     o = oracle.accept_sampling(cand.cpu().numpy(), tl.cpu().numpy().astype(np.float64),
                                st.L.numpy(), u.cpu().numpy().astype(np.float64), 1.0,
                                draft_probs=dense)
-    check(g, o, cand, L, max_ambiguous=0.34)
+    check(g, o, cand, L, max_ambiguous=1 / 32)
