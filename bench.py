@@ -286,7 +286,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, wl, L, W)
+        res["cpu_baseline"] = cpu_baseline(cfg, wl, L.tolist(), W, anchor.cpu().numpy(),
+                                             post.cpu().numpy(), T)
     print(json.dumps(res), flush=True)
 
 
@@ -380,15 +381,18 @@ def selector_pass(dfl, synth, cfg, wl, cw, cache, anchor, Ld, ptd, max_prefix, t
             "rank": r}
 
 
-def cpu_baseline(cfg, wl, L, W_dev):
-    """The oracle (fp64 numpy, unmodified) on the host cores: one full draft
-    pass for the first request of the workload, plus a 64-row context
-    injection.  It reads the same weights as the GPU run (copied to host) and
-    random context K/V of the same shape."""
+def cpu_baseline(cfg, wl, L, W_dev, anchor, post, T_inj):
+    """The oracle (numpy, unmodified steps) on the host cores, in its fp32
+    timing setting, on the same units the GPU leg times: one draft pass for
+    the workload's batch, one accept of that batch, and one context injection
+    of the GPU leg's row count (row-local, so rows/s scales linearly).  Each
+    unit is timed three times; the medians are reported.  It reads the same
+    weights as the GPU run (copied to host, untimed) and random context K/V of
+    the same shape."""
     import numpy as np
-    import torch
 
     import oracle
+    from oracle.precision import working_precision
     from threadpoolctl import threadpool_info
 
     t0 = time.time()
@@ -398,34 +402,54 @@ def cpu_baseline(cfg, wl, L, W_dev):
 
     W = {k: host(v) for k, v in W_dev.items() if k != "layers"}
     W["layers"] = [{k: host(v) for k, v in Lw.items()} for Lw in W_dev["layers"]]
-    H, D, nkv, F = cfg.hidden, cfg.head_dim, cfg.n_kv_heads, cfg.feat_dim
-    L0 = int(L[0])
-    P = cfg.page_size
-    npg = (L0 + 2 * cfg.block_size + P - 1) // P
+    nkv, D, F, P, S = cfg.n_kv_heads, cfg.head_dim, cfg.feat_dim, cfg.page_size, cfg.block_size
+    B = len(L)
+    Ls = np.asarray(L, np.int64)
+    npg = (Ls + 2 * S + P - 1) // P
+    pt = np.full((B, int(npg.max())), -1, np.int64)
+    off = 0
+    for r in range(B):
+        pt[r, :npg[r]] = off + np.arange(npg[r])
+        off += int(npg[r])
     g = np.random.default_rng(wl.seed)
     cache = oracle.OracleCache.__new__(oracle.OracleCache)
-    cache.k = [g.standard_normal((npg * P, nkv, D)) for _ in range(cfg.n_layers)]
-    cache.v = [g.standard_normal((npg * P, nkv, D)) for _ in range(cfg.n_layers)]
-    pt = np.arange(npg)[None, :]
+    cache.k = [g.standard_normal((off * P, nkv, D), dtype=np.float32) for _ in range(cfg.n_layers)]
+    cache.v = [g.standard_normal((off * P, nkv, D), dtype=np.float32) for _ in range(cfg.n_layers)]
+    anc = np.asarray(anchor, np.int64)
+    post = np.asarray(post, np.int64)
+    feats = (g.standard_normal((T_inj, F), dtype=np.float32) * 0.02)
+    pos = np.arange(T_inj)
+    slots = pos % (off * P)
     copy_s = time.time() - t0
-    t1 = time.time()
-    oracle.draft_block(cfg, W, cache, [7], [L0], pt)
-    t_draft = time.time() - t1
-    rows = 64
-    f = (g.standard_normal((rows, F)) * 0.02).astype(np.float32)
-    t2 = time.time()
-    oracle.project_context(cfg, W, cache, f, np.arange(rows), np.arange(rows))
-    t_inj = time.time() - t2
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t = time.time()
+            fn()
+            ts.append(time.time() - t)
+        return float(np.median(ts)), ts
+
+    with working_precision("f32"):
+        d = {}
+        t_draft, r_draft = med3(lambda: d.update(oracle.draft_block(cfg, W, cache, anc, Ls, pt)))
+        t_acc, r_acc = med3(lambda: oracle.accept(d["candidates"], post, Ls))
+        t_inj, r_inj = med3(lambda: oracle.project_context(cfg, W, cache, feats, pos, slots))
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else len(os.sched_getaffinity(0))
-    return {"value": round(1.0 / t_draft, 5), "unit": "draft blocks/s", "cores": threads,
+    ctx = f"{int(Ls.min())}" if Ls.min() == Ls.max() else f"{int(Ls.min())}..{int(Ls.max())}"
+    return {"value": round(B / t_draft, 5), "unit": "draft blocks/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"one full draft pass of 1 request ({cfg.n_layers} layers, context {L0}, "
-                      f"block {cfg.block_size}, vocab {cfg.vocab}) in fp64 numpy: {t_draft:.2f} s; "
-                      f"64-row context injection: {t_inj:.2f} s; weights copied from the GPU "
-                      f"run ({copy_s:.1f} s, untimed)",
-            "drafted_tokens_per_s": round((cfg.block_size - 1) / t_draft, 4),
-            "context_tokens_per_s": round(rows / t_inj, 2)}
+            "sample": f"fp32 oracle, median of 3 runs per unit: one draft pass of the batch "
+                      f"({B} x block {S}, {cfg.n_layers} layers, context {ctx}, vocab "
+                      f"{cfg.vocab}), one accept of the batch, one {T_inj}-row context "
+                      f"injection; weights copied from the GPU run ({copy_s:.1f} s, untimed)",
+            "drafted_tokens_per_s": round(B * (S - 1) / t_draft, 4),
+            "draft_pass_s": {"median": round(t_draft, 4), "runs": [round(t, 4) for t in r_draft]},
+            "accept_s": {"median": round(t_acc, 6), "runs": [round(t, 6) for t in r_acc]},
+            "injection": {"rows": T_inj, "median_s": round(t_inj, 4),
+                          "runs": [round(t, 4) for t in r_inj],
+                          "context_tokens_per_s": round(T_inj / t_inj, 2)}}
 
 
 if __name__ == "__main__":

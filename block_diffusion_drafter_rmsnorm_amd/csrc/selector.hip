@@ -11,7 +11,8 @@
 //               position as predecessor p;
 //   walk:       per request, position by position, the row of the chosen
 //               predecessor: greedy first maximum or an inverse-CDF draw from
-//               softmax(row / T); q_rows = that softmax.
+//               softmax(row / T); q_rows = the distribution the choice was
+//               drawn from (that softmax, or one-hot on the greedy choice).
 //
 // Kernels: topk_tiles_kernel (one workgroup per row: only the 128-column
 // tiles whose lm_head argmax partial reaches the K-th largest tile maximum can
@@ -472,17 +473,18 @@ __global__ __launch_bounds__(kT) void lattice_walk_kernel(
     float m = v == v ? v : kNegInf;
     int best = lane < K ? lane : kNoIdx;
     wave_best(m, best);
-    const float e = lane < K ? expf(v * sc - m * sc) : 0.f;
-    const float q = e * (1.0f / wave_sum(e));
-    if (lane < K) q_rows[((int64_t)b * J + j) * K + lane] = q;
     int pick = best;
+    float q = lane == best ? 1.f : 0.f;  // greedy: all mass on the choice
     if (uni) {
+      const float e = lane < K ? expf(v * sc - m * sc) : 0.f;
+      q = e * (1.0f / wave_sum(e));
       // inverse CDF: the first slot whose running sum of q exceeds the draw
       const float x = us[j];
       const float c = row_incl_scan(q);  // K <= 16: the candidates sit in row 0
       const uint64_t hit = __ballot(lane < K && c > x);
       pick = hit ? __ffsll((unsigned long long)hit) - 1 : K - 1;
     }
+    if (lane < K) q_rows[((int64_t)b * J + j) * K + lane] = q;
     if (lane == 0) candidates[(int64_t)b * S + 1 + j] = cb[j * K + pick];
     p = pick;
   }

@@ -444,8 +444,11 @@ dflash_status dflash_relay_stash(const dflash_request_pool* pool, const int32_t*
  * y_j the row after the final RMSNorm; and the walk: from the anchor's row,
  * the chosen candidate's row at the next position, taking the first maximum
  * (uniforms NULL) or the smallest candidate whose running sum of
- * softmax(row / temperature) exceeds uniforms[b, j].  q_rows[b, j, :] =
- * softmax(row) (softmax(row / temperature) when sampling) of the row walked;
+ * softmax(row / temperature) exceeds uniforms[b, j].  q_rows[b, j, :] is
+ * the distribution the choice was drawn from: softmax(row / temperature) of
+ * the row walked when sampling, one-hot on the chosen slot when greedy (the
+ * proposal of a greedy walk is a point mass), so either feeds
+ * dflash_accept_sampling_sparse as it is;
  * candidates[b] = [anchor, chosen tokens].  The selector weights' values,
  * top_k and rank are the caller's (the pages give none).
  *

@@ -1,4 +1,5 @@
-"""The three operations of the DFlash draft-and-accept path, fp64.
+"""The three operations of the DFlash draft-and-accept path, fp64 (fp32 under
+the timing setting of oracle.precision).
 
 Notation: H hidden, nq / nkv query / kv heads, D head_dim, G = nq / nkv,
 S block size (anchor included), B requests, L_r committed prefix of request r,
@@ -9,11 +10,13 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import round_kv
+from .precision import real
 from .primitives import rms_norm, rope_neox, silu, block_attention
 
 
 def _f64(a):
-    return np.asarray(a, dtype=np.float64)
+    """a in the working precision (fp64 unless the timing setting is on)."""
+    return np.asarray(a, dtype=real())
 
 
 def _qkv_split(w_qkv, cfg):
@@ -23,9 +26,10 @@ def _qkv_split(w_qkv, cfg):
 
 
 def _linear_chunked(x, w, chunk=16384):
-    """x @ w.T with w converted to fp64 one block of output rows at a time."""
+    """x @ w.T with w converted to the working precision one block of output
+    rows at a time."""
     w = np.asarray(w)
-    out = np.empty(x.shape[:-1] + (w.shape[0],), dtype=np.float64)
+    out = np.empty(x.shape[:-1] + (w.shape[0],), dtype=real())
     for n0 in range(0, w.shape[0], chunk):
         out[..., n0:n0 + chunk] = x @ _f64(w[n0:n0 + chunk]).T
     return out
@@ -39,8 +43,8 @@ class OracleCache:
 
     def __init__(self, cfg, num_slots):
         shp = (num_slots, cfg.n_kv_heads, cfg.head_dim)
-        self.k = [np.full(shp, np.nan) for _ in range(cfg.n_layers)]
-        self.v = [np.full(shp, np.nan) for _ in range(cfg.n_layers)]
+        self.k = [np.full(shp, np.nan, dtype=real()) for _ in range(cfg.n_layers)]
+        self.v = [np.full(shp, np.nan, dtype=real()) for _ in range(cfg.n_layers)]
 
     def copy(self):
         c = OracleCache.__new__(OracleCache)
@@ -160,7 +164,7 @@ def draft_block(cfg, W, cache, anchor, prefix_len, page_table, rope=True, reques
         if rope:
             q = rope_neox(q, pos[reqs][:, :, None], cfg.rope_theta)
             k = rope_neox(k, pos[reqs][:, :, None], cfg.rope_theta)
-        o = np.empty((b, S, nq, D))
+        o = np.empty((b, S, nq, D), dtype=real())
         W_l = cfg.window(l)
         for i, r in enumerate(reqs):
             lo = 0

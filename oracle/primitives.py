@@ -1,4 +1,5 @@
-"""Primitive operations of the draft model, fp64.
+"""Primitive operations of the draft model, fp64 (fp32 under the timing
+setting of oracle.precision).
 
 * rms_norm: RMSNorm with a learned gain, used by hidden_norm (the fc +
   hidden_norm projection of the fused target features), the per-head Q/K
@@ -16,33 +17,35 @@
 """
 import numpy as np
 
+from .precision import real
+
 
 def rms_norm(x, g, eps):
     """g * x / sqrt(mean(x^2) + eps) over the last axis."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=real())
     ms = np.mean(x * x, axis=-1, keepdims=True)
-    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=real())
 
 
 def rope_neox(x, pos, theta):
     """Rotate pairs (x[i], x[i + D/2]) by angle pos * theta^(-2i/D)."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=real())
     D = x.shape[-1]
     half = D // 2
-    inv_freq = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / D)
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+    inv_freq = float(theta) ** (-2.0 * np.arange(half, dtype=real()) / D)
+    ang = np.asarray(pos, dtype=real())[..., None] * inv_freq
     c, s = np.cos(ang), np.sin(ang)
     a, b = x[..., :half], x[..., half:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
 def silu(z):
-    z = np.asarray(z, dtype=np.float64)
+    z = np.asarray(z, dtype=real())
     return z / (1.0 + np.exp(-z))
 
 
 def softmax(s, axis=-1):
-    s = np.asarray(s, dtype=np.float64)
+    s = np.asarray(s, dtype=real())
     m = np.max(s, axis=axis, keepdims=True)
     e = np.exp(s - m)
     return e / np.sum(e, axis=axis, keepdims=True)
@@ -61,12 +64,12 @@ def block_attention(q, k_ctx, v_ctx, ctx_pos, k_blk, v_blk, q_pos, window):
     Query head h reads kv head h // (nq / nkv).  Scale 1/sqrt(D).
     Returns o [S, nq, D].
     """
-    q = np.asarray(q, np.float64)
+    q = np.asarray(q, real())
     S, nq, D = q.shape
     nkv = k_blk.shape[1]
     G = nq // nkv
-    keys = np.concatenate([np.asarray(k_ctx, np.float64), np.asarray(k_blk, np.float64)], 0)
-    vals = np.concatenate([np.asarray(v_ctx, np.float64), np.asarray(v_blk, np.float64)], 0)
+    keys = np.concatenate([np.asarray(k_ctx, real()), np.asarray(k_blk, real())], 0)
+    vals = np.concatenate([np.asarray(v_ctx, real()), np.asarray(v_blk, real())], 0)
     n = k_ctx.shape[0]
     visible = np.ones((S, n + S), dtype=bool)
     if window and n:

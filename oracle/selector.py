@@ -16,21 +16,24 @@ gives: candidates, then the lattice, then the walk.
 * Walk: position by position, the row of the predecessor actually chosen;
   greedy takes the first maximum (in candidate order), sampling draws from
   softmax(row / T) by inverse CDF at a caller-supplied uniform.  q_rows[j] is
-  softmax(row) of the chosen predecessor's row (the realised proposal
-  distribution the sampled verify needs); the walk does not search for the
-  best full path.
+  the realised proposal distribution the sampled verify needs (the section on
+  sampling asks the verify to use the distribution the walk actually drew
+  from): softmax(row / T) of the chosen predecessor's row when sampling, the
+  point mass on the chosen slot when greedy.  The walk does not search for
+  the best full path.
 
 Readings (the section leaves them open): y_j is the final-normed hidden row
 (the lm_head's input); U is the unary logit as the lm_head computes it (the
 act-dtype logits); K = 8 and r = 64 by default; the same softmax temperature
-T is used for sampling and for q_rows when sampling (T = 1 for greedy).
+T is used for sampling and for q_rows.
 
 Pins (tests/test_oracle_selector.py): with the compatibility term switched
 off (A = 0) the greedy walk returns the plain argmax drafts of the draft pass;
 a planted compatibility that favours one successor after a given
 predecessor is followed; a lattice where greedy and the best full path differ
-shows the walk is greedy; q_rows are distributions whose argmax is the
-greedy choice.
+shows the walk is greedy; greedy q_rows are one-hot on the choice, and fed
+to the sampled verify they give the point-mass verify's decisions and
+target-distributed tokens (softmax rows there would not).
 """
 import numpy as np
 
@@ -76,15 +79,17 @@ def walk(cand, score, uniforms=None, temperature=1.0):
     draft = np.zeros((B, J), np.int64)
     q_rows = np.zeros((B, J, K))
     chosen = np.zeros((B, J), np.int64)
-    T = float(temperature) if uniforms is not None else 1.0
+    T = float(temperature)
     for b in range(B):
         p = 0
         for j in range(J):
             row = score[b, j, p]
-            q = _softmax(row / T)
             if uniforms is None:
                 k = int(np.argmax(row))                    # first maximum
+                q = np.zeros(K)
+                q[k] = 1.0                                 # a point mass: nothing was drawn
             else:
+                q = _softmax(row / T)
                 c = np.cumsum(q)
                 hit = np.nonzero(c > float(uniforms[b, j]) * c[-1])[0]
                 k = int(hit[0]) if hit.size else K - 1

@@ -313,3 +313,34 @@ def test_selector_then_sparse_verify():
                                st.L.numpy(), u.cpu().numpy().astype(np.float64), 1.0,
                                draft_probs=dense)
     check(g, o, cand, L, max_ambiguous=1 / 32)
+
+
+def test_greedy_selector_q_rows_give_the_point_mass_verify():
+    """After a greedy walk the selector's q rows are one-hot on the drafted
+    token, so the sparse verify fed with them takes the decisions of the
+    point-mass verify (the argmax drafter's case; section on sampling with the
+    proposal distribution the walk actually used)."""
+    from tests.gpu_harness import Setup
+    from workloads.configs import get_workload
+    m = dfl()
+    st = Setup(get_workload("small_bf16"))
+    cfg, B, S, K = st.cfg, st.B, st.S, 8
+    dt = synth._DT[cfg.act_dtype]
+    sel = m.Selector(synth.normal((cfg.vocab, 64), 0.3, 2, "sel_a", dt, "cuda"),
+                     synth.normal((cfg.vocab, 64), 0.3, 2, "sel_b", dt, "cuda"),
+                     synth.normal((64, cfg.hidden), 0.02, 2, "sel_wh", dt, "cuda"), K)
+    mp = int(st.L.max())
+    ws = m.workspace(m.selector_workspace_bytes(cfg, sel, B, mp))
+    pos = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    slots, cand = torch.empty_like(pos), torch.empty_like(pos)
+    cids = torch.empty((B, S - 1, K), dtype=torch.int32, device="cuda")
+    q = torch.empty((B, S - 1, K), dtype=torch.float32, device="cuda")
+    m.dflash_draft_block_selector(cfg, st.c_weights(), st.cache, sel, st.anchor.cuda(),
+                                  st.L.cuda(), st.pt.cuda(), mp, pos, slots, cand, cids, q, ws)
+    tl = synth.normal((B, S, cfg.vocab), 2.0, 8, "sel_target", torch.float32, "cuda")
+    u = torch.rand(B, S, generator=torch.Generator("cuda").manual_seed(5), device="cuda")
+    L = st.L.cuda()
+    g = _run_sparse(cand, tl, cids, q, u, L, 0.9)
+    o = oracle.accept_sampling(cand.cpu().numpy(), tl.cpu().numpy().astype(np.float64),
+                               st.L.numpy(), u.cpu().numpy().astype(np.float64), 0.9)
+    check(g, o, cand, L, max_ambiguous=1 / 32)

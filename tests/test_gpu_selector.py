@@ -7,8 +7,10 @@ rows for the compatibility term.  The GPU forms W_h y from the bf16 pass, so a
 lattice score differs from the oracle's by the bf16 error of the pass (the
 same ~1e-2 of scale as the logits); the walk is compared along the GPU's own
 path: wherever the oracle's row for the same predecessor has a top-2 gap above
-GAP, the GPU's choice must be the oracle's; q_rows must match the softmax of
-that row within QTOL.  With the compatibility switched off the selector must
+GAP, the GPU's choice must be the oracle's; the greedy walk's q_rows must be
+one-hot on the GPU's own choice, bit for bit (the proposal of a greedy walk
+is a point mass), and the sampled walk's must match the softmax of the row
+walked within QTOL.  With the compatibility switched off the selector must
 reproduce the plain draft pass exactly (same logits, same tie rule).
 """
 import numpy as np
@@ -92,9 +94,8 @@ def test_selector_parity(name, K):
             if K == 1 or srt[0] - srt[1] > GAP:
                 n_clear += 1
                 assert k == int(np.argmax(row)), (b, j, k, row)
-            q = np.exp(row - row.max())
-            q /= q.sum()
-            assert np.allclose(g["q_rows"].numpy()[b, j], q, atol=QTOL), (b, j)
+            assert np.array_equal(g["q_rows"].numpy()[b, j], np.eye(K, dtype=np.float32)[k]), \
+                (b, j)
             p = k
     assert n_clear >= 0.7 * n_all, (n_clear, n_all)
 
@@ -113,16 +114,27 @@ def test_selector_without_compatibility_is_the_plain_draft():
 def test_selector_sampled_walk_draws_from_its_q_rows():
     st = Setup(get_workload("small_bf16_wide"))
     K, T = 8, 0.8
-    _, _, _, sel = _selector(st.cfg, 64, K, 5)
+    A, Bt, Wh, sel = _selector(st.cfg, 64, K, 5)
     B, S = st.B, st.S
     u = torch.rand(B, S - 1, generator=torch.Generator("cuda").manual_seed(4), device="cuda")
     g = _run(st, sel, K, uniforms=u, T=T)
     u = u.cpu().numpy().astype(np.float64)
     cand, gc, q = g["cand_ids"].numpy(), g["candidates"].numpy(), g["q_rows"].numpy()
     assert np.allclose(q.sum(-1), 1.0, atol=1e-5)
+    # q_rows are the softmax of the row walked, rows taken from the oracle's
+    # lattice on the GPU's logits along the GPU's path
+    d = oracle.draft_block(st.cfg, st.np_W(), st.oracle_cache(), st.anchor.numpy(),
+                           st.L.numpy(), st.pt.numpy())
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    o = select(f(g["logits"]), d["hidden"], st.anchor.numpy(), f(A), f(Bt), f(Wh), k=K)
     for b in range(B):
+        p = 0
         for j in range(S - 1):
             k = int(np.nonzero(cand[b, j] == gc[b, 1 + j])[0][0])
+            e = np.exp((o["score"][b, j, p] - o["score"][b, j, p].max()) / T)
+            # a score error ds moves a softmax entry by at most ds / (4 T)
+            assert np.allclose(q[b, j], e / e.sum(), atol=QTOL / T), (b, j)
+            p = k
             c = np.cumsum(q[b, j].astype(np.float64))
             lo = c[k - 1] if k > 0 else 0.0
             assert lo - 1e-5 <= u[b, j] and (u[b, j] < c[k] + 1e-5 or k == K - 1), (b, j, k)

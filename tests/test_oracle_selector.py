@@ -4,8 +4,11 @@ and DFlash 2 Implementation", section on DFlash 2: candidates, lattice, walk).
 With the learned compatibility switched off the selector must reduce to the
 plain draft (top-1 candidate = the argmax the draft pass already pins); a
 planted compatibility must steer the walk; the walk is greedy, not a best-path
-search; q_rows are the softmax of the row actually used; top-k orders by
-value with ties to the lower id; the sampled walk draws from q_rows.
+search; top-k orders by value with ties to the lower id; the sampled walk
+draws from q_rows, the softmax of the row actually used.  q_rows are the
+proposal the walk drew from (section on sampling with the distribution the
+walk actually used): after a greedy walk they are one-hot, and fed to the
+sampled verify they keep it lossless, which softmax rows would not.
 """
 import numpy as np
 
@@ -92,7 +95,71 @@ def test_walk_is_greedy_not_best_path():
     score[0, 1, 1] = [5.0, 0.0]              # the best full path would go 1 -> 0
     draft, q, chosen = walk(cand, score)
     assert chosen.tolist() == [[0, 0]] and draft.tolist() == [[10, 20]]
-    assert np.allclose(q[0, 1], [0.5, 0.5])
+    assert q[0].tolist() == [[1.0, 0.0], [1.0, 0.0]]   # a tie still puts all mass on the choice
+
+
+def _scatter(cand_ids, q_rows, V):
+    """q_rows over the candidate slots -> [B, J, V] over the vocabulary."""
+    B, J, K = cand_ids.shape
+    dense = np.zeros((B, J, V))
+    for b in range(B):
+        for j in range(J):
+            np.add.at(dense[b, j], cand_ids[b, j], q_rows[b, j])
+    return dense
+
+
+def test_greedy_q_rows_are_the_point_mass_the_verify_assumes():
+    """Greedy q_rows scattered over the vocabulary are exactly the point mass
+    on the drafted token, so the sampled verify takes the same decisions with
+    them as with no proposal given (the argmax drafter's case)."""
+    rng = np.random.default_rng(5)
+    B, J, K, V = 6, 7, 4, 23
+    cand = np.stack([np.stack([rng.permutation(V)[:K] for _ in range(J)]) for _ in range(B)])
+    score = rng.standard_normal((B, J, K, K))
+    score[:, 0, 1:] = -np.inf
+    draft, q, chosen = walk(cand, score)
+    dense = _scatter(cand, q, V)
+    assert np.array_equal(dense, np.eye(V)[draft])
+    candidates = np.concatenate([rng.integers(0, V, (B, 1)), draft], 1)
+    tl = rng.standard_normal((B, J + 1, V)) * 1.5
+    L = rng.integers(0, 100, B)
+    for trial in range(20):
+        u = rng.random((B, J + 1))
+        a = oracle.accept_sampling(candidates, tl, L, u, 0.9, draft_probs=dense)
+        b = oracle.accept_sampling(candidates, tl, L, u, 0.9)
+        assert np.array_equal(a["out_tokens"], b["out_tokens"])
+        assert np.array_equal(a["accept_len"], b["accept_len"])
+
+
+def test_greedy_walk_with_its_q_rows_emits_target_distributed_tokens():
+    """The first emitted token of a greedily drafted block, verified with the
+    walk's q_rows, follows the target's p (chi-square on seeded draws); the
+    same block verified with softmax rows in their place does not."""
+    rng = np.random.default_rng(6)
+    n, K, V = 20000, 4, 5
+    cand = np.array([[[3, 1, 4, 0]]])
+    score = np.full((1, 1, K, K), -np.inf)
+    score[0, 0, 0] = [1.0, 0.6, 0.2, -0.3]
+    draft, q, _ = walk(cand, score)
+    assert draft.tolist() == [[3]]
+    p_logits = np.array([0.1, 0.9, -0.2, 0.3, 0.5])
+    p = np.exp(p_logits) / np.exp(p_logits).sum()
+    candidates = np.tile([[2, 3]], (n, 1))
+    tl = np.tile(np.stack([p_logits, np.zeros(V)])[None], (n, 1, 1))
+    u = rng.random((n, 2))
+    soft = np.exp(score[0, 0, 0]) / np.exp(score[0, 0, 0]).sum()
+
+    def first_tokens(qk):
+        dense = np.tile(_scatter(cand, qk, V), (n, 1, 1))
+        return oracle.accept_sampling(candidates, tl, np.zeros(n, np.int64), u, 1.0,
+                                      draft_probs=dense)["out_tokens"][:, 0]
+
+    def chi2(tok):
+        counts = np.bincount(tok, minlength=V)
+        return np.sum((counts - n * p) ** 2 / (n * p))
+
+    assert chi2(first_tokens(q)) < 23.5                  # 4 degrees of freedom, p = 1e-4
+    assert chi2(first_tokens(soft[None, None])) > 100.0  # the unrealised proposal is biased
 
 
 def test_lattice_rows_use_the_previous_candidates():
