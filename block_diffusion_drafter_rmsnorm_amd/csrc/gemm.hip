@@ -46,6 +46,7 @@ constexpr int kQkvWaves = 4;    // its waves per workgroup
 GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow, int ksw) {
   GemmPlan p;
   p.rows = false;
+  p.tall = false;
   p.NSL = p.NW = p.kw = 0;
   p.KSW = 1;
   // (128-column tiles: up to 32 rows, so the per-wave partial tiles fit in LDS)
@@ -98,6 +99,19 @@ GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow, int ksw) {
     kc = (kc + 31) / 32 * 32;
     p.Kc = kc;
     p.KS = (K + kc - 1) / kc;
+    return p;
+  }
+  if (p.fat && M <= 128 && (Ncols + BN - 1) / BN >= 512) {
+    // 65..128 rows and at least two 128-column tiles per CU (the lm_head):
+    // gemm_tall, the whole K per workgroup.  (With fewer tiles, split K and
+    // one workgroup per CU, gemm_fat's 128 x 128 tiles measured faster.)
+    p.tall = true;
+    p.BM = 128;
+    p.MB = 0;
+    p.m_tiles = 1;
+    p.n_tiles = (Ncols + BN - 1) / BN;
+    p.Kc = K;
+    p.KS = 1;
     return p;
   }
   if (p.fat) {
@@ -953,6 +967,98 @@ __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, i
   }
 }
 
+// ---------------------------------------------------------------- tall tiles
+// 65..128 rows (bf16) with many column tiles (the lm_head): every weight byte
+// is used by at most 128 rows, so the kernel is bound by the weight stream.
+// One 128 x 128 tile per workgroup (all rows, one 128-column tile) of 8 waves
+// (2 x 4, each 64 x 32: 4 x 2 MFMA blocks), K in 32-wide stages copied
+// straight into LDS as in gemm_big (a wave copies one 16-row A piece and one
+// packed B slab: 2 KB of the stage's 16 KB), a ring of GT_NS stages with
+// GT_NS - 1 in flight, one barrier per stage; the ring and the epilogue tile
+// share 68 KB, so two workgroups run on a CU (48 KB of weights in flight per
+// CU; a deeper ring with one workgroup per CU measured slower).  Column tiles
+// run in the XCD-grouped order of the other tiled kernels, so the A rows stay
+// in each XCD's L2.  K is whole (a multiple of 32, as every K here is).
+constexpr int GT_NS = 4;
+constexpr int GT_STAGE = 128 * 32 + 8 * kChunkElems;  // bf16: A [128][32], B [8 slabs][64][8]
+
+// Wait until at most `later` stages of 2 copies per wave are in flight.
+template <int K> __device__ __forceinline__ void gt_wait(int later) {
+  if constexpr (K <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= K) wait_vmcnt<2 * K>();
+    else gt_wait<K - 1>(later);
+  }
+}
+
+template <class Epi>
+__global__ __launch_bounds__(512) void gemm_tall(ASrcPlain<bf16_t> asrc, int M, int K, int n_tiles,
+                                                 Epi epi) {
+  constexpr int RING = GT_NS * GT_STAGE * 2, TILE = 128 * LDT * 4;
+  constexpr int SMEM = RING > TILE ? RING : TILE;  // the epilogue tile reuses the ring
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  bf16_t* const ring = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, r16 = lane & 15, g4 = lane >> 4;
+  // XCD x (= workgroup id mod 8) takes a contiguous range of column tiles
+  const int per = (n_tiles + 7) / 8;
+  const int nt = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (nt >= n_tiles) return;  // padding of the last XCD's range
+  // this wave's A piece (rows 16 wave .. + 16; lane: row l / 4, 8 columns at
+  // 8 (l % 4); rows past M read row M - 1) and B slab (slab `wave` of tile nt)
+  const bf16_t* ag = asrc.A +
+                     (int64_t)block_row(imin(wave * 16 + lane / 4, M - 1), asrc.S) * asrc.lda +
+                     (lane % 4) * 8;
+  const bf16_t* bg = epi.bslab(nt, wave) + lane * 8;
+  auto issue = [&](int c) {  // stage of K columns [32 c, 32 c + 32)
+    bf16_t* stg = ring + (c % GT_NS) * GT_STAGE;
+    dma16(ag + c * 32, stg + wave * 512);
+    dma16(bg + (int64_t)c * kChunkElems, stg + 128 * 32 + wave * 512);
+  };
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_it = K / 32;
+#pragma unroll
+  for (int c = 0; c < GT_NS - 1; ++c)
+    if (c < n_it) issue(c);
+  for (int it = 0; it < n_it; ++it) {
+    // this lane's copies of stage it are done once at most those of the later
+    // stages in flight remain; the barrier then covers every wave, and also
+    // guarantees that every wave has finished reading stage it - 1, whose
+    // buffer the next issue overwrites
+    gt_wait<GT_NS - 2>(imin(GT_NS - 2, n_it - 1 - it));
+    __builtin_amdgcn_s_barrier();
+    if (it + GT_NS - 1 < n_it) issue(it + GT_NS - 1);
+    const bf16_t* stg = ring + (it % GT_NS) * GT_STAGE;
+    Frag<bf16_t> bf[2], af[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_frag(bf[j], stg + 128 * 32 + (wn * 2 + j) * 512 + lane * 8);
+    load_frag(af[0], stg + (wm * 64 + r16) * 32 + g4 * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i + 1 < 4) load_frag(af[(i + 1) & 1], stg + (wm * 64 + (i + 1) * 16 + r16) * 32 + g4 * 8);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mma(acc[i][j], af[i & 1], bf[j]);
+    }
+  }
+  __syncthreads();  // every wave is done with the ring: the tile takes its place
+  float* tile = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tile[(wm * 64 + i * 16 + g4 * 4 + e) * LDT + wn * 32 + j * 16 + r16] = acc[i][j][e];
+  __syncthreads();
+  epi.prepare(128, 0, M, tid);
+  epi.apply(tile, 128, 0, M, nt, tid);
+}
+
 // Split-K reduction: one workgroup per 4 rows of a tile.  Thread t sums the
 // splits q = t/128, t/128 + 2, ... of one float4 column (in split order, all
 // loads issued before the adds); the two halves are then added in a fixed
@@ -1655,6 +1761,13 @@ static void launch_big(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPl
                        p.KS, p.m_tiles, M, (const float*)partial, epi);
 }
 
+template <class Epi>
+static void launch_tall(const ASrcPlain<bf16_t>& asrc, int M, int K, const GemmPlan& p,
+                        const Epi& epi, hipStream_t st) {
+  const int grid = (p.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_tall<Epi>), dim3(grid), dim3(512), 0, st, asrc, M, K, p.n_tiles, epi);
+}
+
 // Slabs per workgroup of an epilogue that runs on narrow tiles (0: it needs
 // whole 128-column tiles).
 template <class E, class = void> struct NarrowSlabs {
@@ -1728,6 +1841,10 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
   if constexpr (sizeof(T) == 2) {
     if (p.big) {
       launch_big(asrc, M, K, p, (Ncols + BN - 1) / BN, epi, ws.partial, st);
+      return hipGetLastError();
+    }
+    if (p.tall) {
+      launch_tall(asrc, M, K, p, epi, st);
       return hipGetLastError();
     }
     if (p.fat) {

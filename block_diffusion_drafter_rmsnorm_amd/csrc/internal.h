@@ -25,6 +25,7 @@ struct GemmPlan {
   int KSW;       //   K ranges across workgroups (1 unless the caller adds partials)
   bool fat;      // LDS-tiled kernel
   bool big;      // 256 x 256 tiles, no split K (n_tiles counts 256 columns)
+  bool tall;     // 65..128 rows: one 128 x 128 tile per column tile, deep copy ring
   int BM;        // rows per tile (16 MB for the streaming kernel; 128 or 256)
   int MB;        // 16-row blocks per workgroup tile of the streaming kernel (1, 2, 4)
   int m_tiles;   // ceil(M / BM)

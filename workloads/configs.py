@@ -105,6 +105,11 @@ SMALL_BF16_WIDE = DFlashConfig(hidden=2048, n_layers=1, n_q_heads=16, n_kv_heads
                                head_dim=128, inter=2560, vocab=4099, n_target_layers=2,
                                target_hidden=1088, block_size=16, mask_token_id=4097,
                                sliding_window=(96,))
+# A vocabulary of 70001 (547 128-column tiles, the last one ragged): at 65..128
+# rows the lm_head takes the tall-tile path.
+SMALL_BF16_VOCAB_WIDE = DFlashConfig(hidden=256, n_layers=1, n_q_heads=4, n_kv_heads=1,
+                                     head_dim=64, inter=512, vocab=70001, n_target_layers=2,
+                                     target_hidden=256, block_size=16, mask_token_id=69990)
 # A vocabulary wide enough (32777, an odd number of 128-column tiles) that the
 # lm_head of 24 x 15 rows takes the 256 x 256-tile path with a ragged last
 # row tile and a half-empty last column tile.
@@ -142,6 +147,13 @@ WORKLOADS = {
                                 commit=(1, 16), seed=4),
     "small_bf16_vocab": Workload("small_bf16_vocab", SMALL_BF16_VOCAB, batch=24, ctx=(3, 90),
                                  commit=(1, 16), seed=5),
+    # 65..128 rows: 7 x 16 = 112 rows (128-row tiles, every GEMM with a split
+    # K); 8 x 16 = 128 rows over a 70001-token vocabulary (the lm_head's 120
+    # rows on the tall-tile path)
+    "small_bf16_tall": Workload("small_bf16_tall", SMALL_BF16_WIDE, batch=7, ctx=(20, 200),
+                                commit=(1, 16), seed=6),
+    "small_bf16_vocab_tall": Workload("small_bf16_vocab_tall", SMALL_BF16_VOCAB_WIDE, batch=8,
+                                      ctx=(3, 90), commit=(1, 16), seed=7),
 }
 
 
