@@ -197,7 +197,7 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   L.o = cv.take(ab * (size_t)M * nq * D);
   L.cs = (float2*)cv.take(sizeof(float2) * (size_t)M * (D / 2));
   // one (O, m, l) partial of 64 query rows per attention workgroup
-  const bool dma = c->act_dtype == DFLASH_BF16 && c->kv_dtype == DFLASH_BF16;
+  const bool dma = attn_uses_dma(c->act_dtype, c->kv_dtype, D);
   size_t max_launch = 1;
   for (int l = 0; l < c->n_layers; ++l) {
     L.plans[l] = plan_attention(layer_max_keys(c, l, max_prefix), B, nkv, dma);

@@ -50,6 +50,11 @@ constexpr int kDeepSteps = 8;                       // workgroup size of the dee
 //   with all of its steps in flight at once (kDeepSteps LDS stages);
 //   otherwise W = 768 (three per CU, 3 stages).  Other caches: 512.  W
 //   grows (in multiples of 256) so that no range exceeds kMaxSteps units.
+bool attn_uses_dma(int act_dtype, int kv_dtype, int head_dim) {
+  return act_dtype == DFLASH_BF16 &&
+         (kv_dtype == DFLASH_BF16 || (kv_dtype == DFLASH_FP8_E4M3 && head_dim == 128));
+}
+
 AttnPlan plan_attention(int max_keys, int B, int nkv, bool dma) {
   AttnPlan p;
   p.kps = 0;
@@ -646,69 +651,118 @@ template <int DPW, int K> __device__ __forceinline__ void attn_wait_steps(int la
   }
 }
 
-// One part of a segment on the bf16 cache: the block's own keys (when blk)
-// and n_ctx context steps from kbeg, staged NS deep straight from global
-// memory into LDS, then this wave's unnormalised O^T and (m, l) per query row
-// at partial slot `base`.  The page list (physical page of logical page
-// pfirst + i in pages[i]) and Q are in place; every wave of the workgroup
-// calls it.
-template <int D, int NS>
+// Exchanges with the lane 16 (32) apart, by the gfx950 row-swap instructions
+// (VALU, no LDS round trip): permlane16_swap(x, x) returns x's rows as
+// (0 0 2 2) and (1 1 3 3), permlane32_swap(x, x) its halves as (lo lo) and
+// (hi hi); a lane takes the copy that is not its own.
+__device__ __forceinline__ float lane_xor16(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+
+// Cache element type of the direct-to-LDS kernels: K and V bytes of one
+// 32-key step, and the LDS the staging takes (the ring; an fp8 cache also
+// keeps the block's own bf16 keys in a buffer of their own).
+template <typename KT, int D, int NS> struct DmaStage {
+  static constexpr bool F8 = std::is_same<KT, fp8_t>::value;
+  static constexpr int BYTES = 64 * D * (int)sizeof(KT);      // K and V of one step
+  static constexpr int BLK = F8 ? 64 * D * 2 : 0;              // the block's bf16 step
+  static constexpr int LDS = NS * BYTES + BLK;
+};
+
+// One part of a segment on a bf16 or an E4M3 cache: the block's own keys
+// (when blk) and n_ctx context steps from kbeg, staged NS deep straight from
+// global memory into LDS, then this wave's unnormalised O^T and (m, l) per
+// query row at partial slot `base`.  The page list (physical page of logical
+// page pfirst + i in pages[i]) and Q are in place; every wave of the workgroup
+// calls it.  `stg` is the DmaStage LDS of the workgroup.
+//
+// E4M3 cache (D = 128): a step's K and V bytes go to LDS as they lie in the
+// cache (a wave copies one 1 KB K piece and one 1 KB V^T piece), and a wave
+// decodes its fragments to bf16 as it reads them (8 codes per lane, by the
+// conversion instruction: exact).  The block's own keys are bf16; they are
+// copied first, into their own buffer, and computed before the context steps.
+template <int D, int NS, typename KT>
 __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L, int lo, int blk,
                                          int n_ctx, int kbeg, int kend, int pfirst,
-                                         const int* pages, bf16_t (*stg_s)[64 * D],
+                                         const int* pages, char* stg,
                                          const Frag<bf16_t> (&qf)[D / 32], int64_t base) {
   using CT = bf16_t;
-  constexpr int OPW = D / 64;         // K (and V) DMAs per wave per step
-  constexpr int DPW = 2 * OPW;        // DMAs per wave per step
+  using DS = DmaStage<KT, D, NS>;
+  constexpr bool F8 = DS::F8;
+  static_assert(!F8 || D == 128, "the E4M3 staging covers head_dim 128");
+  constexpr int OPW = D / 64;                 // bf16: K (and V) copies per wave per step
+  constexpr int DPW = F8 ? 2 : 2 * OPW;       // copies per wave per context step
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, r16 = lane & 15,
             g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
   const bool qlive = wave * 16 < R;
   const int rho = imin(wave * 16 + r16, R - 1);
   const int jrow = rho % S;
-  // Steps: the block's own keys first (one 16-key page, both halves pointing
-  // at it) when blk, then the context steps.
-  const int n_seq = n_ctx + blk;
-  const CT* kc = static_cast<const CT*>(a.kc);
-  const CT* vc = static_cast<const CT*>(a.vc);
+  const KT* kc = static_cast<const KT*>(a.kc);
+  const KT* vc = static_cast<const KT*>(a.vc);
   const CT* kblk = static_cast<const CT*>(a.kblk) + (int64_t)(r * a.nkv + g) * 16 * D;
   const CT* vblk = static_cast<const CT*>(a.vblk) + (int64_t)(r * a.nkv + g) * D * 16;
   // this lane's K row inside a half (key 8 (r16/4) + 4h + r16%4 of the step:
   // page half r16 / 8, row within it) and V^T key offset (page half g4 / 2)
   const int krow0 = (8 * (r16 >> 2) + (r16 & 3)) & 15;  // + 4 h
   const int khalf = r16 >> 3, vhalf = g4 >> 1, voff = 8 * (g4 & 1);
-  auto issue = [&](int s) {
-    CT* stg = stg_s[s % NS];
-    const CT* kp[2];
-    const CT* vp[2];
-    int vstride;
-    if (s < blk) {
-      kp[0] = kp[1] = kblk;
-      vp[0] = vp[1] = vblk;
-      vstride = 16;
-    } else {
-      const int key0 = kbeg + 32 * (s - blk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int kj = key0 + 16 * j;
-        const int64_t page = pages[kj / a.P - pfirst];
-        const int off = kj % a.P;
-        kp[j] = kc + ((page * a.nkv + g) * a.P + off) * D;
-        vp[j] = vc + (page * a.nkv + g) * (int64_t)D * a.P + off;
-      }
-      vstride = a.P;
-    }
+  char* const blkbuf = stg + NS * DS::BYTES;  // (E4M3 only)
+  // bf16 step (the block's, or a context step of a bf16 cache) into `dst`:
+  // K [kop = h * D/32 + ks][lane][8], V [db][lane][8]
+  auto issue_bf16 = [&](CT* dst, const CT* const* kp, const CT* const* vp, int vstride) {
     const CT* kl = khalf ? kp[1] : kp[0];
     const CT* vl = vhalf ? vp[1] : vp[0];
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int kop = wave * OPW + i, h = kop / (D / 32), ks = kop % (D / 32);
-      attn_dma16(kl + (krow0 + 4 * h) * D + 32 * ks + 8 * g4, stg + kop * 512);
+      attn_dma16(kl + (krow0 + 4 * h) * D + 32 * ks + 8 * g4, dst + kop * 512);
     }
 #pragma unroll
     for (int i = 0; i < OPW; ++i) {
       const int db = wave * OPW + i;
-      attn_dma16(vl + (int64_t)(16 * db + r16) * vstride + voff, stg + 32 * D + db * 512);
+      attn_dma16(vl + (int64_t)(16 * db + r16) * vstride + voff, dst + 32 * D + db * 512);
+    }
+  };
+  // the next context step (keys kbeg + 32 t ..) into ring slot `slot`.  E4M3: piece
+  // kop = wave (score half h = wave / 2, dims 64 c .. with c = wave % 2)
+  // holds, in lane l, 16 dims from 64 c + 16 g4 of step key 8 (r16 / 4) +
+  // 4 h + r16 % 4 (page half r16 / 8, row krow0 + 4 h in it); piece vop =
+  // wave holds, in lane l, the 16 keys of page half wave / 2 of dim 64 c + l
+  // Steps are issued in order (t = 0, 1, ...): the page-list index and the
+  // offset inside the page of the next step's first key advance by 32 keys
+  // per call instead of being divided out (the page size is a multiple of 16,
+  // so a 16-key half never straddles pages).
+  int nx_pg = 0, nx_off = kbeg % a.P;  // kbeg's page is pages[0] (pfirst = kbeg / P)
+  auto issue_ctx = [&](int slot) {
+    char* dst = stg + slot * DS::BYTES;
+    const KT* kp[2];
+    const KT* vp[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t page = pages[nx_pg];
+      kp[j] = kc + ((page * a.nkv + g) * a.P + nx_off) * D;
+      vp[j] = vc + (page * a.nkv + g) * (int64_t)D * a.P + nx_off;
+      nx_off += 16;
+      if (nx_off == a.P) {
+        nx_off = 0;
+        ++nx_pg;
+      }
+    }
+    if constexpr (F8) {
+      const int h = wave >> 1, c = wave & 1;
+      attn_dma16((khalf ? kp[1] : kp[0]) + (krow0 + 4 * h) * D + 64 * c + 16 * g4,
+                 dst + wave * 1024);
+      attn_dma16(vp[h] + (int64_t)(64 * c + lane) * a.P, dst + 4096 + wave * 1024);
+    } else {
+      issue_bf16(reinterpret_cast<CT*>(dst), reinterpret_cast<const CT* const*>(kp),
+                 reinterpret_cast<const CT* const*>(vp), a.P);
     }
   };
 
@@ -719,9 +773,37 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
   for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // one staged step: keys t0 + 8 g4 + e are this lane's elements e = 0..7
-  auto compute = [&](const CT* stg, int t0, bool is_blk) {
-    const CT* Ks = stg;
-    const CT* Vs = stg + 32 * D;
+  auto compute = [&](const char* st, int t0, bool is_blk) {
+    // bf16 fragments at st (the bf16 layout), or E4M3 ones decoded on the read
+    const bool f8 = F8 && !is_blk;
+    const CT* Ks = reinterpret_cast<const CT*>(st);
+    const CT* Vs = Ks + 32 * D;
+    auto kfrag = [&](Frag<CT>& f, int h, int ks) {
+      if (f8) {
+        // K piece h * 2 + ks / 2, record (16 ((ks % 2) * 2 + g4 / 2) + r16),
+        // byte 8 (g4 % 2): dims 32 ks + 8 g4 .. + 8 of the lane's row
+        Raw8<fp8_t> raw;
+        raw.v = *reinterpret_cast<const uint2*>(
+            st + (h * 2 + ks / 2) * 1024 + (16 * ((ks & 1) * 2 + (g4 >> 1)) + r16) * 16 +
+            8 * (g4 & 1));
+        raw_to_frag<CT, fp8_t>(f, raw);
+      } else {
+        load_frag(f, Ks + ((h * (D / 32) + ks) * 64 + lane) * 8);
+      }
+    };
+    auto vfrag = [&](Frag<CT>& f, int db) {
+      if (f8) {
+        // V^T piece (g4 / 2) * 2 + db / 4, record 16 (db % 4) + r16, byte
+        // 8 (g4 % 2): keys 8 g4 .. + 8 of dim 16 db + r16
+        Raw8<fp8_t> raw;
+        raw.v = *reinterpret_cast<const uint2*>(
+            st + 4096 + ((g4 >> 1) * 2 + db / 4) * 1024 + (16 * (db & 3) + r16) * 16 +
+            8 * (g4 & 1));
+        raw_to_frag<CT, fp8_t>(f, raw);
+      } else {
+        load_frag(f, Vs + (db * 64 + lane) * 8);
+      }
+    };
     const bool full = is_blk ? false : (t0 >= lo && t0 + 32 <= kend);
     unsigned keep = 0xffu;
     if (!full) {
@@ -733,13 +815,16 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
         keep |= (ok ? 1u : 0u) << e;
       }
     }
+    // a sliding window hides keys only from steps that start at least a window
+    // below the block's last row (the first steps of the range)
+    const bool wmask = !is_blk && a.window > 0 && (L + S - 1) - t0 >= a.window;
     unsigned vis = keep;
-    if (!is_blk && a.window > 0) {
+    if (wmask) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if ((qpos - (t0 + 8 * g4 + e)) >= a.window) vis &= ~(1u << e);
     }
-    const bool masked = !full || (!is_blk && a.window > 0);
+    const bool masked = !full || wmask;
     f32x4 sacc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -747,7 +832,7 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         Frag<CT> kf;
-        load_frag(kf, Ks + ((h * (D / 32) + ks) * 64 + lane) * 8);
+        kfrag(kf, h, ks);
         mma(sacc[h], kf, qf[ks]);
       }
     }
@@ -759,8 +844,8 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
       if (masked && !((vis >> e) & 1u)) sv[e] = -INFINITY;
       mx = fmaxf(mx, sv[e]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, lane_xor16(mx, lane));
+    mx = fmaxf(mx, lane_xor32(mx, lane));
     // lazy reference maximum: it moves only when a step's maximum exceeds it
     // by more than 8 (log2 units), so probabilities stay below 2^8 and O, l
     // are rescaled rarely; O / l does not depend on the reference
@@ -774,8 +859,8 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
       sv[e] = __builtin_amdgcn_exp2f(sv[e] - msub);
       sum += sv[e];
     }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
+    sum += lane_xor16(sum, lane);
+    sum += lane_xor32(sum, lane);
     if (move) {
       const float alpha = __builtin_amdgcn_exp2f(mold - msub);
       lq *= alpha;
@@ -789,7 +874,7 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       Frag<CT> vf;
-      load_frag(vf, Vs + (db * 64 + lane) * 8);
+      vfrag(vf, db);
       // keys outside the range (first and last steps only) are zeroed: their
       // memory may hold anything
       if (!full) frag_keep(vf, keep);
@@ -797,20 +882,58 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
     }
   };
 
-  // pipeline: steps s + 1 .. s + NS - 1 in flight while step s computes
+  if constexpr (F8) {
+    // the block's keys first (4 bf16 copies per wave, older than every
+    // context copy), then context steps 0 .. NS - 2 in flight
+    const int n_pro = imin(NS - 1, n_ctx);
+    if (blk) {
+      const CT* kp[2] = {kblk, kblk};
+      const CT* vp[2] = {vblk, vblk};
+      issue_bf16(reinterpret_cast<CT*>(blkbuf), kp, vp, 16);
+    }
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < n_seq) issue(s);
-  for (int s = 0; s < n_seq; ++s) {
-    // wait for this wave's DMAs of step s (those of later steps may stay in
-    // flight), then for every wave's
-    attn_wait_steps<DPW, NS - 2>(imin(NS - 2, n_seq - 1 - s));
-    lds_barrier();
-    // the buffer of step s - 1: every wave has finished with it
-    if (s + NS - 1 < n_seq) issue(s + NS - 1);
-    if (qlive) {
-      const bool is_blk = s < blk;
-      compute(stg_s[s % NS], is_blk ? 0 : kbeg + 32 * (s - blk), is_blk);
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < n_ctx) issue_ctx(t);
+    if (blk) {
+      attn_wait_steps<DPW, NS - 1>(n_pro);  // all but the context steps' copies
+      lds_barrier();
+      if (qlive) compute(blkbuf, 0, true);
+    }
+    for (int t = 0; t < n_ctx; ++t) {
+      attn_wait_steps<DPW, NS - 2>(imin(NS - 2, n_ctx - 1 - t));
+      lds_barrier();
+      // the slot of step t - 1: every wave has finished with it
+      if (t + NS - 1 < n_ctx) issue_ctx((t + NS - 1) % NS);
+      if (qlive) compute(stg + (t % NS) * DS::BYTES, kbeg + 32 * t, false);
+    }
+  } else {
+    // Steps: the block's own keys first (one 16-key page, both halves
+    // pointing at it) when blk, then the context steps; steps s + 1 .. s +
+    // NS - 1 in flight while step s computes
+    const int n_seq = n_ctx + blk;
+    auto issue = [&](int s) {
+      if (s < blk) {
+        const CT* kp[2] = {kblk, kblk};
+        const CT* vp[2] = {vblk, vblk};
+        issue_bf16(reinterpret_cast<CT*>(stg + (s % NS) * DS::BYTES), kp, vp, 16);
+      } else {
+        issue_ctx(s % NS);  // context step s - blk
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < n_seq) issue(s);
+    for (int s = 0; s < n_seq; ++s) {
+      // wait for this wave's copies of step s (those of later steps may stay
+      // in flight), then for every wave's
+      attn_wait_steps<DPW, NS - 2>(imin(NS - 2, n_seq - 1 - s));
+      lds_barrier();
+      // the buffer of step s - 1: every wave has finished with it
+      if (s + NS - 1 < n_seq) issue(s + NS - 1);
+      if (qlive) {
+        const bool is_blk = s < blk;
+        compute(stg + (s % NS) * DS::BYTES, is_blk ? 0 : kbeg + 32 * (s - blk), is_blk);
+      }
     }
   }
 
@@ -825,12 +948,11 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
   }
 }
 
-template <int D, int NS>
-__global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs a) {
+template <int D, int NS, typename KT>
+__global__ __launch_bounds__(256, NS <= 4 ? 3 : 1) void attn_dma_kernel(AttnArgs a) {
   using CT = bf16_t;
-  constexpr int STAGE = 64 * D;       // elements of one staged step
   __shared__ int pages[kMaxChunkPages];
-  __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
+  __shared__ __attribute__((aligned(1024))) char stg[DmaStage<KT, D, NS>::LDS];
   __shared__ int red[12];
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, r16 = lane & 15,
             g4 = lane >> 4;
@@ -876,7 +998,7 @@ __global__ __launch_bounds__(256, NS == 3 ? 3 : 1) void attn_dma_kernel(AttnArgs
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   lds_barrier();
 
-  dma_part<D, NS>(a, r, g, L, lo, blk, n_ctx, kbeg, kend, pfirst, pages, stg_s, qf, base);
+  dma_part<D, NS, KT>(a, r, g, L, lo, blk, n_ctx, kbeg, kend, pfirst, pages, stg, qf, base);
   // the next part reuses the stage buffers and the page list
   __syncthreads();
   }
@@ -908,12 +1030,11 @@ __device__ __forceinline__ PartGeom part_geom(const AttnArgs& a, int L, int part
   return q;
 }
 
-template <int D, int NS>
+template <int D, int NS, typename KT>
 __global__ __launch_bounds__(256, 1) void attn_dma_aligned(AttnArgs a) {
   using CT = bf16_t;
-  constexpr int STAGE = 64 * D;
   __shared__ int pages[kMaxChunkPages];
-  __shared__ __attribute__((aligned(1024))) CT stg_s[NS][STAGE];
+  __shared__ __attribute__((aligned(1024))) char stg[DmaStage<KT, D, NS>::LDS];
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4;
   const int S = a.S, R = a.G * S;
   const int rho = imin(wave * 16 + (lane & 15), R - 1);
@@ -945,8 +1066,8 @@ __global__ __launch_bounds__(256, 1) void attn_dma_aligned(AttnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the page list are in
   lds_barrier();
-  dma_part<D, NS>(a, r, g, L, q.lo, q.blk, q.n_ctx, q.kbeg, q.kend, q.pfirst, pages, stg_s, qf,
-                  (int64_t)blockIdx.x * 64);
+  dma_part<D, NS, KT>(a, r, g, L, q.lo, q.blk, q.n_ctx, q.kbeg, q.kend, q.pfirst, pages, stg, qf,
+                      (int64_t)blockIdx.x * 64);
 }
 
 // Combine the partials of one query row: one wave per row.  A partial in
@@ -1054,13 +1175,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __res
 template <typename CT, typename KT, int D>
 static hipError_t run_attn(const AttnArgs& a, const AttnPlan& plan, void* out, hipStream_t st) {
   const dim3 grid((unsigned)plan.n_launch);
-  if constexpr (std::is_same<CT, bf16_t>::value && std::is_same<KT, bf16_t>::value) {
+  constexpr bool kDmaF8 = std::is_same<KT, fp8_t>::value && D == 128;
+  if constexpr (std::is_same<CT, bf16_t>::value && (std::is_same<KT, bf16_t>::value || kDmaF8)) {
+    // three workgroups per CU: 3 stages of a bf16 cache, 4 of an E4M3 one
+    // (half the bytes per step) in the same LDS
+    constexpr int NS3 = kDmaF8 ? 4 : 3;
     if (plan.kps > 0)
-      hipLaunchKernelGGL((attn_dma_aligned<D, kDeepSteps>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_dma_aligned<D, kDeepSteps, KT>), grid, dim3(256), 0, st, a);
     else if (plan.stages == kDeepSteps)
-      hipLaunchKernelGGL((attn_dma_kernel<D, kDeepSteps>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_dma_kernel<D, kDeepSteps, KT>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_dma_kernel<D, 3>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_dma_kernel<D, NS3, KT>), grid, dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL((attn_split_kernel<CT, KT, D>), grid, dim3(256), 0, st, a);
   }
@@ -1080,7 +1205,7 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             const AttnPlan& plan,
                             float* o_part, float2* ml_part, int4* seg, void* out,
                             hipStream_t st) {
-  const bool dma = dt != DFLASH_F32 && kv_dt != DFLASH_FP8_E4M3;
+  const bool dma = attn_uses_dma(dt, kv_dt, D);
   if ((plan.stages != 0) != dma || !plan.fits) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q; a.kblk = kblk; a.vblk = vblk; a.kc = kc; a.vc = vc;

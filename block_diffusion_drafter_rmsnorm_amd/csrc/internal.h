@@ -196,6 +196,9 @@ struct AttnPlan {
 // max_keys: the most context keys a request sees on the layer; dma: the cache
 // and compute types are bf16 (the direct-to-LDS kernel runs).
 AttnPlan plan_attention(int max_keys, int B, int nkv, bool dma);
+// Whether block attention stages the cache straight into LDS (bf16 compute on
+// a bf16 cache, or on an E4M3 cache with head_dim 128).
+bool attn_uses_dma(int act_dtype, int kv_dtype, int head_dim);
 hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void* kblk,
                             const void* vblk,
                             const void* kc, const void* vc, const int32_t* page_table,
