@@ -276,7 +276,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(wl.name),
-                     "kernel": "gemm_stream<EpiLogits> lm_head + argmax partials "
+                     "kernel": "gemm_rows<EpiLogits> lm_head + argmax partials "
                                "(+ argmax reduce), dflash_lm_head_argmax",
                      "bytes_per_launch": lm_bytes,
                      "avg_launch_us": round(lm_avg_s * 1e6, 2)},

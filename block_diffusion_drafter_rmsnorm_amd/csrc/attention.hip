@@ -60,10 +60,12 @@ AttnPlan plan_attention(int max_keys, int B, int nkv, bool dma) {
   p.kps = 0;
   const int64_t units_max = 1 + ((int64_t)(max_keys > 0 ? max_keys : 0) + 31 + 31) / 32;
   const int64_t u_max = units_max * B * nkv;
-  if (dma && (int64_t)B * nkv <= 64) {
-    // Few segments (small batches): kps workgroups per segment, none crossing
-    // a segment, at most 256 in all unless a part would exceed kMaxSteps, and
-    // at least ~2 context steps each.  The split is by the context length
+  if (dma && (int64_t)B * nkv <= 16) {
+    // Few segments (batch 1 or 2): kps >= 16 workgroups per segment, none
+    // crossing a segment, at most 256 in all unless a part would exceed
+    // kMaxSteps, and at least ~2 context steps each.  (With more segments the
+    // byte-range partition at three workgroups per CU streams faster: 64
+    // segments of 16384 keys took 120 us that way, 245 us aligned.)  The split is by the context length
     // the host bounds (max_prefix), so every workgroup knows its key range
     // before any length arrives (aligned kernel).
     const int segs = B * nkv;
