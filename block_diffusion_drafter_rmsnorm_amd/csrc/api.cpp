@@ -323,6 +323,7 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
   const ContextWs L = layout_context(cfg, chunk, workspace);
   if (workspace == nullptr || workspace_bytes < L.bytes)
     return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   KVTargets tg;
   memset(&tg, 0, sizeof tg);
@@ -448,6 +449,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   const DraftWs L = layout_draft(cfg, batch, max_prefix_len, workspace);
   if (workspace == nullptr || workspace_bytes < L.bytes)
     return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
   return draft_core(cfg, w, cache, anchor, prefix_len, page_table, max_pages, batch,
                     max_prefix_len, block_ids, positions, slots, candidates, logits, L,
                     static_cast<hipStream_t>(stream));
@@ -628,6 +630,7 @@ dflash_status dflash_draft_block_selector(
                                         workspace ? static_cast<char*>(workspace) + d : nullptr);
   if (workspace == nullptr || workspace_bytes < d + SL.bytes)
     return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, d + SL.bytes);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* lg = logits ? logits : SL.logits;
   if ((s = draft_core(cfg, w, cache, anchor, prefix_len, page_table, max_pages, batch,
@@ -672,6 +675,7 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* lm_hea
   const LmHeadWs L = layout_lm_head(cfg, rows, workspace);
   if (workspace == nullptr || workspace_bytes < L.bytes)
     return fail(DFLASH_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.bytes);
+  if (!aligned16(workspace)) return fail(DFLASH_EINVAL, "workspace is not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if ((e = gemm_logits(cfg->act_dtype, asrc_plain(hidden, cfg->hidden), rows, cfg->hidden, lm_head,

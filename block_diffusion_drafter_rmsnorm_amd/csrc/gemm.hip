@@ -220,6 +220,37 @@ struct RowScale {
       __syncthreads();
       return;
     }
+    if ((n_ss & 3) == 0 && n_ss <= 512) {
+      // 16-byte loads: a row's <= 512 partials are one or two float4 per
+      // lane; eight rows' loads go out together
+      constexpr int G4 = 8;
+      const int nq = n_ss > 256 ? 2 : 1;
+      for (int r0 = wave; r0 < rows; r0 += nw * G4) {
+        float4 v[G4][2];
+#pragma unroll
+        for (int u = 0; u < G4; ++u) {
+          const int r = r0 + nw * u;
+          const float* p = ss + (int64_t)block_row(imin(m0 + r, M - 1), S) * n_ss;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int t = 4 * (lane + 64 * q);
+            v[u][q] = (r < rows && q < nq && t < n_ss) ? *reinterpret_cast<const float4*>(p + t)
+                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < G4; ++u) {
+          const int r = r0 + nw * u;
+          if (r >= rows) break;
+          const float acc = ((v[u][0].x + v[u][0].y) + (v[u][0].z + v[u][0].w)) +
+                            ((v[u][1].x + v[u][1].y) + (v[u][1].z + v[u][1].w));
+          const float inv = 1.0f / sqrtf(wave_sum(acc) / (float)H + eps);
+          if (lane == 0) out[r] = inv;
+        }
+      }
+      __syncthreads();
+      return;
+    }
     constexpr int G = 4;  // rows per wave batch
     constexpr int Q = 8;  // partials per lane held at once (n_ss <= 512 in one pass)
     for (int r0 = wave; r0 < rows; r0 += nw * G) {

@@ -33,7 +33,8 @@
  *     projection matrices (fc, w_qkv, w_o, w_gate, w_up, w_down, lm_head) are
  *     passed fragment-packed: dflash_pack_matrix turns a row-major [out, in]
  *     matrix (y = x W^T) into that layout once, when the weights are loaded.
- *   - Calls that share a workspace must be ordered on one stream.
+ *   - Calls that share a workspace must be ordered on one stream.  A
+ *     workspace must be 16-byte aligned (DFLASH_EINVAL otherwise).
  */
 #ifndef DFLASH_H
 #define DFLASH_H

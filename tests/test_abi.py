@@ -106,6 +106,14 @@ def test_null_and_workspace_errors():
     st = lib.dflash_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, F, F, 4,
                                 1, 64, None, F, F, F, None, F, 16, None)
     assert st == -3
+    # a workspace off a 16-byte boundary
+    st = lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, 512,
+                                    F, F, None, 1, 4, ctypes.c_void_p(fake + 8), 1 << 30, None)
+    assert st == -1 and b"aligned" in lib.dflash_last_error()
+    st = lib.dflash_draft_block(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, F, F, 4,
+                                1, 64, None, F, F, F, None, ctypes.c_void_p(fake + 4), 1 << 30,
+                                None)
+    assert st == -1 and b"aligned" in lib.dflash_last_error()
     # zero rows / zero batch: nothing to do, no launch
     assert lib.dflash_project_context(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), F, 512,
                                       F, F, None, 0, 4, F, 16, None) == 0
