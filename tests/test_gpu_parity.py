@@ -439,3 +439,33 @@ def test_draft_block_window_ring_parity(name, window):
     sure = argmax_checked_rows(o["logits"], m_tol)
     cand = out["candidates"].cpu().numpy()
     assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
+
+
+# ---------------------------------------------------------------- page sizes
+@pytest.mark.parametrize("name,P,batch", [("small_bf16", 32, 3), ("small_bf16", 48, 12),
+                                          ("small_swa_fp8", 32, 4), ("small_swa_fp8", 48, 20),
+                                          ("small_swa_fp8", 64, 9)])
+def test_draft_block_page_sizes(name, P, batch):
+    """Pages of 32, 48 and 64 keys: a 32-key step's two 16-key halves may sit
+    in one page or straddle two, and the page-list index advances per step.
+    Up to 16 (request, kv head) segments take the aligned partition, 12 x 2
+    and 20 x 1 segments the byte partition; the E4M3 cache (head_dim 128)
+    runs its direct-to-LDS path on both."""
+    wl = get_workload(name)
+    cfg = dataclasses.replace(wl.cfg, page_size=P)
+    wl = dataclasses.replace(wl, cfg=cfg, batch=batch)
+    _print(f"[page size parity] {name} P={P} B={batch} segments={batch * cfg.n_kv_heads}")
+    st = Setup(wl)
+    out = st.draft()
+    o = oracle.draft_block(cfg, st.np_W(), st.oracle_cache(), st.anchor.numpy(), st.L.numpy(),
+                           st.pt.numpy())
+    assert np.array_equal(out["slots"].cpu().numpy(), o["slots"])
+    rel_tol, m_tol = tol(cfg)
+    gl = out["logits"].float().cpu().numpy()
+    rel = logits_row_rel_err(gl, o["logits"])
+    _print(f"  logits max rel err {rel.max():.3e}")
+    assert rel.max() <= rel_tol
+    sure = argmax_checked_rows(o["logits"], m_tol)
+    cand = out["candidates"].cpu().numpy()
+    assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
+    assert np.array_equal(cand[:, 1:], np.argmax(gl, axis=-1))
