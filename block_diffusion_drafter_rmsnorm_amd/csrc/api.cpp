@@ -129,7 +129,7 @@ struct Carver {
 constexpr int kInjectChunk = 8192;  // context rows per injection pass
 
 struct ContextWs {
-  float2* cs; void* cg; float* ss; GemmScratch gs; size_t bytes;
+  float2* cs; void* cg; float* ss; float* kv_raw; GemmScratch gs; size_t bytes;
 };
 
 int64_t inject_chunk_rows(int64_t rows) { return rows < kInjectChunk ? rows : kInjectChunk; }
@@ -162,6 +162,9 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   probe(M);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
+  // fp32 K/V partials of the narrow path (a call of <= 64 rows)
+  const int nraw = kv_inject_raw_floats(M, c->n_layers, c->n_kv_heads, c->head_dim);
+  L.kv_raw = nraw > 0 ? (float*)cv.take(sizeof(float) * (size_t)nraw) : nullptr;
   L.bytes = cv.off;
   return L;
 }
@@ -351,7 +354,7 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
     if ((e = gemm_kv_inject(dt, cfg->kv_dtype, cin, M, cfg->hidden, tg, cfg->n_layers,
                             cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, L.cs,
                             slots + t0, valid_rows, rows_per_req > 0 ? rows_per_req : 1, t0,
-                            cfg->page_size, cache->num_pages, L.gs, st)) != hipSuccess)
+                            cfg->page_size, cache->num_pages, L.kv_raw, L.gs, st)) != hipSuccess)
       return hip_fail(e, "kv inject gemm");
   }
   return DFLASH_OK;

@@ -533,9 +533,12 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
   const int kr0 = imin(K, kq * kq_len), kr1 = imin(K, kr0 + kq_len);
   const Epi epi = epi_all.nsplit(kq);
 
+  // slab addresses from the kernel argument itself (nsplit changes outputs
+  // only): a table indexed at run time stays in the argument segment rather
+  // than in scratch memory under the workgroup's copy
   const T* bp[NSW];  // this lane's record in chunk 0 of each of the wave's slabs
 #pragma unroll
-  for (int s = 0; s < NSW; ++s) bp[s] = epi.nslab(n0 + 16 * (sg * NSW + s)) + lane * 8;
+  for (int s = 0; s < NSW; ++s) bp[s] = epi_all.nslab(n0 + 16 * (sg * NSW + s)) + lane * 8;
   typename ASrc::template State<MB> as;
   asrc.template setup<MB>(as, m0, M, r16);
 
@@ -1290,6 +1293,30 @@ template <typename T> struct EpiQKVStore : EpiStoreF32<T> {
   }
 };
 
+// Layers the narrow K/V store covers.
+constexpr int kKVStoreLayers = DFLASH_MAX_LAYERS;
+
+// The K/V store of an injection of <= 64 rows: EpiStoreF32 over the stacked
+// K/V rows of every layer (column n of layer l = n / (2 nkv D) is row nq D +
+// n % (2 nkv D) of that layer's w_qkv), on kQkvSlabs slabs per workgroup; its
+// consumer adds the K-range partials and applies k_norm, RoPE and the cache
+// write.
+template <typename T> struct EpiKVStore : EpiStoreF32<T> {
+  static constexpr int kNarrow = kQkvSlabs;
+  int per;                     // 2 nkv D
+  int qoff;                    // nq D
+  const void* wl[kKVStoreLayers];  // the layers' w_qkv
+  __device__ EpiKVStore nsplit(int kq) const {
+    EpiKVStore e = *this;
+    if (kq > 0) e.out += kq * this->split_stride;
+    return e;
+  }
+  __device__ const T* nslab(int n0) const {
+    const int n = imin(n0, this->N - 1), l = n / per, w = n % per;
+    return static_cast<const T*>(wl[l]) + (int64_t)((qoff + w) / 16) * slab_elems(this->K);
+  }
+};
+
 template <typename T> struct EpiResidual {
   const T* W; int N; int K; float* x; float* ss; NextNorm<T> nn;
   static constexpr int kNarrow = 1;
@@ -1993,6 +2020,60 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   }
 }
 
+// K/V of an injection of <= 64 rows from the fp32 partials the narrow K/V
+// store wrote (raw [ksw][M][Ly * 2 nkv * D], hidden_norm applied): one wave
+// per (row, layer, K or V head).  The partials are added in range order; K
+// heads get the layer's k_norm and RoPE; both are rounded to the cache type
+// and written at the row's slot (K [page][head][P][D], V [page][head][D][P]).
+// Rows past their request's valid prefix and slots outside the pool are not
+// written.  The same arithmetic as EpiKVInject on the same fp32 values.
+template <typename T, typename KT>
+__global__ __launch_bounds__(256) void kv_norm_rope_store_kernel(
+    const float* __restrict__ raw, int ksw, int M, int n_layers, int nkv, int D, KVTargets tg,
+    float eps, const float2* __restrict__ cs, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ valid, int rpr, int64_t row0, int P, int64_t num_slots) {
+  const int lane = threadIdx.x & 63, HH = n_layers * 2 * nkv, half = D / 2;
+  const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (item >= M * HH) return;  // wave-uniform
+  const int m = item / HH, gh = item % HH, l = gh / (2 * nkv), hk = gh % (2 * nkv);
+  const int64_t t = row0 + m;
+  if (valid != nullptr && (int)(t % rpr) >= valid[t / rpr]) return;
+  const int64_t slot = slots[m];
+  if (slot < 0 || slot >= num_slots) return;
+  const bool act = lane < half;
+  const int64_t pstride = (int64_t)M * HH * D;
+  const float* src = raw + (int64_t)m * HH * D + (int64_t)gh * D;
+  float p0[4], p1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    p0[k] = (act && k < ksw) ? src[k * pstride + lane] : 0.f;
+    p1[k] = (act && k < ksw) ? src[k * pstride + lane + half] : 0.f;
+  }
+  float x0 = p0[0], x1 = p1[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    x0 += p0[k];
+    x1 += p1[k];
+  }
+  const int64_t page = slot / P, off = slot % P;
+  if (hk < nkv) {
+    float o0 = x0, o1 = x1;
+    norm_rope_pair<T>(x0, x1, lane, D, act, static_cast<const T*>(tg.k_norm[l]), eps,
+                      cs + (int64_t)m * half, o0, o1);
+    KT* dst = static_cast<KT*>(tg.kc[l]) + ((page * nkv + hk) * P + off) * D;
+    if (act) {
+      dst[lane] = Num<KT>::from_f(o0);
+      dst[lane + half] = Num<KT>::from_f(o1);
+    }
+  } else {
+    KT* dst = static_cast<KT*>(tg.vc[l]) + ((page * nkv + (hk - nkv)) * D) * P + off;
+    if (act) {
+      dst[(int64_t)lane * P] = Num<KT>::from_f(x0);
+      dst[(int64_t)(lane + half) * P] = Num<KT>::from_f(x1);
+    }
+  }
+}
+
 hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const void* qn,
                     const void* kn, int nq, int nkv, int D, float eps, const float2* cs, void* q,
                     void* k, void* v, int S, float* raw, const GemmScratch& ws, hipStream_t st) {
@@ -2033,13 +2114,59 @@ hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const
   return run_any<float>(a, M, H, ncols, e, ws, st);
 }
 
+template <typename T, typename KT>
+static hipError_t kv_inject_narrow(const ASrc& a, int M, int H, const KVTargets& t, int n_layers,
+                                   int nq, int nkv, int D, float eps, const float2* cs,
+                                   const int32_t* slots, const int32_t* valid_rows,
+                                   int rows_per_req, int64_t row0, int page_size, int64_t ns,
+                                   float* raw, const GemmScratch& ws, hipStream_t st) {
+  const int ncols = n_layers * 2 * nkv * D;
+  const int ksw = qkv_k_splits(ncols);
+  EpiKVStore<T> ep;
+  static_cast<EpiStoreF32<T>&>(ep) =
+      EpiStoreF32<T>{nullptr, ncols, H, raw, ncols, nullptr, NextNorm<T>{nullptr, nullptr},
+                     row_scale(a), (int64_t)M * ncols};
+  ep.per = 2 * nkv * D;
+  ep.qoff = nq * D;
+  for (int l = 0; l < kKVStoreLayers; ++l) ep.wl[l] = t.w_qkv[l];
+  hipError_t e = run_any<T>(a, M, H, ncols, ep, ws, st, ksw);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((M * n_layers * 2 * nkv + 3) / 4);
+  hipLaunchKernelGGL((kv_norm_rope_store_kernel<T, KT>), dim3(grid), dim3(256), 0, st, raw, ksw,
+                     M, n_layers, nkv, D, t, eps, cs, slots, valid_rows, rows_per_req, row0,
+                     page_size, ns);
+  return hipGetLastError();
+}
+
+int kv_inject_raw_floats(int M, int n_layers, int nkv, int D) {
+  if (M > 64 || n_layers > kKVStoreLayers) return 0;
+  const int ncols = n_layers * 2 * nkv * D;
+  return qkv_k_splits(ncols) * M * ncols;
+}
+
 hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
                           const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
-                          int64_t row0, int page_size, int64_t num_pages, const GemmScratch& ws,
-                          hipStream_t st) {
+                          int64_t row0, int page_size, int64_t num_pages, float* raw,
+                          const GemmScratch& ws, hipStream_t st) {
   const int64_t ns = num_pages * page_size;
   const int ncols = n_layers * 2 * nkv * D;
+  if (raw != nullptr && M <= 64 && n_layers <= kKVStoreLayers) {
+    // narrow K/V store into fp32 (K split over workgroups), then the norms,
+    // RoPE and cache writes in a small kernel that adds the partials
+    if (dt == DFLASH_BF16) {
+      if (kv_dt == DFLASH_FP8_E4M3)
+        return kv_inject_narrow<bf16_t, fp8_t>(a, M, H, t, n_layers, nq, nkv, D, eps, cs, slots,
+                                               valid_rows, rows_per_req, row0, page_size, ns,
+                                               raw, ws, st);
+      return kv_inject_narrow<bf16_t, bf16_t>(a, M, H, t, n_layers, nq, nkv, D, eps, cs, slots,
+                                              valid_rows, rows_per_req, row0, page_size, ns,
+                                              raw, ws, st);
+    }
+    return kv_inject_narrow<float, float>(a, M, H, t, n_layers, nq, nkv, D, eps, cs, slots,
+                                          valid_rows, rows_per_req, row0, page_size, ns, raw, ws,
+                                          st);
+  }
   if (dt == DFLASH_BF16) {
     if (kv_dt == DFLASH_FP8_E4M3) {
       EpiKVInject<bf16_t, fp8_t> e{t, H, n_layers, nq, nkv, D, eps, cs, slots, valid_rows,

@@ -243,10 +243,11 @@ def _compare_pools(st, before, o_cache, written):
 
 
 @pytest.mark.parametrize("name", SMALL)
-@pytest.mark.parametrize("grid", [None, (5, 16), (19, 16), 300])
+@pytest.mark.parametrize("grid", [None, (3, 16), (5, 16), (19, 16), 300])
 def test_project_context_parity(name, grid):
     """Rows 77 and 5 x 16 (one 128-row tile), 19 x 16 and 300 (256-row tiles,
-    ragged last tile), with and without a prefix-valid request grid."""
+    ragged last tile), with and without a prefix-valid request grid; 3 x 16
+    (48 rows: the narrow K/V store and its norm/RoPE/write kernel)."""
     wl = get_workload(name)
     cfg = wl.cfg
     _print(f"[inject parity] {name} grid={grid}")

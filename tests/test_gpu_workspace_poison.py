@@ -54,6 +54,14 @@ def test_draft_and_injection_ignore_workspace_contents(name):
         return [t.clone() for t in st.cache.k + st.cache.v]
     _both(inject, m.context_workspace_bytes(cfg, 76))
 
+    # 48 rows: the narrow K/V store's fp32 partials live in the workspace
+    valid3 = torch.tensor([5, 16, 0], dtype=torch.int32)
+
+    def inject_narrow(ws):
+        st.inject(feats[:48], pos[:48], slots[:48], valid3, 3, 16, ws=ws)
+        return [t.clone() for t in st.cache.k + st.cache.v]
+    _both(inject_narrow, m.context_workspace_bytes(cfg, 48))
+
 
 def test_selector_and_verify_ignore_workspace_contents():
     m = dfl()
