@@ -162,6 +162,11 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   probe(M);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
+  // 1/rms per row for the tiled K/V GEMM (chunks of more than 64 rows)
+  if (M > 64) {
+    L.gs.rstd = (float*)cv.take(sizeof(float) * (size_t)M);
+    L.gs.rstd_floats = (size_t)M;
+  }
   // fp32 K/V partials of the narrow path (a call of <= 64 rows)
   const int nraw = kv_inject_raw_floats(M, c->n_layers, c->n_kv_heads, c->head_dim);
   L.kv_raw = nraw > 0 ? (float*)cv.take(sizeof(float) * (size_t)nraw) : nullptr;
@@ -225,6 +230,11 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
     if (gemm_partial_floats(p) > pf) pf = gemm_partial_floats(p);
   L.gs.partial = (float*)cv.take(sizeof(float) * (pf ? pf : 1));
   L.gs.partial_floats = pf;
+  // 1/rms per row for the tiled GEMMs (more than 64 block rows)
+  if (M > 64) {
+    L.gs.rstd = (float*)cv.take(sizeof(float) * (size_t)M);
+    L.gs.rstd_floats = (size_t)M;
+  }
   L.bytes = cv.off;
   return L;
 }

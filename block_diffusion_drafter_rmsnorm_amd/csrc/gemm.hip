@@ -26,6 +26,9 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace dflash {
 
 constexpr int BN = 128;      // output columns per workgroup tile
@@ -208,6 +211,9 @@ struct RowScale {
   int H;
   float eps;
   int S;
+  // the values fill() computes, already computed for every GEMM row m (by
+  // row_rstd_kernel, with fill() itself); nullable
+  const float* pre;
   // 1/rms of the tile's rows m0 .. m0+rows-1 into out[] (LDS), one wave per row
   // (the row's partial sums spread over the lanes, all of a batch of G rows'
   // loads issued before any is summed; each lane adds its values in a fixed
@@ -215,6 +221,11 @@ struct RowScale {
   // ends with a barrier.
   __device__ __forceinline__ void fill(float* out, int rows, int m0, int M, int tid) const {
     const int lane = tid & 63, wave = tid >> 6, nw = (int)(blockDim.x >> 6);
+    if (pre != nullptr) {
+      for (int r = tid; r < rows; r += (int)blockDim.x) out[r] = pre[imin(m0 + r, M - 1)];
+      __syncthreads();
+      return;
+    }
     if (ss == nullptr) {
       for (int r = tid; r < rows; r += (int)blockDim.x) out[r] = 1.0f;
       __syncthreads();
@@ -1883,6 +1894,20 @@ static void launch_rows(const AS& asrc, int M, int K, const GemmPlan& p, const E
   launch_rows_mb<T, NSL, 8>(asrc, M, K, p, epi, st);
 }
 
+// 1/rms of GEMM rows [16 b, 16 b + 16) into out: RowScale::fill itself, so the
+// values are the ones the tiles would compute.
+constexpr int kRstdRows = 16;
+__global__ __launch_bounds__(256) void row_rstd_kernel(RowScale rs, int M, float* __restrict__ out) {
+  const int m0 = (int)blockIdx.x * kRstdRows, rows = imin(kRstdRows, M - m0);
+  float* srs = row_scale_lds();
+  rs.fill(srs, rows, m0, M, (int)threadIdx.x);  // ends with a barrier
+  if ((int)threadIdx.x < rows) out[m0 + threadIdx.x] = srs[threadIdx.x];
+}
+
+template <class E, class = void> struct HasRowScale : std::false_type {};
+template <class E>
+struct HasRowScale<E, decltype((void)std::declval<const E&>().rs)> : std::true_type {};
+
 template <typename T, class AS, class Epi>
 static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& epi,
                            const GemmScratch& ws, hipStream_t st, int ksw = 1) {
@@ -1893,6 +1918,18 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
     if (p.rows) {
       launch_rows<T, NAR>(asrc, M, K, p, epi, st);
       return hipGetLastError();
+    }
+  }
+  // tiled kernels: the row scales once per row, ahead of the GEMM, rather than
+  // once per tile (each tile would re-read its rows' H / 16 sums of squares)
+  if constexpr (HasRowScale<Epi>::value) {
+    if (epi.rs.ss != nullptr && epi.rs.pre == nullptr && ws.rstd != nullptr &&
+        (size_t)M <= ws.rstd_floats) {
+      hipLaunchKernelGGL(row_rstd_kernel, dim3((unsigned)((M + kRstdRows - 1) / kRstdRows)),
+                         dim3(256), 0, st, epi.rs, M, ws.rstd);
+      Epi e = epi;
+      e.rs.pre = ws.rstd;
+      return run_gemm<T>(asrc, M, K, Ncols, e, ws, st, ksw);
     }
   }
   if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
@@ -1927,7 +1964,7 @@ static hipError_t run_any(const ASrc& a, int M, int K, int Ncols, const Epi& epi
 }
 
 static RowScale row_scale(const ASrc& a) {
-  return RowScale{a.ss, a.n_ss, a.H, a.eps, a.S_skip};
+  return RowScale{a.ss, a.n_ss, a.H, a.eps, a.S_skip, nullptr};
 }
 
 hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, int N, float* out,

@@ -13,6 +13,10 @@ namespace dflash {
 struct GemmScratch {
   float* partial;
   size_t partial_floats;
+  // 1/rms of each row of a row-scaled GEMM of more than 64 rows, computed once
+  // before the GEMM instead of by every tile (nullable: the tiles compute it)
+  float* rstd = nullptr;
+  size_t rstd_floats = 0;
 };
 
 // Launch geometry of a GEMM C[M, Ncols] = A[M, K] W^T: the weight-streaming
