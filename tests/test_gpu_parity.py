@@ -243,11 +243,13 @@ def _compare_pools(st, before, o_cache, written):
 
 
 @pytest.mark.parametrize("name", SMALL)
-@pytest.mark.parametrize("grid", [None, (3, 16), (5, 16), (19, 16), 300])
+@pytest.mark.parametrize("grid", [None, (3, 16), (4, 16), 65, (5, 16), (19, 16), 300])
 def test_project_context_parity(name, grid):
     """Rows 77 and 5 x 16 (one 128-row tile), 19 x 16 and 300 (256-row tiles,
     ragged last tile), with and without a prefix-valid request grid; 3 x 16
-    (48 rows: the narrow K/V store and its norm/RoPE/write kernel)."""
+    and 4 x 16 (48 and 64 rows: the narrow K/V store and its norm/RoPE/write
+    kernel, the second at its largest size) and 65 rows (the first size the
+    tiled GEMMs take, with the row scales computed ahead of them)."""
     wl = get_workload(name)
     cfg = wl.cfg
     _print(f"[inject parity] {name} grid={grid}")
