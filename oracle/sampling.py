@@ -68,8 +68,8 @@ def accept_sampling(candidates, target_logits, prefix_len, uniforms, target_temp
     draft_probs   [B, S-1, V] or None: q itself (takes precedence over draft_logits)
     uniforms      [B, S]     draws in [0, 1): acceptance draws, then the token draw
     Returns the greedy accept's outputs (accept_len, commit_len, out_tokens,
-    next_anchor, new_seq_len) plus, per request, what a checker needs to judge
-    a computation done in another precision: `margin` (the smallest relative
+    next_anchor, new_seq_len) plus, per request, what a comparison with a
+    computation done in another precision needs: `margin` (the smallest relative
     gap |u q(y) - p(y)| / max(u q(y), p(y)) over the decisions taken; inf when
     both sides are exactly 0), `weights` (the unnormalised
     weights the final token was drawn from) and `draw` (u * their sum).
