@@ -268,6 +268,32 @@ def test_project_context_parity(name, grid):
     _compare_pools(st, before, o_cache, slots.numpy()[live])
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "small_swa_fp8", "tiny_f32"])
+@pytest.mark.parametrize("T", [48, 77, 300])
+def test_project_context_slots_outside_the_pool(name, T):
+    """Rows whose slot lies outside the pool (negative, or at or past
+    num_pages * page_size) are skipped by every K/V path (the narrow store's
+    write kernel at 48 rows, the tiled epilogues at 77 and 300 rows): the
+    other rows match the oracle and no other slot changes."""
+    wl = get_workload(name)
+    cfg = wl.cfg
+    _print(f"[inject outside pool] {name} T={T}")
+    st = Setup(wl, extra_tokens=max(2 * cfg.block_size, T))
+    feats, pos, slots, _ = _inject_case(st, T, 900 + T)
+    n_slots = st.num_pages * cfg.page_size
+    g = torch.Generator().manual_seed(T)
+    bad = torch.randperm(T, generator=g)[: max(T // 8, 3)]
+    for i, b in enumerate(bad.tolist()):
+        slots[b] = -1 - i if i % 2 == 0 else n_slots + i
+    before = st.oracle_cache()
+    o_cache = before.copy()
+    st.inject(feats, pos, slots)
+    keep = (slots >= 0) & (slots < n_slots)
+    oracle.project_context(cfg, st.np_W(), o_cache, feats[keep].float().numpy(),
+                           pos[keep].numpy(), slots[keep].numpy())
+    _compare_pools(st, before, o_cache, slots[keep].numpy())
+
+
 def test_project_context_large_tiles():
     """8192 rows of the hidden-2048 model: the fc GEMM takes the 256 x 256-tile
     path.  The oracle recomputes a sample of rows (injection is row-local)."""
