@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # host-sanitized one through it); by default the in-tree library.
 LIB_PATH = os.environ.get("DFLASH_LIBRARY") or os.path.join(_HERE, "libdflash.so")
 MAX_LAYERS = 16
+CHECKS = 4  # DFLASH_CHECKS: (count, first index) pairs of a checked-mode report
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 _DT_CODE = {"f32": F32, "bf16": BF16, "fp8_e4m3": FP8_E4M3}
@@ -88,6 +89,8 @@ EXPORTED = ["dflash_context_workspace_bytes", "dflash_draft_workspace_bytes",
             "dflash_packed_matrix_bytes", "dflash_pack_matrix",
             "dflash_draft_block_noalloc_limit", "dflash_draft_block_noalloc",
             "dflash_relay_resolve", "dflash_relay_stash",
+            "dflash_check_draft_inputs", "dflash_check_context_inputs",
+            "dflash_check_accept_inputs",
             "dflash_status_string", "dflash_last_error"]
 
 
@@ -153,6 +156,12 @@ def _load():
     lib.dflash_packed_matrix_bytes.restype = SZ
     lib.dflash_pack_matrix.argtypes = [P, P, I32, I32, I32, P]
     lib.dflash_pack_matrix.restype = I32
+    lib.dflash_check_draft_inputs.argtypes = [cfgp, kvp, P, P, P, I32, I32, I32, P, P]
+    lib.dflash_check_draft_inputs.restype = I32
+    lib.dflash_check_context_inputs.argtypes = [cfgp, kvp, P, P, P, I32, I32, P, P]
+    lib.dflash_check_context_inputs.restype = I32
+    lib.dflash_check_accept_inputs.argtypes = [P, P, P, I32, I32, I32, P, P]
+    lib.dflash_check_accept_inputs.restype = I32
     lib.dflash_status_string.argtypes = [I32]
     lib.dflash_status_string.restype = ctypes.c_char_p
     lib.dflash_last_error.argtypes = []
@@ -289,13 +298,85 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+# ---------------------------------------------------------------- checked mode
+# Device-side checks of the values the calls read from device memory (the
+# rules are listed with dflash_check_*_inputs in dflash.h).  Each returns
+# {rule: (count, first index)} for the rules that have violations; the
+# `checked=True` flag of the calls below runs them first, synchronises, and
+# raises ValueError instead of launching when any rule is violated.
+CHECK_RULES = {
+    "draft": ("anchor id outside [0, vocab)", "prefix_len outside [0, max_prefix_len]",
+              "block does not fit the page-table row", "page-table entry outside the pool"),
+    "context": ("live row's slot outside the pool", "live row's position < 0",
+                "valid_rows outside [0, rows_per_req]"),
+    "accept": ("candidate id outside [0, vocab)", "posterior id outside [0, vocab)",
+               "prefix_len < 0"),
+}
+
+
+def _report(kind: str, report: torch.Tensor) -> Dict[str, tuple]:
+    r = report.cpu().tolist()  # synchronises with the stream the check ran on
+    names = CHECK_RULES[kind]
+    return {names[k]: (r[2 * k], r[2 * k + 1]) for k in range(len(names)) if r[2 * k] > 0}
+
+
+def _report_buffer(device) -> torch.Tensor:
+    return torch.empty(2 * CHECKS, dtype=torch.int32, device=device)
+
+
+def check_draft_inputs(cfg, cache: KVCache, anchor: torch.Tensor, prefix_len: torch.Tensor,
+                       page_table: torch.Tensor, max_prefix_len: int, stream=None,
+                       c_cfg: Optional[CConfig] = None, c_cache: Optional[CKVCache] = None):
+    c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
+    c_cache = c_cache if c_cache is not None else cache.c_struct()
+    report = _report_buffer(anchor.device)
+    _check(_lib.dflash_check_draft_inputs(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), _ptr(anchor), _ptr(prefix_len),
+        _ptr(page_table), int(page_table.shape[1]), int(anchor.shape[0]), int(max_prefix_len),
+        _ptr(report), _stream(stream)))
+    return _report("draft", report)
+
+
+def check_context_inputs(cfg, cache: KVCache, positions: torch.Tensor, slots: torch.Tensor,
+                         valid_rows: Optional[torch.Tensor], n_req: int, rows_per_req: int,
+                         stream=None, c_cfg: Optional[CConfig] = None,
+                         c_cache: Optional[CKVCache] = None):
+    c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
+    c_cache = c_cache if c_cache is not None else cache.c_struct()
+    report = _report_buffer(slots.device)
+    _check(_lib.dflash_check_context_inputs(
+        ctypes.byref(c_cfg), ctypes.byref(c_cache), _ptr(positions), _ptr(slots),
+        _ptr(valid_rows), int(n_req), int(rows_per_req), _ptr(report), _stream(stream)))
+    return _report("context", report)
+
+
+def check_accept_inputs(candidates: torch.Tensor, posterior: torch.Tensor,
+                        prefix_len: torch.Tensor, vocab: int, stream=None):
+    B, S = candidates.shape
+    report = _report_buffer(candidates.device)
+    _check(_lib.dflash_check_accept_inputs(_ptr(candidates), _ptr(posterior), _ptr(prefix_len),
+                                           int(B), int(S), int(vocab), _ptr(report),
+                                           _stream(stream)))
+    return _report("accept", report)
+
+
+def _raise_if(found: Dict[str, tuple], call: str):
+    if found:
+        raise ValueError(f"{call}: device inputs break the contract: " +
+                         "; ".join(f"{k} ({n}x, first at {i})" for k, (n, i) in found.items()))
+
+
 def dflash_project_context(cfg, weights: CWeights, cache: KVCache, feats: torch.Tensor,
                            positions: torch.Tensor, slots: torch.Tensor,
                            valid_rows: Optional[torch.Tensor], n_req: int, rows_per_req: int,
                            ws: torch.Tensor, stream=None, c_cfg: Optional[CConfig] = None,
-                           c_cache: Optional[CKVCache] = None):
+                           c_cache: Optional[CKVCache] = None, checked: bool = False):
     c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
     c_cache = c_cache if c_cache is not None else cache.c_struct()
+    if checked:
+        _raise_if(check_context_inputs(cfg, cache, positions, slots, valid_rows, n_req,
+                                       rows_per_req, stream, c_cfg, c_cache),
+                  "dflash_project_context")
     _check(_lib.dflash_project_context(
         ctypes.byref(c_cfg), ctypes.byref(weights), ctypes.byref(c_cache), _ptr(feats),
         int(feats.stride(0)), _ptr(positions), _ptr(slots), _ptr(valid_rows), int(n_req),
@@ -307,9 +388,13 @@ def dflash_draft_block(cfg, weights: CWeights, cache: KVCache, anchor: torch.Ten
                        positions: torch.Tensor, slots: torch.Tensor, candidates: torch.Tensor,
                        ws: torch.Tensor, block_ids: Optional[torch.Tensor] = None,
                        logits: Optional[torch.Tensor] = None, stream=None,
-                       c_cfg: Optional[CConfig] = None, c_cache: Optional[CKVCache] = None):
+                       c_cfg: Optional[CConfig] = None, c_cache: Optional[CKVCache] = None,
+                       checked: bool = False):
     c_cfg = c_cfg if c_cfg is not None else make_config(cfg)
     c_cache = c_cache if c_cache is not None else cache.c_struct()
+    if checked:
+        _raise_if(check_draft_inputs(cfg, cache, anchor, prefix_len, page_table, max_prefix_len,
+                                     stream, c_cfg, c_cache), "dflash_draft_block")
     _check(_lib.dflash_draft_block(
         ctypes.byref(c_cfg), ctypes.byref(weights), ctypes.byref(c_cache), _ptr(anchor),
         _ptr(prefix_len), _ptr(page_table), int(page_table.shape[1]), int(anchor.shape[0]),
@@ -340,8 +425,13 @@ def dflash_draft_block_noalloc(cfg, weights: CWeights, cache: KVCache, anchor: t
 
 def dflash_accept(candidates: torch.Tensor, posterior: torch.Tensor, prefix_len: torch.Tensor,
                   accept_len: torch.Tensor, commit_len: torch.Tensor, out_tokens: torch.Tensor,
-                  next_anchor: torch.Tensor, new_seq_len: torch.Tensor, stream=None):
+                  next_anchor: torch.Tensor, new_seq_len: torch.Tensor, stream=None,
+                  checked_vocab: Optional[int] = None):
+    """checked_vocab: run the checked mode with this vocabulary size first."""
     B, S = candidates.shape
+    if checked_vocab is not None:
+        _raise_if(check_accept_inputs(candidates, posterior, prefix_len, checked_vocab, stream),
+                  "dflash_accept")
     _check(_lib.dflash_accept(_ptr(candidates), _ptr(posterior), _ptr(prefix_len), int(B), int(S),
                               _ptr(accept_len), _ptr(commit_len), _ptr(out_tokens),
                               _ptr(next_anchor), _ptr(new_seq_len), _stream(stream)))

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdflash.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
-SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "sampling.hip", "selector.hip", "reserve.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "sampling.hip", "selector.hip", "reserve.hip",
+           "noalloc.hip", "check.hip", "api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 vector ops stay off (plain scalar fp32 code only)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -579,6 +579,61 @@ dflash_status dflash_release_pages(const int32_t* mask, int32_t batch, const int
   return DFLASH_OK;
 }
 
+dflash_status dflash_check_draft_inputs(const dflash_config* cfg, const dflash_kv_cache* cache,
+                                        const int32_t* anchor, const int32_t* prefix_len,
+                                        const int32_t* page_table, int32_t max_pages,
+                                        int32_t batch, int32_t max_prefix_len, int32_t* report,
+                                        void* stream) {
+  if (!cfg || !cache || !report) return fail(DFLASH_EINVAL, "NULL pointer argument");
+  if (batch < 0 || max_prefix_len < 0 || max_pages < 1)
+    return fail(DFLASH_EINVAL, "batch, max_prefix_len or max_pages out of range");
+  if (batch > 0 && (!anchor || !prefix_len || !page_table))
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  if (cfg->page_size < 1 || cfg->block_size < 1 || cfg->vocab < 1)
+    return fail(DFLASH_EINVAL, "page_size, block_size or vocab out of range");
+  hipError_t e = launch_check_draft(anchor, prefix_len, page_table, max_pages, batch,
+                                    max_prefix_len, cfg->block_size, cfg->page_size, cfg->vocab,
+                                    cache->num_pages, cfg->context_window > 0 ? cfg->context_window
+                                                                              : 0,
+                                    report, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "check draft inputs");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_check_context_inputs(const dflash_config* cfg, const dflash_kv_cache* cache,
+                                          const int32_t* positions, const int32_t* slots,
+                                          const int32_t* valid_rows, int32_t n_req,
+                                          int32_t rows_per_req, int32_t* report, void* stream) {
+  if (!cfg || !cache || !report) return fail(DFLASH_EINVAL, "NULL pointer argument");
+  if (n_req < 0 || rows_per_req < 0) return fail(DFLASH_EINVAL, "negative row counts");
+  if ((int64_t)n_req * rows_per_req > INT32_MAX)
+    return fail(DFLASH_EINVAL, "more than 2^31 - 1 rows");
+  if ((int64_t)n_req * rows_per_req > 0 && (!positions || !slots))
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  if (cfg->page_size < 1) return fail(DFLASH_EINVAL, "page_size out of range");
+  hipError_t e = launch_check_context(positions, slots, valid_rows, n_req, rows_per_req,
+                                      cache->num_pages * cfg->page_size, report,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "check context inputs");
+  return DFLASH_OK;
+}
+
+dflash_status dflash_check_accept_inputs(const int32_t* candidates, const int32_t* posterior,
+                                         const int32_t* prefix_len, int32_t batch,
+                                         int32_t block_size, int32_t vocab, int32_t* report,
+                                         void* stream) {
+  if (!report) return fail(DFLASH_EINVAL, "NULL pointer argument");
+  if (batch < 0 || block_size < 1 || vocab < 1)
+    return fail(DFLASH_EINVAL, "batch, block_size or vocab out of range");
+  if ((int64_t)batch * block_size > INT32_MAX) return fail(DFLASH_EINVAL, "batch too large");
+  if (batch > 0 && (!candidates || !posterior || !prefix_len))
+    return fail(DFLASH_EINVAL, "NULL pointer argument");
+  hipError_t e = launch_check_accept(candidates, posterior, prefix_len, batch, block_size, vocab,
+                                     report, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "check accept inputs");
+  return DFLASH_OK;
+}
+
 // Workspace of the selector stage, carved after the draft pass's.
 struct SelectorWs {
   void* logits; float* unary; float* w; GemmScratch gs; size_t bytes;

@@ -166,6 +166,18 @@ hipError_t launch_accept_sampling(int dt, int vec, const int32_t* cand, const vo
                                   int32_t* next_anchor, int32_t* new_seq_len, hipStream_t st);
 
 // ---- cache reservation (reserve.hip)
+// checked mode (check.hip): reset `report`, then add each rule's violations
+hipError_t launch_check_draft(const int32_t* anchor, const int32_t* prefix_len,
+                              const int32_t* page_table, int max_pages, int batch, int max_prefix,
+                              int S, int P, int vocab, int64_t num_pages, int cwin,
+                              int32_t* report, hipStream_t st);
+hipError_t launch_check_context(const int32_t* positions, const int32_t* slots,
+                                const int32_t* valid, int n_req, int rpr, int64_t num_slots,
+                                int32_t* report, hipStream_t st);
+hipError_t launch_check_accept(const int32_t* cand, const int32_t* post,
+                               const int32_t* prefix_len, int B, int S, int vocab,
+                               int32_t* report, hipStream_t st);
+
 hipError_t launch_reserve(const int32_t* seq_len, int B, int S, int P, int32_t* pt, int max_pages,
                           int32_t* n_pages, const int32_t* free_pages, int capacity,
                           int32_t* free_count, int32_t* status, hipStream_t st);

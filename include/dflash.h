@@ -499,6 +499,58 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* lm_hea
                                     const void* hidden, int32_t rows, void* logits, int32_t* ids,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Checked mode (tests and debugging; not for the serving loop).  The calls
+ * above check what the host sees; the values they read from device memory
+ * are the caller's contract, which their kernels only clamp.  These calls
+ * check that contract on the device: each launches two small kernels on
+ * `stream` that write `report` (device memory, 2 * DFLASH_CHECKS int32:
+ * per rule k, report[2k] = the number of violations and report[2k+1] = the
+ * smallest index among them, INT32_MAX when there is none) and reads nothing
+ * back, so the caller synchronises and reads the report.  Rules without a
+ * meaning for a call report 0, INT32_MAX.  No other call runs them.
+ *
+ * dflash_check_draft_inputs, for dflash_draft_block's arguments (indices r =
+ * batch row):
+ *   0  anchor[r] outside [0, vocab)
+ *   1  prefix_len[r] outside [0, max_prefix_len]
+ *   2  without a draft window (context_window 0): prefix_len[r] + block_size
+ *      > max_pages * page_size (the block does not fit the page-table row)
+ *   3  a page-table entry the pass reads outside [0, num_pages): the entries
+ *      of the logical pages holding keys [lo, prefix_len[r] + block_size),
+ *      lo = max(0, prefix_len[r] - context_window) with a draft window (a
+ *      ring row: logical page p at entry p mod max_pages) and 0 without one
+ *      (entries below max_pages); prefix_len[r] clamped to [0,
+ *      max_prefix_len] for this rule; index r * max_pages + entry
+ * dflash_check_context_inputs, for dflash_project_context's (indices t = row,
+ * r = request; a live row is one with t mod rows_per_req < valid_rows[t /
+ * rows_per_req], every row when valid_rows is NULL):
+ *   0  a live row's slot outside [0, num_pages * page_size)
+ *   1  a live row's position < 0
+ *   2  valid_rows[r] outside [0, rows_per_req]
+ * dflash_check_accept_inputs, for dflash_accept's (indices i = r *
+ * block_size + j, r):
+ *   0  candidates[i] outside [0, vocab)
+ *   1  posterior[i] outside [0, vocab)
+ *   2  prefix_len[r] < 0
+ * Errors: DFLASH_EINVAL for NULL pointers (valid_rows may be NULL) or
+ * negative sizes; DFLASH_EHIP for a launch failure.
+ */
+#define DFLASH_CHECKS 4
+dflash_status dflash_check_draft_inputs(const dflash_config* cfg, const dflash_kv_cache* cache,
+                                        const int32_t* anchor, const int32_t* prefix_len,
+                                        const int32_t* page_table, int32_t max_pages,
+                                        int32_t batch, int32_t max_prefix_len, int32_t* report,
+                                        void* stream);
+dflash_status dflash_check_context_inputs(const dflash_config* cfg, const dflash_kv_cache* cache,
+                                          const int32_t* positions, const int32_t* slots,
+                                          const int32_t* valid_rows, int32_t n_req,
+                                          int32_t rows_per_req, int32_t* report, void* stream);
+dflash_status dflash_check_accept_inputs(const int32_t* candidates, const int32_t* posterior,
+                                         const int32_t* prefix_len, int32_t batch,
+                                         int32_t block_size, int32_t vocab, int32_t* report,
+                                         void* stream);
+
 const char* dflash_status_string(dflash_status s);
 const char* dflash_last_error(void);
 

@@ -279,3 +279,36 @@ def test_relay_argument_errors():
     # an empty batch is a no-op
     p.n_pages = None
     assert lib.dflash_relay_stash(ctypes.byref(p), None, 0, fake, fake, None, None, None) == 0
+
+
+def test_checked_mode_argument_errors():
+    """The checked-mode calls refuse NULL pointers and negative sizes before any
+    launch; an empty batch or row set only resets the report (not run here:
+    that is a launch).  Their report size matches the binding's."""
+    lib = dfl.raw_lib()
+    fake = ctypes.c_void_p(0x100000)
+    c = dfl.make_config(TINY)
+    kv = dfl.CKVCache()
+    kv.num_pages = 4
+    assert lib.dflash_check_draft_inputs(None, ctypes.byref(kv), fake, fake, fake, 4, 1, 64,
+                                         fake, None) == -1
+    assert lib.dflash_check_draft_inputs(ctypes.byref(c), ctypes.byref(kv), fake, fake, fake, 4,
+                                         1, 64, None, None) == -1
+    assert lib.dflash_check_draft_inputs(ctypes.byref(c), ctypes.byref(kv), None, fake, fake, 4,
+                                         1, 64, fake, None) == -1
+    assert lib.dflash_check_draft_inputs(ctypes.byref(c), ctypes.byref(kv), fake, fake, fake, 0,
+                                         1, 64, fake, None) == -1
+    assert lib.dflash_check_draft_inputs(ctypes.byref(c), ctypes.byref(kv), fake, fake, fake, 4,
+                                         -1, 64, fake, None) == -1
+    assert lib.dflash_check_context_inputs(ctypes.byref(c), ctypes.byref(kv), fake, fake, None,
+                                           -1, 4, fake, None) == -1
+    assert lib.dflash_check_context_inputs(ctypes.byref(c), ctypes.byref(kv), None, fake, None,
+                                           1, 4, fake, None) == -1
+    assert lib.dflash_check_context_inputs(ctypes.byref(c), ctypes.byref(kv), fake, fake, None,
+                                           1 << 16, 1 << 16, fake, None) == -1
+    assert lib.dflash_check_accept_inputs(fake, fake, fake, 2, 0, 100, fake, None) == -1
+    assert lib.dflash_check_accept_inputs(fake, None, fake, 2, 4, 100, fake, None) == -1
+    assert lib.dflash_check_accept_inputs(fake, fake, fake, 2, 4, 0, fake, None) == -1
+    assert lib.dflash_check_accept_inputs(fake, fake, fake, 2, 4, 100, None, None) == -1
+    header = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    assert f"#define DFLASH_CHECKS {dfl.CHECKS}" in header
