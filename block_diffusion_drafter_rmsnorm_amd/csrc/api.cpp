@@ -587,6 +587,8 @@ dflash_status dflash_check_draft_inputs(const dflash_config* cfg, const dflash_k
   if (!cfg || !cache || !report) return fail(DFLASH_EINVAL, "NULL pointer argument");
   if (batch < 0 || max_prefix_len < 0 || max_pages < 1)
     return fail(DFLASH_EINVAL, "batch, max_prefix_len or max_pages out of range");
+  if ((int64_t)batch * max_pages > INT32_MAX)
+    return fail(DFLASH_EINVAL, "batch * max_pages exceeds the int32 report index");
   if (batch > 0 && (!anchor || !prefix_len || !page_table))
     return fail(DFLASH_EINVAL, "NULL pointer argument");
   if (cfg->page_size < 1 || cfg->block_size < 1 || cfg->vocab < 1)

@@ -533,8 +533,10 @@ dflash_status dflash_lm_head_argmax(const dflash_config* cfg, const void* lm_hea
  *   0  candidates[i] outside [0, vocab)
  *   1  posterior[i] outside [0, vocab)
  *   2  prefix_len[r] < 0
- * Errors: DFLASH_EINVAL for NULL pointers (valid_rows may be NULL) or
- * negative sizes; DFLASH_EHIP for a launch failure.
+ * Errors: DFLASH_EINVAL for NULL pointers (valid_rows may be NULL), negative
+ * sizes, or indices that would not fit an int32 (batch * max_pages, n_req *
+ * rows_per_req, batch * block_size above 2^31 - 1); DFLASH_EHIP for a launch
+ * failure.
  */
 #define DFLASH_CHECKS 4
 dflash_status dflash_check_draft_inputs(const dflash_config* cfg, const dflash_kv_cache* cache,
