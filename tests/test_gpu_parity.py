@@ -192,6 +192,47 @@ def test_draft_block_parity(name):
     assert np.array_equal(cand[:, 1:], np.argmax(gl, axis=-1))
 
 
+EDGE_LENGTHS = [
+    ("small_bf16", [0, 0]),                                          # no context at all
+    ("small_bf16", [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 150]),  # byte partition
+    ("small_swa_fp8", [0, 1, 23, 24, 25, 39, 40, 41]),               # window edges, aligned
+    ("small_swa_fp8", [0, 2, 5, 8, 13, 21, 24, 31, 32, 33, 40, 41, 47, 48, 64, 65, 80, 95,
+                       96, 97]),                                     # E4M3, byte partition
+    ("tiny_f32", [0, 3, 4, 5]),
+    ("small_f32_d64", [0, 1, 31, 32, 33]),
+]
+
+
+@pytest.mark.parametrize("name,lengths", EDGE_LENGTHS)
+def test_draft_block_edge_lengths(name, lengths):
+    """Context lengths at the edges: none, one key, one short of / at / past a
+    page and a 32-key step, at the sliding windows' edges; every attention
+    path (aligned and byte partitions, bf16 / E4M3 / fp32 caches, head_dim 64
+    and 128)."""
+    wl = dataclasses.replace(get_workload(name), batch=len(lengths))
+    cfg = wl.cfg
+    _print(f"[draft edge lengths] {name} L={lengths}")
+    st = Setup(wl, random_cache=False)
+    st.L = torch.tensor(lengths, dtype=torch.int32)
+    st.pt, st.num_pages = synth.page_table(st.L, cfg, st.seed, 2 * cfg.block_size)
+    K, V = synth.kv_pool_random(cfg, st.num_pages, st.seed, st.device)
+    st.cache = dfl().KVCache(K, V, st.num_pages)
+    out = st.draft()
+    o = oracle.draft_block(cfg, st.np_W(), st.oracle_cache(), st.anchor.numpy(), st.L.numpy(),
+                           st.pt.numpy())
+    assert np.array_equal(out["positions"].cpu().numpy(), o["positions"])
+    assert np.array_equal(out["slots"].cpu().numpy(), o["slots"])
+    rel_tol, m_tol = tol(cfg)
+    gl = out["logits"].float().cpu().numpy()
+    rel = logits_row_rel_err(gl, o["logits"])
+    _print(f"  logits max rel err {rel.max():.3e}")
+    assert rel.max() <= rel_tol
+    cand = out["candidates"].cpu().numpy()
+    sure = argmax_checked_rows(o["logits"], m_tol)
+    assert np.array_equal(cand[:, 1:][sure], o["draft_ids"][sure])
+    assert np.array_equal(cand[:, 1:], np.argmax(gl, axis=-1))
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "tiny_f32"])
 def test_draft_block_deterministic(name):
     st = Setup(get_workload(name))
