@@ -335,6 +335,32 @@ def test_project_context_slots_outside_the_pool(name, T):
     _compare_pools(st, before, o_cache, slots[keep].numpy())
 
 
+def test_empty_calls_change_nothing():
+    """Zero rows to inject (no requests, or requests of no rows) and a draft
+    pass over an empty batch return OK and leave the cache bit-identical;
+    the checked-mode calls on them report nothing."""
+    m = dfl()
+    wl = get_workload("small_bf16")
+    cfg = wl.cfg
+    st = Setup(wl)
+    before = [t.clone() for t in st.cache.k + st.cache.v]
+    d = st.device
+    ws = m.workspace(m.context_workspace_bytes(cfg, 1), d)
+    e_feats = torch.empty((0, cfg.feat_dim), dtype=torch.bfloat16, device=d)
+    e_i = torch.empty(0, dtype=torch.int32, device=d)
+    for n_req, rpr in ((0, 16), (3, 0)):
+        m.dflash_project_context(cfg, st.c_weights(), st.cache, e_feats, e_i, e_i,
+                                 torch.zeros(max(n_req, 1), dtype=torch.int32, device=d), n_req,
+                                 rpr, ws, checked=True)
+    e2 = torch.empty((0, cfg.block_size), dtype=torch.int32, device=d)
+    m.dflash_draft_block(cfg, st.c_weights(), st.cache, e_i, e_i,
+                         torch.zeros((0, 4), dtype=torch.int32, device=d), 0, e2, e2.clone(),
+                         e2.clone(), m.workspace(m.draft_workspace_bytes(cfg, 0, 0), d),
+                         checked=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, st.cache.k + st.cache.v))
+
+
 def test_project_context_large_tiles():
     """8192 rows of the hidden-2048 model: the fc GEMM takes the 256 x 256-tile
     path.  The oracle recomputes a sample of rows (injection is row-local)."""
