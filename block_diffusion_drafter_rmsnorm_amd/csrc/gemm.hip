@@ -65,10 +65,10 @@ GemmPlan plan_gemm(int M, int Ncols, int K, bool bf16, int narrow, int ksw) {
     p.m_tiles = (M + p.BM - 1) / p.BM;
     p.n_tiles = (Ncols + 16 * p.NSL - 1) / (16 * p.NSL);
     // waves per workgroup: 16 when the tiles fit one round of 16 waves per CU
-    // (4096 waves on the chip), else 8; the lm_head's 128-column tiles take 8
-    // = 4 slab pairs x 2 K splits.  fp32: 8.
+    // (4096 waves on the chip), else 8; the lm_head's 128-column tiles take 16
+    // = 4 slab pairs x 4 K splits (measured faster than 8 = 4 x 2).  fp32: 8.
     if (!bf16) p.NW = 8;
-    else if (p.NSL == 8) p.NW = 8;
+    else if (p.NSL == 8) p.NW = 16;
     else if (ksw > 1) p.NW = kQkvWaves;  // the QKV store split over workgroups
     else if (p.NSL == 1) p.NW = p.n_tiles <= 256 ? 16 : 8;  // (narrow_rows: <= 8 x NW items)
     else p.NW = 8;  // (gate/up: 8 measured faster than 4)
@@ -1886,6 +1886,9 @@ template <typename T, int NSL, class AS, class Epi>
 static void launch_rows(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
                         hipStream_t st) {
   if constexpr (sizeof(T) == 2 && NSL == 1) {
+    if (p.NW == 16) return launch_rows_mb<T, NSL, 16>(asrc, M, K, p, epi, st);
+  }
+  if constexpr (sizeof(T) == 2 && NSL == 8) {
     if (p.NW == 16) return launch_rows_mb<T, NSL, 16>(asrc, M, K, p, epi, st);
   }
   if constexpr (sizeof(T) == 2 && NSL == 2) {
