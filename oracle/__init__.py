@@ -19,7 +19,8 @@ library cross-checks, brute force); see each function for its pins.
 from .formats import round_bf16, round_e4m3, e4m3_decode, e4m3_encode, round_kv  # noqa: F401
 from .primitives import rms_norm, rope_neox, silu, softmax, block_attention  # noqa: F401
 from .dflash import (block_prep, project_context, draft_block, accept,  # noqa: F401
-                     greedy_posterior, accept_logits, OracleCache, speculative_decode)
+                     greedy_posterior, accept_logits, OracleCache, speculative_decode,
+                     select_draft_tokens)
 from .sampling import accept_sampling  # noqa: F401
 from . import selector  # noqa: F401
 from . import relay  # noqa: F401

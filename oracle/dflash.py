@@ -181,11 +181,20 @@ def draft_block(cfg, W, cache, anchor, prefix_len, page_table, rope=True, reques
         act = silu(h2 @ _f64(Lw["w_gate"]).T) * (h2 @ _f64(Lw["w_up"]).T)
         x = x + act @ _f64(Lw["w_down"]).T
     y = rms_norm(x[:, 1:, :], _f64(W["final_norm"]), cfg.rms_eps)
-    logits = _linear_chunked(y, W["lm_head"])
-    draft = np.argmax(logits, axis=-1)
+    logits, draft = select_draft_tokens(y, W["lm_head"])
     cand = np.concatenate([np.asarray(anchor, np.int64)[reqs][:, None], draft], axis=1)
     return {"block_ids": ids, "positions": pos, "slots": slots, "logits": logits,
             "draft_ids": draft, "candidates": cand, "requests": reqs, "hidden": y}
+
+
+def select_draft_tokens(y, lm_head):
+    """The selection step on final draft hidden rows ("Inside SGLang ...",
+    Step 4: the target's lm_head turns each normalised row into logits, the
+    greedy draft token is their argmax).  y [..., H] (already through the final
+    RMSNorm), lm_head [V, H]; returns logits = y lm_head^T [..., V] and the
+    first index among equal maxima [...]."""
+    logits = _linear_chunked(_f64(y), lm_head)
+    return logits, np.argmax(logits, axis=-1)
 
 
 def accept(candidates, posterior, prefix_len):

@@ -338,6 +338,45 @@ def test_draft_translation_invariance():
     assert np.array_equal(a["slots"], b["slots"])
 
 
+def test_select_draft_tokens_brute_force():
+    """Selection step on rows spanning the oracle's 16384-row weight chunks:
+    every logit against a pure-Python dot product, each id against a scan
+    that keeps the first maximum, and a planted tie that the lower index wins."""
+    rng = np.random.default_rng(5)
+    V, H = 16384 + 37, 3
+    y = rng.standard_normal((2, H))
+    lm = rng.standard_normal((V, H)).astype(np.float32)
+    # row 1: a tie between columns on both sides of the chunk edge
+    lm[16390] = lm[100] = 10.0 * np.sign(y[1]).astype(np.float32)
+    logits, ids = oracle.select_draft_tokens(y, lm)
+    assert logits.shape == (2, V) and ids.shape == (2,)
+    for r in range(2):
+        ref = [sum(float(y[r, h]) * float(lm[v, h]) for h in range(H)) for v in range(V)]
+        assert np.allclose(logits[r], ref, rtol=1e-13, atol=1e-13)
+        best = 0
+        for v in range(1, V):
+            if ref[v] > ref[best]:
+                best = v
+        assert int(ids[r]) == best
+    assert int(ids[1]) == 100
+
+
+def test_select_draft_tokens_one_hot_rows():
+    """A one-hot hidden row e_h reads column h of the lm_head: logits equal it
+    exactly and the id is that column's argmax; a batch shape carries through."""
+    rng = np.random.default_rng(6)
+    V, H = 501, 8
+    lm = rng.standard_normal((V, H))
+    y = np.zeros((2, 4, H))
+    for i in range(8):
+        y[i // 4, i % 4, i] = 1.0
+    logits, ids = oracle.select_draft_tokens(y, lm)
+    assert logits.shape == (2, 4, V)
+    for i in range(8):
+        assert np.array_equal(logits[i // 4, i % 4], lm[:, i])
+        assert int(ids[i // 4, i % 4]) == int(np.argmax(lm[:, i]))
+
+
 def test_draft_planted_argmax():
     cfg = TINY
     W, pt, npages = _setup(cfg)
