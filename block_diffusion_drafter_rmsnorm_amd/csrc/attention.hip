@@ -774,8 +774,12 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one staged step: keys t0 + 8 g4 + e are this lane's elements e = 0..7
-  auto compute = [&](const char* st, int t0, bool is_blk) {
+  // one staged step: keys t0 + 8 g4 + e are this lane's elements e = 0..7.
+  // kMasked (a compile-time tag) keeps the masks of the range edges, the
+  // sliding window and the block's own keys; most steps need none, and with
+  // the masks in the code the compiler computes them and selects on every step
+  auto step = [&](const char* st, int t0, bool is_blk, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     // bf16 fragments at st (the bf16 layout), or E4M3 ones decoded on the read
     const bool f8 = F8 && !is_blk;
     const CT* Ks = reinterpret_cast<const CT*>(st);
@@ -806,27 +810,26 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
         load_frag(f, Vs + (db * 64 + lane) * 8);
       }
     };
-    const bool full = is_blk ? false : (t0 >= lo && t0 + 32 <= kend);
-    unsigned keep = 0xffu;
-    if (!full) {
-      keep = 0;
+    // keep: this lane's keys inside the step's range; vis: also visible to its
+    // query row under the sliding window
+    unsigned keep = 0xffu, vis = 0xffu;
+    if constexpr (kMasked) {
+      if (is_blk || t0 < lo || t0 + 32 > kend) {
+        keep = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = 8 * g4 + e;
-        const bool ok = is_blk ? (kk < S) : (t0 + kk >= lo && t0 + kk < kend);
-        keep |= (ok ? 1u : 0u) << e;
+        for (int e = 0; e < 8; ++e) {
+          const int kk = 8 * g4 + e;
+          const bool ok = is_blk ? (kk < S) : (t0 + kk >= lo && t0 + kk < kend);
+          keep |= (ok ? 1u : 0u) << e;
+        }
+      }
+      vis = keep;
+      if (!is_blk && a.window > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((qpos - (t0 + 8 * g4 + e)) >= a.window) vis &= ~(1u << e);
       }
     }
-    // a sliding window hides keys only from steps that start at least a window
-    // below the block's last row (the first steps of the range)
-    const bool wmask = !is_blk && a.window > 0 && (L + S - 1) - t0 >= a.window;
-    unsigned vis = keep;
-    if (wmask) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((qpos - (t0 + 8 * g4 + e)) >= a.window) vis &= ~(1u << e);
-    }
-    const bool masked = !full || wmask;
     f32x4 sacc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -843,7 +846,9 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sv[e] = sacc[e >> 2][e & 3] * a.scale_log2;
-      if (masked && !((vis >> e) & 1u)) sv[e] = -INFINITY;
+      if constexpr (kMasked) {
+        if (!((vis >> e) & 1u)) sv[e] = -INFINITY;
+      }
       mx = fmaxf(mx, sv[e]);
     }
     mx = fmaxf(mx, lane_xor16(mx, lane));
@@ -879,9 +884,19 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
       vfrag(vf, db);
       // keys outside the range (first and last steps only) are zeroed: their
       // memory may hold anything
-      if (!full) frag_keep(vf, keep);
+      if constexpr (kMasked) frag_keep(vf, keep);
       mma(o[db], vf, pf);
     }
+  };
+  // a step needs no mask when its 32 keys lie inside the range and no sliding
+  // window reaches them (the same for every lane: a scalar branch)
+  auto compute = [&](const char* st, int t0, bool is_blk) {
+    const bool plain = !is_blk && t0 >= lo && t0 + 32 <= kend &&
+                       !(a.window > 0 && (L + S - 1) - t0 >= a.window);
+    if (__builtin_amdgcn_readfirstlane(plain ? 1 : 0))
+      step(st, t0, is_blk, std::false_type{});
+    else
+      step(st, t0, is_blk, std::true_type{});
   };
 
   if constexpr (F8) {
