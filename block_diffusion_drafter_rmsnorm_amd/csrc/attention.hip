@@ -670,7 +670,7 @@ __device__ __forceinline__ float lane_xor32(float x, int lane) {
 
 // Cache element type of the direct-to-LDS kernels: K and V bytes of one
 // 32-key step, and the LDS the staging takes (the ring; an fp8 cache also
-// keeps the block's own bf16 keys in a buffer of their own).
+// has one bf16 step buffer: the block's own keys, then each decoded step).
 template <typename KT, int D, int NS> struct DmaStage {
   static constexpr bool F8 = std::is_same<KT, fp8_t>::value;
   static constexpr int BYTES = 64 * D * (int)sizeof(KT);      // K and V of one step
@@ -686,10 +686,12 @@ template <typename KT, int D, int NS> struct DmaStage {
 // calls it.  `stg` is the DmaStage LDS of the workgroup.
 //
 // E4M3 cache (D = 128): a step's K and V bytes go to LDS as they lie in the
-// cache (a wave copies one 1 KB K piece and one 1 KB V^T piece), and a wave
-// decodes its fragments to bf16 as it reads them (8 codes per lane, by the
-// conversion instruction: exact).  The block's own keys are bf16; they are
-// copied first, into their own buffer, and computed before the context steps.
+// cache (a wave copies one 1 KB K piece and one 1 KB V^T piece); each wave
+// then decodes the two pieces it copied to bf16 (exact) into the bf16 step
+// buffer, in the layout of a bf16 step, and after a barrier every wave reads
+// its fragments from there: each code is converted once per workgroup rather
+// than once per wave.  The block's own keys are bf16; they are copied first,
+// into that buffer, and computed before the context steps.
 template <int D, int NS, typename KT>
 __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L, int lo, int blk,
                                          int n_ctx, int kbeg, int kend, int pfirst,
@@ -715,7 +717,7 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
   // page half r16 / 8, row within it) and V^T key offset (page half g4 / 2)
   const int krow0 = (8 * (r16 >> 2) + (r16 & 3)) & 15;  // + 4 h
   const int khalf = r16 >> 3, vhalf = g4 >> 1, voff = 8 * (g4 & 1);
-  char* const blkbuf = stg + NS * DS::BYTES;  // (E4M3 only)
+  char* const blkbuf = stg + NS * DS::BYTES;  // bf16 step buffer (E4M3 only)
   // bf16 step (the block's, or a context step of a bf16 cache) into `dst`:
   // K [kop = h * D/32 + ks][lane][8], V [db][lane][8]
   auto issue_bf16 = [&](CT* dst, const CT* const* kp, const CT* const* vp, int vstride) {
@@ -780,36 +782,13 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
   // the masks in the code the compiler computes them and selects on every step
   auto step = [&](const char* st, int t0, bool is_blk, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
-    // bf16 fragments at st (the bf16 layout), or E4M3 ones decoded on the read
-    const bool f8 = F8 && !is_blk;
+    // bf16 fragments at st, in the bf16 step layout
     const CT* Ks = reinterpret_cast<const CT*>(st);
     const CT* Vs = Ks + 32 * D;
     auto kfrag = [&](Frag<CT>& f, int h, int ks) {
-      if (f8) {
-        // K piece h * 2 + ks / 2, record (16 ((ks % 2) * 2 + g4 / 2) + r16),
-        // byte 8 (g4 % 2): dims 32 ks + 8 g4 .. + 8 of the lane's row
-        Raw8<fp8_t> raw;
-        raw.v = *reinterpret_cast<const uint2*>(
-            st + (h * 2 + ks / 2) * 1024 + (16 * ((ks & 1) * 2 + (g4 >> 1)) + r16) * 16 +
-            8 * (g4 & 1));
-        raw_to_frag<CT, fp8_t>(f, raw);
-      } else {
-        load_frag(f, Ks + ((h * (D / 32) + ks) * 64 + lane) * 8);
-      }
+      load_frag(f, Ks + ((h * (D / 32) + ks) * 64 + lane) * 8);
     };
-    auto vfrag = [&](Frag<CT>& f, int db) {
-      if (f8) {
-        // V^T piece (g4 / 2) * 2 + db / 4, record 16 (db % 4) + r16, byte
-        // 8 (g4 % 2): keys 8 g4 .. + 8 of dim 16 db + r16
-        Raw8<fp8_t> raw;
-        raw.v = *reinterpret_cast<const uint2*>(
-            st + 4096 + ((g4 >> 1) * 2 + db / 4) * 1024 + (16 * (db & 3) + r16) * 16 +
-            8 * (g4 & 1));
-        raw_to_frag<CT, fp8_t>(f, raw);
-      } else {
-        load_frag(f, Vs + (db * 64 + lane) * 8);
-      }
-    };
+    auto vfrag = [&](Frag<CT>& f, int db) { load_frag(f, Vs + (db * 64 + lane) * 8); };
     // keep: this lane's keys inside the step's range; vis: also visible to its
     // query row under the sliding window
     unsigned keep = 0xffu, vis = 0xffu;
@@ -900,6 +879,34 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
   };
 
   if constexpr (F8) {
+    // E4M3 step in ring slot `src` -> bf16 in blkbuf, in the bf16 step layout.
+    // Each wave decodes the two pieces it copied (16 codes per lane each) and
+    // writes them as two 8-element records.  K piece `wave` (h = wave / 2, c =
+    // wave % 2), lane (r16, g4): dims 64 c + 16 g4 .. + 16 of its key row, i.e.
+    // operand h * D/32 + 2 c + g4 / 2, records of lanes (r16, 2 (g4 % 2)) and
+    // (r16, 2 (g4 % 2) + 1).  V^T piece `wave`, lane l: keys 16 h .. + 16 of
+    // dim 64 c + l, i.e. operand 4 c + l / 16, records of lanes (l % 16, 2 h)
+    // and (l % 16, 2 h + 1).
+    auto decode_f8 = [&](const char* src) {
+      CT* dst = reinterpret_cast<CT*>(blkbuf);
+      const int h = wave >> 1, c = wave & 1;
+      const uint4 kr = *reinterpret_cast<const uint4*>(src + wave * 1024 + lane * 16);
+      const uint4 vr = *reinterpret_cast<const uint4*>(src + 4096 + wave * 1024 + lane * 16);
+      Raw8<fp8_t> r[4];
+      r[0].v = make_uint2(kr.x, kr.y);
+      r[1].v = make_uint2(kr.z, kr.w);
+      r[2].v = make_uint2(vr.x, vr.y);
+      r[3].v = make_uint2(vr.z, vr.w);
+      Frag<CT> f[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw_to_frag<CT, fp8_t>(f[i], r[i]);
+      const int kop = h * (D / 32) + 2 * c + (g4 >> 1), kg = 2 * (g4 & 1);
+      const int vop = 4 * c + (lane >> 4), vr16 = lane & 15;
+      *reinterpret_cast<uint4*>(dst + (kop * 64 + kg * 16 + r16) * 8) = f[0].v;
+      *reinterpret_cast<uint4*>(dst + (kop * 64 + (kg + 1) * 16 + r16) * 8) = f[1].v;
+      *reinterpret_cast<uint4*>(dst + 32 * D + (vop * 64 + 2 * h * 16 + vr16) * 8) = f[2].v;
+      *reinterpret_cast<uint4*>(dst + 32 * D + (vop * 64 + (2 * h + 1) * 16 + vr16) * 8) = f[3].v;
+    };
     // the block's keys first (4 bf16 copies per wave, older than every
     // context copy), then context steps 0 .. NS - 2 in flight
     const int n_pro = imin(NS - 1, n_ctx);
@@ -918,10 +925,13 @@ __device__ __forceinline__ void dma_part(const AttnArgs& a, int r, int g, int L,
     }
     for (int t = 0; t < n_ctx; ++t) {
       attn_wait_steps<DPW, NS - 2>(imin(NS - 2, n_ctx - 1 - t));
+      // step t is in its slot; every wave has finished with blkbuf (the block
+      // step or step t - 1) and with the slot of step t - 1
       lds_barrier();
-      // the slot of step t - 1: every wave has finished with it
       if (t + NS - 1 < n_ctx) issue_ctx((t + NS - 1) % NS);
-      if (qlive) compute(stg + (t % NS) * DS::BYTES, kbeg + 32 * t, false);
+      decode_f8(stg + (t % NS) * DS::BYTES);
+      lds_barrier();
+      if (qlive) compute(blkbuf, kbeg + 32 * t, false);
     }
   } else {
     // Steps: the block's own keys first (one 16-key page, both halves
