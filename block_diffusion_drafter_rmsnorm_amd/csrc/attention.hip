@@ -17,9 +17,11 @@
 // sees them: no causal mask), laid out by the QKV epilogue as one extra page.
 // On a sliding layer context key i is visible to the row at logical position
 // p iff p - i < W; the range starts at L - W + 1 (rounded down to 32 keys,
-// the extra keys masked).  Two staging kernels: a bf16 cache is copied
-// straight from global memory into LDS; fp8 (decoded once, exactly, to bf16)
-// and fp32 caches go through registers.
+// the extra keys masked).  Two staging kernels: a bf16 cache, and an E4M3
+// cache with head_dim 128, are copied straight from global memory into LDS
+// (E4M3 steps then decoded once per workgroup, exactly, to bf16 in LDS);
+// fp32 caches and head_dim 64 E4M3 ones go through registers (decoded once
+// per workgroup on the way).
 #include <type_traits>
 
 #include "common.h"
