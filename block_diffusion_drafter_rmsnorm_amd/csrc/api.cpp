@@ -139,7 +139,8 @@ ContextWs layout_context(const dflash_config* c, int64_t chunk, void* ws) {
   ContextWs L;
   const int M = (int)chunk;
   L.cs = (float2*)cv.take(sizeof(float2) * M * (c->head_dim / 2));
-  L.cg = cv.take((size_t)act_bytes(c->act_dtype) * M * c->hidden);
+  // (a last chunk of <= 64 rows keeps it in 16 x 32 blocks: at most 64 rows)
+  L.cg = cv.take((size_t)act_bytes(c->act_dtype) * act_rows(M) * c->hidden);
   L.ss = (float*)cv.take(sizeof(float) * (size_t)M * ss_tiles(c->hidden));
   // the last chunk of a call can be any size up to `chunk`: take the worst
   // case over row counts.  A plan depends on the row count only through its
@@ -197,12 +198,14 @@ DraftWs layout_draft(const dflash_config* c, int B, int max_prefix, void* ws) {
   const size_t ab = act_bytes(c->act_dtype);
   L.x = (float*)cv.take(sizeof(float) * (size_t)M * H);
   L.ss = (float*)cv.take(sizeof(float) * (size_t)M * ss_tiles(H));
-  L.xg = cv.take(ab * (size_t)M * H);
-  L.act = cv.take(ab * (size_t)M * I);
+  // the GEMMs' A operands, in 16 x 32 blocks (rows rounded up to 16) at <= 64 rows
+  const size_t Ma = (size_t)act_rows(M);
+  L.xg = cv.take(ab * Ma * H);
+  L.act = cv.take(ab * Ma * I);
   L.q = cv.take(ab * (size_t)M * nq * D);
   L.kb = cv.take(ab * (size_t)B * nkv * 16 * D);
   L.vb = cv.take(ab * (size_t)B * nkv * 16 * D);
-  L.o = cv.take(ab * (size_t)M * nq * D);
+  L.o = cv.take(ab * Ma * nq * D);
   L.cs = (float2*)cv.take(sizeof(float2) * (size_t)M * (D / 2));
   // one (O, m, l) partial of 64 query rows per attention workgroup
   const bool dma = attn_uses_dma(c->act_dtype, c->kv_dtype, D);
@@ -356,11 +359,12 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
     // c = fc(f): the fc epilogue writes c * hidden_norm (act dtype) and the
     // row sums of squares of c; the K/V GEMM streams the former and scales
     // its rows by 1/rms(c) (RMSNorm by linearity)
+    const int blk = act_blocked(M);
     if ((e = gemm_store_f32(dt, asrc_plain(f, feat_row_stride), M, cfg->feat_dim, w->fc,
-                            cfg->hidden, nullptr, L.ss, L.cg, w->hidden_norm, L.gs, st)) !=
+                            cfg->hidden, nullptr, L.ss, L.cg, blk, w->hidden_norm, L.gs, st)) !=
         hipSuccess)
       return hip_fail(e, "fc gemm");
-    const ASrc cin = asrc_normed(L.cg, cfg->hidden, L.ss, cfg->rms_eps);
+    const ASrc cin = asrc_normed(L.cg, cfg->hidden, L.ss, cfg->rms_eps, 0, blk);
     if ((e = gemm_kv_inject(dt, cfg->kv_dtype, cin, M, cfg->hidden, tg, cfg->n_layers,
                             cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, L.cs,
                             slots + t0, valid_rows, rows_per_req > 0 ? rows_per_req : 1, t0,
@@ -412,12 +416,15 @@ static dflash_status draft_core(const dflash_config* cfg, const dflash_weights* 
   const float eps = cfg->rms_eps;
   // Every RMSNorm is applied by linearity: the producer of the residual x writes
   // xg = x * g_next (act dtype) and the row sums of squares of x; the consumer
-  // GEMM streams xg and scales its output rows by 1/rms(x).
+  // GEMM streams xg and scales its output rows by 1/rms(x).  The GEMMs' A
+  // operands (xg, the attention output, the SwiGLU activations) sit in 16 x 32
+  // blocks when the pass has at most 64 block rows.
+  const int blk = act_blocked(M);
   if ((e = launch_block_prep(dt, *cfg, w->embed, anchor, prefix_len, page_table, max_pages, batch,
-                             block_ids, positions, slots, candidates, L.x, L.ss, n_ss, L.xg,
+                             block_ids, positions, slots, candidates, L.x, L.ss, n_ss, L.xg, blk,
                              w->layer[0].in_norm, L.cs, st)) != hipSuccess)
     return hip_fail(e, "block prep");
-  const ASrc xin = asrc_normed(L.xg, H, L.ss, eps);
+  const ASrc xin = asrc_normed(L.xg, H, L.ss, eps, 0, blk);
   for (int l = 0; l < cfg->n_layers; ++l) {
     const dflash_layer_weights& W = w->layer[l];
     const void* g_after = (l + 1 < cfg->n_layers) ? w->layer[l + 1].in_norm : w->final_norm;
@@ -427,19 +434,21 @@ static dflash_status draft_core(const dflash_config* cfg, const dflash_weights* 
     if ((e = launch_attention(dt, cfg->kv_dtype, D, L.q, L.kb, L.vb, cache->k[l], cache->v[l],
                               page_table, max_pages, cache->num_pages, prefix_len, max_prefix_len,
                               batch, S, nq, nkv, cfg->page_size, cfg->sliding_window[l],
-                              cfg->context_window, L.plans[l], L.o_part, L.ml_part, L.seg, L.o, st)) != hipSuccess)
+                              cfg->context_window, L.plans[l], L.o_part, L.ml_part, L.seg, L.o,
+                              blk, st)) != hipSuccess)
       return hip_fail(e, "attention");
-    if ((e = gemm_residual(dt, asrc_plain(L.o, nq * D), M, nq * D, W.w_o, H, L.x, L.ss, L.xg,
-                           W.post_norm, L.gs, st)) != hipSuccess)
+    if ((e = gemm_residual(dt, asrc_plain(L.o, nq * D, 0, blk), M, nq * D, W.w_o, H, L.x, L.ss,
+                           L.xg, blk, W.post_norm, L.gs, st)) != hipSuccess)
       return hip_fail(e, "o-proj gemm");
-    if ((e = gemm_silu_mul(dt, xin, M, H, W.w_gate, W.w_up, I, L.act, L.gs, st)) != hipSuccess)
+    if ((e = gemm_silu_mul(dt, xin, M, H, W.w_gate, W.w_up, I, L.act, blk, L.gs, st)) !=
+        hipSuccess)
       return hip_fail(e, "gate/up gemm");
-    if ((e = gemm_residual(dt, asrc_plain(L.act, I), M, I, W.w_down, H, L.x, L.ss, L.xg, g_after,
-                           L.gs, st)) != hipSuccess)
+    if ((e = gemm_residual(dt, asrc_plain(L.act, I, 0, blk), M, I, W.w_down, H, L.x, L.ss, L.xg,
+                           blk, g_after, L.gs, st)) != hipSuccess)
       return hip_fail(e, "down gemm");
   }
   // final norm of rows 1..S-1 of every block, applied by the lm_head GEMM
-  if ((e = gemm_logits(dt, asrc_normed(L.xg, H, L.ss, eps, S), M1, H, w->lm_head, cfg->vocab,
+  if ((e = gemm_logits(dt, asrc_normed(L.xg, H, L.ss, eps, S, blk), M1, H, w->lm_head, cfg->vocab,
                        logits, L.lm_part, L.gs, st)) != hipSuccess)
     return hip_fail(e, "lm_head gemm");
   if ((e = launch_argmax_reduce(L.lm_part, M1, logits_tiles(cfg->vocab), S, candidates, st)) !=
@@ -715,8 +724,10 @@ dflash_status dflash_draft_block_selector(
                        st)) != hipSuccess)
     return hip_fail(e, "top-k");
   // w_j = W_h y_j for the final-normed rows 1..S-1 (the norm applied by linearity)
-  if ((e = gemm_store_f32(cfg->act_dtype, asrc_normed(L.xg, cfg->hidden, L.ss, cfg->rms_eps, S),
-                          M1, cfg->hidden, sel->w_h, sel->rank, SL.w, nullptr, nullptr, nullptr,
+  if ((e = gemm_store_f32(cfg->act_dtype,
+                          asrc_normed(L.xg, cfg->hidden, L.ss, cfg->rms_eps, S,
+                                      act_blocked((int64_t)batch * S)),
+                          M1, cfg->hidden, sel->w_h, sel->rank, SL.w, nullptr, nullptr, 0, nullptr,
                           SL.gs, st)) != hipSuccess)
     return hip_fail(e, "selector projection");
   if ((e = launch_lattice_walk(cfg->act_dtype, cand_ids, SL.unary, SL.w, sel->a, sel->b, anchor,

@@ -116,6 +116,7 @@ struct AttnArgs {
   float scale_log2;
   float* o_part; float2* ml_part;  // per partial slot: [64 rows][D], [64 rows]
   int4* seg;                       // per request: (units before it per head, units, U, -)
+  int o_blk;                       // the output [M, nq D] in the 16 x 32 blocks of act_off
 };
 
 // Inclusive prefix sum over a wave.
@@ -1192,7 +1193,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __res
   }
   if (lane < LPP) {
     const int hl = rho / a.S, j = rho % a.S;
-    CT* dst = out + ((int64_t)(r * a.S + j) * a.nq + g * a.G + hl) * D + d0;
+    // 4 columns inside one 32-column block
+    CT* dst = out + act_off(r * a.S + j, (g * a.G + hl) * D + d0, (int64_t)a.nq * D, a.o_blk);
     const float inv = 1.0f / den;
     dst[0] = Num<CT>::from_f(acc.x * inv);
     dst[1] = Num<CT>::from_f(acc.y * inv);
@@ -1232,7 +1234,7 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             const int32_t* prefix_len, int max_prefix, int B, int S, int nq,
                             int nkv, int page_size, int window, int ctx_window,
                             const AttnPlan& plan,
-                            float* o_part, float2* ml_part, int4* seg, void* out,
+                            float* o_part, float2* ml_part, int4* seg, void* out, int out_blk,
                             hipStream_t st) {
   const bool dma = attn_uses_dma(dt, kv_dt, D);
   if ((plan.stages != 0) != dma || !plan.fits) return hipErrorInvalidValue;
@@ -1246,6 +1248,7 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
   a.W = plan.n_launch;
   a.scale_log2 = LOG2E / sqrtf((float)D);
   a.o_part = o_part; a.ml_part = ml_part; a.seg = seg;
+  a.o_blk = out_blk;
   if (dt == DFLASH_F32) {
     if (D == 64) return run_attn<float, float, 64>(a, plan, out, st);
     return run_attn<float, float, 128>(a, plan, out, st);

@@ -348,3 +348,16 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+// ---------------------------------------------------------------- activations
+// Offset of element (r, k) of an activation matrix.  blk == 0: row-major with
+// row stride ld.  blk == 1 (the operands of calls of at most 64 rows, which
+// the narrow GEMMs stream): 16 x 32 blocks, ld the row width K (a multiple of
+// 32) -- block (r / 16, k / 32) at ((r / 16) (K / 32) + k / 32) 512, element
+// (r mod 16) 32 + k mod 32 inside it -- so the 16 rows x 32 columns of an MFMA
+// A fragment are one contiguous 1 KB (bf16) rather than 16 separate 64-byte
+// pieces of 16 rows.  A blocked matrix takes its row count rounded up to 16.
+__host__ __device__ __forceinline__ int64_t act_off(int r, int k, int64_t ld, int blk) {
+  return blk ? ((int64_t)(r >> 4) * (ld >> 5) + (k >> 5)) * 512 + (r & 15) * 32 + (k & 31)
+             : (int64_t)r * ld + k;
+}

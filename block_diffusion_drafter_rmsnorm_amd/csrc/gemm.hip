@@ -188,6 +188,7 @@ template <typename T> struct ASrcPlain {
   const T* A;
   int64_t lda;
   int S;
+  int blk;  // A in the 16 x 32 blocks of act_off (lda = its width): streaming kernels only
   template <int MB> struct State {
     const T* p[MB];
   };
@@ -195,11 +196,13 @@ template <typename T> struct ASrcPlain {
   __device__ __forceinline__ void setup(State<MB>& s, int m0, int M, int r16) const {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      s.p[mb] = A + (int64_t)block_row(imin(m0 + mb * 16 + r16, M - 1), S) * lda;
+      s.p[mb] = A + act_off(block_row(imin(m0 + mb * 16 + r16, M - 1), S), 0, lda, blk);
   }
+  // the 8 elements at column k of this lane's row (k mod 32 a multiple of 8):
+  // column block k / 32 is 32 (row-major) or 512 (blocked) elements on
   template <int MB>
   __device__ __forceinline__ void load(Frag<T>& f, const State<MB>& s, int mb, int k) const {
-    load_frag(f, s.p[mb] + k);
+    load_frag(f, s.p[mb] + (int64_t)(k >> 5) * (blk ? 512 : 32) + (k & 31));
   }
 };
 
@@ -386,6 +389,7 @@ __device__ __forceinline__ float* row_scale_lds() {
 template <typename T> struct NextNorm {
   T* xg;
   const T* g;
+  int blk;  // xg in the 16 x 32 blocks of act_off
 };
 
 // ---------------------------------------------------------------- main kernel
@@ -666,7 +670,7 @@ __device__ __forceinline__ void narrow_rows(int rows, int m0, int M, int n0, int
       if (nn.xg != nullptr) {
         // the gain prefetched for the first two items, loaded for later ones
         const float gj = j < 2 ? pre.g[j < 2 ? j : 0] : Num<T>::to_f(nn.g[t.n]);
-        nn.xg[(int64_t)t.m * N + t.n] = Num<T>::from_f(v * gj);
+        nn.xg[act_off(t.m, t.n, N, nn.blk)] = Num<T>::from_f(v * gj);
       }
     }
     if (ss != nullptr) {
@@ -1220,7 +1224,7 @@ __device__ __forceinline__ void for_rows(int rows, int m0, int M, int nt, int N,
         if (n < N) {
           const float v = f(r, c, m, n, iv[u][h]);
           sq[h] = v * v;
-          if (nn.xg != nullptr) nn.xg[(int64_t)m * N + n] = Num<T>::from_f(v * gn[h]);
+          if (nn.xg != nullptr) nn.xg[act_off(m, n, N, nn.blk)] = Num<T>::from_f(v * gn[h]);
         }
       }
       if (ss != nullptr) {
@@ -1396,6 +1400,7 @@ template <typename T> struct EpiResidual {
 // Tile columns 0..63 are gate rows nt*64.., columns 64..127 the matching up rows.
 template <typename T> struct EpiSiluMul {
   const T* Wg; const T* Wu; int I; int K; T* act; RowScale rs;
+  int blk;  // act in the 16 x 32 blocks of act_off
   static constexpr int kNarrow = 2;
   static constexpr bool kRowScale = true;
   __device__ EpiSiluMul nsplit(int) const { return *this; }
@@ -1413,7 +1418,7 @@ template <typename T> struct EpiSiluMul {
       if (m < M && n < I) {
         const float sc = srs[r];
         const float g = t[r * LDT + c] * sc, u = t[r * LDT + 64 + c] * sc;
-        act[(int64_t)m * I + n] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
+        act[act_off(m, n, I, blk)] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
       }
     }
   }
@@ -1443,7 +1448,7 @@ template <typename T> struct EpiSiluMul {
       if (m < M && n < I) {
         const float sc = srs[r];
         const float g = t[r * ldt + 32 * pb + i] * sc, u = t[r * ldt + 32 * pb + 16 + i] * sc;
-        act[(int64_t)m * I + n] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
+        act[act_off(m, n, I, blk)] = Num<T>::from_f(g / (1.0f + __expf(-g)) * u);
       }
     }
   }
@@ -1937,6 +1942,8 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
   }
   if (p.KS > 1 && gemm_partial_floats(p) > ws.partial_floats) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
+    // the tiled kernels read A row-major (blocked A only below 65 rows)
+    if ((p.big || p.tall || p.fat) && asrc.blk) return hipErrorInvalidValue;
     if (p.big) {
       launch_big(asrc, M, K, p, (Ncols + BN - 1) / BN, epi, ws.partial, st);
       return hipGetLastError();
@@ -1962,7 +1969,7 @@ static hipError_t run_gemm(const AS& asrc, int M, int K, int Ncols, const Epi& e
 template <typename T, class Epi>
 static hipError_t run_any(const ASrc& a, int M, int K, int Ncols, const Epi& epi,
                           const GemmScratch& ws, hipStream_t st, int ksw = 1) {
-  const ASrcPlain<T> s{static_cast<const T*>(a.a), a.lda, a.S_skip};
+  const ASrcPlain<T> s{static_cast<const T*>(a.a), a.lda, a.S_skip, a.blk};
   return run_gemm<T>(s, M, K, Ncols, epi, ws, st, ksw);
 }
 
@@ -1971,39 +1978,41 @@ static RowScale row_scale(const ASrc& a) {
 }
 
 hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, int N, float* out,
-                          float* ss, void* xg, const void* g_next, const GemmScratch& ws,
-                          hipStream_t st) {
+                          float* ss, void* xg, int xg_blk, const void* g_next,
+                          const GemmScratch& ws, hipStream_t st) {
   if (dt == DFLASH_BF16) {
     EpiStoreF32<bf16_t> e{(const bf16_t*)W, N, K, out, N, ss,
-                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next}, row_scale(a)};
+                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next, xg_blk},
+                          row_scale(a)};
     return run_any<bf16_t>(a, M, K, N, e, ws, st);
   }
   EpiStoreF32<float> e{(const float*)W, N, K, out, N, ss,
-                       NextNorm<float>{(float*)xg, (const float*)g_next}, row_scale(a)};
+                       NextNorm<float>{(float*)xg, (const float*)g_next, xg_blk}, row_scale(a)};
   return run_any<float>(a, M, K, N, e, ws, st);
 }
 
 hipError_t gemm_residual(int dt, const ASrc& a, int M, int K, const void* W, int N, float* x,
-                         float* ss, void* xg, const void* g_next, const GemmScratch& ws,
-                         hipStream_t st) {
+                         float* ss, void* xg, int xg_blk, const void* g_next,
+                         const GemmScratch& ws, hipStream_t st) {
   if (dt == DFLASH_BF16) {
     EpiResidual<bf16_t> e{(const bf16_t*)W, N, K, x, ss,
-                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next}};
+                          NextNorm<bf16_t>{(bf16_t*)xg, (const bf16_t*)g_next, xg_blk}};
     return run_any<bf16_t>(a, M, K, N, e, ws, st);
   }
   EpiResidual<float> e{(const float*)W, N, K, x, ss,
-                       NextNorm<float>{(float*)xg, (const float*)g_next}};
+                       NextNorm<float>{(float*)xg, (const float*)g_next, xg_blk}};
   return run_any<float>(a, M, K, N, e, ws, st);
 }
 
 hipError_t gemm_silu_mul(int dt, const ASrc& a, int M, int K, const void* Wg, const void* Wu,
-                         int I, void* act, const GemmScratch& ws, hipStream_t st) {
+                         int I, void* act, int act_blk, const GemmScratch& ws, hipStream_t st) {
   const int ncols = ((I + 63) / 64) * BN;
   if (dt == DFLASH_BF16) {
-    EpiSiluMul<bf16_t> e{(const bf16_t*)Wg, (const bf16_t*)Wu, I, K, (bf16_t*)act, row_scale(a)};
+    EpiSiluMul<bf16_t> e{(const bf16_t*)Wg, (const bf16_t*)Wu, I, K, (bf16_t*)act, row_scale(a),
+                         act_blk};
     return run_any<bf16_t>(a, M, K, ncols, e, ws, st);
   }
-  EpiSiluMul<float> e{(const float*)Wg, (const float*)Wu, I, K, (float*)act, row_scale(a)};
+  EpiSiluMul<float> e{(const float*)Wg, (const float*)Wu, I, K, (float*)act, row_scale(a), act_blk};
   return run_any<float>(a, M, K, ncols, e, ws, st);
 }
 
@@ -2129,14 +2138,14 @@ hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const
     hipError_t e;
     if (dt == DFLASH_BF16) {
       EpiQKVStore<bf16_t> ep{{(const bf16_t*)Wqkv, ncols, H, raw, ncols, nullptr,
-                              NextNorm<bf16_t>{nullptr, nullptr}, row_scale(a), pstride}};
+                              NextNorm<bf16_t>{nullptr, nullptr, 0}, row_scale(a), pstride}};
       if ((e = run_any<bf16_t>(a, M, H, ncols, ep, ws, st, ksw)) != hipSuccess) return e;
       hipLaunchKernelGGL(qk_norm_rope_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, raw, ksw, M,
                          nq, nkv, D, (const bf16_t*)qn, (const bf16_t*)kn, eps, cs, (bf16_t*)q,
                          (bf16_t*)k, (bf16_t*)v, S);
     } else {
       EpiQKVStore<float> ep{{(const float*)Wqkv, ncols, H, raw, ncols, nullptr,
-                             NextNorm<float>{nullptr, nullptr}, row_scale(a), pstride}};
+                             NextNorm<float>{nullptr, nullptr, 0}, row_scale(a), pstride}};
       if ((e = run_any<float>(a, M, H, ncols, ep, ws, st, ksw)) != hipSuccess) return e;
       hipLaunchKernelGGL(qk_norm_rope_kernel<float>, dim3(grid), dim3(256), 0, st, raw, ksw, M,
                          nq, nkv, D, (const float*)qn, (const float*)kn, eps, cs, (float*)q,

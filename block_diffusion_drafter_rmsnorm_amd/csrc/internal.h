@@ -55,10 +55,13 @@ struct KVTargets {
   void* vc[DFLASH_MAX_LAYERS];
 };
 
-// A operand of a GEMM: rows of T with row stride lda.  S_skip > 0 maps GEMM row
-// m to A row (m / (S-1)) * S + m % (S-1) + 1.  When ss != null the A rows are
-// x * g of an RMSNorm and each output row is scaled by 1/rms(x), from the sums
-// of squares ss[row * n_ss + t] of columns [16 t, 16 t + 16) of x (width H).
+// A operand of a GEMM: rows of T with row stride lda, or (blk = 1) in the
+// 16 x 32 blocks of act_off (common.h) with lda the row width; blocked A goes
+// only to calls of at most 64 rows (the narrow and streaming kernels).  S_skip
+// > 0 maps GEMM row m to A row (m / (S-1)) * S + m % (S-1) + 1.  When ss !=
+// null the A rows are x * g of an RMSNorm and each output row is scaled by
+// 1/rms(x), from the sums of squares ss[row * n_ss + t] of columns [16 t, 16 t
+// + 16) of x (width H).
 struct ASrc {
   const void* a;
   int64_t lda;
@@ -67,33 +70,40 @@ struct ASrc {
   int H;
   float eps;
   int S_skip;
+  int blk;
 };
-inline ASrc asrc_plain(const void* a, int64_t lda, int S_skip = 0) {
-  return ASrc{a, lda, nullptr, 0, 0, 0.f, S_skip};
+inline ASrc asrc_plain(const void* a, int64_t lda, int S_skip = 0, int blk = 0) {
+  return ASrc{a, lda, nullptr, 0, 0, 0.f, S_skip, blk};
 }
-inline ASrc asrc_normed(const void* xg, int H, const float* ss, float eps, int S_skip = 0) {
-  return ASrc{xg, H, ss, (H + 15) / 16, H, eps, S_skip};
+inline ASrc asrc_normed(const void* xg, int H, const float* ss, float eps, int S_skip = 0,
+                        int blk = 0) {
+  return ASrc{xg, H, ss, (H + 15) / 16, H, eps, S_skip, blk};
 }
+// Whether a call of M rows keeps its activations (the GEMMs' A operands) in
+// 16 x 32 blocks, and the rows such a matrix takes.
+inline int act_blocked(int64_t M) { return M <= 64 ? 1 : 0; }
+inline int64_t act_rows(int64_t M) { return act_blocked(M) ? (M + 15) / 16 * 16 : M; }
 // 16-column groups of a row: the granularity of the row sums of squares (one
 // packed weight slab of output columns, the narrowest tile a GEMM writes)
 __host__ __device__ inline int ss_tiles(int H) { return (H + 15) / 16; }
 
 // y = A W^T: out[M, N] fp32 (nullable), per-128-column row sums of squares of y
-// into ss (nullable) and xg = y * g_next rounded to the act dtype (nullable)
+// into ss (nullable) and xg = y * g_next rounded to the act dtype (nullable;
+// in 16 x 32 blocks when xg_blk)
 // Fragment-packed weight layout read by every GEMM (see gemm.hip).
 size_t packed_matrix_elems(int rows, int cols);
 hipError_t pack_matrix(int dt, const void* src, void* dst, int rows, int cols, hipStream_t st);
 
 hipError_t gemm_store_f32(int dt, const ASrc& a, int M, int K, const void* W, int N, float* out,
-                          float* ss, void* xg, const void* g_next, const GemmScratch& ws,
-                          hipStream_t st);
+                          float* ss, void* xg, int xg_blk, const void* g_next,
+                          const GemmScratch& ws, hipStream_t st);
 // x[M, N] += A W^T (x fp32, ld N), then ss / xg of the new x as above
 hipError_t gemm_residual(int dt, const ASrc& a, int M, int K, const void* W, int N, float* x,
-                         float* ss, void* xg, const void* g_next, const GemmScratch& ws,
-                         hipStream_t st);
-// act[M, I] = silu(A Wg^T) * (A Wu^T)
+                         float* ss, void* xg, int xg_blk, const void* g_next,
+                         const GemmScratch& ws, hipStream_t st);
+// act[M, I] = silu(A Wg^T) * (A Wu^T) (in 16 x 32 blocks when act_blk)
 hipError_t gemm_silu_mul(int dt, const ASrc& a, int M, int K, const void* Wg, const void* Wu,
-                         int I, void* act, const GemmScratch& ws, hipStream_t st);
+                         int I, void* act, int act_blk, const GemmScratch& ws, hipStream_t st);
 // q/k/v of the block rows with per-head RMSNorm + RoPE on q and k; q -> [M, nq, D],
 // k -> kblk [B][nkv][16][D], v -> vblk [B][nkv][D][16] (block row j = m % S).
 // raw (nullable, [M][(nq + 2 nkv) D] fp32): with M <= 64 the GEMM runs on
@@ -121,13 +131,14 @@ int logits_tiles(int V);
 // ---- elementwise / small kernels
 // block ids / positions / slots, the embedding rows into x (fp32) with their
 // sums of squares (ss[row * n_ss] = total, the other n_ss - 1 entries zero),
-// xg = x * g_first rounded to the act dtype, and the RoPE table of the block rows
+// xg = x * g_first rounded to the act dtype (in 16 x 32 blocks when xg_blk),
+// and the RoPE table of the block rows
 hipError_t launch_block_prep(int dt, const dflash_config& c, const void* embed,
                              const int32_t* anchor, const int32_t* prefix_len,
                              const int32_t* page_table, int max_pages, int B, int32_t* block_ids,
                              int32_t* positions, int32_t* slots, int32_t* candidates, float* x,
-                             float* ss, int n_ss, void* xg, const void* g_first, float2* cs,
-                             hipStream_t st);
+                             float* ss, int n_ss, void* xg, int xg_blk, const void* g_first,
+                             float2* cs, hipStream_t st);
 hipError_t launch_rope_table(const int32_t* positions, int rows, int D, float theta, float2* cs,
                              hipStream_t st);
 hipError_t launch_argmax_reduce(const float2* part, int M, int n_tiles, int S, int32_t* candidates,
@@ -225,7 +236,8 @@ hipError_t launch_attention(int dt, int kv_dt, int D, const void* q, const void*
                             int max_prefix, int B,
                             int S, int nq, int nkv, int page_size, int window, int ctx_window,
                             const AttnPlan& plan,
-                            float* o_part, float2* ml_part, int4* seg, void* out, hipStream_t st);
+                            float* o_part, float2* ml_part, int4* seg, void* out, int out_blk,
+                            hipStream_t st);
 
 // Record msg as the calling thread's last error (dflash_last_error) and return s.
 dflash_status set_error(dflash_status s, const char* msg);

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void block_prep_kernel(
     double log_theta, const int32_t* __restrict__ anchor, const int32_t* __restrict__ prefix_len,
     const int32_t* __restrict__ pt, int max_pages, int32_t* block_ids, int32_t* positions,
     int32_t* slots, int32_t* candidates, float* __restrict__ x, float* __restrict__ ss, int n_ss,
-    T* __restrict__ xg, const T* __restrict__ g_first, float2* __restrict__ cs) {
+    T* __restrict__ xg, int xg_blk, const T* __restrict__ g_first, float2* __restrict__ cs) {
   __shared__ float red[4];
   const int row = blockIdx.x, r = row / S, j = row % S, tid = threadIdx.x;
   int id = (j == 0) ? anchor[r] : mask_id;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void block_prep_kernel(
     float* xo = x + (int64_t)row * H + c0;
     *reinterpret_cast<float4*>(xo) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(xo + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    T* go = xg + (int64_t)row * H + c0;
+    T* go = xg + act_off(row, c0, H, xg_blk);  // 8 columns inside one 32-column block
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       go[i] = Num<T>::from_f(v[i] * g[i]);
@@ -87,20 +87,20 @@ hipError_t launch_block_prep(int dt, const dflash_config& c, const void* embed,
                              const int32_t* anchor, const int32_t* prefix_len,
                              const int32_t* page_table, int max_pages, int B, int32_t* block_ids,
                              int32_t* positions, int32_t* slots, int32_t* candidates, float* x,
-                             float* ss, int n_ss, void* xg, const void* g_first, float2* cs,
-                             hipStream_t st) {
+                             float* ss, int n_ss, void* xg, int xg_blk, const void* g_first,
+                             float2* cs, hipStream_t st) {
   const dim3 grid((unsigned)(B * c.block_size));
   const double lt = log((double)c.rope_theta);
   if (dt == DFLASH_BF16)
     hipLaunchKernelGGL(block_prep_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)embed,
                        c.vocab, c.hidden, c.block_size, c.mask_token_id, c.page_size, c.head_dim,
                        lt, anchor, prefix_len, page_table, max_pages, block_ids, positions, slots,
-                       candidates, x, ss, n_ss, (bf16_t*)xg, (const bf16_t*)g_first, cs);
+                       candidates, x, ss, n_ss, (bf16_t*)xg, xg_blk, (const bf16_t*)g_first, cs);
   else
     hipLaunchKernelGGL(block_prep_kernel<float>, grid, dim3(256), 0, st, (const float*)embed,
                        c.vocab, c.hidden, c.block_size, c.mask_token_id, c.page_size, c.head_dim,
                        lt, anchor, prefix_len, page_table, max_pages, block_ids, positions, slots,
-                       candidates, x, ss, n_ss, (float*)xg, (const float*)g_first, cs);
+                       candidates, x, ss, n_ss, (float*)xg, xg_blk, (const float*)g_first, cs);
   return hipGetLastError();
 }
 
