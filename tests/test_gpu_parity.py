@@ -164,9 +164,18 @@ def test_pack_matrix_layout(dtype, shape):
 
 
 # ---------------------------------------------------------------- draft pass
-@pytest.mark.parametrize("name", SMALL)
-def test_draft_block_parity(name):
+# (name, batch): besides each workload's own batch, block-row counts that are
+# not multiples of 16 (3 x 8 = 24, 5 x 8 = 40, 3 x 5 = 15 rows), where the
+# activations of a pass of at most 64 rows fill their last 16-row block partly
+DRAFT_CASES = [(n, None) for n in SMALL] + [("small_swa_fp8", 3), ("small_swa_fp8", 5),
+                                            ("small_f32_d64", 3)]
+
+
+@pytest.mark.parametrize("name,batch", DRAFT_CASES)
+def test_draft_block_parity(name, batch):
     wl = get_workload(name)
+    if batch is not None:
+        wl = dataclasses.replace(wl, batch=batch)
     cfg = wl.cfg
     _print(f"[draft parity] {name} B={wl.batch} S={cfg.block_size}")
     st = Setup(wl)
@@ -284,13 +293,14 @@ def _compare_pools(st, before, o_cache, written):
 
 
 @pytest.mark.parametrize("name", SMALL)
-@pytest.mark.parametrize("grid", [None, (3, 16), (4, 16), 65, (5, 16), (19, 16), 300])
+@pytest.mark.parametrize("grid", [None, (3, 16), (4, 16), 23, (3, 7), 65, (5, 16), (19, 16), 300])
 def test_project_context_parity(name, grid):
     """Rows 77 and 5 x 16 (one 128-row tile), 19 x 16 and 300 (256-row tiles,
     ragged last tile), with and without a prefix-valid request grid; 3 x 16
     and 4 x 16 (48 and 64 rows: the narrow K/V store and its norm/RoPE/write
-    kernel, the second at its largest size) and 65 rows (the first size the
-    tiled GEMMs take, with the row scales computed ahead of them)."""
+    kernel, the second at its largest size), 23 and 3 x 7 rows (the fc output
+    in 16 x 32 blocks with a partly filled last block) and 65 rows (the first
+    size the tiled GEMMs take, with the row scales computed ahead of them)."""
     wl = get_workload(name)
     cfg = wl.cfg
     _print(f"[inject parity] {name} grid={grid}")
