@@ -354,7 +354,10 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
   for (int64_t t0 = 0; t0 < T; t0 += chunk) {
     const int M = (int)((T - t0) < chunk ? (T - t0) : chunk);
     const void* f = static_cast<const char*>(feats) + (size_t)t0 * feat_row_stride * act_bytes(dt);
-    if ((e = launch_rope_table(positions + t0, M, cfg->head_dim, cfg->rope_theta, L.cs, st)) != hipSuccess)
+    // the tiled K/V path reads a RoPE table; the narrow one forms its own
+    if (!kv_inject_is_narrow(M, cfg->n_layers, L.kv_raw) &&
+        (e = launch_rope_table(positions + t0, M, cfg->head_dim, cfg->rope_theta, L.cs, st)) !=
+            hipSuccess)
       return hip_fail(e, "rope table");
     // c = fc(f): the fc epilogue writes c * hidden_norm (act dtype) and the
     // row sums of squares of c; the K/V GEMM streams the former and scales
@@ -367,7 +370,8 @@ dflash_status dflash_project_context(const dflash_config* cfg, const dflash_weig
     const ASrc cin = asrc_normed(L.cg, cfg->hidden, L.ss, cfg->rms_eps, 0, blk);
     if ((e = gemm_kv_inject(dt, cfg->kv_dtype, cin, M, cfg->hidden, tg, cfg->n_layers,
                             cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, L.cs,
-                            slots + t0, valid_rows, rows_per_req > 0 ? rows_per_req : 1, t0,
+                            positions + t0, cfg->rope_theta, slots + t0, valid_rows,
+                            rows_per_req > 0 ? rows_per_req : 1, t0,
                             cfg->page_size, cache->num_pages, L.kv_raw, L.gs, st)) != hipSuccess)
       return hip_fail(e, "kv inject gemm");
   }

@@ -361,3 +361,11 @@ __host__ __device__ __forceinline__ int64_t act_off(int r, int k, int64_t ld, in
   return blk ? ((int64_t)(r >> 4) * (ld >> 5) + (k >> 5)) * 512 + (r & 15) * 32 + (k & 31)
              : (int64_t)r * ld + k;
 }
+
+// RoPE (cos, sin) of pos * theta^(-2i/D), the angle formed and reduced in fp64.
+__device__ __forceinline__ float2 rope_cs(int pos, int i, int D, double log_theta) {
+  const double inv = exp(-(2.0 * (double)i / (double)D) * log_theta);
+  double s, c;
+  sincos((double)pos * inv, &s, &c);
+  return make_float2((float)c, (float)s);
+}

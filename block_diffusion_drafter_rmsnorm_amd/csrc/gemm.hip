@@ -1457,17 +1457,24 @@ template <typename T> struct EpiSiluMul {
 // Per-head RMSNorm (gain g) followed by neox RoPE with the row's (cos, sin)
 // table; lane i < D/2 owns the pair (i, i + D/2).  Returns the rotated pair.
 template <typename T>
-__device__ __forceinline__ void norm_rope_pair(float x0, float x1, int i, int D, bool active,
-                                               const T* g, float eps, const float2* cs_row,
-                                               float& o0, float& o1) {
+__device__ __forceinline__ void norm_rope_pair_c(float x0, float x1, int i, int D, bool active,
+                                                 const T* g, float eps, float2 c, float& o0,
+                                                 float& o1) {
   const float ss = wave_sum(active ? x0 * x0 + x1 * x1 : 0.f);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
   if (!active) return;
   const float y0 = x0 * inv * Num<T>::to_f(g[i]);
   const float y1 = x1 * inv * Num<T>::to_f(g[i + D / 2]);
-  const float2 c = cs_row[i];
   o0 = y0 * c.x - y1 * c.y;
   o1 = y1 * c.x + y0 * c.y;
+}
+// ... with the pair's (cos, sin) from the row's table
+template <typename T>
+__device__ __forceinline__ void norm_rope_pair(float x0, float x1, int i, int D, bool active,
+                                               const T* g, float eps, const float2* cs_row,
+                                               float& o0, float& o1) {
+  norm_rope_pair_c<T>(x0, x1, i, D, active, g, eps, active ? cs_row[i] : make_float2(1.f, 0.f),
+                      o0, o1);
 }
 
 // q -> [M, nq, D]; the block's k and v -> one 16-key "page" per (request, kv
@@ -2079,7 +2086,8 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
 template <typename T, typename KT>
 __global__ __launch_bounds__(256) void kv_norm_rope_store_kernel(
     const float* __restrict__ raw, int ksw, int M, int n_layers, int nkv, int D, KVTargets tg,
-    float eps, const float2* __restrict__ cs, const int32_t* __restrict__ slots,
+    float eps, const int32_t* __restrict__ positions, double log_theta,
+    const int32_t* __restrict__ slots,
     const int32_t* __restrict__ valid, int rpr, int64_t row0, int P, int64_t num_slots) {
   const int lane = threadIdx.x & 63, HH = n_layers * 2 * nkv, half = D / 2;
   const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
@@ -2106,9 +2114,12 @@ __global__ __launch_bounds__(256) void kv_norm_rope_store_kernel(
   }
   const int64_t page = slot / P, off = slot % P;
   if (hk < nkv) {
+    // the row's (cos, sin) pair of this lane, formed here (the same function
+    // the tiled path's table takes): no table kernel for a small injection
+    float2 c = make_float2(1.f, 0.f);
+    if (act) c = rope_cs(positions[m], lane, D, log_theta);
     float o0 = x0, o1 = x1;
-    norm_rope_pair<T>(x0, x1, lane, D, act, static_cast<const T*>(tg.k_norm[l]), eps,
-                      cs + (int64_t)m * half, o0, o1);
+    norm_rope_pair_c<T>(x0, x1, lane, D, act, static_cast<const T*>(tg.k_norm[l]), eps, c, o0, o1);
     KT* dst = static_cast<KT*>(tg.kc[l]) + ((page * nkv + hk) * P + off) * D;
     if (act) {
       dst[lane] = Num<KT>::from_f(o0);
@@ -2165,8 +2176,8 @@ hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const
 
 template <typename T, typename KT>
 static hipError_t kv_inject_narrow(const ASrc& a, int M, int H, const KVTargets& t, int n_layers,
-                                   int nq, int nkv, int D, float eps, const float2* cs,
-                                   const int32_t* slots, const int32_t* valid_rows,
+                                   int nq, int nkv, int D, float eps, const int32_t* positions,
+                                   double log_theta, const int32_t* slots, const int32_t* valid_rows,
                                    int rows_per_req, int64_t row0, int page_size, int64_t ns,
                                    float* raw, const GemmScratch& ws, hipStream_t st) {
   const int ncols = n_layers * 2 * nkv * D;
@@ -2182,9 +2193,13 @@ static hipError_t kv_inject_narrow(const ASrc& a, int M, int H, const KVTargets&
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((M * n_layers * 2 * nkv + 3) / 4);
   hipLaunchKernelGGL((kv_norm_rope_store_kernel<T, KT>), dim3(grid), dim3(256), 0, st, raw, ksw,
-                     M, n_layers, nkv, D, t, eps, cs, slots, valid_rows, rows_per_req, row0,
-                     page_size, ns);
+                     M, n_layers, nkv, D, t, eps, positions, log_theta, slots, valid_rows,
+                     rows_per_req, row0, page_size, ns);
   return hipGetLastError();
+}
+
+bool kv_inject_is_narrow(int M, int n_layers, const float* raw) {
+  return raw != nullptr && M <= 64 && n_layers <= kKVStoreLayers;
 }
 
 int kv_inject_raw_floats(int M, int n_layers, int nkv, int D) {
@@ -2195,26 +2210,29 @@ int kv_inject_raw_floats(int M, int n_layers, int nkv, int D) {
 
 hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
-                          const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
-                          int64_t row0, int page_size, int64_t num_pages, float* raw,
-                          const GemmScratch& ws, hipStream_t st) {
+                          const int32_t* positions, float rope_theta, const int32_t* slots,
+                          const int32_t* valid_rows, int rows_per_req, int64_t row0,
+                          int page_size, int64_t num_pages, float* raw, const GemmScratch& ws,
+                          hipStream_t st) {
   const int64_t ns = num_pages * page_size;
   const int ncols = n_layers * 2 * nkv * D;
-  if (raw != nullptr && M <= 64 && n_layers <= kKVStoreLayers) {
+  if (kv_inject_is_narrow(M, n_layers, raw)) {
     // narrow K/V store into fp32 (K split over workgroups), then the norms,
-    // RoPE and cache writes in a small kernel that adds the partials
+    // RoPE (its (cos, sin) formed from the positions) and cache writes in a
+    // small kernel that adds the partials
+    const double lt = log((double)rope_theta);
     if (dt == DFLASH_BF16) {
       if (kv_dt == DFLASH_FP8_E4M3)
-        return kv_inject_narrow<bf16_t, fp8_t>(a, M, H, t, n_layers, nq, nkv, D, eps, cs, slots,
-                                               valid_rows, rows_per_req, row0, page_size, ns,
-                                               raw, ws, st);
-      return kv_inject_narrow<bf16_t, bf16_t>(a, M, H, t, n_layers, nq, nkv, D, eps, cs, slots,
-                                              valid_rows, rows_per_req, row0, page_size, ns,
-                                              raw, ws, st);
+        return kv_inject_narrow<bf16_t, fp8_t>(a, M, H, t, n_layers, nq, nkv, D, eps, positions,
+                                               lt, slots, valid_rows, rows_per_req, row0,
+                                               page_size, ns, raw, ws, st);
+      return kv_inject_narrow<bf16_t, bf16_t>(a, M, H, t, n_layers, nq, nkv, D, eps, positions,
+                                              lt, slots, valid_rows, rows_per_req, row0,
+                                              page_size, ns, raw, ws, st);
     }
-    return kv_inject_narrow<float, float>(a, M, H, t, n_layers, nq, nkv, D, eps, cs, slots,
-                                          valid_rows, rows_per_req, row0, page_size, ns, raw, ws,
-                                          st);
+    return kv_inject_narrow<float, float>(a, M, H, t, n_layers, nq, nkv, D, eps, positions, lt,
+                                          slots, valid_rows, rows_per_req, row0, page_size, ns,
+                                          raw, ws, st);
   }
   if (dt == DFLASH_BF16) {
     if (kv_dt == DFLASH_FP8_E4M3) {

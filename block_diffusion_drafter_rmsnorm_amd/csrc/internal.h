@@ -116,12 +116,17 @@ hipError_t gemm_qkv(int dt, const ASrc& a, int M, int H, const void* Wqkv, const
 // row row0 + m of the [n_req, rows_per_req] grid (valid_rows indexed by grid
 // request; slots by GEMM row).
 // raw (nullable): fp32 scratch of kv_inject_raw_floats(M, ...) floats; with it
-// and M <= 64 the K/V GEMM is the narrow store plus a norm/RoPE/write kernel.
+// and M <= 64 (kv_inject_is_narrow) the K/V GEMM is the narrow store plus a
+// norm/RoPE/write kernel, which forms each row's RoPE (cos, sin) from
+// positions[m] and rope_theta; the tiled path reads them from the table cs
+// [M][D/2] (launch_rope_table), which the narrow path does not read.
+bool kv_inject_is_narrow(int M, int n_layers, const float* raw);
 hipError_t gemm_kv_inject(int dt, int kv_dt, const ASrc& a, int M, int H, const KVTargets& t,
                           int n_layers, int nq, int nkv, int D, float eps, const float2* cs,
-                          const int32_t* slots, const int32_t* valid_rows, int rows_per_req,
-                          int64_t row0, int page_size, int64_t num_pages, float* raw,
-                          const GemmScratch& ws, hipStream_t st);
+                          const int32_t* positions, float rope_theta, const int32_t* slots,
+                          const int32_t* valid_rows, int rows_per_req, int64_t row0,
+                          int page_size, int64_t num_pages, float* raw, const GemmScratch& ws,
+                          hipStream_t st);
 int kv_inject_raw_floats(int M, int n_layers, int nkv, int D);
 // logits[M, V] (nullable) and per-tile argmax partials (value, index) [M, n_tiles]
 hipError_t gemm_logits(int dt, const ASrc& a, int M, int H, const void* Wlm, int V, void* logits,

@@ -6,14 +6,6 @@
 
 namespace dflash {
 
-// (cos, sin) of pos * theta^(-2i/D), angle formed and reduced in fp64.
-__device__ __forceinline__ float2 rope_cs(int pos, int i, int D, double log_theta) {
-  const double inv = exp(-(2.0 * (double)i / (double)D) * log_theta);
-  double s, c;
-  sincos((double)pos * inv, &s, &c);
-  return make_float2((float)c, (float)s);
-}
-
 __global__ void rope_table_kernel(const int32_t* __restrict__ pos, int rows, int D,
                                   double log_theta, float2* __restrict__ cs) {
   const int half = D / 2;
