@@ -206,6 +206,28 @@ template <typename T> struct ASrcPlain {
   }
 };
 
+// A of a 16-row tile held in LDS in MFMA fragment order (the narrow kernel
+// copies it there first): the fragment of columns 32 c .. 32 c + 31 at c * 512
+// elements, lane l's 8 elements (row l mod 16, columns 32 c + 8 (l / 16) ..)
+// at l * 8 of it, so every read is one contiguous 1 KB.
+template <typename T> struct ASrcImg {
+  const T* img;
+  template <int MB> struct State {
+    const T* p;
+  };
+  template <int MB>
+  __device__ __forceinline__ void setup(State<MB>& s, int, int, int) const {
+    s.p = img + (threadIdx.x & 63) * 8;
+  }
+  template <int MB>
+  __device__ __forceinline__ void load(Frag<T>& f, const State<MB>& s, int, int k) const {
+    load_frag(f, s.p + (k >> 5) * 512);
+  }
+};
+// Columns of A that the LDS image of the narrow lm_head kernel holds at most
+// (16 rows x 4096 bf16 = 128 KB, sharing LDS with the partial-tile buffer).
+constexpr int kImgK = 4096;
+
 // Per-row 1/rms from the sums of squares ss[row * n_ss + t] of a width-H row
 // (ss == null: no scaling).  GEMM row m uses ss row block_row(m, S).
 struct RowScale {
@@ -392,6 +414,28 @@ template <typename T> struct NextNorm {
   int blk;  // xg in the 16 x 32 blocks of act_off
 };
 
+// 16 bytes per lane from global memory into LDS at (wave-uniform base) + 16 *
+// lane.  Inline assembly, so the compiler's wait insertion does not treat the
+// load as a pending LDS write before every LDS read (it would wait for all
+// stages in flight); the kernel waits for its stages itself, before the
+// barrier that precedes the reads.
+__device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  // m0 (the LDS base of the copy) is saved and restored inside the block, so
+  // whatever the surrounding code keeps in m0 survives; the copy reads m0 when
+  // it issues (the compiler's own code for these copies rewrites m0 right
+  // after each one)
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------- main kernel
 // Fragments of one 64-wide K step (two 32-column chunks c, c+1): the lane's
 // record of each chunk of its two slabs (B) and the matching 8 K elements
@@ -399,18 +443,26 @@ template <typename T> struct NextNorm {
 // registers so the next step's weight loads are in flight during the MFMAs.
 template <typename T, int MB, class ASrc, int NSL = 2> struct Step64 {
   Frag<T> a0[MB], a1[MB], b0[NSL], b1[NSL];
-  __device__ __forceinline__ void load(const ASrc& asrc, const typename ASrc::template State<MB>& as,
-                                       const T* const* bp, int c, int g4) {
+  __device__ __forceinline__ void load_b(const T* const* bp, int c) {
 #pragma unroll
     for (int nb = 0; nb < NSL; ++nb) {
       load_frag(b0[nb], bp[nb] + (int64_t)c * kChunkElems);
       load_frag(b1[nb], bp[nb] + (int64_t)(c + 1) * kChunkElems);
     }
+  }
+  __device__ __forceinline__ void load_a(const ASrc& asrc,
+                                         const typename ASrc::template State<MB>& as, int c,
+                                         int g4) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       asrc.template load<MB>(a0[mb], as, mb, c * 32 + g4 * 8);
       asrc.template load<MB>(a1[mb], as, mb, c * 32 + 32 + g4 * 8);
     }
+  }
+  __device__ __forceinline__ void load(const ASrc& asrc, const typename ASrc::template State<MB>& as,
+                                       const T* const* bp, int c, int g4) {
+    load_b(bp, c);
+    load_a(asrc, as, c, g4);
   }
   __device__ __forceinline__ void mma_into(f32x4 (&acc)[MB][NSL]) const {
 #pragma unroll
@@ -526,7 +578,8 @@ __global__ __launch_bounds__(256) void gemm_stream(ASrc asrc, int M, int K, int 
 // columns [n0, n0 + 16) of the epilogue's column space; nprepare() as
 // prepare(); napply(tile, ldt, rows, m0, M, n0, ncols, tid) over columns
 // [n0, n0 + ncols) with ncols a multiple of 16.
-template <typename T, int MB, int NSL, int NSW, int NW, int NB, int MINW, class ASrc, class Epi>
+template <typename T, int MB, int NSL, int NSW, int NW, int NB, int MINW, class ASrc, class Epi,
+          bool SA = false>
 __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int K, int kq_len,
                                                            int ksw, int m_tiles, Epi epi_all) {
   constexpr int TR = 16 * MB, TC = 16 * NSL;
@@ -535,7 +588,14 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
   constexpr int NG = NSL / NSW;  // slab groups; wave = ks * NG + group
   constexpr int KSPL = NW / NG;  // K splits
   static_assert(NSL % NSW == 0 && NW % NG == 0, "waves cover slab groups x K splits");
-  __shared__ float red[NW * TR * WC];
+  static_assert(!SA || (MB == 1 && sizeof(T) == 2), "the LDS image holds 16 bf16 rows");
+  // SA: the tile's A rows copied once into an LDS image that every wave reads
+  // (the NG waves of a K split would each load the same A fragments), sharing
+  // LDS with the partial tiles, which are written only after every wave has
+  // left the K loop
+  constexpr int RED_BYTES = NW * TR * WC * 4, IMG_BYTES = SA ? 16 * kImgK * 2 : 0;
+  __shared__ __attribute__((aligned(1024))) char lbuf[RED_BYTES > IMG_BYTES ? RED_BYTES : IMG_BYTES];
+  float* const red = reinterpret_cast<float*>(lbuf);
   __shared__ float tile[TR * LDR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = (int)blockIdx.x % ksw, rest = (int)blockIdx.x / ksw;
@@ -554,8 +614,23 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
   const T* bp[NSW];  // this lane's record in chunk 0 of each of the wave's slabs
 #pragma unroll
   for (int s = 0; s < NSW; ++s) bp[s] = epi_all.nslab(n0 + 16 * (sg * NSW + s)) + lane * 8;
-  typename ASrc::template State<MB> as;
-  asrc.template setup<MB>(as, m0, M, r16);
+  if constexpr (SA) {
+    // the image: the fragment of columns 32 c .. copied by wave c mod NW (lane
+    // l: 16 bytes of row l mod 16 at column 32 c + 8 (l / 16)), every copy
+    // issued before any weight load
+    const int r = imin(m0 + (lane & 15), M - 1);
+    const T* arow = asrc.A + act_off(block_row(r, asrc.S), 0, asrc.lda, asrc.blk) + (lane >> 4) * 8;
+    const int64_t cstride = asrc.blk ? 512 : 32;
+    for (int c = wave; c < K / 32; c += NW)
+      dma16(arow + c * cstride, reinterpret_cast<T*>(lbuf) + c * 512);
+  }
+  auto src = [&]() {
+    if constexpr (SA) return ASrcImg<T>{reinterpret_cast<const T*>(lbuf)};
+    else return asrc;
+  }();
+  using AS = decltype(src);
+  typename AS::template State<MB> as;
+  src.template setup<MB>(as, m0, M, r16);
 
   f32x4 acc[MB][NSW];
 #pragma unroll
@@ -568,25 +643,47 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
   // contiguous run of the slabs at a time; an odd last 32-chunk goes to split 0.
   const int c0 = kr0 / 32;  // first chunk (kr0, kr1 are multiples of 32)
   const int steps = (kr1 - kr0) / 64;
-  if (((kr1 - kr0) & 32) && ksp == 0) {  // the odd chunk
-    const int c = kr1 / 32 - 1;
-    Frag<T> b0[NSW];
+  auto odd_chunk = [&]() {
+    if (((kr1 - kr0) & 32) && ksp == 0) {  // the odd chunk
+      const int c = kr1 / 32 - 1;
+      Frag<T> b0[NSW];
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) load_frag(b0[s], bp[s] + (int64_t)c * kChunkElems);
+      for (int s = 0; s < NSW; ++s) load_frag(b0[s], bp[s] + (int64_t)c * kChunkElems);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      Frag<T> a0;
-      asrc.template load<MB>(a0, as, mb, c * 32 + g4 * 8);
+      for (int mb = 0; mb < MB; ++mb) {
+        Frag<T> a0;
+        src.template load<MB>(a0, as, mb, c * 32 + g4 * 8);
 #pragma unroll
-      for (int s = 0; s < NSW; ++s) mma(acc[mb][s], a0, b0[s]);
+        for (int s = 0; s < NSW; ++s) mma(acc[mb][s], a0, b0[s]);
+      }
     }
-  }
+  };
+  if constexpr (!SA) odd_chunk();
   const int n64 = steps > ksp ? (steps - ksp + KSPL - 1) / KSPL : 0;
   auto chunk_of = [&](int st) { return c0 + 2 * (ksp + st * KSPL); };
-  Step64<T, MB, ASrc, NSW> buf[NB];
+  Step64<T, MB, AS, NSW> buf[NB];
+  if constexpr (SA) {
+    // the first steps' weight loads go out, then the wait for this lane's
+    // image copies (older than those loads: at most their 2 NSW per step may
+    // stay in flight) and the barrier that covers every wave's copies
 #pragma unroll
-  for (int b = 0; b < NB - 1; ++b)
-    if (b < n64) buf[b].load(asrc, as, bp, chunk_of(b), g4);
+    for (int b = 0; b < NB - 1; ++b)
+      if (b < n64) buf[b].load_b(bp, chunk_of(b));
+    static_assert(NB - 1 <= 2 && 2 * NSW * 2 <= 63, "waits below cover the prologue");
+    const int in_flight = imin(NB - 1, n64);
+    if (in_flight >= 2) wait_vmcnt<4 * NSW>();
+    else if (in_flight == 1) wait_vmcnt<2 * NSW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+      if (b < n64) buf[b].load_a(src, as, chunk_of(b), g4);
+    odd_chunk();
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+      if (b < n64) buf[b].load(src, as, bp, chunk_of(b), g4);
+  }
   // while those loads are in flight: the loads of what the epilogue reads
   // (residual, gains) and of the sums of squares behind the row scales
   NarrowPre pre;
@@ -597,7 +694,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
     for (int b = 0; b < NB; ++b) {
       const int st = i + b, nxt = st + NB - 1;
       if (st < n64) {
-        if (nxt < n64) buf[(b + NB - 1) % NB].load(asrc, as, bp, chunk_of(nxt), g4);
+        if (nxt < n64) buf[(b + NB - 1) % NB].load(src, as, bp, chunk_of(nxt), g4);
         buf[b].mma_into(acc);
       }
     }
@@ -606,6 +703,7 @@ __global__ __launch_bounds__(NW * 64, MINW) void gemm_rows(ASrc asrc, int M, int
   // barrier below), this wave's partial tile, then the sum over the K splits
   // in split order
   epi.nrow_fin(pre, row_scale_lds(), TR, m0, M, wave, NW, lane);
+  if constexpr (SA) __syncthreads();  // every wave is done with the image
   float* mine = red + wave * (TR * WC);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -860,28 +958,6 @@ __global__ __launch_bounds__(256) void gemm_fat(ASrcPlain<bf16_t> asrc, int M, i
 // Same XCD-grouped tile order as gemm_fat; epilogue in 128 x 128 quarters.
 constexpr int GB_STAGE = 256 * 32 + 256 * 32;  // bf16 elements: A [256][32], B [16 slabs][64][8]
 constexpr int GB_NS = 4;
-
-// 16 bytes per lane from global memory into LDS at (wave-uniform base) + 16 *
-// lane.  Inline assembly, so the compiler's wait insertion does not treat the
-// load as a pending LDS write before every LDS read (it would wait for all
-// stages in flight); the kernel waits for its stages itself, before the
-// barrier that precedes the reads.
-__device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
-  // m0 (the LDS base of the copy) is saved and restored inside the block, so
-  // whatever the surrounding code keeps in m0 survives; the copy reads m0 when
-  // it issues (the compiler's own code for these copies rewrites m0 right
-  // after each one)
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(l)
-      : "memory");
-}
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <class Epi>
 __global__ __launch_bounds__(512) void gemm_big(ASrcPlain<bf16_t> asrc, int M, int K, int m_tiles,
@@ -1876,9 +1952,18 @@ static void launch_rows_cfg(const AS& asrc, int M, int K, const GemmPlan& p, con
   constexpr int BUDGET = (MINW == 4 ? 128 : (MINW == 3 ? 168 : 256)) - FIXED;
   constexpr int NB0 = BUDGET / STEP;
   constexpr int NB = NB0 < 1 ? 1 : (NB0 > 6 ? 6 : NB0);
-  hipLaunchKernelGGL((gemm_rows<T, MB, NSL, NSW, NW, NB, MINW, AS, Epi>),
-                     dim3((unsigned)(p.n_tiles * p.m_tiles * p.KSW)), dim3(NW * 64), 0, st, asrc,
-                     M, K, p.kw, p.KSW, p.m_tiles, epi);
+  const dim3 grid((unsigned)(p.n_tiles * p.m_tiles * p.KSW));
+  // the lm_head's 16-wave workgroups at up to 16 rows: A through one LDS image
+  // (its four slab-pair waves per K split would each load the same A)
+  if constexpr (sizeof(T) == 2 && MB == 1 && NSL == 8 && NW == 16) {
+    if (K <= kImgK && p.KSW == 1) {
+      hipLaunchKernelGGL((gemm_rows<T, MB, NSL, NSW, NW, NB, MINW, AS, Epi, true>), grid,
+                         dim3(NW * 64), 0, st, asrc, M, K, p.kw, p.KSW, p.m_tiles, epi);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_rows<T, MB, NSL, NSW, NW, NB, MINW, AS, Epi>), grid, dim3(NW * 64), 0,
+                     st, asrc, M, K, p.kw, p.KSW, p.m_tiles, epi);
 }
 template <typename T, int NSL, int NW, class AS, class Epi>
 static void launch_rows_mb(const AS& asrc, int M, int K, const GemmPlan& p, const Epi& epi,
