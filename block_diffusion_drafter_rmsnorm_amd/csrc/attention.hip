@@ -1133,9 +1133,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, CT* __res
   }
   const int slot_off = a.kps > 0 ? 0 : r * a.nkv + g;
   auto prow = [&](int s) { return ((int64_t)w_lo + s + slot_off) * 64 + rho; };
-  // with U < W some ranges are empty: those workgroups wrote nothing
+  // with U < W some ranges are empty: those workgroups wrote nothing (with U
+  // >= W consecutive starts floor(w U / W) differ by at least one, so every
+  // range holds a unit and the 64-bit divisions below are skipped)
   auto has_range = [&](int s) {
-    if (a.kps > 0) return true;
+    if (a.kps > 0 || U >= a.W) return true;
     const int64_t w = (int64_t)w_lo + s;
     return range_start(w + 1, U, a.W) > range_start(w, U, a.W);
   };
