@@ -117,3 +117,22 @@ def test_lm_head_argmax_qwen3_8b_sampled_rows(rows):
     o_logits, o_ids = oracle.select_draft_tokens(hid[sample].double().cpu().numpy(),
                                                  lm.cpu().float().numpy())
     _check(cfg, ids, gl, ids_only, o_logits, o_ids, planted, sample)
+
+
+@pytest.mark.parametrize("hidden", [4096, 4128])
+def test_lm_head_argmax_lds_image_boundary(hidden):
+    """At up to 16 rows the narrow lm_head reads A from an LDS image when the
+    hidden size is at most 4096 and from global memory above it: 7 rows at
+    hidden 4096 (the largest image) and 4128 (the first size past it)."""
+    import dataclasses
+    m = dfl()
+    cfg = dataclasses.replace(get_workload("small_bf16").cfg, hidden=hidden)
+    rows = 7
+    _print(f"[lm_head image boundary] hidden {hidden} rows {rows} V {cfg.vocab}")
+    lm, hid, planted = _inputs(cfg, rows, seed=hidden)
+    packed = m.dflash_pack_matrix(lm)
+    ids, gl = _run(cfg, packed, hid)
+    ids_only, _ = _run(cfg, packed, hid, want_logits=False)
+    o_logits, o_ids = oracle.select_draft_tokens(hid.double().cpu().numpy(),
+                                                 lm.double().cpu().numpy())
+    _check(cfg, ids, gl, ids_only, o_logits, o_ids, planted, np.arange(rows))
